@@ -1,0 +1,54 @@
+"""Plant plausible mistakes in a copy of the oracle and check the pins catch each.
+
+Every mutant is a one-spot edit of oracle.c (a dropped term, a wrong sign, a
+wrong index or shift, a transposed output, the other common nibble order),
+compiled on the CPU into a temporary library; the oracle pin suite then runs in
+a child process against it and must fail.  Nothing here touches a GPU.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+from oracle import build as obuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PIN_FILES = ["tests/test_oracle_decode.py", "tests/test_oracle_gemv.py", "tests/test_oracle_swiglu.py"]
+
+MUTANTS = {
+    "f16_exponent_bias": ("ldexp((double)(1024 + m), e - 25)", "ldexp((double)(1024 + m), e - 24)"),
+    "f16_subnormal_scale": ("ldexp((double)m, -24)", "ldexp((double)m, -25)"),
+    "q8_0_unsigned_codes": ("int q = (int8_t)blk[2 + l];", "int q = blk[2 + l];"),
+    "q4_0_interleaved_nibbles": (
+        "out[b * 32 + l] = (double)(lo - 8) * d;\n                out[b * 32 + 16 + l] = (double)(hi - 8) * d;",
+        "out[b * 32 + 2 * l] = (double)(lo - 8) * d;\n                out[b * 32 + 2 * l + 1] = (double)(hi - 8) * d;"),
+    "q4_0_dropped_offset": ("out[b * 32 + l] = (double)(lo - 8) * d;", "out[b * 32 + l] = (double)(lo) * d;"),
+    "q4_0_offset_7": ("out[b * 32 + 16 + l] = (double)(hi - 8) * d;", "out[b * 32 + 16 + l] = (double)(hi - 7) * d;"),
+    "q4_k_min_added": ("* (double)q - dmin * (double)m", "* (double)q + dmin * (double)m"),
+    "q4_k_min_dropped": ("* (double)q - dmin * (double)m", "* (double)q"),
+    "q4_k_scale_high_bits_shift": ("((q[j - 4] >> 6) << 4)", "((q[j - 4] >> 4) << 4)"),
+    "q4_k_min_high_bits_from_wrong_byte": ("((q[j] >> 6) << 4)", "((q[j - 4] >> 6) << 4)"),
+    "q4_k_nibble_parity": ("(s % 2 == 0) ? (chunk[l] & 0x0F)", "(s % 2 == 1) ? (chunk[l] & 0x0F)"),
+    "q4_k_chunk_stride": ("qs + 32 * (s / 2)", "qs + 16 * s"),
+    "i8row_first_row_scale": ("double s = (double)row_scale[r];", "double s = (double)row_scale[0];"),
+    "gemv_output_transposed": ("y[t * nr + (o - row_begin)] = acc;", "y[(o - row_begin) * n_tok + t] = acc;"),
+    "gemv_dropped_x": ("double p = row[j] * (double)xt[j];", "double p = row[j];"),
+    "gemv_signed_magnitude": ("mag += fabs(p);\n            }\n            y[t * nr", "mag += p;\n            }\n            y[t * nr"),
+    "silu_sign": ("return g / (1.0 + exp(-g));", "return g / (1.0 + exp(g));"),
+    "swiglu_gate_up_swapped": ("h[i] = oracle_silu(g[i]) * u[i];", "h[i] = oracle_silu(u[i]) * g[i];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(obuild.SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/not found"
+    mpath = tmp_path / "oracle_mutant.c"
+    mpath.write_text(src.replace(old, new))
+    lib = obuild.build(out=str(tmp_path / "liboracle_mutant.so"), src=str(mpath), werror=False)
+    env = dict(os.environ, ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", *PIN_FILES],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
