@@ -1,0 +1,221 @@
+"""Python binding of libqgemv.so (the C ABI declared in include/qgemv.h).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the computation runs in the library's gfx950
+kernels.  The entry points keep the C names (qgemv_q4_0, swiglu_ffn, qdequant,
+qgemv_repack_q4_0, ...) and raise QGemvError on a nonzero status.  There is no
+CPU fallback: if the library is missing, importing this module fails.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "FORMATS", "QGemvError", "lib", "packed_bytes", "max_cols", "repack",
+    "qgemv", "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_k", "qgemv_i8row",
+    "swiglu_gate_up", "swiglu_ffn", "qdequant", "layout_version", "set_launch_override",
+    "qgemv_repack_q4_0", "qgemv_repack_q8_0", "qgemv_repack_q4_k", "qgemv_repack_i8row",
+]
+
+FORMATS = {"q4_0": 0, "q8_0": 1, "q4_k": 2, "i8row": 3}
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950) first")
+
+lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+
+lib.qgemv_layout_version.restype = _I
+lib.qgemv_status_string.argtypes = [_I]
+lib.qgemv_status_string.restype = ctypes.c_char_p
+lib.qgemv_max_cols.restype = _I64
+lib.qgemv_packed_bytes.argtypes = [_I, _I64, _I64]
+lib.qgemv_packed_bytes.restype = _I64
+for _n in ("qgemv_repack_q4_0", "qgemv_repack_q8_0", "qgemv_repack_q4_k"):
+    getattr(lib, _n).argtypes = [_P, _P, _I64, _I64, _P]
+    getattr(lib, _n).restype = _I
+lib.qgemv_repack_i8row.argtypes = [_P, _P, _P, _I64, _I64, _P]
+lib.qgemv_repack_i8row.restype = _I
+for _n in ("qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_k", "qgemv_i8row"):
+    getattr(lib, _n).argtypes = [_P, _P, _P, _I64, _I64, _I64, _P]
+    getattr(lib, _n).restype = _I
+lib.qgemv.argtypes = [_I, _P, _P, _P, _I64, _I64, _I64, _P]
+lib.qgemv.restype = _I
+lib.swiglu_gate_up.argtypes = [_I, _P, _P, _P, _P, _I64, _I64, _I64, _P]
+lib.swiglu_gate_up.restype = _I
+lib.swiglu_ffn.argtypes = [_I, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
+lib.swiglu_ffn.restype = _I
+lib.qdequant.argtypes = [_I, _P, _P, _I64, _I64, _P]
+lib.qdequant.restype = _I
+lib.qgemv_set_launch_override.argtypes = [_I, _I, _I]
+lib.qgemv_set_launch_override.restype = _I
+
+
+class QGemvError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = int(status)
+        msg = lib.qgemv_status_string(self.status).decode()
+        super().__init__(f"{what}: {msg} (status {self.status})")
+
+
+def _check(st, what):
+    if st != 0:
+        raise QGemvError(st, what)
+
+
+def _fmt(fmt):
+    return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        return int(t)
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and isinstance(t, torch.Tensor):
+            if not t.is_cuda:
+                raise ValueError("tensors must live on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+def layout_version() -> int:
+    return lib.qgemv_layout_version()
+
+
+def max_cols() -> int:
+    v = lib.qgemv_max_cols()
+    if v < 0:
+        raise QGemvError(v, "qgemv_max_cols")
+    return v
+
+
+def packed_bytes(fmt, rows, cols) -> int:
+    v = lib.qgemv_packed_bytes(_fmt(fmt), rows, cols)
+    if v < 0:
+        raise QGemvError(v, "qgemv_packed_bytes")
+    return v
+
+
+def set_launch_override(lpr=0, r=0, waves=0):
+    _check(lib.qgemv_set_launch_override(lpr, r, waves), "qgemv_set_launch_override")
+
+
+# ------------------------------------------------------------- repack ------
+def qgemv_repack_q4_0(raw, packed, rows, cols, stream=None):
+    _dev(raw, packed)
+    _check(lib.qgemv_repack_q4_0(_ptr(raw), _ptr(packed), rows, cols, _stream(stream)), "qgemv_repack_q4_0")
+
+
+def qgemv_repack_q8_0(raw, packed, rows, cols, stream=None):
+    _dev(raw, packed)
+    _check(lib.qgemv_repack_q8_0(_ptr(raw), _ptr(packed), rows, cols, _stream(stream)), "qgemv_repack_q8_0")
+
+
+def qgemv_repack_q4_k(raw, packed, rows, cols, stream=None):
+    _dev(raw, packed)
+    _check(lib.qgemv_repack_q4_k(_ptr(raw), _ptr(packed), rows, cols, _stream(stream)), "qgemv_repack_q4_k")
+
+
+def qgemv_repack_i8row(q, row_scale, packed, rows, cols, stream=None):
+    _dev(q, row_scale, packed)
+    _check(lib.qgemv_repack_i8row(_ptr(q), _ptr(row_scale), _ptr(packed), rows, cols, _stream(stream)),
+           "qgemv_repack_i8row")
+
+
+def repack(fmt, raw, rows, cols, row_scale=None, stream=None) -> torch.Tensor:
+    """Allocate (torch) and fill a packed buffer from raw blocks on the GPU."""
+    f = _fmt(fmt)
+    nbytes = packed_bytes(f, rows, cols)
+    dev = raw.device
+    packed = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+    off = (-packed.data_ptr()) % 256
+    packed = packed[off:off + nbytes]
+    if f == 0:
+        qgemv_repack_q4_0(raw, packed, rows, cols, stream)
+    elif f == 1:
+        qgemv_repack_q8_0(raw, packed, rows, cols, stream)
+    elif f == 2:
+        qgemv_repack_q4_k(raw, packed, rows, cols, stream)
+    else:
+        qgemv_repack_i8row(raw, row_scale, packed, rows, cols, stream)
+    return packed
+
+
+# ------------------------------------------------------------- products ----
+def _y(y, shape, dev):
+    if y is None:
+        return torch.empty(shape, dtype=torch.float32, device=dev)
+    return y
+
+
+def qgemv(fmt, packed, x, rows, cols, y=None, stream=None) -> torch.Tensor:
+    """y [n_tok][rows] = W x, x fp32 [n_tok][cols] (or [cols])."""
+    n_tok = x.numel() // cols
+    y = _y(y, (rows,) if x.dim() == 1 else (n_tok, rows), x.device)
+    _dev(packed, x, y)
+    _check(lib.qgemv(_fmt(fmt), _ptr(packed), _ptr(x), _ptr(y), rows, cols, n_tok, _stream(stream)), "qgemv")
+    return y
+
+
+def _gemv_named(name, fmtid):
+    cfn = getattr(lib, name)
+
+    def f(packed, x, y, rows, cols, n_tok=1, stream=None):
+        _dev(packed, x, y)
+        _check(cfn(_ptr(packed), _ptr(x), _ptr(y), rows, cols, n_tok, _stream(stream)), name)
+        return y
+    f.__name__ = name
+    f.__doc__ = f"Binding of {name}(packed, x, y, rows, cols, n_tok, stream)."
+    return f
+
+
+qgemv_q4_0 = _gemv_named("qgemv_q4_0", 0)
+qgemv_q8_0 = _gemv_named("qgemv_q8_0", 1)
+qgemv_q4_k = _gemv_named("qgemv_q4_k", 2)
+qgemv_i8row = _gemv_named("qgemv_i8row", 3)
+
+
+def swiglu_gate_up(fmt, wg, wu, x, d_model, ffn, h=None, stream=None) -> torch.Tensor:
+    n_tok = x.numel() // d_model
+    h = _y(h, (n_tok, ffn), x.device)
+    _dev(wg, wu, x, h)
+    _check(lib.swiglu_gate_up(_fmt(fmt), _ptr(wg), _ptr(wu), _ptr(x), _ptr(h), d_model, ffn, n_tok,
+                              _stream(stream)), "swiglu_gate_up")
+    return h
+
+
+def swiglu_ffn(fmt, wg, wu, wd, x, d_model, ffn, out=None, h_scratch=None, stream=None):
+    """(out, h): out [n_tok][d_model] = Wd (silu(Wg x) * (Wu x)); h is the scratch."""
+    n_tok = x.numel() // d_model
+    out = _y(out, (n_tok, d_model), x.device)
+    h_scratch = _y(h_scratch, (n_tok, ffn), x.device)
+    _dev(wg, wu, wd, x, out, h_scratch)
+    _check(lib.swiglu_ffn(_fmt(fmt), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(x), _ptr(out), _ptr(h_scratch),
+                          h_scratch.numel(), d_model, ffn, n_tok, _stream(stream)), "swiglu_ffn")
+    return out, h_scratch
+
+
+def qdequant(fmt, packed, rows, cols, w_out=None, stream=None) -> torch.Tensor:
+    w_out = _y(w_out, (rows, cols), packed.device)
+    _dev(packed, w_out)
+    _check(lib.qdequant(_fmt(fmt), _ptr(packed), _ptr(w_out), rows, cols, _stream(stream)), "qdequant")
+    return w_out

@@ -1,0 +1,249 @@
+// The C-ABI entry points: synchronous argument validation, then kernel
+// enqueue on the caller's stream.  Errors are returned as values and nothing
+// is enqueued on any error (the refusal discipline of the Go "llm" package's
+// tests and of llamini.cpp, which rejects what it cannot read rather than
+// misreading it).
+#include <atomic>
+#include <mutex>
+
+#include "qg_internal.h"
+
+using namespace qg;
+
+namespace {
+
+bool valid_fmt(int fmt) { return fmt >= QG_Q4_0 && fmt <= QG_I8ROW; }
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void *a, int64_t na, const void *b, int64_t nb)
+{
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int64_t> g_max_cols[kMaxDevices];
+std::once_flag g_init_flag;
+
+void init_cache()
+{
+    for (auto &v : g_max_cols) v.store(0);
+}
+
+// Largest cols whose staged activation row fits one workgroup's LDS.
+int64_t max_cols_current()
+{
+    std::call_once(g_init_flag, init_cache);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QG_ERR_DEVICE;
+    int64_t v = g_max_cols[dev].load();
+    if (v > 0) return v;
+    int lds = 0;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || lds <= 0)
+        return QG_ERR_DEVICE;
+    // bytes per column: 36 floats per 32 columns
+    v = ((int64_t)lds / (kXStride * 4)) * kChunk;
+    v -= v % 256;
+    g_max_cols[dev].store(v);
+    return v;
+}
+
+// Common checks of a [rows][cols] product with x [n_tok][cols] -> y [n_tok][rows].
+int check_product(int fmt, const void *packed, const float *x, const float *y, int64_t rows,
+                  int64_t cols, int64_t n_tok, Layout *L)
+{
+    if (!valid_fmt(fmt)) return QG_ERR_FORMAT;
+    if (!packed || !x || !y) return QG_ERR_NULL;
+    if (n_tok < 1 || n_tok >= (int64_t(1) << 31) || !layout_for(fmt, rows, cols, L)) return QG_ERR_SHAPE;
+    const int64_t mc = max_cols_current();
+    if (mc < 0) return (int)mc;
+    if (cols > mc) return QG_ERR_SHAPE;
+    if (!aligned(packed, kPlaneAlign) || !aligned(x, 16) || !aligned(y, 16)) return QG_ERR_ALIGN;
+    if (overlap(x, n_tok * cols * 4, y, n_tok * rows * 4) || overlap(packed, L->total, y, n_tok * rows * 4))
+        return QG_ERR_ALIAS;
+    return QG_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int qgemv_layout_version(void) { return kLayoutVersion; }
+
+const char *qgemv_status_string(int status)
+{
+    switch (status) {
+    case QG_OK: return "ok";
+    case QG_ERR_NULL: return "null pointer argument";
+    case QG_ERR_SHAPE: return "invalid shape (rows/cols/n_tok out of range or not a block multiple)";
+    case QG_ERR_ALIGN: return "misaligned pointer (packed needs 256 bytes, activations 16 bytes)";
+    case QG_ERR_FORMAT: return "unknown format";
+    case QG_ERR_ALIAS: return "an output buffer overlaps an input or another output";
+    case QG_ERR_SCRATCH: return "scratch buffer too small";
+    case QG_ERR_LAUNCH: return "kernel launch failed";
+    case QG_ERR_DEVICE: return "no usable HIP device";
+    default: return "unknown status";
+    }
+}
+
+int64_t qgemv_max_cols(void) { return max_cols_current(); }
+
+int64_t qgemv_packed_bytes(int fmt, int64_t rows, int64_t cols)
+{
+    if (!valid_fmt(fmt)) return QG_ERR_FORMAT;
+    Layout L;
+    if (!layout_for(fmt, rows, cols, &L)) return QG_ERR_SHAPE;
+    return L.total;
+}
+
+static int repack_common(int fmt, const void *raw, const float *row_scale, void *packed, int64_t rows,
+                         int64_t cols, void *stream)
+{
+    if (!valid_fmt(fmt)) return QG_ERR_FORMAT;
+    if (!raw || !packed || (fmt == QG_I8ROW && !row_scale)) return QG_ERR_NULL;
+    Layout L;
+    if (!layout_for(fmt, rows, cols, &L)) return QG_ERR_SHAPE;
+    if (!aligned(packed, kPlaneAlign)) return QG_ERR_ALIGN;
+    if (fmt == QG_I8ROW && (!aligned(raw, 16) || !aligned(row_scale, 4))) return QG_ERR_ALIGN;
+    int64_t raw_bytes;
+    switch (fmt) {
+    case QG_Q4_0: raw_bytes = rows * (cols / 32) * 18; break;
+    case QG_Q8_0: raw_bytes = rows * (cols / 32) * 34; break;
+    case QG_Q4_K: raw_bytes = rows * (cols / 256) * 144; break;
+    default: raw_bytes = rows * cols; break;
+    }
+    if (overlap(raw, raw_bytes, packed, L.total)) return QG_ERR_ALIAS;
+    if (fmt == QG_I8ROW && overlap(row_scale, rows * 4, packed, L.total)) return QG_ERR_ALIAS;
+    if (launch_repack(fmt, raw, row_scale, static_cast<uint8_t *>(packed), rows, cols, (hipStream_t)stream) !=
+        hipSuccess)
+        return QG_ERR_LAUNCH;
+    return QG_OK;
+}
+
+int qgemv_repack_q4_0(const void *raw, void *packed, int64_t rows, int64_t cols, void *stream)
+{
+    return repack_common(QG_Q4_0, raw, nullptr, packed, rows, cols, stream);
+}
+int qgemv_repack_q8_0(const void *raw, void *packed, int64_t rows, int64_t cols, void *stream)
+{
+    return repack_common(QG_Q8_0, raw, nullptr, packed, rows, cols, stream);
+}
+int qgemv_repack_q4_k(const void *raw, void *packed, int64_t rows, int64_t cols, void *stream)
+{
+    return repack_common(QG_Q4_K, raw, nullptr, packed, rows, cols, stream);
+}
+int qgemv_repack_i8row(const int8_t *q, const float *row_scale, void *packed, int64_t rows, int64_t cols,
+                       void *stream)
+{
+    return repack_common(QG_I8ROW, q, row_scale, packed, rows, cols, stream);
+}
+
+int qgemv(int fmt, const void *packed, const float *x, float *y, int64_t rows, int64_t cols, int64_t n_tok,
+          void *stream)
+{
+    Layout L;
+    int st = check_product(fmt, packed, x, y, rows, cols, n_tok, &L);
+    if (st) return st;
+    const GemvCfg cfg = choose_cfg(fmt, rows, cols, 1);
+    for (int64_t t = 0; t < n_tok; t++) {
+        if (launch_gemv(fmt, static_cast<const uint8_t *>(packed), x + t * cols, y + t * rows, rows, cols,
+                        (hipStream_t)stream, cfg) != hipSuccess)
+            return QG_ERR_LAUNCH;
+    }
+    return QG_OK;
+}
+
+int qgemv_q4_0(const void *packed, const float *x, float *y, int64_t rows, int64_t cols, int64_t n_tok,
+               void *stream)
+{
+    return qgemv(QG_Q4_0, packed, x, y, rows, cols, n_tok, stream);
+}
+int qgemv_q8_0(const void *packed, const float *x, float *y, int64_t rows, int64_t cols, int64_t n_tok,
+               void *stream)
+{
+    return qgemv(QG_Q8_0, packed, x, y, rows, cols, n_tok, stream);
+}
+int qgemv_q4_k(const void *packed, const float *x, float *y, int64_t rows, int64_t cols, int64_t n_tok,
+               void *stream)
+{
+    return qgemv(QG_Q4_K, packed, x, y, rows, cols, n_tok, stream);
+}
+int qgemv_i8row(const void *packed, const float *x, float *y, int64_t rows, int64_t cols, int64_t n_tok,
+                void *stream)
+{
+    return qgemv(QG_I8ROW, packed, x, y, rows, cols, n_tok, stream);
+}
+
+int swiglu_gate_up(int fmt, const void *wg, const void *wu, const float *x, float *h, int64_t d_model,
+                   int64_t ffn, int64_t n_tok, void *stream)
+{
+    Layout L;
+    int st = check_product(fmt, wg, x, h, ffn, d_model, n_tok, &L);
+    if (st) return st;
+    if (!wu) return QG_ERR_NULL;
+    if (!aligned(wu, kPlaneAlign)) return QG_ERR_ALIGN;
+    if (overlap(wu, L.total, h, n_tok * ffn * 4)) return QG_ERR_ALIAS;
+    const GemvCfg cfg = choose_cfg(fmt, ffn, d_model, 2);
+    for (int64_t t = 0; t < n_tok; t++) {
+        if (launch_gate_up(fmt, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu),
+                           x + t * d_model, h + t * ffn, ffn, d_model, (hipStream_t)stream, cfg) != hipSuccess)
+            return QG_ERR_LAUNCH;
+    }
+    return QG_OK;
+}
+
+int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const float *x, float *out,
+               float *h_scratch, int64_t h_scratch_elems, int64_t d_model, int64_t ffn, int64_t n_tok,
+               void *stream)
+{
+    if (!valid_fmt(fmt)) return QG_ERR_FORMAT;
+    if (!wg || !wu || !wd || !x || !out || !h_scratch) return QG_ERR_NULL;
+    Layout Lg, Ld;
+    if (n_tok < 1 || n_tok >= (int64_t(1) << 31) || !layout_for(fmt, ffn, d_model, &Lg) ||
+        !layout_for(fmt, d_model, ffn, &Ld))
+        return QG_ERR_SHAPE;
+    const int64_t mc = max_cols_current();
+    if (mc < 0) return (int)mc;
+    if (d_model > mc || ffn > mc) return QG_ERR_SHAPE;
+    if (h_scratch_elems < n_tok * ffn) return QG_ERR_SCRATCH;
+    if (!aligned(wg, kPlaneAlign) || !aligned(wu, kPlaneAlign) || !aligned(wd, kPlaneAlign) || !aligned(x, 16) ||
+        !aligned(out, 16) || !aligned(h_scratch, 16))
+        return QG_ERR_ALIGN;
+    const int64_t xb = n_tok * d_model * 4, hb = n_tok * ffn * 4;
+    if (overlap(x, xb, out, xb) || overlap(x, xb, h_scratch, hb) || overlap(out, xb, h_scratch, hb) ||
+        overlap(wg, Lg.total, h_scratch, hb) || overlap(wu, Lg.total, h_scratch, hb) ||
+        overlap(wd, Ld.total, h_scratch, hb) || overlap(wg, Lg.total, out, xb) || overlap(wu, Lg.total, out, xb) ||
+        overlap(wd, Ld.total, out, xb))
+        return QG_ERR_ALIAS;
+    const GemvCfg cg = choose_cfg(fmt, ffn, d_model, 2);
+    const GemvCfg cd = choose_cfg(fmt, d_model, ffn, 1);
+    hipStream_t s = (hipStream_t)stream;
+    for (int64_t t = 0; t < n_tok; t++) {
+        if (launch_gate_up(fmt, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), x + t * d_model,
+                           h_scratch + t * ffn, ffn, d_model, s, cg) != hipSuccess)
+            return QG_ERR_LAUNCH;
+    }
+    for (int64_t t = 0; t < n_tok; t++) {
+        if (launch_gemv(fmt, static_cast<const uint8_t *>(wd), h_scratch + t * ffn, out + t * d_model, d_model, ffn,
+                        s, cd) != hipSuccess)
+            return QG_ERR_LAUNCH;
+    }
+    return QG_OK;
+}
+
+int qdequant(int fmt, const void *packed, float *w_out, int64_t rows, int64_t cols, void *stream)
+{
+    if (!valid_fmt(fmt)) return QG_ERR_FORMAT;
+    if (!packed || !w_out) return QG_ERR_NULL;
+    Layout L;
+    if (!layout_for(fmt, rows, cols, &L)) return QG_ERR_SHAPE;
+    if (!aligned(packed, kPlaneAlign) || !aligned(w_out, 16)) return QG_ERR_ALIGN;
+    if (overlap(packed, L.total, w_out, rows * cols * 4)) return QG_ERR_ALIAS;
+    if (launch_dequant(fmt, static_cast<const uint8_t *>(packed), w_out, rows, cols, (hipStream_t)stream) !=
+        hipSuccess)
+        return QG_ERR_LAUNCH;
+    return QG_OK;
+}
+
+} // extern "C"

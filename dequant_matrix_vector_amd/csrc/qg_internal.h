@@ -1,0 +1,63 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qgemv.h"
+
+namespace qg {
+
+constexpr int kChunk = 32;           // weights per lane work item (a Q4_0/Q8_0 block, a Q4_K sub-block)
+constexpr int kXStride = 36;         // LDS floats per staged x chunk: 32 values + chunk sum + 3 pad
+constexpr int64_t kPlaneAlign = 256; // packed plane alignment
+constexpr int kLayoutVersion = 1;
+
+inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// Packed layout v1: a quant plane [rows][row_qbytes] followed (at a 256-byte
+// boundary) by a scale plane.
+//   Q4_0  quant row = cols/2 bytes, 16 B per block, nibble order of the raw
+//         block; scale plane f16 [rows][cols/32].
+//   Q8_0  quant row = cols bytes (int8, column order); scale plane f16 [rows][cols/32].
+//   Q4_K  quant row = cols/2 bytes, 16 B per 32-wide sub-block, re-ordered so
+//         byte l holds element l (low nibble) and l+16 (high nibble) of that
+//         sub-block; scale plane = the raw 16-byte super-block headers
+//         (d, dmin, scales[12]) [rows][cols/256].
+//   I8ROW quant row = cols bytes; scale plane fp32 [rows].
+struct Layout {
+    int64_t row_qbytes;   // bytes per row in the quant plane
+    int64_t qplane_bytes; // rows * row_qbytes
+    int64_t splane_off;   // offset of the scale plane
+    int64_t splane_bytes;
+    int64_t total;
+};
+
+bool layout_for(int fmt, int64_t rows, int64_t cols, Layout *L);
+
+// Launch configuration of the GEMV kernels.
+struct GemvCfg {
+    int lpr;    // lanes cooperating on one row (8, 16, 32, 64)
+    int r;      // rows per lane group sharing each staged x chunk (1, 2, 4)
+    int waves;  // waves per workgroup
+};
+
+GemvCfg choose_cfg(int fmt, int64_t rows, int64_t cols, int nmat);
+
+// Optional override of the heuristic (tuning sweeps); lpr == 0 clears it.
+extern "C" int qgemv_set_launch_override(int lpr, int r, int waves);
+bool launch_override(GemvCfg *c);
+
+// Kernel launchers (enqueue only; arguments already validated).
+hipError_t launch_gemv(int fmt, const uint8_t *packed, const float *x, float *y, int64_t rows,
+                       int64_t cols, hipStream_t s, const GemvCfg &cfg);
+hipError_t launch_gate_up(int fmt, const uint8_t *wg, const uint8_t *wu, const float *x, float *h,
+                          int64_t ffn, int64_t d_model, hipStream_t s, const GemvCfg &cfg);
+hipError_t launch_repack(int fmt, const void *raw, const float *row_scale, uint8_t *packed,
+                         int64_t rows, int64_t cols, hipStream_t s);
+hipError_t launch_dequant(int fmt, const uint8_t *packed, float *w, int64_t rows, int64_t cols,
+                          hipStream_t s);
+
+size_t gemv_lds_bytes(int64_t cols);
+
+} // namespace qg

@@ -1,0 +1,159 @@
+/*
+ * qgemv: block-quantized matrix-vector product for single-token LLM decode on
+ * MI355X (gfx950), with dequantization fused into the dot product, and the
+ * SwiGLU feed-forward block built from it.
+ *
+ * C ABI.  Every pointer argument except `stream` is DEVICE memory owned by the
+ * caller; the library allocates nothing and keeps no mutable global state
+ * beyond a lazily read per-device property cache.  `stream` is a hipStream_t
+ * passed as void* (NULL = the legacy null stream).
+ *
+ * Errors are returned, never thrown: every entry point validates its arguments
+ * synchronously and, on any error, returns a negative qg_status and enqueues
+ * nothing.  On success the work is enqueued on `stream` and the call returns
+ * immediately; device-side faults surface at the caller's next synchronization.
+ * A kernel launch that the runtime rejects returns QG_ERR_LAUNCH.
+ * Calls on different streams are independent and thread-safe.
+ *
+ * Definitions the operations follow (pages cited by title and section):
+ *  - y = W x with W stored one row per output: "Running an LLM, then forgetting
+ *    it" (the llmoxide blog), section 1 "A neuron is a dot product"; the matmul
+ *    of dasLLAMA-00, section 8.7.1.4 "Five small functions".
+ *  - Batched tokens: x is [n_tok][cols], y is [n_tok][rows], row-major (llmoxide
+ *    blog, section 11 "Prefill and decode").
+ *  - Each dot product decodes its row's blocks on the fly (llmoxide blog,
+ *    section 10 "Loading weights"; "Building llamini.cpp", section "Optimizing
+ *    for CPU, and finding out what was actually true").
+ *  - Block formats: Q8_0 (llmoxide blog section 10: f16 scale + 32 int8, 34 B);
+ *    Q4_0 (Go "llm" package README, Design points: 18-byte blocks; w=(q-8)*d);
+ *    Q4_K (llamini.cpp post, "What I reimplemented": 256-weight super-blocks,
+ *    six-bit scale/min pairs unpacked by get_scale_min_k4, 144 B); per-row
+ *    symmetric INT8 (minillm-cpp README, Quantization paragraph: one scale per
+ *    output row).  The byte layouts of the raw blocks are spelled out below.
+ *  - SwiGLU: gate = Wg x, up = Wu x, h = silu(gate) * up, out = Wd h (llmoxide
+ *    blog, section 2 "Layers, and the bend between them"; dasLLAMA-00, section
+ *    8.7.1.6.3); no residual add and no normalization inside.
+ *  - Load-time repack of raw blocks into aligned planes: Go "llm" package
+ *    README, Design points (its Q4_0 blocks become aligned u32 quants and f32
+ *    scales; here the f16 scales are kept, so the bytes streamed per weight are
+ *    exactly the raw format's).
+ *
+ * Raw block layouts (little-endian; a tensor is [rows][cols/B] blocks,
+ * row-major; block b of a row covers columns [B*b, B*b+B)):
+ *   Q4_0  B=32, 18 bytes: f16 d; 16 code bytes, byte l holding column l in its
+ *         low nibble and column l+16 in its high nibble; w = (q - 8) * d.
+ *   Q8_0  B=32, 34 bytes: f16 d; 32 int8 codes in column order; w = d * q.
+ *   Q4_K  B=256, 144 bytes: f16 d; f16 dmin; 12 bytes of six-bit (sc, m)
+ *         pairs for the eight 32-wide sub-blocks (get_scale_min_k4 packing);
+ *         128 code bytes, byte 32c+l holding element l of sub-block 2c (low
+ *         nibble) and of sub-block 2c+1 (high nibble); w = d*sc*q - dmin*m.
+ *   I8ROW int8 codes [rows][cols] plus fp32 scales [rows]; w = s_row * q.
+ *
+ * Shape rules: rows, cols, n_tok >= 1; cols a multiple of 32 (Q4_0, Q8_0,
+ * I8ROW) or of 256 (Q4_K); cols <= qgemv_max_cols(); rows, cols < 2^31.
+ * Alignment: packed buffers 256 bytes; x, y, h, out and w_out 16 bytes.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QG_OK = 0,
+    QG_ERR_NULL = -1,    /* a required pointer is NULL */
+    QG_ERR_SHAPE = -2,   /* rows/cols/n_tok out of range or not a block multiple */
+    QG_ERR_ALIGN = -3,   /* a pointer breaks the alignment rule */
+    QG_ERR_FORMAT = -4,  /* unknown format code */
+    QG_ERR_ALIAS = -5,   /* an output overlaps an input or another output */
+    QG_ERR_SCRATCH = -6, /* the caller's scratch buffer is too small */
+    QG_ERR_LAUNCH = -7,  /* the HIP runtime rejected a launch */
+    QG_ERR_DEVICE = -8   /* no usable HIP device / device query failed */
+} qg_status;
+
+typedef enum { QG_Q4_0 = 0, QG_Q8_0 = 1, QG_Q4_K = 2, QG_I8ROW = 3 } qg_format;
+
+/* Version of the packed (repacked) layout; packed buffers are only valid for
+ * the library that wrote them. */
+int qgemv_layout_version(void);
+
+/* Human-readable text for a qg_status (static storage, never NULL). */
+const char *qgemv_status_string(int status);
+
+/* Largest supported cols for the current device (bounded by the LDS that
+ * stages one activation row per workgroup), or a negative qg_status. */
+int64_t qgemv_max_cols(void);
+
+/* Bytes of the packed buffer for a [rows][cols] tensor of format fmt, or a
+ * negative qg_status if the shape or format is invalid.  The packed buffer
+ * holds exactly the raw format's bytes (quant plane + scale plane), plus
+ * padding to 256-byte plane boundaries. */
+int64_t qgemv_packed_bytes(int fmt, int64_t rows, int64_t cols);
+
+/* Load-time repack: raw blocks (device, layout above) -> packed planes
+ * (device, qgemv_packed_bytes bytes, 256-byte aligned).  raw must not
+ * overlap packed.  For I8ROW, q is the int8 code matrix and row_scale the fp32
+ * per-row scales. */
+int qgemv_repack_q4_0(const void *raw, void *packed, int64_t rows, int64_t cols, void *stream);
+int qgemv_repack_q8_0(const void *raw, void *packed, int64_t rows, int64_t cols, void *stream);
+int qgemv_repack_q4_k(const void *raw, void *packed, int64_t rows, int64_t cols, void *stream);
+int qgemv_repack_i8row(const int8_t *q, const float *row_scale, void *packed, int64_t rows,
+                       int64_t cols, void *stream);
+
+/* y[t][i] = sum_j Wdeq[i][j] * x[t][j] for t < n_tok, i < rows.
+ * packed: made by the matching qgemv_repack_*; x: fp32 [n_tok][cols];
+ * y: fp32 [n_tok][rows], overwritten.  x must not overlap y.
+ * fp32 accumulation; n_tok == 1 runs the fused dequant-dot GEMV kernels,
+ * n_tok > 1 the batched path. */
+int qgemv_q4_0(const void *packed, const float *x, float *y, int64_t rows, int64_t cols,
+               int64_t n_tok, void *stream);
+int qgemv_q8_0(const void *packed, const float *x, float *y, int64_t rows, int64_t cols,
+               int64_t n_tok, void *stream);
+int qgemv_q4_k(const void *packed, const float *x, float *y, int64_t rows, int64_t cols,
+               int64_t n_tok, void *stream);
+int qgemv_i8row(const void *packed, const float *x, float *y, int64_t rows, int64_t cols,
+                int64_t n_tok, void *stream);
+
+/* Format-generic form of the four calls above. */
+int qgemv(int fmt, const void *packed, const float *x, float *y, int64_t rows, int64_t cols,
+          int64_t n_tok, void *stream);
+
+/* First half of the SwiGLU block: h[t][i] = silu(Wg x)[t][i] * (Wu x)[t][i],
+ * silu(g) = g / (1 + exp(-g)).  wg, wu: packed [ffn][d_model] of format fmt;
+ * x: fp32 [n_tok][d_model]; h: fp32 [n_tok][ffn], overwritten, must not
+ * overlap x. */
+int swiglu_gate_up(int fmt, const void *wg, const void *wu, const float *x, float *h,
+                   int64_t d_model, int64_t ffn, int64_t n_tok, void *stream);
+
+/* Whole SwiGLU block: out = Wd (silu(Wg x) * (Wu x)).
+ * wd: packed [d_model][ffn]; x: fp32 [n_tok][d_model]; out: fp32
+ * [n_tok][d_model], overwritten; h_scratch: caller-owned fp32 scratch of
+ * h_scratch_elems >= n_tok*ffn elements, left holding h on return (so the
+ * caller can inspect the intermediate).  x, out and h_scratch must be
+ * pairwise disjoint.  Two launches on `stream`, no host synchronization. */
+int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const float *x,
+               float *out, float *h_scratch, int64_t h_scratch_elems, int64_t d_model,
+               int64_t ffn, int64_t n_tok, void *stream);
+
+/* Test export: the packed tensor decoded to fp32 [rows][cols] (each weight its
+ * exact value rounded once to binary32).  Not used on the hot path. */
+int qdequant(int fmt, const void *packed, float *w_out, int64_t rows, int64_t cols, void *stream);
+
+/* Tuning hook for launch-shape sweeps: force the GEMV kernels' lanes per row
+ * (8, 16, 32 or 64), rows per lane group (1, 2 or 4; the gate/up kernel caps it
+ * at 2) and waves per workgroup (1..8) for subsequent calls in this process;
+ * lpr == 0 restores the built-in choice.  Results do not depend on the shape
+ * except through summation order (every choice stays within the fp32 bound).
+ * Process-global and not synchronized: set it only while no other thread is
+ * enqueueing work. */
+int qgemv_set_launch_override(int lpr, int r, int waves);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

@@ -1,0 +1,70 @@
+"""The C-ABI library loads and exports every function include/qgemv.h declares.
+
+CPU only: nothing here launches a kernel or queries a device; the refusal
+checks exercised return before any HIP call (format, null pointer and shape
+are validated first).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "dequant_matrix_vector_amd", "libqgemv.so")
+HEADER = os.path.join(ROOT, "include", "qgemv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libqgemv.so is not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_k", "qgemv_i8row", "swiglu_ffn", "qdequant",
+              "qgemv_repack_q4_0", "qgemv_repack_q8_0", "qgemv_repack_q4_k", "qgemv_repack_i8row",
+              "qgemv_packed_bytes", "qgemv_status_string"):
+        assert n in names, n
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_host_only_queries(lib):
+    lib.qgemv_packed_bytes.restype = ctypes.c_int64
+    lib.qgemv_packed_bytes.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64]
+    # quant plane padded to 256 B, then the scale plane, padded to 256 B
+    assert lib.qgemv_packed_bytes(0, 17408, 5120) == 17408 * 2560 + 17408 * 160 * 2
+    assert lib.qgemv_packed_bytes(1, 49152, 576) == 49152 * 576 + 49152 * 18 * 2
+    assert lib.qgemv_packed_bytes(2, 3, 256) == 512 + 256
+    assert lib.qgemv_packed_bytes(3, 5, 32) == 256 + 256
+    assert lib.qgemv_packed_bytes(0, 4, 48) == -2     # not a block multiple
+    assert lib.qgemv_packed_bytes(9, 4, 64) == -4     # unknown format
+    lib.qgemv_status_string.restype = ctypes.c_char_p
+    assert lib.qgemv_status_string(0) == b"ok"
+    assert b"shape" in lib.qgemv_status_string(-2)
+    assert lib.qgemv_layout_version() == 1
+
+
+def test_refusals_before_any_device_call(lib):
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    lib.qgemv.argtypes = [ctypes.c_int, P, P, P, I64, I64, I64, P]
+    fake = ctypes.c_void_p(0x100000)
+    assert lib.qgemv(7, fake, fake, fake, 4, 32, 1, None) == -4
+    assert lib.qgemv(0, None, fake, fake, 4, 32, 1, None) == -1
+    assert lib.qgemv(0, fake, fake, fake, 4, 33, 1, None) == -2
+    assert lib.qgemv(0, fake, fake, fake, 0, 32, 1, None) == -2
+    assert lib.qgemv(0, fake, fake, fake, 4, 32, 0, None) == -2
+    assert lib.qgemv(2, fake, fake, fake, 4, 300, 1, None) == -2
