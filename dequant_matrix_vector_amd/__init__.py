@@ -52,7 +52,7 @@ lib.swiglu_ffn.argtypes = [_I, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _
 lib.swiglu_ffn.restype = _I
 lib.qdequant.argtypes = [_I, _P, _P, _I64, _I64, _P]
 lib.qdequant.restype = _I
-lib.qgemv_set_launch_override.argtypes = [_I, _I, _I]
+lib.qgemv_set_launch_override.argtypes = [_I, _I, _I, _I, _I, _I]
 lib.qgemv_set_launch_override.restype = _I
 
 
@@ -115,8 +115,9 @@ def packed_bytes(fmt, rows, cols) -> int:
     return v
 
 
-def set_launch_override(lpr=0, r=0, waves=0):
-    _check(lib.qgemv_set_launch_override(lpr, r, waves), "qgemv_set_launch_override")
+def set_launch_override(lpr=0, r=0, waves=0, depth=2, max_wg=0, cpl=1):
+    """Force a GEMV launch shape (tuning); lpr=0 restores the built-in choice."""
+    _check(lib.qgemv_set_launch_override(lpr, r, waves, depth, max_wg, cpl), "qgemv_set_launch_override")
 
 
 # ------------------------------------------------------------- repack ------

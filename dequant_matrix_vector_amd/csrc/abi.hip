@@ -24,11 +24,13 @@ bool overlap(const void *a, int64_t na, const void *b, int64_t nb)
 
 constexpr int kMaxDevices = 64;
 std::atomic<int64_t> g_max_cols[kMaxDevices];
+std::atomic<int> g_cu_count[kMaxDevices];
 std::once_flag g_init_flag;
 
 void init_cache()
 {
     for (auto &v : g_max_cols) v.store(0);
+    for (auto &v : g_cu_count) v.store(0);
 }
 
 // Largest cols whose staged activation row fits one workgroup's LDS.
@@ -42,8 +44,8 @@ int64_t max_cols_current()
     int lds = 0;
     if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || lds <= 0)
         return QG_ERR_DEVICE;
-    // bytes per column: 36 floats per 32 columns
-    v = ((int64_t)lds / (kXStride * 4)) * kChunk;
+    // 36 floats per 32 columns, plus one spare 36-float slot
+    v = ((int64_t)lds / (kXStride * 4) - 1) * kChunk;
     v -= v % 256;
     g_max_cols[dev].store(v);
     return v;
@@ -66,6 +68,20 @@ int check_product(int fmt, const void *packed, const float *x, const float *y, i
 }
 
 } // namespace
+
+namespace qg {
+int cu_count()
+{
+    std::call_once(g_init_flag, init_cache);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int v = g_cu_count[dev].load();
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    g_cu_count[dev].store(v);
+    return v;
+}
+} // namespace qg
 
 extern "C" {
 

@@ -1,0 +1,18 @@
+// GEMV kernel instantiations for one weight format (see gemv_impl.h).
+#include "gemv_impl.h"
+
+namespace qg {
+
+template <>
+hipError_t gemv_dispatch<QG_I8ROW, 1>(const gemv_detail::GemvParams &p, const GemvCfg &c, hipStream_t s)
+{
+    return gemv_detail::dispatch<QG_I8ROW, 1>(p, c, s);
+}
+
+template <>
+hipError_t gemv_dispatch<QG_I8ROW, 2>(const gemv_detail::GemvParams &p, const GemvCfg &c, hipStream_t s)
+{
+    return gemv_detail::dispatch<QG_I8ROW, 2>(p, c, s);
+}
+
+} // namespace qg

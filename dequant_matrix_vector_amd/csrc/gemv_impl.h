@@ -1,0 +1,542 @@
+// Fused dequant-dot GEMV kernels for gfx950 (wave64, fp32 accumulation).
+//
+// y = W x with W block-quantized, one token: the decode-time product that sets
+// decode speed because every weight is streamed once for one multiply-add
+// (llmoxide blog, section 11 "Prefill and decode"); each dot product decodes
+// its row's blocks on the fly and never materializes floats (llmoxide blog,
+// section 10 "Loading weights").
+//
+// Work decomposition
+//   * A 32-weight "chunk" (a Q4_0 or Q8_0 block, a Q4_K sub-block, 32 int8 of
+//     an I8ROW row) is the unit of decode; a lane takes CPL adjacent chunks
+//     (a "group") per pass, so the group's CPL scales arrive in one 2-, 4- or
+//     8-byte load.
+//   * LPR lanes share a row: lane `sl` takes group sl, sl+LPR, ...;
+//     consecutive lanes read consecutive pieces of the quant plane.
+//   * Each lane group owns R rows (times NMAT matrices for the fused gate/up),
+//     so one staged x chunk read from LDS feeds R*NMAT chunks of weights.
+//   * The workgroup stages x once into LDS (36 floats per chunk: the 32
+//     values, the chunk sum, padding that spreads consecutive chunks over all
+//     LDS banks), then each wave streams its rows; partial sums are combined
+//     across the LPR lanes by a fixed xor-shuffle tree (deterministic: no
+//     atomics).
+//
+// 4-bit decode (Q4_0, Q4_K): a 32-bit word of packed nibbles is masked with
+// 0x000F000F / 0x00F000F0 (and again after a byte shift) so that each 16-bit
+// half holds one code in its low mantissa bits: as a binary16 subnormal its
+// value is q*2^-24 (or q*2^-20 for the nibble one position up).  x was staged
+// pre-multiplied by 2^24 (first 16 elements of a chunk) or 2^20 (last 16), so
+// v_fma_mix_f32 (binary16 operand converted exactly inside the fma) adds
+// exactly q*x before its single rounding.  Five integer ops decode eight codes.
+// The Q4_0 offset of 8 and the Q4_K minimum are folded in per chunk through the
+// staged chunk sum, accumulated in the same order as the codes so that all-8
+// codes cancel exactly.
+//
+// 8-bit decode (Q8_0, I8ROW): each signed byte converts with one SDWA
+// v_cvt_f32_i32 (sign-extending byte select) and feeds one fma.
+#pragma once
+#include <atomic>
+#include <type_traits>
+
+#include "qg_internal.h"
+
+namespace qg {
+
+namespace gemv_detail {
+
+struct GemvParams {
+    const uint8_t *q[2];  // packed tensors (quant plane at offset 0)
+    const float *x;       // [cols]
+    float *y;             // [rows]
+    int64_t rows;
+    int64_t row_qbytes;
+    int64_t soff;         // scale plane offset inside each packed tensor
+    int nchunk;           // cols / 32
+};
+
+__device__ __forceinline__ float half_lo(uint32_t v)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+}
+__device__ __forceinline__ float half_hi(uint32_t v)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
+
+// sum_l q_l * x_l over one chunk of 4-bit codes, x pre-scaled as described
+// above.  Element order of the sum: for word k, 4k, 4k+2, 4k+16, 4k+18, 4k+1,
+// 4k+3, 4k+17, 4k+19 -- the staging of the chunk sum uses the same order.
+__device__ __forceinline__ float dot_q4_chunk(uint4 q, const float4 (&xv)[8])
+{
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    float t = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const uint32_t t0 = w[k] & 0x000F000Fu;
+        const uint32_t t1 = w[k] & 0x00F000F0u;
+        const uint32_t s = w[k] >> 8;
+        const uint32_t t2 = s & 0x000F000Fu;
+        const uint32_t t3 = s & 0x00F000F0u;
+        const float4 xl = xv[k], xh = xv[4 + k];
+        t = __builtin_fmaf(half_lo(t0), xl.x, t);
+        t = __builtin_fmaf(half_hi(t0), xl.z, t);
+        t = __builtin_fmaf(half_lo(t1), xh.x, t);
+        t = __builtin_fmaf(half_hi(t1), xh.z, t);
+        t = __builtin_fmaf(half_lo(t2), xl.y, t);
+        t = __builtin_fmaf(half_hi(t2), xl.w, t);
+        t = __builtin_fmaf(half_lo(t3), xh.y, t);
+        t = __builtin_fmaf(half_hi(t3), xh.w, t);
+    }
+    return t;
+}
+
+__device__ __forceinline__ float dot_i8_word(uint32_t w, float4 xv, float t)
+{
+    t = __builtin_fmaf((float)(int8_t)(w), xv.x, t);
+    t = __builtin_fmaf((float)(int8_t)(w >> 8), xv.y, t);
+    t = __builtin_fmaf((float)(int8_t)(w >> 16), xv.z, t);
+    t = __builtin_fmaf((float)(int8_t)(w >> 24), xv.w, t);
+    return t;
+}
+
+// t + sum_l q_l * x_l over 32 int8 codes in column order.
+__device__ __forceinline__ float dot_i8_chunk(uint4 a, uint4 b, const float4 (&xv)[8], float t)
+{
+    t = dot_i8_word(a.x, xv[0], t);
+    t = dot_i8_word(a.y, xv[1], t);
+    t = dot_i8_word(a.z, xv[2], t);
+    t = dot_i8_word(a.w, xv[3], t);
+    t = dot_i8_word(b.x, xv[4], t);
+    t = dot_i8_word(b.y, xv[5], t);
+    t = dot_i8_word(b.z, xv[6], t);
+    t = dot_i8_word(b.w, xv[7], t);
+    return t;
+}
+
+template <int FMT> struct Fmt;
+template <> struct Fmt<QG_Q4_0> { static constexpr bool kPrescale = true; static constexpr int kWords = 1; };
+template <> struct Fmt<QG_Q4_K> { static constexpr bool kPrescale = true; static constexpr int kWords = 1; };
+template <> struct Fmt<QG_Q8_0> { static constexpr bool kPrescale = false; static constexpr int kWords = 2; };
+template <> struct Fmt<QG_I8ROW> { static constexpr bool kPrescale = false; static constexpr int kWords = 2; };
+
+// ------------------------------------------------------------ x staging --
+// Per chunk: 32 values (scaled by 2^24 / 2^20 for the 4-bit formats) and,
+// for those, the chunk sum in the decode order.  A thread issues the loads of
+// its first two chunks before anything else (so they are not queued behind
+// the weight stream) and finishes them after the first weight loads are out.
+struct XStage {
+    float4 v[2][8];
+};
+
+__device__ __forceinline__ void stage_issue(const float *__restrict__ x, int nchunk, XStage &st)
+{
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        int c = (int)threadIdx.x + u * (int)blockDim.x;
+        c = c < nchunk ? c : nchunk - 1;   // valid address; the duplicate is not stored
+        const float4 *src = reinterpret_cast<const float4 *>(x + (int64_t)c * kChunk);
+#pragma unroll
+        for (int k = 0; k < 8; k++) st.v[u][k] = src[k];
+    }
+}
+
+template <bool kPrescale>
+__device__ __forceinline__ void stage_store(float4 (&v)[8], float *xs, int c)
+{
+    float4 *dst = reinterpret_cast<float4 *>(xs + c * kXStride);
+    if (kPrescale) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            sum = sum + v[k].x;
+            sum = sum + v[k].z;
+            sum = sum + v[4 + k].x;
+            sum = sum + v[4 + k].z;
+            sum = sum + v[k].y;
+            sum = sum + v[k].w;
+            sum = sum + v[4 + k].y;
+            sum = sum + v[4 + k].w;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const float sc = k < 4 ? 0x1p24f : 0x1p20f;
+            v[k].x *= sc;
+            v[k].y *= sc;
+            v[k].z *= sc;
+            v[k].w *= sc;
+        }
+        xs[c * kXStride + 32] = sum;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k++) dst[k] = v[k];
+}
+
+template <bool kPrescale>
+__device__ __forceinline__ void stage_finish(const float *__restrict__ x, float *xs, int nchunk, XStage &st)
+{
+    // Branch-free for the first two chunks of each thread (an out-of-range
+    // thread writes to the spare slot after the last chunk): a divergent
+    // branch here would make the compiler wait for every load in flight,
+    // including the weight stream issued after x's loads.
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        const int c = (int)threadIdx.x + u * (int)blockDim.x;
+        stage_store<kPrescale>(st.v[u], xs, c < nchunk ? c : nchunk);
+    }
+}
+
+// Chunks beyond the first two per thread (only when nchunk > 2 * threads),
+// staged synchronously before any weight load is issued.
+template <bool kPrescale>
+__device__ __forceinline__ void stage_rest(const float *__restrict__ x, float *xs, int nchunk)
+{
+    for (int c = (int)threadIdx.x + 2 * (int)blockDim.x; c < nchunk; c += blockDim.x) {
+        const float4 *src = reinterpret_cast<const float4 *>(x + (int64_t)c * kChunk);
+        float4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) v[k] = src[k];
+        stage_store<kPrescale>(v, xs, c);
+    }
+}
+
+// ------------------------------------------------------- weight groups --
+// Registers of CPL adjacent chunks of one row.  f16 scales of two chunks
+// share a 32-bit word (low half = even chunk).
+template <int FMT, int CPL> struct Group;
+template <int CPL> struct Group<QG_Q4_0, CPL> { uint4 q[CPL]; uint32_t d[(CPL + 1) / 2]; };
+template <int CPL> struct Group<QG_Q8_0, CPL> { uint4 q[2 * CPL]; uint32_t d[(CPL + 1) / 2]; };
+template <int CPL> struct Group<QG_Q4_K, CPL> { uint4 q[CPL]; uint4 h; };
+template <int CPL> struct Group<QG_I8ROW, CPL> { uint4 q[2 * CPL]; };
+
+// Load the group starting at chunk c0 (c0 a multiple of CPL).
+template <int FMT, int CPL>
+__device__ __forceinline__ void load_group(Group<FMT, CPL> &o, const uint8_t *qrow, const uint8_t *srow, int c0,
+                                           int nchunk)
+{
+    constexpr int W = Fmt<FMT>::kWords;
+    const uint4 *qp = reinterpret_cast<const uint4 *>(qrow + (int64_t)c0 * 16 * W);
+    (void)nchunk;
+#pragma unroll
+    for (int j = 0; j < CPL * W; j++) o.q[j] = qp[j];
+    if constexpr (FMT == QG_Q4_0 || FMT == QG_Q8_0) {
+        if constexpr (CPL == 1) {
+            o.d[0] = reinterpret_cast<const uint16_t *>(srow)[c0];
+        } else if constexpr (CPL == 2) {
+            o.d[0] = reinterpret_cast<const uint32_t *>(srow)[c0 >> 1];
+        } else {
+            const uint2 v = reinterpret_cast<const uint2 *>(srow)[c0 >> 2];
+            o.d[0] = v.x;
+            o.d[1] = v.y;
+        }
+    } else if constexpr (FMT == QG_Q4_K) {
+        o.h = reinterpret_cast<const uint4 *>(srow)[c0 >> 3];
+    }
+}
+
+// Q4_K: position of sub-block s = chunk mod 8 inside the 12-byte scale field.
+struct Q4KSub {
+    uint32_t shift; // 8 * (s mod 4)
+    bool upper;     // s >= 4
+};
+
+__device__ __forceinline__ Q4KSub q4k_sub(int s)
+{
+    Q4KSub k;
+    k.shift = 8u * (uint32_t)(s & 3);
+    k.upper = (s & 7) >= 4;
+    return k;
+}
+
+// acc += contribution of chunk j of the group, x chunk in xv (+ its sum).
+template <int FMT, int CPL, int J>
+__device__ __forceinline__ float consume(const Group<FMT, CPL> &g, const float4 (&xv)[8], float xsum, float acc,
+                                         const Q4KSub &ks)
+{
+    if constexpr (FMT == QG_Q4_0 || FMT == QG_Q8_0) {
+        const float d = (J & 1) ? half_hi(g.d[J >> 1]) : half_lo(g.d[J >> 1]);
+        if constexpr (FMT == QG_Q4_0) {
+            const float t = dot_q4_chunk(g.q[J], xv);
+            const float u = __builtin_fmaf(-8.0f, xsum, t);  // sum (q-8) x
+            return __builtin_fmaf(d, u, acc);
+        } else {
+            const float t = dot_i8_chunk(g.q[2 * J], g.q[2 * J + 1], xv, 0.0f);
+            return __builtin_fmaf(d, t, acc);
+        }
+    } else if constexpr (FMT == QG_Q4_K) {
+        const float t = dot_q4_chunk(g.q[J], xv);
+        // (sc, m) of this sub-block from the 12-byte field (get_scale_min_k4 of
+        // the llamini.cpp post): bytes 0-3 in h.y, 4-7 in h.z, 8-11 in h.w.
+        const uint32_t a = g.h.y >> ks.shift, b = g.h.z >> ks.shift, c = g.h.w >> ks.shift;
+        const uint32_t sc = ks.upper ? ((c & 0xFu) | ((a >> 2) & 0x30u)) : (a & 63u);
+        const uint32_t m = ks.upper ? (((c >> 4) & 0xFu) | ((b >> 2) & 0x30u)) : (b & 63u);
+        const float D = half_lo(g.h.x) * (float)sc;   // exact
+        const float M = half_hi(g.h.x) * (float)m;    // exact
+        acc = __builtin_fmaf(D, t, acc);
+        return __builtin_fmaf(-M, xsum, acc);
+    } else {
+        return dot_i8_chunk(g.q[2 * J], g.q[2 * J + 1], xv, acc);
+    }
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u)
+{
+    return g / (1.0f + expf(-g)) * u;
+}
+
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (N > 0) {
+        static_for<N - 1>(f);
+        f(std::integral_constant<int, N - 1>{});
+    }
+}
+
+// NMAT = 1: y = W x.  NMAT = 2: y = silu(Wg x) * (Wu x) (the SwiGLU gate/up
+// half, with q[0] = Wg and q[1] = Wu sharing the lane's staged x).
+//
+// A lane makes P = nchunk / (LPR*CPL) full passes over its row (group sl +
+// k*LPR in pass k); the remaining chunks are one partial pass handled chunk by
+// chunk.  The full passes run through a ring of D register stages: the loop
+// body is straight-line code over the D stages (no branches, so the
+// compiler's wait counts stay exact), and the refill of a stage is issued
+// right after the stage is consumed, D-1 stage computations before it is
+// needed.  Refill indices are clamped to the last full pass, so the final
+// refills re-read (cached) valid data instead of branching.  The first stages
+// are issued right after x's loads and before the workgroup waits for x to be
+// staged, and the next row batch's stages before the current batch's
+// reduction.  Batches of G*R rows go to waves in grid-stride order.
+template <int FMT, int LPR, int R, int NMAT, int D, int CPL>
+__global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
+{
+    extern __shared__ float4 qg_lds[];
+    float *xs = reinterpret_cast<float *>(qg_lds);
+
+    constexpr int G = 64 / LPR;
+    constexpr int GS = LPR * CPL;        // chunks covered by one pass of a row
+    const int lane = threadIdx.x & 63;
+    const int g = lane / LPR, sl = lane % LPR;
+    const int waves = blockDim.x >> 6;
+    const int64_t nbatch = (p.rows + G * R - 1) / (G * R);
+    const int64_t bstride = (int64_t)gridDim.x * waves;
+    int64_t batch = (int64_t)blockIdx.x * waves + (threadIdx.x >> 6);
+    const int P = p.nchunk / GS;         // full passes (uniform)
+
+    Q4KSub ks[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; j++) ks[j] = q4k_sub(sl * CPL + j);   // GS is a multiple of 8
+
+    const uint8_t *qrow[NMAT][R];
+    const uint8_t *srow[NMAT][R];
+    Group<FMT, CPL> st[D][NMAT][R];
+
+    auto set_rows = [&](int64_t b) {
+        const int64_t row0 = b * (G * R) + (int64_t)g * R;
+#pragma unroll
+        for (int m = 0; m < NMAT; m++) {
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                int64_t row = row0 + r;
+                row = row < p.rows ? row : p.rows - 1;   // ragged tail: read a valid row, store nothing
+                qrow[m][r] = p.q[m] + row * p.row_qbytes;
+                const uint8_t *sp = p.q[m] + p.soff;
+                if (FMT == QG_Q4_0 || FMT == QG_Q8_0) srow[m][r] = sp + row * p.nchunk * 2;
+                else if (FMT == QG_Q4_K) srow[m][r] = sp + row * (p.nchunk / 8) * 16;
+                else srow[m][r] = sp + row * 4;
+            }
+        }
+    };
+    auto load_stage = [&](int s, int pass) {
+        // the clamp only matters when P == 0 (a row shorter than one pass):
+        // the prologue then reads some valid group that is never consumed
+        int c0 = (sl + pass * LPR) * CPL;
+        c0 = c0 < p.nchunk - CPL ? c0 : p.nchunk - CPL;
+#pragma unroll
+        for (int m = 0; m < NMAT; m++)
+#pragma unroll
+            for (int r = 0; r < R; r++) load_group<FMT, CPL>(st[s][m][r], qrow[m][r], srow[m][r], c0, p.nchunk);
+    };
+    auto prologue = [&]() {
+        const int last = P > 0 ? P - 1 : 0;
+#pragma unroll
+        for (int s = 0; s < D; s++) load_stage(s, s < last ? s : last);
+    };
+    auto read_x = [&](int c, float4 (&xv)[8]) -> float {
+        const float4 *xp = reinterpret_cast<const float4 *>(xs + c * kXStride);
+#pragma unroll
+        for (int k = 0; k < 8; k++) xv[k] = xp[k];
+        return Fmt<FMT>::kPrescale ? xs[c * kXStride + 32] : 0.0f;
+    };
+    auto compute = [&](const Group<FMT, CPL> (&regs)[NMAT][R], int c0, float (&acc)[NMAT][R]) {
+        static_for<CPL>([&](auto jj) {
+            constexpr int J = decltype(jj)::value;
+            float4 xv[8];
+            const float xsum = read_x(c0 + J, xv);
+#pragma unroll
+            for (int m = 0; m < NMAT; m++)
+#pragma unroll
+                for (int r = 0; r < R; r++) acc[m][r] = consume<FMT, CPL, J>(regs[m][r], xv, xsum, acc[m][r], ks[J]);
+        });
+    };
+
+    {
+        // No branches until the barrier: a join here would make the compiler
+        // wait for every load in flight, the weight stream included.
+        XStage xst;
+        stage_issue(p.x, p.nchunk, xst);
+        stage_rest<Fmt<FMT>::kPrescale>(p.x, xs, p.nchunk);
+        __builtin_amdgcn_sched_barrier(0);
+        set_rows(batch < nbatch ? batch : nbatch - 1);   // idle waves read a valid row
+        prologue();
+        // x's loads went out first, so finishing the staging waits for them
+        // only, not for the weight loads behind them
+        __builtin_amdgcn_sched_barrier(0);
+        stage_finish<Fmt<FMT>::kPrescale>(p.x, xs, p.nchunk, xst);
+    }
+    __syncthreads();
+
+    for (; batch < nbatch; batch += bstride) {
+        float acc[NMAT][R];
+#pragma unroll
+        for (int m = 0; m < NMAT; m++)
+#pragma unroll
+            for (int r = 0; r < R; r++) acc[m][r] = 0.0f;
+
+        int k = 0;
+        for (; k + D <= P; k += D) {
+#pragma unroll
+            for (int s = 0; s < D; s++) {
+                compute(st[s], (sl + (k + s) * LPR) * CPL, acc);
+                const int nxt = k + s + D;
+                load_stage(s, nxt < P ? nxt : P - 1);
+                // keep the refill here: without this fence the scheduler may
+                // sink it past the next stages' arithmetic, shortening the time
+                // the loads have to land
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < D; s++)      // remaining full passes (fewer than D), uniform branch
+            if (k + s < P) compute(st[s], (sl + (k + s) * LPR) * CPL, acc);
+        // the partial pass, chunk by chunk
+#pragma unroll
+        for (int j = 0; j < CPL; j++) {
+            const int c = (sl + P * LPR) * CPL + j;
+            if (c < p.nchunk) {
+                Group<FMT, 1> tl[NMAT][R];
+#pragma unroll
+                for (int m = 0; m < NMAT; m++)
+#pragma unroll
+                    for (int r = 0; r < R; r++) load_group<FMT, 1>(tl[m][r], qrow[m][r], srow[m][r], c, p.nchunk);
+                float4 xv[8];
+                const float xsum = read_x(c, xv);
+                const Q4KSub kt = q4k_sub(c);
+#pragma unroll
+                for (int m = 0; m < NMAT; m++)
+#pragma unroll
+                    for (int r = 0; r < R; r++) acc[m][r] = consume<FMT, 1, 0>(tl[m][r], xv, xsum, acc[m][r], kt);
+            }
+        }
+
+        float scale[NMAT][R];
+#pragma unroll
+        for (int m = 0; m < NMAT; m++)
+#pragma unroll
+            for (int r = 0; r < R; r++)
+                scale[m][r] = FMT == QG_I8ROW ? *reinterpret_cast<const float *>(srow[m][r]) : 1.0f;
+        const int64_t row0 = batch * (G * R) + (int64_t)g * R;
+        const int64_t nb = batch + bstride;
+        if (nb < nbatch) {               // next batch starts streaming before this one is reduced
+            set_rows(nb);
+            prologue();
+        }
+
+        // combine the LPR partial sums of each row (fixed tree)
+#pragma unroll
+        for (int m = 0; m < NMAT; m++)
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                float v = acc[m][r];
+#pragma unroll
+                for (int off = LPR / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+                acc[m][r] = v;
+            }
+        if (sl == 0) {
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                const int64_t row = row0 + r;
+                if (row < p.rows) {
+                    float v[NMAT];
+#pragma unroll
+                    for (int m = 0; m < NMAT; m++) v[m] = acc[m][r] * scale[m][r];
+                    if (NMAT == 1) p.y[row] = v[0];
+                    else p.y[row] = silu_mul(v[0], v[NMAT - 1]);
+                }
+            }
+        }
+    }
+}
+
+template <int FMT, int LPR, int R, int NMAT, int D, int CPL>
+hipError_t go(const GemvParams &p, const GemvCfg &c, hipStream_t s)
+{
+    constexpr int G = 64 / LPR;
+    const int64_t batches = (p.rows + G * R - 1) / (G * R);
+    int64_t nwg = (batches + c.waves - 1) / c.waves;
+    if (c.max_wg > 0 && nwg > c.max_wg) nwg = c.max_wg;
+    const size_t lds = gemv_lds_bytes((int64_t)p.nchunk * kChunk);
+    auto kern = gemv_kernel<FMT, LPR, R, NMAT, D, CPL>;
+    if (lds > 65536) {
+        // largest dynamic LDS size already allowed for this instantiation, per device
+        static std::atomic<int> configured_lds[64];
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+        if ((int)lds > configured_lds[dev].load(std::memory_order_relaxed)) {
+            hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            configured_lds[dev].store((int)lds, std::memory_order_relaxed);
+        }
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(64 * c.waves), lds, s, p);
+    return hipGetLastError();
+}
+
+template <int FMT, int NMAT, int D, int CPL>
+hipError_t dispatch_lr(const GemvParams &p, const GemvCfg &c, hipStream_t s)
+{
+#define QG_CASE(L, RR) \
+    if (c.lpr == L && c.r == RR) return go<FMT, L, RR, NMAT, D, CPL>(p, c, s);
+    QG_CASE(8, 1) QG_CASE(16, 1) QG_CASE(32, 1) QG_CASE(64, 1)
+    QG_CASE(8, 2) QG_CASE(16, 2) QG_CASE(32, 2) QG_CASE(64, 2)
+#undef QG_CASE
+    return hipErrorInvalidValue;
+}
+
+template <int FMT, int NMAT, int D>
+hipError_t dispatch_cpl(const GemvParams &p, const GemvCfg &c, hipStream_t s)
+{
+    switch (c.cpl) {
+    case 1: return dispatch_lr<FMT, NMAT, D, 1>(p, c, s);
+    case 2: return dispatch_lr<FMT, NMAT, D, 2>(p, c, s);
+    case 4: return dispatch_lr<FMT, NMAT, D, 4>(p, c, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int FMT, int NMAT>
+hipError_t dispatch(const GemvParams &p, const GemvCfg &c, hipStream_t s)
+{
+    switch (c.depth) {
+    case 2: return dispatch_cpl<FMT, NMAT, 2>(p, c, s);
+    case 4: return dispatch_cpl<FMT, NMAT, 4>(p, c, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+} // namespace gemv_detail
+
+// Per-format entry points, each instantiated in its own translation unit.
+template <int FMT, int NMAT>
+hipError_t gemv_dispatch(const gemv_detail::GemvParams &p, const GemvCfg &c, hipStream_t s);
+
+} // namespace qg

@@ -40,12 +40,18 @@ struct GemvCfg {
     int lpr;    // lanes cooperating on one row (8, 16, 32, 64)
     int r;      // rows per lane group sharing each staged x chunk (1, 2, 4)
     int waves;  // waves per workgroup
+    int depth;  // prefetch ring depth per lane (2, 4)
+    int max_wg; // cap on workgroups (grid-stride over row batches); 0 = one batch per wave
+    int cpl;    // adjacent chunks per lane per pass (1, 2, 4)
 };
 
 GemvCfg choose_cfg(int fmt, int64_t rows, int64_t cols, int nmat);
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int cu_count();
+
 // Optional override of the heuristic (tuning sweeps); lpr == 0 clears it.
-extern "C" int qgemv_set_launch_override(int lpr, int r, int waves);
+extern "C" int qgemv_set_launch_override(int lpr, int r, int waves, int depth, int max_wg, int cpl);
 bool launch_override(GemvCfg *c);
 
 // Kernel launchers (enqueue only; arguments already validated).

@@ -144,13 +144,15 @@ int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const fl
 int qdequant(int fmt, const void *packed, float *w_out, int64_t rows, int64_t cols, void *stream);
 
 /* Tuning hook for launch-shape sweeps: force the GEMV kernels' lanes per row
- * (8, 16, 32 or 64), rows per lane group (1, 2 or 4; the gate/up kernel caps it
- * at 2) and waves per workgroup (1..8) for subsequent calls in this process;
- * lpr == 0 restores the built-in choice.  Results do not depend on the shape
- * except through summation order (every choice stays within the fp32 bound).
+ * (8, 16, 32 or 64), rows per lane group (1 or 2), waves per workgroup (1..8),
+ * prefetch depth per lane (2 or 4), a cap on the number of workgroups (0 =
+ * none; with a cap, workgroups loop over row batches) and adjacent 32-weight
+ * chunks per lane per pass (1, 2 or 4) for subsequent calls in this process;
+ * lpr == 0 restores the built-in choice.  Results depend on the shape only
+ * through summation order (every choice stays within the fp32 bound).
  * Process-global and not synchronized: set it only while no other thread is
- * enqueueing work. */
-int qgemv_set_launch_override(int lpr, int r, int waves);
+ * enqueueing work.  Returns QG_ERR_SHAPE for values outside these sets. */
+int qgemv_set_launch_override(int lpr, int r, int waves, int depth, int max_wg, int cpl);
 
 #ifdef __cplusplus
 }

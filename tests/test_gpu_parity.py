@@ -136,7 +136,8 @@ def test_batched_tokens_match_single(fmt):
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_every_launch_shape(fmt):
-    # every lanes-per-row / rows-per-group / waves choice the tuning hook allows
+    # every lanes-per-row / rows-per-group / waves / prefetch-depth choice the
+    # tuning hook allows, with and without a grid-stride workgroup cap
     rows, cols = 203, {"q4_0": 1536, "q8_0": 1536, "q4_k": 2048, "i8row": 1536}[fmt]
     t = _tensor(fmt, rows, cols, 800)
     packed = G.upload(t)
@@ -144,11 +145,61 @@ def test_every_launch_shape(fmt):
     yr, S = oracle.gemv(fmt, t.raw, x, rows, cols, row_scale=t.row_scale)
     try:
         for lpr in (8, 16, 32, 64):
-            for r in (1, 2, 4):
+            for r in (1, 2):
                 for waves in (1, 4, 8):
-                    G.qg().set_launch_override(lpr, r, waves)
-                    y = G.gemv_gpu(t, packed, x)
-                    G.check_bound(y, yr, S, what=f"{fmt} lpr={lpr} r={r} waves={waves}")
+                    for depth in (2, 4):
+                        for max_wg in (0, 3):
+                            for cpl in (1, 2, 4):
+                                G.qg().set_launch_override(lpr, r, waves, depth, max_wg, cpl)
+                                y = G.gemv_gpu(t, packed, x)
+                                G.check_bound(y, yr, S, what=f"{fmt} lpr={lpr} r={r} waves={waves} "
+                                                             f"depth={depth} max_wg={max_wg} cpl={cpl}")
+    finally:
+        G.qg().set_launch_override(0)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gate_up_every_launch_shape(fmt):
+    d_model, ffn = (2048, 203) if fmt == "q4_k" else (1536, 203)   # ragged ffn rows
+    rng = np.random.default_rng(850)
+    g = synth.make_tensor(fmt, ffn, d_model, rng)
+    u = synth.make_tensor(fmt, ffn, d_model, rng)
+    pg, pu = G.upload(g), G.upload(u)
+    x = np.random.default_rng(851).standard_normal((1, d_model)).astype(np.float32)
+    r = {}
+    r["g"], r["Sg"] = oracle.gemv(fmt, g.raw, x, ffn, d_model, row_scale=g.row_scale)
+    r["u"], r["Su"] = oracle.gemv(fmt, u.raw, x, ffn, d_model, row_scale=u.row_scale)
+    r["h"] = np.array([[oracle.silu(v) for v in r["g"][0]]]) * r["u"]
+    hb = G.h_bound(r)
+    xd = G.torch.from_numpy(x).to(G.dev())
+    try:
+        for lpr in (8, 16, 32, 64):
+            for rr in (1, 2):
+                for waves in (1, 4, 8):
+                    for depth in (2, 4):
+                        for max_wg in (0, 3):
+                            for cpl in (1, 2, 4):
+                                G.qg().set_launch_override(lpr, rr, waves, depth, max_wg, cpl)
+                                h = G.qg().swiglu_gate_up(fmt, pg, pu, xd, d_model, ffn)
+                                G.torch.cuda.synchronize()
+                                err = np.abs(h.cpu().numpy() - r["h"])
+                                assert np.all(err <= hb), (fmt, lpr, rr, waves, depth, max_wg, cpl)
+    finally:
+        G.qg().set_launch_override(0)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+def test_grouped_scales_with_odd_chunk_rows(fmt):
+    # 288 columns = 9 chunks per row: grouped scale loads must not be used
+    rows, cols = 77, 288
+    t = _tensor(fmt, rows, cols, 870)
+    packed = G.upload(t)
+    x = np.random.default_rng(871).standard_normal(cols).astype(np.float32)
+    yr, S = oracle.gemv(fmt, t.raw, x, rows, cols, row_scale=t.row_scale)
+    try:
+        for cpl in (2, 4):
+            G.qg().set_launch_override(8, 1, 4, 2, 0, cpl)
+            G.check_bound(G.gemv_gpu(t, packed, x), yr, S, what=f"{fmt} cpl={cpl} 9 chunks")
     finally:
         G.qg().set_launch_override(0)
 
