@@ -17,6 +17,7 @@ cpu_baseline: the CPU oracle (scalar C, binary64) on the same workload.
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
 """
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -37,7 +38,74 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--warm", action="store_true", help="also report a cache-resident (single copy) rate")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload report")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="finish with a plain 256 MiB device copy (known bytes, for scaling HBM counters)")
     return ap.parse_args()
+
+
+class TimingEvents:
+    """HIP events created for timing only (hipEventDisableSystemFence): recording
+    them adds no system-scope cache writeback between the kernels they bracket.
+    Uses the HIP runtime torch already loaded (same soname)."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.lib.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(e)
+
+    def record(self, i, stream_ptr):
+        if self.lib.hipEventRecord(self.ev[i], ctypes.c_void_p(stream_ptr)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, i, j):
+        out = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(out), self.ev[i], self.ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def close(self):
+        for e in self.ev:
+            self.lib.hipEventDestroy(e)
+        self.ev = []
+
+
+GEMV_SOURCES = ("dequant_matrix_vector_amd/csrc/gemv_impl.h", "dequant_matrix_vector_amd/csrc/gemv_q4_0.hip",
+                "dequant_matrix_vector_amd/csrc/gemv.hip")
+TRAFFIC_PROFILE = "profiles/gemv_q4_0_27b_ffn_hbm_counters.md"
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fused gate/up kernel from the committed
+    rocprofv3 counter summary, or None if the kernel sources changed since the
+    counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", "`")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in GEMV_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if fields.get("gemv_source_sha256_16") != h.hexdigest()[:16]:
+        return None
+    try:
+        return int(fields["traffic_gate_up_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(tens, x, w, min_seconds):
@@ -55,6 +123,76 @@ def cpu_baseline(tens, x, w, min_seconds):
     return {"value": round(wb / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"full FFN (gate, up, down) x {reps} runs, {el:.1f} s, {per * 1e3:.0f} ms per FFN, "
                       f"1 thread, binary64 scalar C"}
+
+
+def workload_report(qg, synth, torch, np, dev, graph_iters=20):
+    """Device time per step of every workload, from HIP graph replays.
+
+    A step is the workload's whole hot path: the FFN (gate/up + down) for the
+    FFN workloads, every listed GEMV for the layer workloads (their gate/up
+    pair through the fused gate/up kernel).  Packed copies rotate across the
+    graph's steps; when the copies reach 1 GiB the weights stream from HBM
+    ("hbm"), otherwise they may sit in the 256 MB Infinity Cache ("cache")."""
+    rep = {}
+    plans = [(synth.CFG1, 1), (synth.CFG2, 1), (synth.CFG3, 1), (synth.CFG4, 1),
+             (synth.CFG5, 8), (synth.CFG5, 128)]
+    for w, n_tok in plans:
+        tens = synth.gen_workload(w)
+        wbytes = sum(t.weight_bytes for t in tens)
+        ncopy = int(min(graph_iters, max(1, -(-ROTATE_BYTES // wbytes))))
+        raws = [(torch.from_numpy(t.raw).to(dev),
+                 None if t.row_scale is None else torch.from_numpy(t.row_scale).to(dev)) for t in tens]
+        copies = [[qg.repack(t.fmt, r, t.rows, t.cols, row_scale=rs) for (r, rs), t in zip(raws, tens)]
+                  for _ in range(ncopy)]
+        del raws
+        names = [t.name for t in tens]
+        xs = {c: torch.randn((n_tok, c), device=dev) for c in {t.cols for t in tens}}
+        outs = {t.name: torch.empty((n_tok, t.rows), device=dev) for t in tens}
+        h = torch.empty((n_tok, w.ffn), device=dev)
+
+        def step(i):
+            pk = copies[i % ncopy]
+            if "gate" in names and "up" in names:
+                gi, ui = names.index("gate"), names.index("up")
+                tg = tens[gi]
+                # stream=None: the binding takes torch's current stream, which is the
+                # capture stream inside the graph
+                qg.swiglu_gate_up(tg.fmt, pk[gi], pk[ui], xs[tg.cols], tg.cols, tg.rows, h=h)
+            for j, t in enumerate(tens):
+                if t.name in ("gate", "up"):
+                    continue
+                xin = h if t.name == "down" else xs[t.cols]
+                qg.qgemv(t.fmt, pk[j], xin, t.rows, t.cols, y=outs[t.name])
+
+        for i in range(3):
+            step(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(graph_iters):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * graph_iters)
+        key = f"cfg{w.cfg_id}" + (f"_n{n_tok}" if w.n_tok != (1,) else "")
+        rep[key] = {"workload": w.name, "n_tok": n_tok, "us_per_step": round(us, 2),
+                    "weight_bytes": wbytes, "GBs": round(wbytes / us / 1e3, 1),
+                    "pct_hbm_peak": round(100 * wbytes / us / 1e3 / HBM_PEAK_GBS, 1),
+                    "resident": "hbm" if ncopy * wbytes >= ROTATE_BYTES else "cache",
+                    "launches_per_step": (1 if "gate" in names else 0) + sum(t.name not in ("gate", "up") for t in tens)}
+        if n_tok > 1:
+            flops = 2 * n_tok * sum(t.rows * t.cols for t in tens)
+            rep[key]["TFLOPs"] = round(flops / us / 1e6, 2)
+        del copies, g
+        torch.cuda.empty_cache()
+    return rep
 
 
 def main():
@@ -93,26 +231,27 @@ def main():
     def step(i, ev=None):
         g, u, dn = copies[i % ncopy]
         if ev is not None:
-            ev[0].record(stream)
+            ev.record(3 * i, sptr)
         qg.swiglu_gate_up("q4_0", g, u, xd, d_model, ffn, h=h, stream=sptr)
         if ev is not None:
-            ev[1].record(stream)
+            ev.record(3 * i + 1, sptr)
         qg.qgemv("q4_0", dn, h, d_model, ffn, y=out, stream=sptr)
         if ev is not None:
-            ev[2].record(stream)
+            ev.record(3 * i + 2, sptr)
 
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    evs = TimingEvents(3 * a.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(a.steps):
-        step(i, evs[i])
+        step(i, evs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gu_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    dn_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    gu_ms = [evs.ms(3 * i, 3 * i + 1) for i in range(a.steps)]
+    dn_ms = [evs.ms(3 * i + 1, 3 * i + 2) for i in range(a.steps)]
+    evs.close()
     ms_per_step = wall * 1e3 / a.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     gu_avg = float(np.mean(gu_ms))
@@ -158,11 +297,21 @@ def main():
                    "format": "q4_0", "d_model": d_model, "ffn": ffn, "n_tok": 1,
                    "weight_bytes_per_step": step_bytes, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "fused gate/up GEMV (gemv_kernel<Q4_0, NMAT=2>)",
                      "bytes_per_launch": gu_bytes},
         "detail": detail,
     }
+    if a.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if not a.no_workloads:
+        del copies
+        torch.cuda.empty_cache()
+        rec["workloads"] = workload_report(qg, synth, torch, np, dev)
     if not a.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(tens, x, w, a.cpu_seconds)
     print(json.dumps(rec), flush=True)
