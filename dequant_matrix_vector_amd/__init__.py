@@ -15,6 +15,7 @@ __all__ = [
     "FORMATS", "QGemvError", "lib", "packed_bytes", "max_cols", "repack",
     "qgemv", "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_k", "qgemv_i8row",
     "swiglu_gate_up", "swiglu_ffn", "qdequant", "layout_version", "set_launch_override",
+    "set_prefill_override", "swiglu_ffn_scratch_elems",
     "qgemv_repack_q4_0", "qgemv_repack_q8_0", "qgemv_repack_q4_k", "qgemv_repack_i8row",
 ]
 
@@ -50,10 +51,14 @@ lib.swiglu_gate_up.argtypes = [_I, _P, _P, _P, _P, _I64, _I64, _I64, _P]
 lib.swiglu_gate_up.restype = _I
 lib.swiglu_ffn.argtypes = [_I, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
 lib.swiglu_ffn.restype = _I
+lib.swiglu_ffn_scratch_elems.argtypes = [_I, _I64, _I64, _I64]
+lib.swiglu_ffn_scratch_elems.restype = _I64
 lib.qdequant.argtypes = [_I, _P, _P, _I64, _I64, _P]
 lib.qdequant.restype = _I
 lib.qgemv_set_launch_override.argtypes = [_I, _I, _I, _I, _I, _I]
 lib.qgemv_set_launch_override.restype = _I
+lib.qgemv_set_prefill_override.argtypes = [_I, _I, _I, _I, _I]
+lib.qgemv_set_prefill_override.restype = _I
 
 
 class QGemvError(RuntimeError):
@@ -118,6 +123,14 @@ def packed_bytes(fmt, rows, cols) -> int:
 def set_launch_override(lpr=0, r=0, waves=0, depth=2, max_wg=0, cpl=1):
     """Force a GEMV launch shape (tuning); lpr=0 restores the built-in choice."""
     _check(lib.qgemv_set_launch_override(lpr, r, waves, depth, max_wg, cpl), "qgemv_set_launch_override")
+
+
+def set_prefill_override(mtr=0, ntw=0, waves=0, run=0, ksplit=0):
+    """Force the matrix-core tile shape (Q4_0, n_tok > 1); mtr=0 restores the
+    built-in choice, mtr=-1 turns the matrix-core path off (per-token GEMV)."""
+    if mtr > 0 and run == 0:
+        run = 1
+    _check(lib.qgemv_set_prefill_override(mtr, ntw, waves, run, ksplit), "qgemv_set_prefill_override")
 
 
 # ------------------------------------------------------------- repack ------
@@ -204,15 +217,24 @@ def swiglu_gate_up(fmt, wg, wu, x, d_model, ffn, h=None, stream=None) -> torch.T
     return h
 
 
+def swiglu_ffn_scratch_elems(fmt, d_model, ffn, n_tok) -> int:
+    v = lib.swiglu_ffn_scratch_elems(_fmt(fmt), d_model, ffn, n_tok)
+    _check(v if v < 0 else 0, "swiglu_ffn_scratch_elems")
+    return v
+
+
 def swiglu_ffn(fmt, wg, wu, wd, x, d_model, ffn, out=None, h_scratch=None, stream=None):
-    """(out, h): out [n_tok][d_model] = Wd (silu(Wg x) * (Wu x)); h is the scratch."""
+    """(out, h): out [n_tok][d_model] = Wd (silu(Wg x) * (Wu x)); h [n_tok][ffn]
+    is a view of the scratch (allocated at swiglu_ffn_scratch_elems if None)."""
     n_tok = x.numel() // d_model
     out = _y(out, (n_tok, d_model), x.device)
-    h_scratch = _y(h_scratch, (n_tok, ffn), x.device)
+    if h_scratch is None:
+        h_scratch = torch.empty(swiglu_ffn_scratch_elems(fmt, d_model, ffn, n_tok), dtype=torch.float32,
+                                device=x.device)
     _dev(wg, wu, wd, x, out, h_scratch)
     _check(lib.swiglu_ffn(_fmt(fmt), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(x), _ptr(out), _ptr(h_scratch),
                           h_scratch.numel(), d_model, ffn, n_tok, _stream(stream)), "swiglu_ffn")
-    return out, h_scratch
+    return out, h_scratch.view(-1)[:n_tok * ffn].view(n_tok, ffn)
 
 
 def qdequant(fmt, packed, rows, cols, w_out=None, stream=None) -> torch.Tensor:

@@ -161,6 +161,11 @@ int qgemv(int fmt, const void *packed, const float *x, float *y, int64_t rows, i
     Layout L;
     int st = check_product(fmt, packed, x, y, rows, cols, n_tok, &L);
     if (st) return st;
+    if (fmt == QG_Q4_0 && n_tok > 1 && prefill_enabled())
+        return launch_prefill(1, static_cast<const uint8_t *>(packed), nullptr, x, y, rows, cols, n_tok, nullptr, 0,
+                              (hipStream_t)stream) == hipSuccess
+                   ? QG_OK
+                   : QG_ERR_LAUNCH;
     const GemvCfg cfg = choose_cfg(fmt, rows, cols, 1);
     for (int64_t t = 0; t < n_tok; t++) {
         if (launch_gemv(fmt, static_cast<const uint8_t *>(packed), x + t * cols, y + t * rows, rows, cols,
@@ -200,6 +205,11 @@ int swiglu_gate_up(int fmt, const void *wg, const void *wu, const float *x, floa
     if (!wu) return QG_ERR_NULL;
     if (!aligned(wu, kPlaneAlign)) return QG_ERR_ALIGN;
     if (overlap(wu, L.total, h, n_tok * ffn * 4)) return QG_ERR_ALIAS;
+    if (fmt == QG_Q4_0 && n_tok > 1 && prefill_enabled())
+        return launch_prefill(2, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), x, h, ffn,
+                              d_model, n_tok, nullptr, 0, (hipStream_t)stream) == hipSuccess
+                   ? QG_OK
+                   : QG_ERR_LAUNCH;
     const GemvCfg cfg = choose_cfg(fmt, ffn, d_model, 2);
     for (int64_t t = 0; t < n_tok; t++) {
         if (launch_gate_up(fmt, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu),
@@ -207,6 +217,28 @@ int swiglu_gate_up(int fmt, const void *wg, const void *wu, const float *x, floa
             return QG_ERR_LAUNCH;
     }
     return QG_OK;
+}
+
+// Scratch of swiglu_ffn, in floats: h [n_tok][ffn], then, from the next
+// 256-byte boundary, room for the partial sums of a K split on the matrix-core
+// path (Q4_0, n_tok > 1) -- the most that the gate/up or the down product uses.
+static int64_t ffn_part_offset(int64_t d_model, int64_t ffn, int64_t n_tok)
+{
+    (void)d_model;
+    return align_up(n_tok * ffn, kPlaneAlign / 4);
+}
+
+int64_t swiglu_ffn_scratch_elems(int fmt, int64_t d_model, int64_t ffn, int64_t n_tok)
+{
+    if (!valid_fmt(fmt)) return QG_ERR_FORMAT;
+    Layout La, Lb;
+    if (n_tok < 1 || n_tok >= (int64_t(1) << 31) || !layout_for(fmt, ffn, d_model, &La) ||
+        !layout_for(fmt, d_model, ffn, &Lb))
+        return QG_ERR_SHAPE;
+    if (fmt != QG_Q4_0 || n_tok == 1 || !prefill_enabled()) return n_tok * ffn;
+    const int64_t a = prefill_part_elems(2, ffn, d_model, n_tok), b = prefill_part_elems(1, d_model, ffn, n_tok);
+    const int64_t part = a > b ? a : b;
+    return part > 0 ? ffn_part_offset(d_model, ffn, n_tok) + part : n_tok * ffn;
 }
 
 int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const float *x, float *out,
@@ -226,15 +258,27 @@ int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const fl
     if (!aligned(wg, kPlaneAlign) || !aligned(wu, kPlaneAlign) || !aligned(wd, kPlaneAlign) || !aligned(x, 16) ||
         !aligned(out, 16) || !aligned(h_scratch, 16))
         return QG_ERR_ALIGN;
-    const int64_t xb = n_tok * d_model * 4, hb = n_tok * ffn * 4;
+    const int64_t xb = n_tok * d_model * 4, hb = h_scratch_elems * 4;
     if (overlap(x, xb, out, xb) || overlap(x, xb, h_scratch, hb) || overlap(out, xb, h_scratch, hb) ||
         overlap(wg, Lg.total, h_scratch, hb) || overlap(wu, Lg.total, h_scratch, hb) ||
         overlap(wd, Ld.total, h_scratch, hb) || overlap(wg, Lg.total, out, xb) || overlap(wu, Lg.total, out, xb) ||
         overlap(wd, Ld.total, out, xb))
         return QG_ERR_ALIAS;
+    hipStream_t s = (hipStream_t)stream;
+    if (fmt == QG_Q4_0 && n_tok > 1 && prefill_enabled()) {
+        // partial sums of a K split go behind h, when the caller's scratch has room
+        const int64_t po = ffn_part_offset(d_model, ffn, n_tok);
+        float *part = h_scratch_elems > po ? h_scratch + po : nullptr;
+        const int64_t pe = part ? h_scratch_elems - po : 0;
+        if (launch_prefill(2, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), x, h_scratch, ffn,
+                           d_model, n_tok, part, pe, s) != hipSuccess ||
+            launch_prefill(1, static_cast<const uint8_t *>(wd), nullptr, h_scratch, out, d_model, ffn, n_tok, part,
+                           pe, s) != hipSuccess)
+            return QG_ERR_LAUNCH;
+        return QG_OK;
+    }
     const GemvCfg cg = choose_cfg(fmt, ffn, d_model, 2);
     const GemvCfg cd = choose_cfg(fmt, d_model, ffn, 1);
-    hipStream_t s = (hipStream_t)stream;
     for (int64_t t = 0; t < n_tok; t++) {
         if (launch_gate_up(fmt, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), x + t * d_model,
                            h_scratch + t * ffn, ffn, d_model, s, cg) != hipSuccess)

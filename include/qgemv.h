@@ -107,8 +107,15 @@ int qgemv_repack_i8row(const int8_t *q, const float *row_scale, void *packed, in
 /* y[t][i] = sum_j Wdeq[i][j] * x[t][j] for t < n_tok, i < rows.
  * packed: made by the matching qgemv_repack_*; x: fp32 [n_tok][cols];
  * y: fp32 [n_tok][rows], overwritten.  x must not overlap y.
- * fp32 accumulation; n_tok == 1 runs the fused dequant-dot GEMV kernels,
- * n_tok > 1 the batched path. */
+ * n_tok == 1 runs the fused dequant-dot GEMV kernels: exact weights, fp32 x,
+ * fp32 accumulation.  n_tok > 1:
+ *  - Q4_0 runs on the matrix cores (llmoxide blog, section 11 "Prefill and
+ *    decode": with several tokens the product is a real GEMM, each weight
+ *    tile dequantized once for all tokens).  Weights and x are rounded to
+ *    bf16 (nearest even) and multiplied by v_mfma_f32_16x16x32_bf16 with fp32
+ *    accumulation: |y - exact| <= 8e-3 * sum_j |w_ij x_tj| + 1e-7.  One launch,
+ *    no workspace.
+ *  - the other formats loop the GEMV over the tokens (fp32 accuracy). */
 int qgemv_q4_0(const void *packed, const float *x, float *y, int64_t rows, int64_t cols,
                int64_t n_tok, void *stream);
 int qgemv_q8_0(const void *packed, const float *x, float *y, int64_t rows, int64_t cols,
@@ -125,19 +132,32 @@ int qgemv(int fmt, const void *packed, const float *x, float *y, int64_t rows, i
 /* First half of the SwiGLU block: h[t][i] = silu(Wg x)[t][i] * (Wu x)[t][i],
  * silu(g) = g / (1 + exp(-g)).  wg, wu: packed [ffn][d_model] of format fmt;
  * x: fp32 [n_tok][d_model]; h: fp32 [n_tok][ffn], overwritten, must not
- * overlap x. */
+ * overlap x.  Q4_0 with n_tok > 1 runs on the matrix cores as qgemv does,
+ * with silu(g) * u applied in the same kernel. */
 int swiglu_gate_up(int fmt, const void *wg, const void *wu, const float *x, float *h,
                    int64_t d_model, int64_t ffn, int64_t n_tok, void *stream);
 
 /* Whole SwiGLU block: out = Wd (silu(Wg x) * (Wu x)).
  * wd: packed [d_model][ffn]; x: fp32 [n_tok][d_model]; out: fp32
  * [n_tok][d_model], overwritten; h_scratch: caller-owned fp32 scratch of
- * h_scratch_elems >= n_tok*ffn elements, left holding h on return (so the
- * caller can inspect the intermediate).  x, out and h_scratch must be
- * pairwise disjoint.  Two launches on `stream`, no host synchronization. */
+ * h_scratch_elems >= n_tok*ffn elements, whose first n_tok*ffn elements hold
+ * h ([n_tok][ffn]) on return (so the caller can inspect the intermediate).
+ * On the matrix-core path (Q4_0, n_tok > 1) a scratch of
+ * swiglu_ffn_scratch_elems() elements (16-byte aligned) also holds the partial
+ * sums that let both products split their K dimension over more workgroups
+ * (deterministic: fixed summation order); with less, the products run
+ * unsplit, with the same accuracy bound.  x, out and the whole declared
+ * scratch must be pairwise disjoint.  Two launches on `stream` for n_tok == 1,
+ * up to four for Q4_0 with n_tok > 1, else two per token; no host
+ * synchronization. */
 int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const float *x,
                float *out, float *h_scratch, int64_t h_scratch_elems, int64_t d_model,
                int64_t ffn, int64_t n_tok, void *stream);
+
+/* Scratch elements (fp32) for which swiglu_ffn runs its fastest form on the
+ * current device: n_tok*ffn, plus room for partial sums on the matrix-core
+ * path.  Negative qg_status for an invalid shape or format. */
+int64_t swiglu_ffn_scratch_elems(int fmt, int64_t d_model, int64_t ffn, int64_t n_tok);
 
 /* Test export: the packed tensor decoded to fp32 [rows][cols] (each weight its
  * exact value rounded once to binary32).  Not used on the hot path. */
@@ -153,6 +173,19 @@ int qdequant(int fmt, const void *packed, float *w_out, int64_t rows, int64_t co
  * Process-global and not synchronized: set it only while no other thread is
  * enqueueing work.  Returns QG_ERR_SHAPE for values outside these sets. */
 int qgemv_set_launch_override(int lpr, int r, int waves, int depth, int max_wg, int cpl);
+
+/* Tuning hook for the matrix-core path (Q4_0, n_tok > 1): force 16-row tiles
+ * per wave and matrix (mtr 1 or 2), 16-token tiles per workgroup (ntw 1, 2, 4
+ * or 8), waves per workgroup (4 or 8), consecutive 32-weight blocks a lane
+ * reads from a row per pass (run 1, 2 or 4) and the number of K ranges
+ * (ksplit 1..64, 0 = built-in; honoured as far as the caller's scratch holds
+ * the partial sums, and never more than the passes over K).  A shape the
+ * library does not build (it would spill registers or overflow the LDS) runs
+ * as the nearest built one.  mtr == 0 restores the built-in choice; mtr == -1
+ * turns the matrix-core path off, so that n_tok > 1 loops the GEMV over the
+ * tokens (fp32 accuracy), for comparisons.  Same threading rule as
+ * qgemv_set_launch_override.  Returns QG_ERR_SHAPE for other values. */
+int qgemv_set_prefill_override(int mtr, int ntw, int waves, int run, int ksplit);
 
 #ifdef __cplusplus
 }

@@ -8,6 +8,21 @@ import oracle
 REL = 2e-5      # fp32 GEMV bound: |dy| <= REL * sum|w x| + ABS
 ABS = 1e-7
 SILU_REL = 1e-6  # budget for the device exp and divide in h = silu(g) * u
+# matrix-core path (Q4_0, n_tok > 1): weights and x rounded to bf16 (nearest
+# even) before fp32 accumulation, each term off by at most about 2 * 2^-9
+PF_REL = 8e-3
+
+
+def rel_for(fmt, n_tok):
+    """The bound's relative factor for a product of this format and batch."""
+    return PF_REL if (fmt == "q4_0" and n_tok > 1) else REL
+
+
+def bf16_rne(a):
+    """float32 values rounded to bfloat16, nearest even (finite inputs)."""
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32)
 
 
 def dev():
@@ -51,11 +66,30 @@ def silu64(g):
     return g / (1.0 + np.exp(-g))
 
 
-def h_bound(r):
-    """Per-element bound on h = silu(g) u from the GEMV bounds of g and u."""
+def h_bound(r, rel=REL):
+    """Per-element bound on h = silu(g) u from the product bounds of g and u."""
     g, u = r["g"], r["u"]
     sig = 1.0 / (1.0 + np.exp(-g))
     dsilu = sig * (1.0 + g * (1.0 - sig))
-    Bg = REL * r["Sg"] + ABS
-    Bu = REL * r["Su"] + ABS
+    Bg = rel * r["Sg"] + ABS
+    Bu = rel * r["Su"] + ABS
     return np.abs(dsilu * u) * Bg + np.abs(silu64(g)) * Bu + SILU_REL * np.abs(r["h"]) + 1e-30
+
+
+def check_ffn(fmt, tens, x, d_model, ffn, what):
+    rel = rel_for(fmt, x.shape[0])
+    g, u, d = tens
+    pk = [upload(t) for t in tens]
+    xd = torch.from_numpy(np.ascontiguousarray(x)).to(dev())
+    out, h = qg().swiglu_ffn(fmt, pk[0], pk[1], pk[2], xd, d_model, ffn)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    h = h.cpu().numpy()
+    r = oracle.swiglu(fmt, g.raw, u.raw, d.raw, x, d_model, ffn, g.row_scale, u.row_scale, d.row_scale)
+    # stage 1: h against silu(g) u of the oracle
+    hb = h_bound(r, rel)
+    assert np.all(np.abs(h - r["h"]) <= hb), f"{what}: h outside its bound"
+    # stage 2: out against the oracle's down projection of the device's own h
+    yr, S = oracle.gemv(fmt, d.raw, h, d_model, ffn, row_scale=d.row_scale)
+    check_bound(out, yr, S, rel=rel, what=f"{what} down")
+    return out, h, r, hb

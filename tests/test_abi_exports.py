@@ -68,3 +68,15 @@ def test_refusals_before_any_device_call(lib):
     assert lib.qgemv(0, fake, fake, fake, 0, 32, 1, None) == -2
     assert lib.qgemv(0, fake, fake, fake, 4, 32, 0, None) == -2
     assert lib.qgemv(2, fake, fake, fake, 4, 300, 1, None) == -2
+
+
+def test_prefill_override_validation(lib):
+    # host-only: the tile-shape hook validates its arguments without a device
+    f = lib.qgemv_set_prefill_override
+    f.argtypes = [ctypes.c_int] * 5
+    f.restype = ctypes.c_int
+    for bad in ((3, 1, 4, 2, 0), (1, 3, 4, 2, 0), (1, 1, 2, 2, 0), (2, 16, 8, 2, 0), (1, 1, 4, 3, 0),
+                (1, 1, 4, 8, 0), (1, 1, 4, 2, -1), (1, 1, 4, 2, 65)):
+        assert f(*bad) == -2, bad
+    assert f(2, 8, 4, 2, 0) == 0 and f(1, 2, 8, 4, 3) == 0 and f(1, 1, 8, 1, 0) == 0 and f(-1, 0, 0, 0, 0) == 0
+    assert f(0, 0, 0, 0, 0) == 0

@@ -80,15 +80,44 @@ def test_fullsize_swiglu_other_formats(wname, ffn_idx):
     G.check_bound(out, yr, S, what=f"{wname} down")
 
 
+def _row_samples(rows, k=128):
+    return (0, rows // 2 - k // 2, rows - k)
+
+
 def test_fullsize_cfg5_batched_tokens_sampled_rows():
-    # n_tok = 8 and 128 on the 27B-class gate matrix; the oracle checks a
-    # contiguous sample of rows at the start, middle and end of the matrix
+    # n_tok = 8 and 128 on the 27B-class gate matrix (matrix-core path); the
+    # oracle checks a contiguous sample of rows at the start, middle and end
     w = synth.CFG5
     t = synth.gen_tensor(w, 0)
     pk = G.upload(t)
     for n in (8, 128):
         x = synth.gen_x(w, w.d_model, n, which=10 + n)
         y = G.gemv_gpu(t, pk, x)
-        for r0 in (0, t.rows // 2 - 64, t.rows - 128):
+        for r0 in _row_samples(t.rows):
             yr, S = oracle.gemv(t.fmt, t.raw, x, t.rows, t.cols, row_begin=r0, row_end=r0 + 128)
-            G.check_bound(y[:, r0:r0 + 128], yr, S, what=f"cfg5 gate n_tok={n} rows {r0}..")
+            G.check_bound(y[:, r0:r0 + 128], yr, S, rel=G.PF_REL, what=f"cfg5 gate n_tok={n} rows {r0}..")
+
+
+@pytest.mark.parametrize("n_tok", [8, 128])
+def test_fullsize_cfg5_ffn_batched_sampled_rows(n_tok):
+    # the whole 27B-class FFN at n_tok = 8 and 128 through swiglu_ffn, in the
+    # launch configuration bench.py times: h on sampled rows against silu(g) u
+    # of the oracle, out on sampled rows against the oracle's down projection
+    # of the device's own h (all of h is an input there)
+    w = synth.CFG5
+    tens = synth.gen_workload(w)
+    pk = [G.upload(t) for t in tens]
+    x = synth.gen_x(w, w.d_model, n_tok, which=20 + n_tok)
+    xd = G.torch.from_numpy(x).to(G.dev())
+    out, h = G.qg().swiglu_ffn(tens[0].fmt, pk[0], pk[1], pk[2], xd, w.d_model, w.ffn)
+    G.torch.cuda.synchronize()
+    out, h = out.cpu().numpy(), h.cpu().numpy()
+    for r0 in _row_samples(w.ffn):
+        r = {}
+        r["g"], r["Sg"] = oracle.gemv(tens[0].fmt, tens[0].raw, x, w.ffn, w.d_model, row_begin=r0, row_end=r0 + 128)
+        r["u"], r["Su"] = oracle.gemv(tens[1].fmt, tens[1].raw, x, w.ffn, w.d_model, row_begin=r0, row_end=r0 + 128)
+        r["h"] = G.silu64(r["g"]) * r["u"]
+        assert np.all(np.abs(h[:, r0:r0 + 128] - r["h"]) <= G.h_bound(r, G.PF_REL)), f"h rows {r0}.. outside its bound"
+    for r0 in _row_samples(w.d_model):
+        yr, S = oracle.gemv(tens[2].fmt, tens[2].raw, h, w.d_model, w.ffn, row_begin=r0, row_end=r0 + 128)
+        G.check_bound(out[:, r0:r0 + 128], yr, S, rel=G.PF_REL, what=f"cfg5 down n_tok={n_tok} rows {r0}..")

@@ -129,7 +129,14 @@ def test_batched_tokens_match_single(fmt):
     x = np.random.default_rng(701).standard_normal((5, cols)).astype(np.float32)
     yb = G.gemv_gpu(t, packed, x)
     yr, S = oracle.gemv(fmt, t.raw, x, rows, cols, row_scale=t.row_scale)
-    G.check_bound(yb, yr, S, what=f"{fmt} n_tok=5")
+    G.check_bound(yb, yr, S, rel=G.rel_for(fmt, 5), what=f"{fmt} n_tok=5")
+    if fmt == "q4_0":
+        # the matrix-core path switched off: the GEMV loop, fp32 bound
+        try:
+            G.qg().set_prefill_override(-1)
+            G.check_bound(G.gemv_gpu(t, packed, x), yr, S, what=f"{fmt} n_tok=5 GEMV loop")
+        finally:
+            G.qg().set_prefill_override(0)
     for k in range(5):
         G.check_bound(G.gemv_gpu(t, packed, x[k]), yr[k], S[k], what=f"{fmt} token {k}")
 
@@ -211,30 +218,12 @@ def _ffn_tensors(fmt, d_model, ffn, seed):
             synth.make_tensor(fmt, d_model, ffn, rng)]
 
 
-def check_ffn(fmt, tens, x, d_model, ffn, what):
-    g, u, d = tens
-    pk = [G.upload(t) for t in tens]
-    xd = G.torch.from_numpy(np.ascontiguousarray(x)).to(G.dev())
-    out, h = G.qg().swiglu_ffn(fmt, pk[0], pk[1], pk[2], xd, d_model, ffn)
-    G.torch.cuda.synchronize()
-    out = out.cpu().numpy()
-    h = h.cpu().numpy()
-    r = oracle.swiglu(fmt, g.raw, u.raw, d.raw, x, d_model, ffn, g.row_scale, u.row_scale, d.row_scale)
-    # stage 1: h against silu(g) u of the oracle
-    hb = G.h_bound(r)
-    assert np.all(np.abs(h - r["h"]) <= hb), f"{what}: h outside its bound"
-    # stage 2: out against the oracle's down projection of the device's own h
-    yr, S = oracle.gemv(fmt, d.raw, h, d_model, ffn, row_scale=d.row_scale)
-    G.check_bound(out, yr, S, what=f"{what} down")
-    return out, h, r, hb
-
-
 @pytest.mark.parametrize("fmt", FMTS)
 def test_swiglu_small(fmt):
     d_model, ffn = (256, 768) if fmt == "q4_k" else (288, 768)
     tens = _ffn_tensors(fmt, d_model, ffn, 900)
     x = np.random.default_rng(901).standard_normal((1, d_model)).astype(np.float32)
-    out, h, r, hb = check_ffn(fmt, tens, x, d_model, ffn, f"ffn {fmt}")
+    out, h, r, hb = G.check_ffn(fmt, tens, x, d_model, ffn, f"ffn {fmt}")
     # end to end: the h error propagated through |Wd|
     wd = np.abs(oracle.dequant(fmt, tens[2].raw, d_model, ffn, row_scale=tens[2].row_scale).astype(np.float64))
     bound = G.REL * r["Sd"] + wd @ hb[0] + G.ABS
@@ -245,7 +234,7 @@ def test_swiglu_batched_tokens():
     d_model, ffn = 288, 768
     tens = _ffn_tensors("q4_0", d_model, ffn, 950)
     x = np.random.default_rng(951).standard_normal((3, d_model)).astype(np.float32)
-    check_ffn("q4_0", tens, x, d_model, ffn, "ffn q4_0 n_tok=3")
+    G.check_ffn("q4_0", tens, x, d_model, ffn, "ffn q4_0 n_tok=3")
 
 
 def test_swiglu_zero_gate_gives_zero():

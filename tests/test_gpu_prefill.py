@@ -1,0 +1,184 @@
+"""GPU parity of the matrix-core path (Q4_0, n_tok > 1) through the C ABI.
+
+Bars (per element), with S = sum_j |w_ij x_tj| from the oracle:
+  * y and the gate/up products: |y_gpu - y_ref| <= 8e-3 * S + 1e-7 (weights
+    and x rounded to bf16, nearest even, fp32 accumulation);
+  * inputs on which that rounding is exact (codes with power-of-two scales,
+    small-integer x) and whose partial sums are exact in fp32: bit-identical
+    to the oracle, under every tile shape -- this pins the column order the
+    two operands share;
+  * one-hot tokens: y[t][i] is the bf16 rounding (nearest even) of the
+    oracle's weight w[i][c_t], bit for bit;
+  * two runs bit-identical.
+Shapes cover ragged rows (not a multiple of 16, 64 or 4), columns that leave a
+partial 128-wide K step, token counts that leave a partial 16-token tile, and
+every tile shape the library can launch.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+# (rows, cols, n_tok)
+SHAPES = [(1, 32, 2), (5, 96, 3), (150, 288, 17), (131, 576, 16), (64, 1536, 40), (97, 5120, 33),
+          (300, 2048, 130), (40, 17408, 9)]
+# (mtr, ntw, waves, run): every shape the override accepts (shapes the library
+# does not build run as the nearest built one)
+TILES = list(itertools.product((1, 2), (1, 2, 4, 8), (4, 8), (1, 2, 4)))
+
+
+def _pow2_q4_0(rows, cols, rng, lo=-4, hi=3):
+    d = (2.0 ** rng.integers(lo, hi, (rows, cols // 32))).astype(np.float16)
+    return synth.QTensor("w", "q4_0", rows, cols, synth.pack_q4_0(d, rng.integers(0, 16, (rows, cols))))
+
+
+def _run(t, pk, x):
+    return G.gemv_gpu(t, pk, x)
+
+
+@pytest.mark.parametrize("rows,cols,n_tok", SHAPES)
+def test_prefill_within_bound(rows, cols, n_tok):
+    rng = np.random.default_rng(rows * 7 + cols + n_tok)
+    t = synth.make_tensor("q4_0", rows, cols, rng)
+    x = rng.standard_normal((n_tok, cols)).astype(np.float32)
+    y = _run(t, G.upload(t), x)
+    yr, S = oracle.gemv("q4_0", t.raw, x, rows, cols)
+    G.check_bound(y, yr, S, rel=G.PF_REL, what=f"prefill {rows}x{cols} n_tok={n_tok}")
+
+
+def test_prefill_integer_inputs_bit_exact_every_tile():
+    # |(q-8) d x| <= 8 * 4 * 3 and every value a multiple of 2^-4: every
+    # partial sum is exact in fp32, and bf16 holds every w and x exactly
+    rng = np.random.default_rng(1100)
+    rows, cols, n_tok = 150, 1056, 37     # 33 blocks: a partial K step
+    t = _pow2_q4_0(rows, cols, rng)
+    pk = G.upload(t)
+    x = rng.integers(-3, 4, (n_tok, cols)).astype(np.float32)
+    yr, _ = oracle.gemv("q4_0", t.raw, x, rows, cols)
+    try:
+        for tile in TILES:
+            G.qg().set_prefill_override(*tile)
+            y = _run(t, pk, x)
+            assert np.array_equal(y.astype(np.float64), yr), f"tile (mtr, ntw, waves, run) = {tile}"
+    finally:
+        G.qg().set_prefill_override(0)
+
+
+def test_prefill_gate_up_every_tile():
+    # h = silu(Wg x) * (Wu x) with exact products: only the device's exp and
+    # divide separate h from the oracle's
+    rng = np.random.default_rng(1200)
+    d_model, ffn, n_tok = 288, 200, 21
+    tg, tu = _pow2_q4_0(ffn, d_model, rng, -6, -3), _pow2_q4_0(ffn, d_model, rng, -6, -3)
+    pg, pu = G.upload(tg), G.upload(tu)
+    x = rng.integers(-3, 4, (n_tok, d_model)).astype(np.float32)
+    xd = G.torch.from_numpy(x).to(G.dev())
+    r = {}
+    r["g"], r["Sg"] = oracle.gemv("q4_0", tg.raw, x, ffn, d_model)
+    r["u"], r["Su"] = oracle.gemv("q4_0", tu.raw, x, ffn, d_model)
+    r["h"] = G.silu64(r["g"]) * r["u"]
+    hb = G.h_bound(r, rel=0.0)
+    try:
+        for tile in TILES:
+            G.qg().set_prefill_override(*tile)
+            h = G.qg().swiglu_gate_up("q4_0", pg, pu, xd, d_model, ffn)
+            G.torch.cuda.synchronize()
+            h = h.cpu().numpy()
+            assert np.all(np.abs(h - r["h"]) <= hb), f"tile (mtr, ntw, waves, run) = {tile}"
+    finally:
+        G.qg().set_prefill_override(0)
+
+
+def test_prefill_one_hot_tokens_give_bf16_weights():
+    # token t is one-hot at column 32*b_t + t: y[t][:] is column c_t of the
+    # weights rounded to bf16; all 32 positions of a block are covered
+    rng = np.random.default_rng(1300)
+    rows, cols = 70, 2048
+    t = synth.make_tensor("q4_0", rows, cols, rng)
+    nb = cols // 32
+    cs = np.array([32 * ((5 * k) % nb) + k for k in range(32)])
+    x = np.zeros((32, cols), np.float32)
+    x[np.arange(32), cs] = 1.0
+    y = _run(t, G.upload(t), x)
+    w32 = oracle.dequant("q4_0", t.raw, rows, cols).astype(np.float32)   # exact in fp32
+    want = G.bf16_rne(w32[:, cs]).T
+    assert np.array_equal(y, want)
+
+
+def test_prefill_deterministic():
+    rng = np.random.default_rng(1400)
+    rows, cols, n_tok = 300, 5120, 64
+    t = synth.make_tensor("q4_0", rows, cols, rng)
+    pk = G.upload(t)
+    x = rng.standard_normal((n_tok, cols)).astype(np.float32)
+    assert np.array_equal(_run(t, pk, x), _run(t, pk, x))
+
+
+def test_prefill_swiglu_ffn_batched():
+    # SmolLM2-135M-shaped FFN block at 40 tokens, both products on the matrix cores
+    d_model, ffn = 576, 1536
+    rng = np.random.default_rng(1500)
+    tens = [synth.make_tensor("q4_0", ffn, d_model, rng), synth.make_tensor("q4_0", ffn, d_model, rng),
+            synth.make_tensor("q4_0", d_model, ffn, rng)]
+    x = rng.standard_normal((40, d_model)).astype(np.float32)
+    G.check_ffn("q4_0", tens, x, d_model, ffn, "ffn q4_0 n_tok=40")
+
+
+def test_prefill_split_k_exact_and_deterministic():
+    # K split over workgroups (partials in the scratch behind h, summed in
+    # range order): with exact products, h is the same bit for bit for every
+    # split, and each split's out stays within the bound and repeats exactly
+    rng = np.random.default_rng(1600)
+    d_model, ffn, n_tok = 1056, 800, 21     # 9 and 7 K steps: ragged ranges
+    tg, tu = _pow2_q4_0(ffn, d_model, rng, -6, -3), _pow2_q4_0(ffn, d_model, rng, -6, -3)
+    td = synth.make_tensor("q4_0", d_model, ffn, rng)
+    pk = [G.upload(t) for t in (tg, tu, td)]
+    x = rng.integers(-3, 4, (n_tok, d_model)).astype(np.float32)
+    xd = G.torch.from_numpy(x).to(G.dev())
+    r = {}
+    r["g"], r["Sg"] = oracle.gemv("q4_0", tg.raw, x, ffn, d_model)
+    r["u"], r["Su"] = oracle.gemv("q4_0", tu.raw, x, ffn, d_model)
+    r["h"] = G.silu64(r["g"]) * r["u"]
+    hb = G.h_bound(r, rel=0.0)
+    po = (n_tok * ffn + 63) // 64 * 64
+    scratch = G.torch.empty(po + 9 * 2 * n_tok * max(ffn, d_model), dtype=G.torch.float32, device=G.dev())
+    h_ref = None
+    try:
+        for ks in (1, 2, 3, 4, 7, 9):
+            G.qg().set_prefill_override(1, 2, 4, 1, ks)
+            outs = []
+            for _ in range(2):
+                out, h = G.qg().swiglu_ffn("q4_0", pk[0], pk[1], pk[2], xd, d_model, ffn, h_scratch=scratch)
+                G.torch.cuda.synchronize()
+                outs.append(out.cpu().numpy())
+                h = h.cpu().numpy()
+            assert np.all(np.abs(h - r["h"]) <= hb), f"ksplit={ks}: h outside its bound"
+            if h_ref is None:
+                h_ref = h
+            assert np.array_equal(h, h_ref), f"ksplit={ks}: h differs from the unsplit h"
+            assert np.array_equal(outs[0], outs[1]), f"ksplit={ks}: not deterministic"
+            yr, S = oracle.gemv("q4_0", td.raw, h, d_model, ffn)
+            G.check_bound(outs[0], yr, S, rel=G.PF_REL, what=f"ksplit={ks} down")
+    finally:
+        G.qg().set_prefill_override(0)
+
+
+def test_prefill_default_split_uses_scratch():
+    # the built-in choice splits K for a narrow matrix at few tokens, and the
+    # binding sizes the scratch for it
+    ffn, d_model, n_tok = 17408, 512, 8
+    elems = G.qg().swiglu_ffn_scratch_elems("q4_0", d_model, ffn, n_tok)
+    assert elems > n_tok * ffn
+
+
+def test_prefill_override_rejects_bad_shapes():
+    for bad in ((3, 1, 4, 2, 0), (1, 3, 4, 2, 0), (1, 1, 2, 2, 0), (2, 16, 8, 2, 0), (1, 1, 4, 3, 0),
+                (1, 1, 4, 8, 0), (1, 1, 4, 2, -1), (1, 1, 4, 2, 65)):
+        assert G.qg().lib.qgemv_set_prefill_override(*bad) == -2, bad
+    G.qg().set_prefill_override(0)
