@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of MI355X
 ROTATE_BYTES = 1 << 30
 
 
@@ -148,21 +149,25 @@ def workload_report(qg, synth, torch, np, dev, graph_iters=20):
         names = [t.name for t in tens]
         xs = {c: torch.randn((n_tok, c), device=dev) for c in {t.cols for t in tens}}
         outs = {t.name: torch.empty((n_tok, t.rows), device=dev) for t in tens}
-        h = torch.empty((n_tok, w.ffn), device=dev)
+        ffn_names = ("gate", "up", "down")
+        is_ffn = all(n in names for n in ffn_names)
+        gi, ui, di = (names.index(n) for n in ffn_names) if is_ffn else (None, None, None)
+        # the FFN through swiglu_ffn, with the scratch that lets the matrix-core
+        # path split K (h is the scratch's first n_tok*ffn floats)
+        scratch = (torch.empty(qg.swiglu_ffn_scratch_elems(tens[gi].fmt, w.d_model, w.ffn, n_tok), device=dev)
+                   if is_ffn else None)
 
         def step(i):
             pk = copies[i % ncopy]
-            if "gate" in names and "up" in names:
-                gi, ui = names.index("gate"), names.index("up")
-                tg = tens[gi]
+            if is_ffn:
                 # stream=None: the binding takes torch's current stream, which is the
                 # capture stream inside the graph
-                qg.swiglu_gate_up(tg.fmt, pk[gi], pk[ui], xs[tg.cols], tg.cols, tg.rows, h=h)
+                qg.swiglu_ffn(tens[gi].fmt, pk[gi], pk[ui], pk[di], xs[w.d_model], w.d_model, w.ffn,
+                              out=outs["down"], h_scratch=scratch)
             for j, t in enumerate(tens):
-                if t.name in ("gate", "up"):
+                if t.name in ffn_names:
                     continue
-                xin = h if t.name == "down" else xs[t.cols]
-                qg.qgemv(t.fmt, pk[j], xin, t.rows, t.cols, y=outs[t.name])
+                qg.qgemv(t.fmt, pk[j], xs[t.cols], t.rows, t.cols, y=outs[t.name])
 
         for i in range(3):
             step(i)
@@ -186,10 +191,11 @@ def workload_report(qg, synth, torch, np, dev, graph_iters=20):
                     "weight_bytes": wbytes, "GBs": round(wbytes / us / 1e3, 1),
                     "pct_hbm_peak": round(100 * wbytes / us / 1e3 / HBM_PEAK_GBS, 1),
                     "resident": "hbm" if ncopy * wbytes >= ROTATE_BYTES else "cache",
-                    "launches_per_step": (1 if "gate" in names else 0) + sum(t.name not in ("gate", "up") for t in tens)}
+                    "path": "matrix cores (bf16 MFMA)" if (n_tok > 1 and tens[0].fmt == "q4_0") else "GEMV"}
         if n_tok > 1:
             flops = 2 * n_tok * sum(t.rows * t.cols for t in tens)
             rep[key]["TFLOPs"] = round(flops / us / 1e6, 2)
+            rep[key]["pct_bf16_mfma_peak"] = round(100 * flops / us / 1e6 / BF16_MFMA_PEAK_TFLOPS, 1)
         del copies, g
         torch.cuda.empty_cache()
     return rep

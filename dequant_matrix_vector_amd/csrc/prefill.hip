@@ -314,19 +314,36 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_0_kernel(PrefillParams p)
 }
 
 // y[t][i] = sum over K ranges of the partials, in range order (NMAT = 1), or
-// silu(g) * u of the two summed products (NMAT = 2).
-template <int NMAT>
+// silu(g) * u of the two summed products (NMAT = 2).  V outputs per thread
+// (4 when the element count allows 16-byte accesses).
+template <int NMAT, int V>
 __global__ void prefill_reduce_kernel(const float *__restrict__ part, float *__restrict__ y, int64_t n, int ksplit)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    typedef float fv __attribute__((ext_vector_type(V)));
+    const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * V;
     if (i >= n) return;
-    float s[NMAT];
+    fv s[NMAT];
 #pragma unroll
-    for (int m = 0; m < NMAT; m++) s[m] = 0.0f;
-    for (int k = 0; k < ksplit; k++)
+    for (int m = 0; m < NMAT; m++) s[m] = fv(0.0f);
+    int k = 0;
+    for (; k + 4 <= ksplit; k += 4) {   // four ranges' loads in flight, added in range order
+        fv v[4][NMAT];
 #pragma unroll
-        for (int m = 0; m < NMAT; m++) s[m] += part[((int64_t)k * NMAT + m) * n + i];
-    y[i] = NMAT == 1 ? s[0] : s[0] / (1.0f + expf(-s[0])) * s[NMAT - 1];
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int m = 0; m < NMAT; m++) v[j][m] = *reinterpret_cast<const fv *>(part + ((int64_t)(k + j) * NMAT + m) * n + i);
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int m = 0; m < NMAT; m++) s[m] += v[j][m];
+    }
+    for (; k < ksplit; k++)
+#pragma unroll
+        for (int m = 0; m < NMAT; m++) s[m] += *reinterpret_cast<const fv *>(part + ((int64_t)k * NMAT + m) * n + i);
+    fv r;
+#pragma unroll
+    for (int e = 0; e < V; e++) r[e] = NMAT == 1 ? s[0][e] : s[0][e] / (1.0f + expf(-s[0][e])) * s[NMAT - 1][e];
+    *reinterpret_cast<fv *>(y + i) = r;
 }
 
 // LDS of a workgroup: two bf16 x tiles plus one weight area per wave
@@ -351,8 +368,12 @@ hipError_t go_prefill(PrefillParams p, float *y, hipStream_t s)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.ksplit == 1) return e;
     const int64_t n = (int64_t)p.n_tok * p.rows;
-    hipLaunchKernelGGL(prefill_reduce_kernel<NMAT>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                       (const float *)p.y, y, n, p.ksplit);
+    if (n % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0)
+        hipLaunchKernelGGL((prefill_reduce_kernel<NMAT, 4>), dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
+                           (const float *)p.y, y, n, p.ksplit);
+    else
+        hipLaunchKernelGGL((prefill_reduce_kernel<NMAT, 1>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                           (const float *)p.y, y, n, p.ksplit);
     return hipGetLastError();
 }
 
@@ -383,10 +404,11 @@ constexpr bool pf_fits(int nmat, int mtr, int ntw, int waves, int run)
 }
 
 // The built-in tile choice (from sweeps on the 27B-class FFN at 8 and 128
-// tokens): one 16-row tile per matrix and wave, 4 waves, runs of one step, up
-// to 4 token tiles per workgroup (64 tokens share each decoded weight); then K
-// ranges until the grid has about four workgroups per CU (if the caller gave
-// room for the partials).
+// tokens): one 16-row tile per matrix and wave; up to 4 token tiles per
+// workgroup (64 tokens share each decoded weight) with 4 waves and runs of one
+// step, or, for a single token tile, 8 waves sharing it and runs of two steps;
+// then K ranges until the grid has about four workgroups per CU (if the caller
+// gave room for the partials).
 PrefillCfg choose(int nmat, int64_t rows, int64_t cols, int64_t n_tok, int64_t part_elems)
 {
     PrefillCfg c = g_pf_override;
@@ -396,6 +418,7 @@ PrefillCfg choose(int nmat, int64_t rows, int64_t cols, int64_t n_tok, int64_t p
         c.ntw = n_tiles >= 4 ? 4 : (n_tiles >= 2 ? 2 : 1);
         c.waves = 4;
         c.run = 1;
+        if (c.ntw == 1) c.waves = 8, c.run = 2;   // one token tile: 8 waves share each x tile
         c.ksplit = 0;
     }
     // a shape that is not built falls back to the nearest one that is: fewer
