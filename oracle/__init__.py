@@ -57,6 +57,11 @@ def _load():
     lib.oracle_gemv.restype = ctypes.c_int
     lib.oracle_gemv_f64x.argtypes = [ctypes.c_int, P, P, P, I64, I64, I64, P, P]
     lib.oracle_gemv_f64x.restype = ctypes.c_int
+    lib.oracle_rmsnorm.argtypes = [P, P, I64, I64, ctypes.c_double, P, P]
+    lib.oracle_rmsnorm.restype = ctypes.c_int
+    lib.oracle_ffn_block.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, ctypes.c_double, P, I64, I64, I64,
+                                     P, P, P, P, P, P, P, P, P]
+    lib.oracle_ffn_block.restype = ctypes.c_int
     lib.oracle_silu.argtypes = [ctypes.c_double]
     lib.oracle_silu.restype = ctypes.c_double
     lib.oracle_swiglu.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, I64, I64, I64,
@@ -159,4 +164,37 @@ def swiglu(fmt, wg, wu, wd, x, d_model, ffn, sg=None, su=None, sd=None):
                                  _ptr(sd), _ptr(x), d_model, ffn, n_tok,
                                  _ptr(r["g"]), _ptr(r["u"]), _ptr(r["h"]), _ptr(r["out"]),
                                  _ptr(r["Sg"]), _ptr(r["Su"]), _ptr(r["Sd"])), "swiglu")
+    return r
+
+
+def rmsnorm(x, gamma, eps):
+    """(xn, scale): float64 [n_tok][n] and [n_tok] for float32 x [n_tok][n] (or [n])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    squeeze = x.ndim == 1
+    n = x.shape[-1]
+    x2 = x.reshape(-1, n)
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    assert gamma.shape == (n,)
+    out = np.empty(x2.shape, dtype=np.float64)
+    scale = np.empty(x2.shape[0], dtype=np.float64)
+    _check(_load().oracle_rmsnorm(_ptr(x2), _ptr(gamma), n, x2.shape[0], float(eps), _ptr(out), _ptr(scale)),
+           "rmsnorm")
+    return (out[0], scale[0]) if squeeze else (out, scale)
+
+
+def ffn_block(fmt, wg, wu, wd, gamma, eps, x, d_model, ffn, sg=None, su=None, sd=None):
+    """Dict of float64 arrays xn, g, u, h, d, out, Sg, Su, Sd: out = x + Wd(silu(Wg xn)(Wu xn)),
+    xn = rmsnorm(x) * gamma."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1, d_model)
+    n_tok = x.shape[0]
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    r = {k: np.empty((n_tok, ffn), dtype=np.float64) for k in ("g", "u", "h", "Sg", "Su")}
+    for k in ("xn", "d", "out", "Sd"):
+        r[k] = np.empty((n_tok, d_model), dtype=np.float64)
+    wg, wu, wd = _raw(wg), _raw(wu), _raw(wd)
+    sg, su, sd = _scale(sg), _scale(su), _scale(sd)
+    _check(_load().oracle_ffn_block(_fmt(fmt), _ptr(wg), _ptr(sg), _ptr(wu), _ptr(su), _ptr(wd), _ptr(sd),
+                                    _ptr(gamma), float(eps), _ptr(x), d_model, ffn, n_tok,
+                                    _ptr(r["xn"]), _ptr(r["g"]), _ptr(r["u"]), _ptr(r["h"]), _ptr(r["d"]),
+                                    _ptr(r["out"]), _ptr(r["Sg"]), _ptr(r["Su"]), _ptr(r["Sd"])), "ffn_block")
     return r

@@ -36,6 +36,12 @@
  * SwiGLU (section 2 of the llmoxide blog; section 8.7.1.6.3 of dasLLAMA-00):
  *   g = Wg x, u = Wu x, h_j = g_j / (1 + exp(-g_j)) * u_j, out = Wd h.
  *
+ * RMSNorm (section 4 "Keeping the numbers in range" of the llmoxide blog; the
+ * rmsnorm of dasLLAMA-00's "Five small functions"): the mean of the squares
+ * over the row, scale = 1 / sqrt(mean + eps), out_j = x_j * scale * gamma_j.
+ * The FFN block of the residual stream (section 7 "The block, and the
+ * residual stream", same blog): out = x + FFN(rmsnorm(x) * gamma).
+ *
  * Parity pins for every function live in tests/test_oracle_*.py.
  */
 #include <math.h>
@@ -257,4 +263,55 @@ int oracle_swiglu(int fmt, const void *wg, const float *sg, const void *wu, cons
     for (int64_t i = 0; i < n_tok * ffn; i++)
         h[i] = oracle_silu(g[i]) * u[i];
     return oracle_gemv_f64x(fmt, wd, sd, h, d_model, ffn, n_tok, out, Sd);
+}
+
+/* RMSNorm of each token row, binary64: scale[t] = 1/sqrt(sum_j x_j^2 / n + eps),
+ * out[t][j] = x[t][j] * scale[t] * gamma[j].  x float [n_tok][n]. */
+int oracle_rmsnorm(const float *x, const float *gamma, int64_t n, int64_t n_tok, double eps, double *out,
+                   double *scale)
+{
+    if (n < 1 || n_tok < 0)
+        return OR_ERR_SHAPE;
+    for (int64_t t = 0; t < n_tok; t++) {
+        const float *xt = x + t * n;
+        double ss = 0.0;
+        for (int64_t j = 0; j < n; j++)
+            ss += (double)xt[j] * (double)xt[j];
+        const double sc = 1.0 / sqrt(ss / (double)n + eps);
+        scale[t] = sc;
+        for (int64_t j = 0; j < n; j++)
+            out[t * n + j] = (double)xt[j] * sc * (double)gamma[j];
+    }
+    return OR_OK;
+}
+
+/* The FFN block: xn = rmsnorm(x) * gamma; g = Wg xn, u = Wu xn, h = silu(g) u,
+ * d = Wd h, out = x + d.  All outputs binary64, token-major; xn [n_tok][d_model],
+ * g, u, h, Sg, Su [n_tok][ffn], d, out, Sd [n_tok][d_model]. */
+int oracle_ffn_block(int fmt, const void *wg, const float *sg, const void *wu, const float *su,
+                     const void *wd, const float *sd, const float *gamma, double eps, const float *x,
+                     int64_t d_model, int64_t ffn, int64_t n_tok, double *xn, double *g, double *u,
+                     double *h, double *d, double *out, double *Sg, double *Su, double *Sd)
+{
+    double *scale = (double *)malloc(sizeof(double) * (size_t)(n_tok > 0 ? n_tok : 1));
+    if (!scale)
+        return OR_ERR_NOMEM;
+    int st = oracle_rmsnorm(x, gamma, d_model, n_tok, eps, xn, scale);
+    free(scale);
+    if (st)
+        return st;
+    st = oracle_gemv_f64x(fmt, wg, sg, xn, ffn, d_model, n_tok, g, Sg);
+    if (st)
+        return st;
+    st = oracle_gemv_f64x(fmt, wu, su, xn, ffn, d_model, n_tok, u, Su);
+    if (st)
+        return st;
+    for (int64_t i = 0; i < n_tok * ffn; i++)
+        h[i] = oracle_silu(g[i]) * u[i];
+    st = oracle_gemv_f64x(fmt, wd, sd, h, d_model, ffn, n_tok, d, Sd);
+    if (st)
+        return st;
+    for (int64_t i = 0; i < n_tok * d_model; i++)
+        out[i] = (double)x[i] + d[i];
+    return OR_OK;
 }

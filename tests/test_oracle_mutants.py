@@ -14,7 +14,8 @@ import pytest
 from oracle import build as obuild
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-PIN_FILES = ["tests/test_oracle_decode.py", "tests/test_oracle_gemv.py", "tests/test_oracle_swiglu.py"]
+PIN_FILES = ["tests/test_oracle_decode.py", "tests/test_oracle_gemv.py", "tests/test_oracle_swiglu.py",
+             "tests/test_oracle_norm.py"]
 
 MUTANTS = {
     "f16_exponent_bias": ("ldexp((double)(1024 + m), e - 25)", "ldexp((double)(1024 + m), e - 24)"),
@@ -36,7 +37,13 @@ MUTANTS = {
     "gemv_dropped_x": ("double p = row[j] * (double)xt[j];", "double p = row[j];"),
     "gemv_signed_magnitude": ("mag += fabs(p);\n            }\n            y[t * nr", "mag += p;\n            }\n            y[t * nr"),
     "silu_sign": ("return g / (1.0 + exp(-g));", "return g / (1.0 + exp(g));"),
-    "swiglu_gate_up_swapped": ("h[i] = oracle_silu(g[i]) * u[i];", "h[i] = oracle_silu(u[i]) * g[i];"),
+    "swiglu_gate_up_swapped": ("h[i] = oracle_silu(g[i]) * u[i];\n    return", "h[i] = oracle_silu(u[i]) * g[i];\n    return"),
+    "rmsnorm_eps_outside_root": ("1.0 / sqrt(ss / (double)n + eps)", "1.0 / (sqrt(ss / (double)n) + eps)"),
+    "rmsnorm_sum_not_mean": ("sqrt(ss / (double)n + eps)", "sqrt(ss + eps)"),
+    "rmsnorm_gain_dropped": ("* sc * (double)gamma[j]", "* sc"),
+    "rmsnorm_scale_dropped": ("(double)xt[j] * sc * (double)gamma[j]", "(double)xt[j] * (double)gamma[j]"),
+    "block_residual_dropped": ("out[i] = (double)x[i] + d[i];", "out[i] = d[i];"),
+    "block_gate_up_swapped": ("h[i] = oracle_silu(g[i]) * u[i];\n    st =", "h[i] = oracle_silu(u[i]) * g[i];\n    st ="),
 }
 
 
