@@ -15,7 +15,7 @@ __all__ = [
     "FORMATS", "QGemvError", "lib", "packed_bytes", "max_cols", "repack",
     "qgemv", "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_k", "qgemv_i8row",
     "swiglu_gate_up", "swiglu_ffn", "qdequant", "layout_version", "set_launch_override",
-    "set_prefill_override", "swiglu_ffn_scratch_elems",
+    "set_prefill_override", "swiglu_ffn_scratch_elems", "swiglu_ffn_block", "swiglu_ffn_block_scratch_elems",
     "qgemv_repack_q4_0", "qgemv_repack_q8_0", "qgemv_repack_q4_k", "qgemv_repack_i8row",
 ]
 
@@ -53,6 +53,10 @@ lib.swiglu_ffn.argtypes = [_I, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _
 lib.swiglu_ffn.restype = _I
 lib.swiglu_ffn_scratch_elems.argtypes = [_I, _I64, _I64, _I64]
 lib.swiglu_ffn_scratch_elems.restype = _I64
+lib.swiglu_ffn_block.argtypes = [_I, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
+lib.swiglu_ffn_block.restype = _I
+lib.swiglu_ffn_block_scratch_elems.argtypes = [_I, _I64, _I64, _I64]
+lib.swiglu_ffn_block_scratch_elems.restype = _I64
 lib.qdequant.argtypes = [_I, _P, _P, _I64, _I64, _P]
 lib.qdequant.restype = _I
 lib.qgemv_set_launch_override.argtypes = [_I, _I, _I, _I, _I, _I]
@@ -242,3 +246,25 @@ def qdequant(fmt, packed, rows, cols, w_out=None, stream=None) -> torch.Tensor:
     _dev(packed, w_out)
     _check(lib.qdequant(_fmt(fmt), _ptr(packed), _ptr(w_out), rows, cols, _stream(stream)), "qdequant")
     return w_out
+
+
+def swiglu_ffn_block_scratch_elems(fmt, d_model, ffn, n_tok) -> int:
+    v = lib.swiglu_ffn_block_scratch_elems(_fmt(fmt), d_model, ffn, n_tok)
+    _check(v if v < 0 else 0, "swiglu_ffn_block_scratch_elems")
+    return v
+
+
+def swiglu_ffn_block(fmt, wg, wu, wd, gamma, eps, x, d_model, ffn, out=None, h_scratch=None, stream=None):
+    """(out, h): out = x + Wd (silu(Wg xn) * (Wu xn)), xn = rmsnorm(x) * gamma; out may be x
+    (in place).  h [n_tok][ffn] is a view of the scratch (allocated at
+    swiglu_ffn_block_scratch_elems if None)."""
+    n_tok = x.numel() // d_model
+    out = _y(out, (n_tok, d_model), x.device)
+    if h_scratch is None:
+        h_scratch = torch.empty(swiglu_ffn_block_scratch_elems(fmt, d_model, ffn, n_tok), dtype=torch.float32,
+                                device=x.device)
+    _dev(wg, wu, wd, gamma, x, out, h_scratch)
+    _check(lib.swiglu_ffn_block(_fmt(fmt), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(gamma), float(eps), _ptr(x), _ptr(out),
+                                _ptr(h_scratch), h_scratch.numel(), d_model, ffn, n_tok, _stream(stream)),
+           "swiglu_ffn_block")
+    return out, h_scratch.view(-1)[:n_tok * ffn].view(n_tok, ffn)

@@ -292,6 +292,88 @@ int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const fl
     return QG_OK;
 }
 
+// Scratch of swiglu_ffn_block, in floats: h [n_tok][ffn]; on the matrix-core
+// path (Q4_0, n_tok > 1) then the normalized input [n_tok][d_model] and room
+// for split-K partial sums, each from a 256-byte boundary.
+static bool block_on_matrix_cores(int fmt, int64_t n_tok) { return fmt == QG_Q4_0 && n_tok > 1 && prefill_enabled(); }
+
+static int64_t block_xn_offset(int64_t ffn, int64_t n_tok) { return align_up(n_tok * ffn, kPlaneAlign / 4); }
+
+static int64_t block_part_offset(int64_t d_model, int64_t ffn, int64_t n_tok)
+{
+    return align_up(block_xn_offset(ffn, n_tok) + n_tok * d_model, kPlaneAlign / 4);
+}
+
+int64_t swiglu_ffn_block_scratch_elems(int fmt, int64_t d_model, int64_t ffn, int64_t n_tok)
+{
+    if (!valid_fmt(fmt)) return QG_ERR_FORMAT;
+    Layout La, Lb;
+    if (n_tok < 1 || n_tok >= (int64_t(1) << 31) || !layout_for(fmt, ffn, d_model, &La) ||
+        !layout_for(fmt, d_model, ffn, &Lb))
+        return QG_ERR_SHAPE;
+    if (!block_on_matrix_cores(fmt, n_tok)) return n_tok * ffn;
+    const int64_t a = prefill_part_elems(2, ffn, d_model, n_tok), b = prefill_part_elems(1, d_model, ffn, n_tok);
+    const int64_t part = a > b ? a : b;
+    return part > 0 ? block_part_offset(d_model, ffn, n_tok) + part : block_xn_offset(ffn, n_tok) + n_tok * d_model;
+}
+
+int swiglu_ffn_block(int fmt, const void *wg, const void *wu, const void *wd, const float *gamma, float eps,
+                     const float *x, float *out, float *h_scratch, int64_t h_scratch_elems, int64_t d_model,
+                     int64_t ffn, int64_t n_tok, void *stream)
+{
+    if (!valid_fmt(fmt)) return QG_ERR_FORMAT;
+    if (!wg || !wu || !wd || !gamma || !x || !out || !h_scratch) return QG_ERR_NULL;
+    Layout Lg, Ld;
+    if (n_tok < 1 || n_tok >= (int64_t(1) << 31) || !layout_for(fmt, ffn, d_model, &Lg) ||
+        !layout_for(fmt, d_model, ffn, &Ld) || !(eps >= 0.0f) || !(eps <= 3.0e38f))
+        return QG_ERR_SHAPE;
+    const int64_t mc = max_cols_current();
+    if (mc < 0) return (int)mc;
+    if (d_model > mc || ffn > mc) return QG_ERR_SHAPE;
+    const bool mfma = block_on_matrix_cores(fmt, n_tok);
+    const int64_t need = mfma ? block_xn_offset(ffn, n_tok) + n_tok * d_model : n_tok * ffn;
+    if (h_scratch_elems < need) return QG_ERR_SCRATCH;
+    if (!aligned(wg, kPlaneAlign) || !aligned(wu, kPlaneAlign) || !aligned(wd, kPlaneAlign) || !aligned(x, 16) ||
+        !aligned(out, 16) || !aligned(h_scratch, 16) || !aligned(gamma, 16))
+        return QG_ERR_ALIGN;
+    const int64_t xb = n_tok * d_model * 4, hb = h_scratch_elems * 4, gb = d_model * 4;
+    // out may be x itself (the residual stream updated in place) but not partly overlap it
+    if ((out != x && overlap(x, xb, out, xb)) || overlap(x, xb, h_scratch, hb) || overlap(out, xb, h_scratch, hb) ||
+        overlap(gamma, gb, out, xb) || overlap(gamma, gb, h_scratch, hb) || overlap(wg, Lg.total, h_scratch, hb) ||
+        overlap(wu, Lg.total, h_scratch, hb) || overlap(wd, Ld.total, h_scratch, hb) || overlap(wg, Lg.total, out, xb) ||
+        overlap(wu, Lg.total, out, xb) || overlap(wd, Ld.total, out, xb))
+        return QG_ERR_ALIAS;
+    hipStream_t s = (hipStream_t)stream;
+    if (mfma) {
+        // normalized input and partial sums behind h in the scratch
+        float *xn = h_scratch + block_xn_offset(ffn, n_tok);
+        const int64_t po = block_part_offset(d_model, ffn, n_tok);
+        float *part = h_scratch_elems > po ? h_scratch + po : nullptr;
+        const int64_t pe = part ? h_scratch_elems - po : 0;
+        if (launch_rmsnorm(x, gamma, eps, xn, d_model, n_tok, s) != hipSuccess ||
+            launch_prefill(2, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), xn, h_scratch, ffn,
+                           d_model, n_tok, part, pe, s) != hipSuccess ||
+            launch_prefill(1, static_cast<const uint8_t *>(wd), nullptr, h_scratch, out, d_model, ffn, n_tok, part,
+                           pe, s, x) != hipSuccess)
+            return QG_ERR_LAUNCH;
+        return QG_OK;
+    }
+    const GemvCfg cg = choose_cfg(fmt, ffn, d_model, 2);
+    const GemvCfg cd = choose_cfg(fmt, d_model, ffn, 1);
+    // every token's gate/up (which read x) before any down (which may overwrite x)
+    for (int64_t t = 0; t < n_tok; t++) {
+        if (launch_gate_up(fmt, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), x + t * d_model,
+                           h_scratch + t * ffn, ffn, d_model, s, cg, gamma, eps) != hipSuccess)
+            return QG_ERR_LAUNCH;
+    }
+    for (int64_t t = 0; t < n_tok; t++) {
+        if (launch_gemv(fmt, static_cast<const uint8_t *>(wd), h_scratch + t * ffn, out + t * d_model, d_model, ffn,
+                        s, cd, x + t * d_model) != hipSuccess)
+            return QG_ERR_LAUNCH;
+    }
+    return QG_OK;
+}
+
 int qdequant(int fmt, const void *packed, float *w_out, int64_t rows, int64_t cols, void *stream)
 {
     if (!valid_fmt(fmt)) return QG_ERR_FORMAT;

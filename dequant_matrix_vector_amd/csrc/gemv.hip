@@ -12,12 +12,20 @@ namespace {
 template <int NMAT>
 hipError_t dispatch_fmt(int fmt, const GemvParams &p, const GemvCfg &c, hipStream_t s)
 {
+    // NMAT 1 with a residual, NMAT 2 with a normalized input, else plain
+    const int epi = (NMAT == 1 && p.resid) ? 2 : ((NMAT == 2 && p.gamma) ? 1 : 0);
+#define QG_FMT(F)                                                                                  \
+    case F:                                                                                        \
+        if (epi == 0) return gemv_dispatch<F, NMAT, 0>(p, c, s);                                   \
+        if constexpr (NMAT == 2) return gemv_dispatch<F, 2, 1>(p, c, s);                           \
+        else return gemv_dispatch<F, 1, 2>(p, c, s);
     switch (fmt) {
-    case QG_Q4_0: return gemv_dispatch<QG_Q4_0, NMAT>(p, c, s);
-    case QG_Q8_0: return gemv_dispatch<QG_Q8_0, NMAT>(p, c, s);
-    case QG_Q4_K: return gemv_dispatch<QG_Q4_K, NMAT>(p, c, s);
-    case QG_I8ROW: return gemv_dispatch<QG_I8ROW, NMAT>(p, c, s);
+        QG_FMT(QG_Q4_0)
+        QG_FMT(QG_Q8_0)
+        QG_FMT(QG_Q4_K)
+        QG_FMT(QG_I8ROW)
     }
+#undef QG_FMT
     return hipErrorInvalidValue;
 }
 
@@ -114,7 +122,7 @@ GemvCfg choose_cfg(int fmt, int64_t rows, int64_t cols, int nmat)
 }
 
 hipError_t launch_gemv(int fmt, const uint8_t *packed, const float *x, float *y, int64_t rows,
-                       int64_t cols, hipStream_t s, const GemvCfg &cfg)
+                       int64_t cols, hipStream_t s, const GemvCfg &cfg, const float *resid)
 {
     Layout L;
     if (!layout_for(fmt, rows, cols, &L)) return hipErrorInvalidValue;
@@ -127,11 +135,15 @@ hipError_t launch_gemv(int fmt, const uint8_t *packed, const float *x, float *y,
     p.row_qbytes = L.row_qbytes;
     p.soff = L.splane_off;
     p.nchunk = (int)(cols / kChunk);
+    p.gamma = nullptr;
+    p.eps = 0.0f;
+    p.resid = resid;
     return dispatch_fmt<1>(fmt, p, aligned_cfg(fmt, p.nchunk, cfg), s);
 }
 
 hipError_t launch_gate_up(int fmt, const uint8_t *wg, const uint8_t *wu, const float *x, float *h,
-                          int64_t ffn, int64_t d_model, hipStream_t s, const GemvCfg &cfg)
+                          int64_t ffn, int64_t d_model, hipStream_t s, const GemvCfg &cfg, const float *gamma,
+                          float eps)
 {
     Layout L;
     if (!layout_for(fmt, ffn, d_model, &L)) return hipErrorInvalidValue;
@@ -144,6 +156,9 @@ hipError_t launch_gate_up(int fmt, const uint8_t *wg, const uint8_t *wu, const f
     p.row_qbytes = L.row_qbytes;
     p.soff = L.splane_off;
     p.nchunk = (int)(d_model / kChunk);
+    p.gamma = gamma;
+    p.eps = eps;
+    p.resid = nullptr;
     return dispatch_fmt<2>(fmt, p, aligned_cfg(fmt, p.nchunk, cfg), s);
 }
 

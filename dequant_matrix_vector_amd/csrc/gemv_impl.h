@@ -34,6 +34,13 @@
 //
 // 8-bit decode (Q8_0, I8ROW): each signed byte converts with one SDWA
 // v_cvt_f32_i32 (sign-extending byte select) and feeds one fma.
+//
+// Epilogue variants (EPI): 0 plain; 1 (gate/up) the input is RMS-normalized
+// with a per-element gain (llmoxide blog, section 4 "Keeping the numbers in
+// range"): the workgroup stages x*gamma and sums x^2 while staging, and the
+// per-token scale 1/sqrt(mean(x^2) + eps) multiplies the finished dot products
+// (it factors out of every row's sum); 2 (down) adds the residual stream
+// (section 7 "The block, and the residual stream").
 #pragma once
 #include <atomic>
 #include <type_traits>
@@ -52,7 +59,12 @@ struct GemvParams {
     int64_t row_qbytes;
     int64_t soff;         // scale plane offset inside each packed tensor
     int nchunk;           // cols / 32
+    const float *gamma;   // EPI 1: RMSNorm gain [cols]
+    float eps;            // EPI 1: RMSNorm epsilon
+    const float *resid;   // EPI 2: residual [rows], added to y (may be y itself)
 };
+
+enum { kEpiPlain = 0, kEpiNorm = 1, kEpiResid = 2 };
 
 __device__ __forceinline__ float half_lo(uint32_t v)
 {
@@ -124,11 +136,17 @@ template <> struct Fmt<QG_I8ROW> { static constexpr bool kPrescale = false; stat
 // for those, the chunk sum in the decode order.  A thread issues the loads of
 // its first two chunks before anything else (so they are not queued behind
 // the weight stream) and finishes them after the first weight loads are out.
-struct XStage {
+template <bool NORM> struct XStage {
     float4 v[2][8];
 };
+template <> struct XStage<true> {
+    float4 v[2][8];
+    float4 gm[2][8];   // the gain of the same chunks
+};
 
-__device__ __forceinline__ void stage_issue(const float *__restrict__ x, int nchunk, XStage &st)
+template <bool NORM>
+__device__ __forceinline__ void stage_issue(const float *__restrict__ x, const float *__restrict__ gamma, int nchunk,
+                                            XStage<NORM> &st)
 {
 #pragma unroll
     for (int u = 0; u < 2; u++) {
@@ -137,13 +155,36 @@ __device__ __forceinline__ void stage_issue(const float *__restrict__ x, int nch
         const float4 *src = reinterpret_cast<const float4 *>(x + (int64_t)c * kChunk);
 #pragma unroll
         for (int k = 0; k < 8; k++) st.v[u][k] = src[k];
+        if constexpr (NORM) {
+            const float4 *gs = reinterpret_cast<const float4 *>(gamma + (int64_t)c * kChunk);
+#pragma unroll
+            for (int k = 0; k < 8; k++) st.gm[u][k] = gs[k];
+        }
     }
 }
+
+// sum of the squares of one chunk (raw x), in column order
+__device__ __forceinline__ float chunk_sumsq(const float4 (&v)[8])
+{
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        s = __builtin_fmaf(v[k].x, v[k].x, s);
+        s = __builtin_fmaf(v[k].y, v[k].y, s);
+        s = __builtin_fmaf(v[k].z, v[k].z, s);
+        s = __builtin_fmaf(v[k].w, v[k].w, s);
+    }
+    return s;
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <bool kPrescale>
 __device__ __forceinline__ void stage_store(float4 (&v)[8], float *xs, int c)
 {
-    float4 *dst = reinterpret_cast<float4 *>(xs + c * kXStride);
+    // stores through a native vector type: a whole-struct float4 copy becomes a
+    // memcpy, which keeps the staging registers out of registers (in scratch)
+    f32x4 *dst = reinterpret_cast<f32x4 *>(xs + c * kXStride);
     if (kPrescale) {
         float sum = 0.0f;
 #pragma unroll
@@ -168,11 +209,30 @@ __device__ __forceinline__ void stage_store(float4 (&v)[8], float *xs, int c)
         xs[c * kXStride + 32] = sum;
     }
 #pragma unroll
-    for (int k = 0; k < 8; k++) dst[k] = v[k];
+    for (int k = 0; k < 8; k++) dst[k] = f32x4{v[k].x, v[k].y, v[k].z, v[k].w};
 }
 
-template <bool kPrescale>
-__device__ __forceinline__ void stage_finish(const float *__restrict__ x, float *xs, int nchunk, XStage &st)
+// x (times the gain, NORM) -> chunk c of the staging area; NORM adds the raw
+// chunk's sum of squares to ss when `count` (false for the clamped duplicate)
+template <bool kPrescale, bool NORM>
+__device__ __forceinline__ void stage_chunk(float4 (&v)[8], const float4 *gm, float *xs, int c, bool count, float &ss)
+{
+    if constexpr (NORM) {
+        const float q = chunk_sumsq(v);
+        ss += count ? q : 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            v[k].x *= gm[k].x;
+            v[k].y *= gm[k].y;
+            v[k].z *= gm[k].z;
+            v[k].w *= gm[k].w;
+        }
+    }
+    stage_store<kPrescale>(v, xs, c);
+}
+
+template <bool kPrescale, bool NORM>
+__device__ __forceinline__ void stage_finish(float *xs, int nchunk, XStage<NORM> &st, float &ss)
 {
     // Branch-free for the first two chunks of each thread (an out-of-range
     // thread writes to the spare slot after the last chunk): a divergent
@@ -181,21 +241,25 @@ __device__ __forceinline__ void stage_finish(const float *__restrict__ x, float 
 #pragma unroll
     for (int u = 0; u < 2; u++) {
         const int c = (int)threadIdx.x + u * (int)blockDim.x;
-        stage_store<kPrescale>(st.v[u], xs, c < nchunk ? c : nchunk);
+        const float4 *gm = nullptr;
+        if constexpr (NORM) gm = st.gm[u];
+        stage_chunk<kPrescale, NORM>(st.v[u], gm, xs, c < nchunk ? c : nchunk, c < nchunk, ss);
     }
 }
 
 // Chunks beyond the first two per thread (only when nchunk > 2 * threads),
 // staged synchronously before any weight load is issued.
-template <bool kPrescale>
-__device__ __forceinline__ void stage_rest(const float *__restrict__ x, float *xs, int nchunk)
+template <bool kPrescale, bool NORM>
+__device__ __forceinline__ void stage_rest(const float *__restrict__ x, const float *__restrict__ gamma, float *xs,
+                                           int nchunk, float &ss)
 {
     for (int c = (int)threadIdx.x + 2 * (int)blockDim.x; c < nchunk; c += blockDim.x) {
         const float4 *src = reinterpret_cast<const float4 *>(x + (int64_t)c * kChunk);
         float4 v[8];
 #pragma unroll
         for (int k = 0; k < 8; k++) v[k] = src[k];
-        stage_store<kPrescale>(v, xs, c);
+        stage_chunk<kPrescale, NORM>(v, reinterpret_cast<const float4 *>(gamma + (int64_t)c * kChunk), xs, c, true,
+                                     ss);
     }
 }
 
@@ -306,9 +370,10 @@ __device__ __forceinline__ void static_for(F &&f)
 // are issued right after x's loads and before the workgroup waits for x to be
 // staged, and the next row batch's stages before the current batch's
 // reduction.  Batches of G*R rows go to waves in grid-stride order.
-template <int FMT, int LPR, int R, int NMAT, int D, int CPL>
+template <int FMT, int LPR, int R, int NMAT, int D, int CPL, int EPI>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
 {
+    constexpr bool NORM = EPI == kEpiNorm;
     extern __shared__ float4 qg_lds[];
     float *xs = reinterpret_cast<float *>(qg_lds);
 
@@ -379,23 +444,43 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
         });
     };
 
+    float norm_scale = 1.0f;
     {
         // No branches until the barrier: a join here would make the compiler
         // wait for every load in flight, the weight stream included.
-        XStage xst;
-        stage_issue(p.x, p.nchunk, xst);
-        stage_rest<Fmt<FMT>::kPrescale>(p.x, xs, p.nchunk);
+        float ss = 0.0f;   // NORM: this thread's sum of x^2, chunks in a fixed order
+        XStage<NORM> xst;
+        stage_issue<NORM>(p.x, p.gamma, p.nchunk, xst);
+        stage_rest<Fmt<FMT>::kPrescale, NORM>(p.x, p.gamma, xs, p.nchunk, ss);
         __builtin_amdgcn_sched_barrier(0);
         set_rows(batch < nbatch ? batch : nbatch - 1);   // idle waves read a valid row
         prologue();
         // x's loads went out first, so finishing the staging waits for them
         // only, not for the weight loads behind them
         __builtin_amdgcn_sched_barrier(0);
-        stage_finish<Fmt<FMT>::kPrescale>(p.x, xs, p.nchunk, xst);
+        stage_finish<Fmt<FMT>::kPrescale, NORM>(xs, p.nchunk, xst, ss);
+        if constexpr (NORM) {
+            // wave sums (fixed xor tree) into the slots after the spare chunk
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+            if (lane == 0) xs[(p.nchunk + 1) * kXStride + (threadIdx.x >> 6)] = ss;
+        }
     }
     __syncthreads();
+    if constexpr (NORM) {
+        // every workgroup adds the same wave sums in the same order: one scale
+        float tot = 0.0f;
+        for (int w = 0; w < waves; w++) tot += xs[(p.nchunk + 1) * kXStride + w];
+        norm_scale = 1.0f / sqrtf(tot / (float)(p.nchunk * kChunk) + p.eps);
+    }
 
     for (; batch < nbatch; batch += bstride) {
+        float rv[R];   // EPI 2: the residual of this lane group's rows, loaded before the weight stream's waits
+        if constexpr (EPI == kEpiResid) {
+            const int64_t rrow = batch * (G * R) + (int64_t)g * R;
+#pragma unroll
+            for (int r = 0; r < R; r++) rv[r] = p.resid[rrow + r < p.rows ? rrow + r : p.rows - 1];
+        }
         float acc[NMAT][R];
 #pragma unroll
         for (int m = 0; m < NMAT; m++)
@@ -469,6 +554,11 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
                     float v[NMAT];
 #pragma unroll
                     for (int m = 0; m < NMAT; m++) v[m] = acc[m][r] * scale[m][r];
+                    if constexpr (NORM) {
+#pragma unroll
+                        for (int m = 0; m < NMAT; m++) v[m] *= norm_scale;
+                    }
+                    if constexpr (EPI == kEpiResid) v[0] += rv[r];
                     if (NMAT == 1) p.y[row] = v[0];
                     else p.y[row] = silu_mul(v[0], v[NMAT - 1]);
                 }
@@ -477,15 +567,16 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
     }
 }
 
-template <int FMT, int LPR, int R, int NMAT, int D, int CPL>
+template <int FMT, int LPR, int R, int NMAT, int D, int CPL, int EPI>
 hipError_t go(const GemvParams &p, const GemvCfg &c, hipStream_t s)
 {
     constexpr int G = 64 / LPR;
     const int64_t batches = (p.rows + G * R - 1) / (G * R);
     int64_t nwg = (batches + c.waves - 1) / c.waves;
     if (c.max_wg > 0 && nwg > c.max_wg) nwg = c.max_wg;
-    const size_t lds = gemv_lds_bytes((int64_t)p.nchunk * kChunk);
-    auto kern = gemv_kernel<FMT, LPR, R, NMAT, D, CPL>;
+    // NORM: 16 more floats after the spare chunk for the wave sums of x^2
+    const size_t lds = gemv_lds_bytes((int64_t)p.nchunk * kChunk) + (EPI == kEpiNorm ? 64 : 0);
+    auto kern = gemv_kernel<FMT, LPR, R, NMAT, D, CPL, EPI>;
     if (lds > 65536) {
         // largest dynamic LDS size already allowed for this instantiation, per device
         static std::atomic<int> configured_lds[64];
@@ -501,34 +592,34 @@ hipError_t go(const GemvParams &p, const GemvCfg &c, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int FMT, int NMAT, int D, int CPL>
+template <int FMT, int NMAT, int D, int CPL, int EPI>
 hipError_t dispatch_lr(const GemvParams &p, const GemvCfg &c, hipStream_t s)
 {
 #define QG_CASE(L, RR) \
-    if (c.lpr == L && c.r == RR) return go<FMT, L, RR, NMAT, D, CPL>(p, c, s);
+    if (c.lpr == L && c.r == RR) return go<FMT, L, RR, NMAT, D, CPL, EPI>(p, c, s);
     QG_CASE(8, 1) QG_CASE(16, 1) QG_CASE(32, 1) QG_CASE(64, 1)
     QG_CASE(8, 2) QG_CASE(16, 2) QG_CASE(32, 2) QG_CASE(64, 2)
 #undef QG_CASE
     return hipErrorInvalidValue;
 }
 
-template <int FMT, int NMAT, int D>
+template <int FMT, int NMAT, int D, int EPI>
 hipError_t dispatch_cpl(const GemvParams &p, const GemvCfg &c, hipStream_t s)
 {
     switch (c.cpl) {
-    case 1: return dispatch_lr<FMT, NMAT, D, 1>(p, c, s);
-    case 2: return dispatch_lr<FMT, NMAT, D, 2>(p, c, s);
-    case 4: return dispatch_lr<FMT, NMAT, D, 4>(p, c, s);
+    case 1: return dispatch_lr<FMT, NMAT, D, 1, EPI>(p, c, s);
+    case 2: return dispatch_lr<FMT, NMAT, D, 2, EPI>(p, c, s);
+    case 4: return dispatch_lr<FMT, NMAT, D, 4, EPI>(p, c, s);
     }
     return hipErrorInvalidValue;
 }
 
-template <int FMT, int NMAT>
+template <int FMT, int NMAT, int EPI>
 hipError_t dispatch(const GemvParams &p, const GemvCfg &c, hipStream_t s)
 {
     switch (c.depth) {
-    case 2: return dispatch_cpl<FMT, NMAT, 2>(p, c, s);
-    case 4: return dispatch_cpl<FMT, NMAT, 4>(p, c, s);
+    case 2: return dispatch_cpl<FMT, NMAT, 2, EPI>(p, c, s);
+    case 4: return dispatch_cpl<FMT, NMAT, 4, EPI>(p, c, s);
     }
     return hipErrorInvalidValue;
 }
@@ -536,7 +627,8 @@ hipError_t dispatch(const GemvParams &p, const GemvCfg &c, hipStream_t s)
 } // namespace gemv_detail
 
 // Per-format entry points, each instantiated in its own translation unit.
-template <int FMT, int NMAT>
+// EPI: plain, the normalized-input gate/up (NMAT 2) or the residual down (NMAT 1).
+template <int FMT, int NMAT, int EPI>
 hipError_t gemv_dispatch(const gemv_detail::GemvParams &p, const GemvCfg &c, hipStream_t s);
 
 } // namespace qg

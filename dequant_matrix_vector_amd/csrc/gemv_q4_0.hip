@@ -4,15 +4,27 @@
 namespace qg {
 
 template <>
-hipError_t gemv_dispatch<QG_Q4_0, 1>(const gemv_detail::GemvParams &p, const GemvCfg &c, hipStream_t s)
+hipError_t gemv_dispatch<QG_Q4_0, 1, 0>(const gemv_detail::GemvParams &p, const GemvCfg &c, hipStream_t s)
 {
-    return gemv_detail::dispatch<QG_Q4_0, 1>(p, c, s);
+    return gemv_detail::dispatch<QG_Q4_0, 1, gemv_detail::kEpiPlain>(p, c, s);
 }
 
 template <>
-hipError_t gemv_dispatch<QG_Q4_0, 2>(const gemv_detail::GemvParams &p, const GemvCfg &c, hipStream_t s)
+hipError_t gemv_dispatch<QG_Q4_0, 2, 0>(const gemv_detail::GemvParams &p, const GemvCfg &c, hipStream_t s)
 {
-    return gemv_detail::dispatch<QG_Q4_0, 2>(p, c, s);
+    return gemv_detail::dispatch<QG_Q4_0, 2, gemv_detail::kEpiPlain>(p, c, s);
+}
+
+template <>
+hipError_t gemv_dispatch<QG_Q4_0, 2, 1>(const gemv_detail::GemvParams &p, const GemvCfg &c, hipStream_t s)
+{
+    return gemv_detail::dispatch<QG_Q4_0, 2, gemv_detail::kEpiNorm>(p, c, s);
+}
+
+template <>
+hipError_t gemv_dispatch<QG_Q4_0, 1, 2>(const gemv_detail::GemvParams &p, const GemvCfg &c, hipStream_t s)
+{
+    return gemv_detail::dispatch<QG_Q4_0, 1, gemv_detail::kEpiResid>(p, c, s);
 }
 
 } // namespace qg

@@ -49,6 +49,7 @@ struct PrefillParams {
     int tok_groups;
     int ksplit;      // K ranges, one per workgroup of a (row group, token group)
     int spk;         // super-steps per K range; every range is non-empty
+    const float *resid;  // NMAT 1: residual [n_tok][rows] added to y (may be y itself), or null
 };
 
 template <int N, typename F>
@@ -300,7 +301,12 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_0_kernel(PrefillParams p)
                                a[2], a[3]);
                     });
                 } else if (NMAT == 1) {
-                    const f32x4 a = acc[mr][n];
+                    f32x4 a = acc[mr][n];
+                    if (p.resid) {   // the residual stream: read before this thread overwrites it
+                        const float *rp = p.resid + (int64_t)tok * p.rows + row;
+#pragma unroll
+                        for (int i = 0; i < 4; i++) a[i] += row + i < p.rows ? rp[i] : 0.0f;
+                    }
                     store4(p.y + (int64_t)tok * p.rows + row, row, a[0], a[1], a[2], a[3]);
                 } else {
                     const f32x4 gg = acc[mr][n], uu = acc[(NMAT - 1) * MTR + mr][n];
@@ -313,11 +319,13 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_0_kernel(PrefillParams p)
     });
 }
 
-// y[t][i] = sum over K ranges of the partials, in range order (NMAT = 1), or
-// silu(g) * u of the two summed products (NMAT = 2).  V outputs per thread
-// (4 when the element count allows 16-byte accesses).
+// y[t][i] = sum over K ranges of the partials, in range order (NMAT = 1, plus
+// the residual when given), or silu(g) * u of the two summed products
+// (NMAT = 2).  V outputs per thread (4 when the element count allows 16-byte
+// accesses).
 template <int NMAT, int V>
-__global__ void prefill_reduce_kernel(const float *__restrict__ part, float *__restrict__ y, int64_t n, int ksplit)
+__global__ void prefill_reduce_kernel(const float *__restrict__ part, float *y, int64_t n, int ksplit,
+                                      const float *resid)
 {
     typedef float fv __attribute__((ext_vector_type(V)));
     const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * V;
@@ -343,7 +351,29 @@ __global__ void prefill_reduce_kernel(const float *__restrict__ part, float *__r
     fv r;
 #pragma unroll
     for (int e = 0; e < V; e++) r[e] = NMAT == 1 ? s[0][e] : s[0][e] / (1.0f + expf(-s[0][e])) * s[NMAT - 1][e];
+    if (NMAT == 1 && resid) r += *reinterpret_cast<const fv *>(resid + i);
     *reinterpret_cast<fv *>(y + i) = r;
+}
+
+// RMSNorm of one token row per workgroup (llmoxide blog, section 4 "Keeping
+// the numbers in range"): xn_j = x_j * gamma_j / sqrt(mean(x^2) + eps).  The
+// sum of squares runs in a fixed order (thread stride, xor tree, waves in
+// order), so every call gives the same scale.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ x, const float *__restrict__ gamma,
+                                                      float eps, float *__restrict__ xn, int n)
+{
+    __shared__ float wsum[4];
+    const float *xt = x + (int64_t)blockIdx.x * n;
+    float ss = 0.0f;
+    for (int j = threadIdx.x; j < n; j += 256) ss = __builtin_fmaf(xt[j], xt[j], ss);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+    const float sc = 1.0f / sqrtf(tot / (float)n + eps);
+    float *o = xn + (int64_t)blockIdx.x * n;
+    for (int j = threadIdx.x; j < n; j += 256) o[j] = xt[j] * sc * gamma[j];
 }
 
 // LDS of a workgroup: two bf16 x tiles plus one weight area per wave
@@ -368,12 +398,14 @@ hipError_t go_prefill(PrefillParams p, float *y, hipStream_t s)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.ksplit == 1) return e;
     const int64_t n = (int64_t)p.n_tok * p.rows;
-    if (n % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0)
+    const uintptr_t al = reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(p.y) |
+                         reinterpret_cast<uintptr_t>(p.resid);
+    if (n % 4 == 0 && (al & 15) == 0)
         hipLaunchKernelGGL((prefill_reduce_kernel<NMAT, 4>), dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
-                           (const float *)p.y, y, n, p.ksplit);
+                           (const float *)p.y, y, n, p.ksplit, p.resid);
     else
         hipLaunchKernelGGL((prefill_reduce_kernel<NMAT, 1>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                           (const float *)p.y, y, n, p.ksplit);
+                           (const float *)p.y, y, n, p.ksplit, p.resid);
     return hipGetLastError();
 }
 
@@ -477,8 +509,17 @@ int64_t prefill_part_elems(int nmat, int64_t rows, int64_t cols, int64_t n_tok)
     return c.ksplit > 1 ? (int64_t)c.ksplit * nmat * n_tok * rows : 0;
 }
 
+hipError_t launch_rmsnorm(const float *x, const float *gamma, float eps, float *xn, int64_t n, int64_t n_tok,
+                          hipStream_t s)
+{
+    if (n < 1 || n_tok < 1 || n_tok >= (int64_t(1) << 31) || n >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)n_tok), dim3(256), 0, s, x, gamma, eps, xn, (int)n);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill(int nmat, const uint8_t *w0, const uint8_t *w1, const float *x, float *y, int64_t rows,
-                          int64_t cols, int64_t n_tok, float *part, int64_t part_elems, hipStream_t s)
+                          int64_t cols, int64_t n_tok, float *part, int64_t part_elems, hipStream_t s,
+                          const float *resid)
 {
     Layout L;
     if (!layout_for(QG_Q4_0, rows, cols, &L) || n_tok < 1 || n_tok >= (int64_t(1) << 31)) return hipErrorInvalidValue;
@@ -499,6 +540,7 @@ hipError_t launch_prefill(int nmat, const uint8_t *w0, const uint8_t *w1, const 
     p.tok_groups = (int)((n_tok + c.ntw * 16 - 1) / (c.ntw * 16));
     p.ksplit = c.ksplit;
     p.spk = (p.ssteps + c.ksplit - 1) / c.ksplit;
+    p.resid = nmat == 1 ? resid : nullptr;
 #define QG_PF(NM, MR, NT, WV, RN)                                                                  \
     if constexpr (pf_fits(NM, MR, NT, WV, RN))                                                     \
         if (nmat == NM && c.mtr == MR && c.ntw == NT && c.waves == WV && c.run == RN)             \

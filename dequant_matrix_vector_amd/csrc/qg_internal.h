@@ -55,10 +55,13 @@ extern "C" int qgemv_set_launch_override(int lpr, int r, int waves, int depth, i
 bool launch_override(GemvCfg *c);
 
 // Kernel launchers (enqueue only; arguments already validated).
+// resid (may equal y): y = resid + W x.  gamma: the input is RMS-normalized
+// with that gain and eps before the gate/up products.
 hipError_t launch_gemv(int fmt, const uint8_t *packed, const float *x, float *y, int64_t rows,
-                       int64_t cols, hipStream_t s, const GemvCfg &cfg);
+                       int64_t cols, hipStream_t s, const GemvCfg &cfg, const float *resid = nullptr);
 hipError_t launch_gate_up(int fmt, const uint8_t *wg, const uint8_t *wu, const float *x, float *h,
-                          int64_t ffn, int64_t d_model, hipStream_t s, const GemvCfg &cfg);
+                          int64_t ffn, int64_t d_model, hipStream_t s, const GemvCfg &cfg,
+                          const float *gamma = nullptr, float eps = 0.0f);
 hipError_t launch_repack(int fmt, const void *raw, const float *row_scale, uint8_t *packed,
                          int64_t rows, int64_t cols, hipStream_t s);
 hipError_t launch_dequant(int fmt, const uint8_t *packed, float *w, int64_t rows, int64_t cols,
@@ -78,11 +81,15 @@ extern "C" int qgemv_set_prefill_override(int mtr, int ntw, int waves, int run, 
 bool prefill_enabled();   // false after qgemv_set_prefill_override(-1, ...): per-token GEMV loop instead
 // Floats of partial sums the built-in choice splits K into (0: no split).
 int64_t prefill_part_elems(int nmat, int64_t rows, int64_t cols, int64_t n_tok);
-// nmat == 1: y = W0 x.  nmat == 2: y = silu(W0 x) * (W1 x).  x fp32 [n_tok][cols].
-// part (part_elems floats, may be null) lets the K dimension split over
-// workgroups; the partial sums are then added in a second, small launch.
+// nmat == 1: y = W0 x (+ resid, which may equal y).  nmat == 2: y = silu(W0 x) * (W1 x).
+// x fp32 [n_tok][cols].  part (part_elems floats, may be null) lets the K
+// dimension split over workgroups; the partial sums are then added in a
+// second, small launch.
 hipError_t launch_prefill(int nmat, const uint8_t *w0, const uint8_t *w1, const float *x, float *y,
                           int64_t rows, int64_t cols, int64_t n_tok, float *part, int64_t part_elems,
+                          hipStream_t s, const float *resid = nullptr);
+// xn[t][j] = x[t][j] * gamma[j] / sqrt(mean_j x[t][j]^2 + eps), fp32, one workgroup per token.
+hipError_t launch_rmsnorm(const float *x, const float *gamma, float eps, float *xn, int64_t n, int64_t n_tok,
                           hipStream_t s);
 
 } // namespace qg

@@ -154,6 +154,33 @@ int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const fl
                float *out, float *h_scratch, int64_t h_scratch_elems, int64_t d_model,
                int64_t ffn, int64_t n_tok, void *stream);
 
+/* The FFN block of the residual stream: out = x + Wd (silu(Wg xn) * (Wu xn)),
+ * xn = x * gamma / sqrt(mean(x^2) + eps) per token row -- RMSNorm before the
+ * block (llmoxide blog, section 4 "Keeping the numbers in range"; the rmsnorm
+ * of dasLLAMA-00, which uses eps = 1e-5) and the residual add after it (same
+ * blog, section 7 "The block, and the residual stream").
+ * gamma: fp32 [d_model] (16-byte aligned); eps >= 0 and finite; x, out: fp32
+ * [n_tok][d_model]; out may be x itself (the stream updated in place) or must
+ * not overlap it.  h_scratch: >= swiglu_ffn_block_scratch_elems() floats
+ * (QG_ERR_SCRATCH below the minimum that query's comment states), first
+ * n_tok*ffn of them hold h on return.  With n_tok == 1, or formats other than
+ * Q4_0, the norm is fused into the gate/up GEMV (the per-token scale factors
+ * out of every dot product; the workgroup sums x^2 while staging x*gamma) and
+ * the residual into the down GEMV's epilogue: two launches per token.  Q4_0
+ * with n_tok > 1 runs a small RMSNorm launch into the scratch, then the
+ * matrix-core products (residual added in the down product's epilogue or in
+ * its split-K reduce). */
+int swiglu_ffn_block(int fmt, const void *wg, const void *wu, const void *wd, const float *gamma,
+                     float eps, const float *x, float *out, float *h_scratch, int64_t h_scratch_elems,
+                     int64_t d_model, int64_t ffn, int64_t n_tok, void *stream);
+
+/* Scratch elements (fp32) for which swiglu_ffn_block runs its fastest form:
+ * n_tok*ffn on the GEMV path; on the matrix-core path (Q4_0, n_tok > 1) h,
+ * the normalized input (required: together the minimum) and room for
+ * split-K partial sums (optional).  Negative qg_status for an invalid shape
+ * or format. */
+int64_t swiglu_ffn_block_scratch_elems(int fmt, int64_t d_model, int64_t ffn, int64_t n_tok);
+
 /* Scratch elements (fp32) for which swiglu_ffn runs its fastest form on the
  * current device: n_tok*ffn, plus room for partial sums on the matrix-core
  * path.  Negative qg_status for an invalid shape or format. */
