@@ -62,6 +62,8 @@ def _load():
     lib.oracle_ffn_block.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, ctypes.c_double, P, I64, I64, I64,
                                      P, P, P, P, P, P, P, P, P]
     lib.oracle_ffn_block.restype = ctypes.c_int
+    lib.oracle_argmax.argtypes = [P, I64]
+    lib.oracle_argmax.restype = I64
     lib.oracle_silu.argtypes = [ctypes.c_double]
     lib.oracle_silu.restype = ctypes.c_double
     lib.oracle_swiglu.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, I64, I64, I64,
@@ -198,3 +200,12 @@ def ffn_block(fmt, wg, wu, wd, gamma, eps, x, d_model, ffn, sg=None, su=None, sd
                                     _ptr(r["xn"]), _ptr(r["g"]), _ptr(r["u"]), _ptr(r["h"]), _ptr(r["d"]),
                                     _ptr(r["out"]), _ptr(r["Sg"]), _ptr(r["Su"]), _ptr(r["Sd"])), "ffn_block")
     return r
+
+
+def argmax(v) -> int:
+    """First index of the largest value of a float32 vector (greedy sampling)."""
+    v = np.ascontiguousarray(v, dtype=np.float32).reshape(-1)
+    r = _load().oracle_argmax(_ptr(v), v.size)
+    if r < 0:
+        raise ValueError(f"oracle argmax: status {r}")
+    return int(r)

@@ -42,6 +42,10 @@
  * The FFN block of the residual stream (section 7 "The block, and the
  * residual stream", same blog): out = x + FFN(rmsnorm(x) * gamma).
  *
+ * Greedy sampling (dasLLAMA-00's most_likely; the Go "llm" package's Argmax,
+ * first index on ties): start from index 0 and move to a later index only
+ * when its logit is strictly greater.
+ *
  * Parity pins for every function live in tests/test_oracle_*.py.
  */
 #include <math.h>
@@ -314,4 +318,18 @@ int oracle_ffn_block(int fmt, const void *wg, const float *sg, const void *wu, c
     for (int64_t i = 0; i < n_tok * d_model; i++)
         out[i] = (double)x[i] + d[i];
     return OR_OK;
+}
+
+/* Index of the largest of v[0..n), scanning in order and replacing the best
+ * only on a strictly greater value: the first index wins ties, -0 equals +0,
+ * a NaN never replaces the best (and a NaN at index 0 is never replaced). */
+int64_t oracle_argmax(const float *v, int64_t n)
+{
+    if (n < 1)
+        return OR_ERR_SHAPE;
+    int64_t best = 0;
+    for (int64_t i = 1; i < n; i++)
+        if (v[i] > v[best])
+            best = i;
+    return best;
 }

@@ -15,7 +15,7 @@ from oracle import build as obuild
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_FILES = ["tests/test_oracle_decode.py", "tests/test_oracle_gemv.py", "tests/test_oracle_swiglu.py",
-             "tests/test_oracle_norm.py"]
+             "tests/test_oracle_norm.py", "tests/test_oracle_argmax.py"]
 
 MUTANTS = {
     "f16_exponent_bias": ("ldexp((double)(1024 + m), e - 25)", "ldexp((double)(1024 + m), e - 24)"),
@@ -43,6 +43,8 @@ MUTANTS = {
     "rmsnorm_gain_dropped": ("* sc * (double)gamma[j]", "* sc"),
     "rmsnorm_scale_dropped": ("(double)xt[j] * sc * (double)gamma[j]", "(double)xt[j] * (double)gamma[j]"),
     "block_residual_dropped": ("out[i] = (double)x[i] + d[i];", "out[i] = d[i];"),
+    "argmax_last_on_ties": ("if (v[i] > v[best])", "if (v[i] >= v[best])"),
+    "argmax_skips_first": ("int64_t best = 0;\n    for (int64_t i = 1;", "int64_t best = 1;\n    for (int64_t i = 1;"),
     "block_gate_up_swapped": ("h[i] = oracle_silu(g[i]) * u[i];\n    st =", "h[i] = oracle_silu(u[i]) * g[i];\n    st ="),
 }
 
