@@ -16,6 +16,7 @@ __all__ = [
     "qgemv", "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_k", "qgemv_i8row",
     "swiglu_gate_up", "swiglu_ffn", "qdequant", "layout_version", "set_launch_override",
     "set_prefill_override", "swiglu_ffn_scratch_elems", "swiglu_ffn_block", "swiglu_ffn_block_scratch_elems",
+    "qgemv_argmax", "qgemv_head_argmax",
     "qgemv_repack_q4_0", "qgemv_repack_q8_0", "qgemv_repack_q4_k", "qgemv_repack_i8row",
 ]
 
@@ -57,6 +58,10 @@ lib.swiglu_ffn_block.argtypes = [_I, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
 lib.swiglu_ffn_block.restype = _I
 lib.swiglu_ffn_block_scratch_elems.argtypes = [_I, _I64, _I64, _I64]
 lib.swiglu_ffn_block_scratch_elems.restype = _I64
+lib.qgemv_argmax.argtypes = [_P, _P, _I64, _I64, _P]
+lib.qgemv_argmax.restype = _I
+lib.qgemv_head_argmax.argtypes = [_I, _P, _P, _P, _P, _I64, _I64, _I64, _P]
+lib.qgemv_head_argmax.restype = _I
 lib.qdequant.argtypes = [_I, _P, _P, _I64, _I64, _P]
 lib.qdequant.restype = _I
 lib.qgemv_set_launch_override.argtypes = [_I, _I, _I, _I, _I, _I]
@@ -268,3 +273,25 @@ def swiglu_ffn_block(fmt, wg, wu, wd, gamma, eps, x, d_model, ffn, out=None, h_s
                                 _ptr(h_scratch), h_scratch.numel(), d_model, ffn, n_tok, _stream(stream)),
            "swiglu_ffn_block")
     return out, h_scratch.view(-1)[:n_tok * ffn].view(n_tok, ffn)
+
+
+def qgemv_argmax(logits, n, token=None, stream=None) -> torch.Tensor:
+    """int32 [n_tok]: first index of the largest logit of each row of logits [n_tok][n]."""
+    n_tok = logits.numel() // n
+    if token is None:
+        token = torch.empty(n_tok, dtype=torch.int32, device=logits.device)
+    _dev(logits, token)
+    _check(lib.qgemv_argmax(_ptr(logits), _ptr(token), n, n_tok, _stream(stream)), "qgemv_argmax")
+    return token
+
+
+def qgemv_head_argmax(fmt, packed, x, rows, cols, logits=None, token=None, stream=None):
+    """(token int32 [n_tok], logits [n_tok][rows]): the head product then greedy sampling."""
+    n_tok = x.numel() // cols
+    logits = _y(logits, (n_tok, rows), x.device)
+    if token is None:
+        token = torch.empty(n_tok, dtype=torch.int32, device=x.device)
+    _dev(packed, x, logits, token)
+    _check(lib.qgemv_head_argmax(_fmt(fmt), _ptr(packed), _ptr(x), _ptr(logits), _ptr(token), rows, cols, n_tok,
+                                 _stream(stream)), "qgemv_head_argmax")
+    return token, logits

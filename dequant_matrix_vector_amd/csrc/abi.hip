@@ -374,6 +374,31 @@ int swiglu_ffn_block(int fmt, const void *wg, const void *wu, const void *wd, co
     return QG_OK;
 }
 
+int qgemv_argmax(const float *logits, int32_t *token, int64_t n, int64_t n_tok, void *stream)
+{
+    if (!logits || !token) return QG_ERR_NULL;
+    if (n < 1 || n >= (int64_t(1) << 31) || n_tok < 1 || n_tok >= (int64_t(1) << 31)) return QG_ERR_SHAPE;
+    if (!aligned(logits, 4) || !aligned(token, 4)) return QG_ERR_ALIGN;
+    if (overlap(logits, n * n_tok * 4, token, n_tok * 4)) return QG_ERR_ALIAS;
+    return launch_argmax(logits, token, n, n_tok, (hipStream_t)stream) == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+int qgemv_head_argmax(int fmt, const void *packed, const float *x, float *logits, int32_t *token, int64_t rows,
+                      int64_t cols, int64_t n_tok, void *stream)
+{
+    Layout L;
+    int st = check_product(fmt, packed, x, logits, rows, cols, n_tok, &L);
+    if (st) return st;
+    if (!token) return QG_ERR_NULL;
+    if (!aligned(token, 4)) return QG_ERR_ALIGN;
+    if (overlap(token, n_tok * 4, logits, n_tok * rows * 4) || overlap(token, n_tok * 4, x, n_tok * cols * 4) ||
+        overlap(token, n_tok * 4, packed, L.total))
+        return QG_ERR_ALIAS;
+    st = qgemv(fmt, packed, x, logits, rows, cols, n_tok, stream);
+    if (st) return st;
+    return launch_argmax(logits, token, rows, n_tok, (hipStream_t)stream) == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
 int qdequant(int fmt, const void *packed, float *w_out, int64_t rows, int64_t cols, void *stream)
 {
     if (!valid_fmt(fmt)) return QG_ERR_FORMAT;

@@ -88,6 +88,8 @@ int64_t prefill_part_elems(int nmat, int64_t rows, int64_t cols, int64_t n_tok);
 hipError_t launch_prefill(int nmat, const uint8_t *w0, const uint8_t *w1, const float *x, float *y,
                           int64_t rows, int64_t cols, int64_t n_tok, float *part, int64_t part_elems,
                           hipStream_t s, const float *resid = nullptr);
+// token[t] = first index of the largest of logits[t][0..n) (NaN never chosen, unless at index 0).
+hipError_t launch_argmax(const float *logits, int32_t *token, int64_t n, int64_t n_tok, hipStream_t s);
 // xn[t][j] = x[t][j] * gamma[j] / sqrt(mean_j x[t][j]^2 + eps), fp32, one workgroup per token.
 hipError_t launch_rmsnorm(const float *x, const float *gamma, float eps, float *xn, int64_t n, int64_t n_tok,
                           hipStream_t s);

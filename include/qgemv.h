@@ -186,6 +186,21 @@ int64_t swiglu_ffn_block_scratch_elems(int fmt, int64_t d_model, int64_t ffn, in
  * path.  Negative qg_status for an invalid shape or format. */
 int64_t swiglu_ffn_scratch_elems(int fmt, int64_t d_model, int64_t ffn, int64_t n_tok);
 
+/* Greedy sampling on the device: token[t] = index of the largest of
+ * logits[t][0..n), the first on ties (the Go "llm" package's Argmax;
+ * dasLLAMA-00's most_likely moves only on a strictly greater logit, so -0
+ * equals +0, a NaN is never chosen, and a NaN at index 0 keeps index 0).
+ * logits: fp32 [n_tok][n]; token: int32 [n_tok].  One launch, deterministic. */
+int qgemv_argmax(const float *logits, int32_t *token, int64_t n, int64_t n_tok, void *stream);
+
+/* The vocab head then greedy sampling (llmoxide blog section 7: the output
+ * head is one more matrix multiply; Go "llm" package: sampling runs on the
+ * GPU and only the 4-byte token is read back): logits = W x as qgemv (the
+ * same paths and bounds), then qgemv_argmax over each token's logits.
+ * logits: fp32 [n_tok][rows] (kept for the caller); token: int32 [n_tok]. */
+int qgemv_head_argmax(int fmt, const void *packed, const float *x, float *logits, int32_t *token,
+                      int64_t rows, int64_t cols, int64_t n_tok, void *stream);
+
 /* Test export: the packed tensor decoded to fp32 [rows][cols] (each weight its
  * exact value rounded once to binary32).  Not used on the hot path. */
 int qdequant(int fmt, const void *packed, float *w_out, int64_t rows, int64_t cols, void *stream);

@@ -1,0 +1,93 @@
+"""GPU parity of greedy sampling (qgemv_argmax, qgemv_head_argmax) through the C ABI.
+
+Bars:
+  * qgemv_argmax on given logits: the same index as the oracle's in-order scan,
+    bit for bit (integer output), over crafted rows -- planted ties with the
+    maximum, infinities, signed zeros, NaN anywhere and at index 0 -- and sizes
+    around the 64-lane and 256-thread boundaries up to vocabulary widths;
+  * qgemv_head_argmax: the token is the oracle argmax of the device's own
+    logits (unique), and it is a valid argmax of the exact logits: its exact
+    logit is within the two logits' error bounds of the exact maximum.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_argmax(v):
+    vd = G.torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(G.dev())
+    t = G.qg().qgemv_argmax(vd, v.shape[-1])
+    G.torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 255, 256, 257, 1000, 4097, 49152, 151936])
+def test_argmax_random_rows_with_ties(n):
+    rng = np.random.default_rng(n)
+    v = rng.standard_normal((5, n)).astype(np.float32)
+    for t in range(5):   # plant copies of the maximum (ties) at random places
+        k = rng.integers(1, 4)
+        v[t, rng.integers(0, n, k)] = v[t].max() + (t % 2)
+    got = _gpu_argmax(v)
+    assert [int(a) for a in got] == [oracle.argmax(row) for row in v]
+
+
+def test_argmax_special_values():
+    inf, nan = np.inf, np.nan
+    rows = [
+        [1.0, 3.0, 3.0, 2.0], [-inf, -inf, -inf, -inf], [-inf, -3e38, -inf, -inf], [1.0, inf, inf, 0.0],
+        [-0.0, 0.0, -0.0, 0.0], [5.0, nan, 7.0, nan], [nan, 5.0, 9.0, 1.0], [2.0, nan, nan, nan],
+        [nan, nan, nan, nan], [-1.0, -0.5, -0.5, -2.0],
+    ]
+    v = np.array(rows, np.float32)
+    assert [int(a) for a in _gpu_argmax(v)] == [oracle.argmax(r) for r in v]
+    # the same patterns spread over a long row: specials in different lanes and waves
+    n = 3000
+    rng = np.random.default_rng(7)
+    long = rng.uniform(-1, 1, (6, n)).astype(np.float32)
+    long[0, [17, 1200, 2999]] = 5.0                       # three-way tie
+    long[1, ::7] = np.nan                                   # NaNs everywhere except index 0
+    long[2, 0] = np.nan                                     # NaN at index 0
+    long[3, [100, 900]] = np.inf
+    long[4, :] = -np.inf
+    long[4, 2500] = -1e30
+    long[5, :] = 0.0
+    long[5, ::3] = -0.0
+    assert [int(a) for a in _gpu_argmax(long)] == [oracle.argmax(r) for r in long]
+
+
+def _check_head(t, n_tok, seed):
+    pk = G.upload(t)
+    x = np.random.default_rng(seed).standard_normal((n_tok, t.cols)).astype(np.float32)
+    xd = G.torch.from_numpy(x).to(G.dev())
+    tok, logits = G.qg().qgemv_head_argmax(t.fmt, pk, xd, t.rows, t.cols)
+    G.torch.cuda.synchronize()
+    tok, logits = tok.cpu().numpy(), logits.cpu().numpy()
+    yr, S = oracle.gemv(t.fmt, t.raw, x, t.rows, t.cols, row_scale=t.row_scale)
+    rel = G.rel_for(t.fmt, n_tok)
+    for k in range(n_tok):
+        assert int(tok[k]) == oracle.argmax(logits[k])
+        b = rel * S[k] + G.ABS
+        m = int(np.argmax(yr[k]))
+        assert yr[k][tok[k]] >= yr[k][m] - (b[tok[k]] + b[m]), f"token {k}: not a valid argmax of the exact logits"
+
+
+@pytest.mark.parametrize("wname,idx,n_tok", [(synth.CFG2.name, 7, 1), (synth.CFG2.name, 7, 3),
+                                             (synth.CFG4.name, 3, 1)])
+def test_head_argmax_vocab_heads(wname, idx, n_tok):
+    # the SmolLM2-135M Q8_0 head and the SmolLM2-1.7B INT8-row head, 49152 rows
+    w = synth.WORKLOADS[wname]
+    t = synth.gen_tensor(w, idx)
+    assert t.rows == 49152
+    _check_head(t, n_tok, 40 + n_tok)
+
+
+def test_head_argmax_matrix_cores():
+    # a Q4_0 head at 8 tokens runs the product on the matrix cores first
+    t = synth.make_tensor("q4_0", 4096, 1024, np.random.default_rng(45))
+    _check_head(t, 8, 46)
