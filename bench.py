@@ -198,6 +198,86 @@ def workload_report(qg, synth, torch, np, dev, graph_iters=20):
             rep[key]["pct_bf16_mfma_peak"] = round(100 * flops / us / 1e6 / BF16_MFMA_PEAK_TFLOPS, 1)
         del copies, g
         torch.cuda.empty_cache()
+    rep.update(extra_report(qg, synth, torch, np, dev, graph_iters))
+    return rep
+
+
+def _graph_us(torch, step, graph_iters):
+    """Device microseconds per step of `step(i)` replayed from a HIP graph."""
+    for i in range(3):
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(graph_iters):
+            step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (5 * graph_iters)
+
+
+def extra_report(qg, synth, torch, np, dev, graph_iters=20):
+    """The steps around the FFN and the head: the 27B-class FFN block with
+    RMSNorm in and the residual add out (against the bare FFN), and the vocab
+    heads followed by greedy sampling on the device."""
+    rep = {}
+    w = synth.CFG5
+    tens = synth.gen_workload(w)
+    wbytes = sum(t.weight_bytes for t in tens)
+    ncopy = int(min(graph_iters, max(1, -(-ROTATE_BYTES // wbytes))))
+    raws = [torch.from_numpy(t.raw).to(dev) for t in tens]
+    copies = [[qg.repack("q4_0", r, t.rows, t.cols) for r, t in zip(raws, tens)] for _ in range(ncopy)]
+    del raws
+    gamma = torch.rand(w.d_model, device=dev) + 0.5
+    for n_tok in (1, 8):
+        x = torch.randn((n_tok, w.d_model), device=dev)
+        out = torch.empty_like(x)
+        sb = torch.empty(qg.swiglu_ffn_block_scratch_elems("q4_0", w.d_model, w.ffn, n_tok), device=dev)
+        sf = torch.empty(qg.swiglu_ffn_scratch_elems("q4_0", w.d_model, w.ffn, n_tok), device=dev)
+
+        def block(i):
+            c = copies[i % ncopy]
+            qg.swiglu_ffn_block("q4_0", c[0], c[1], c[2], gamma, 1e-5, x, w.d_model, w.ffn, out=out, h_scratch=sb)
+
+        def bare(i):
+            c = copies[i % ncopy]
+            qg.swiglu_ffn("q4_0", c[0], c[1], c[2], x, w.d_model, w.ffn, out=out, h_scratch=sf)
+
+        ub, uf = _graph_us(torch, block, graph_iters), _graph_us(torch, bare, graph_iters)
+        rep[f"cfg5_block_n{n_tok}"] = {"workload": w.name + " + RMSNorm in, residual out", "n_tok": n_tok,
+                                       "us_per_step": round(ub, 2), "ffn_alone_us_per_step": round(uf, 2),
+                                       "GBs": round(wbytes / ub / 1e3, 1)}
+    del copies
+    torch.cuda.empty_cache()
+    for w, idx in ((synth.CFG2, 7), (synth.CFG4, 3)):
+        t = synth.gen_tensor(w, idx)
+        raw = torch.from_numpy(t.raw).to(dev)
+        rs = None if t.row_scale is None else torch.from_numpy(t.row_scale).to(dev)
+        ncopy = int(min(graph_iters, max(1, -(-ROTATE_BYTES // t.weight_bytes))))
+        hc = [qg.repack(t.fmt, raw, t.rows, t.cols, row_scale=rs) for _ in range(ncopy)]
+        del raw
+        x = torch.randn((1, t.cols), device=dev)
+        logits = torch.empty((1, t.rows), device=dev)
+        tok = torch.empty(1, dtype=torch.int32, device=dev)
+
+        def head(i):
+            qg.qgemv_head_argmax(t.fmt, hc[i % ncopy], x, t.rows, t.cols, logits=logits, token=tok)
+
+        def head_only(i):
+            qg.qgemv(t.fmt, hc[i % ncopy], x, t.rows, t.cols, y=logits)
+
+        uh, uo = _graph_us(torch, head, graph_iters), _graph_us(torch, head_only, graph_iters)
+        rep[f"cfg{w.cfg_id}_head_argmax"] = {"workload": f"{w.name}: {t.fmt} head [{t.rows}][{t.cols}] + argmax",
+                                            "us_per_step": round(uh, 2), "head_alone_us_per_step": round(uo, 2),
+                                            "GBs": round(t.weight_bytes / uh / 1e3, 1)}
+        del hc
+        torch.cuda.empty_cache()
     return rep
 
 

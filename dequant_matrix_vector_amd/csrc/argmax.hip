@@ -17,7 +17,8 @@ namespace qg {
 
 namespace {
 
-constexpr int kArgmaxThreads = 256;
+constexpr int kArgmaxThreads = 1024;
+constexpr int kArgmaxUnroll = 16;   // independent float4 loads in flight per thread: 64K logits per round trip
 
 __device__ __forceinline__ void take_better(float &bv, int &bi, float v, int i)
 {
@@ -28,15 +29,37 @@ __device__ __forceinline__ void take_better(float &bv, int &bi, float v, int i)
     }
 }
 
+// V = 4: rows of whole 16-byte pieces (n % 4 == 0, 16-byte aligned); V = 1: any n
+template <int V>
 __global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(const float *__restrict__ logits,
                                                                 int32_t *__restrict__ token, int n)
 {
+    typedef float fv __attribute__((ext_vector_type(V)));
     __shared__ float wv[kArgmaxThreads / 64];
     __shared__ int wi[kArgmaxThreads / 64];
     const float *row = logits + (int64_t)blockIdx.x * n;
+    const fv *rv = reinterpret_cast<const fv *>(row);
+    const int nv = n / V;
     float bv = -__builtin_inff();
     int bi = 0x7FFFFFFF;   // loses to every element, -inf included
-    for (int i = threadIdx.x; i < n; i += kArgmaxThreads) take_better(bv, bi, row[i], i);
+    // piece p = base + k * threads + tid: all kArgmaxUnroll loads issued before any compare
+    constexpr int STEP = kArgmaxThreads * kArgmaxUnroll;
+    for (int base = 0; base < nv; base += STEP) {
+        fv v[kArgmaxUnroll];
+#pragma unroll
+        for (int k = 0; k < kArgmaxUnroll; k++) {
+            const int pc = base + k * kArgmaxThreads + (int)threadIdx.x;
+            v[k] = rv[pc < nv ? pc : nv - 1];
+        }
+#pragma unroll
+        for (int k = 0; k < kArgmaxUnroll; k++) {
+            const int pc = base + k * kArgmaxThreads + (int)threadIdx.x;
+            if (pc < nv) {
+#pragma unroll
+                for (int e = 0; e < V; e++) take_better(bv, bi, v[k][e], pc * V + e);
+            }
+        }
+    }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         const float ov = __shfl_xor(bv, off, 64);
@@ -64,7 +87,10 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(const float *__r
 hipError_t launch_argmax(const float *logits, int32_t *token, int64_t n, int64_t n_tok, hipStream_t s)
 {
     if (n < 1 || n >= (int64_t(1) << 31) || n_tok < 1 || n_tok >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(argmax_kernel, dim3((unsigned)n_tok), dim3(kArgmaxThreads), 0, s, logits, token, (int)n);
+    if (n % 4 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0)
+        hipLaunchKernelGGL(argmax_kernel<4>, dim3((unsigned)n_tok), dim3(kArgmaxThreads), 0, s, logits, token, (int)n);
+    else
+        hipLaunchKernelGGL(argmax_kernel<1>, dim3((unsigned)n_tok), dim3(kArgmaxThreads), 0, s, logits, token, (int)n);
     return hipGetLastError();
 }
 
