@@ -5,7 +5,7 @@ bench.py's cpu_baseline leg, never by the product package.  It wraps the plain
 scalar C in oracle.c (binary64 accumulation, sequential column order) through
 ctypes and shares no code with the HIP library.
 
-Formats (constants match the C side): Q4_0=0, Q8_0=1, Q4_K=2, I8ROW=3.
+Formats (constants match the C side): Q4_0=0, Q8_0=1, Q4_K=2, I8ROW=3, Q6_K=4.
 `raw` is the tensor's raw block bytes ([rows][cols/B] blocks, row-major) as a
 uint8 numpy array; for I8ROW it is the int8 code matrix and `row_scale` holds the
 fp32 per-row scales.
@@ -17,8 +17,8 @@ import numpy as np
 
 from . import build as _build
 
-Q4_0, Q8_0, Q4_K, I8ROW = 0, 1, 2, 3
-FORMATS = {"q4_0": Q4_0, "q8_0": Q8_0, "q4_k": Q4_K, "i8row": I8ROW}
+Q4_0, Q8_0, Q4_K, I8ROW, Q6_K = 0, 1, 2, 3, 4
+FORMATS = {"q4_0": Q4_0, "q8_0": Q8_0, "q4_k": Q4_K, "i8row": I8ROW, "q6_k": Q6_K}
 
 _lib = None
 

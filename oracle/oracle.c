@@ -30,6 +30,17 @@
  *            Reading: d, dmin (f16), scales[12], qs[128]; w = d*sc*q - dmin*m;
  *            qs[32c+l] holds sub-block 2c in its low nibble and 2c+1 in its
  *            high nibble.
+ *   Q6_K  -- section 10 "Loading weights" of the llmoxide blog: a k-quant of
+ *            256-weight super-blocks with their own scales at about 6.6 bits
+ *            per weight; "Building llamini.cpp" (section "What I
+ *            reimplemented") names it the second super-block format of a
+ *            Q4_K_M file.  Reading (the GGUF layout of those files, not
+ *            printed on the pages): 210 bytes = ql[128], qh[64], scales[16]
+ *            (int8, one per 16 columns), d (f16); the 6-bit code of column
+ *            c = 128h + 32j + l (h < 2, j < 4, l < 32) takes its low four bits
+ *            from ql[64h + 32(j mod 2) + l] (low nibble for j < 2, high nibble
+ *            for j >= 2) and its top two bits from bits 2j, 2j+1 of
+ *            qh[32h + l]; w = d * scales[c / 16] * (q - 32).
  *   I8ROW -- minillm-cpp README, Quantization paragraph: symmetric per-channel
  *            int8 with one scale per output row; w = s_row * q.
  *
@@ -58,7 +69,7 @@
 #define OR_ERR_FORMAT -4
 #define OR_ERR_NOMEM -8
 
-enum { OR_Q4_0 = 0, OR_Q8_0 = 1, OR_Q4_K = 2, OR_I8ROW = 3 };
+enum { OR_Q4_0 = 0, OR_Q8_0 = 1, OR_Q4_K = 2, OR_I8ROW = 3, OR_Q6_K = 4 };
 
 /* IEEE 754 binary16 -> binary64, exact (the Go "llm" package documents its
  * F16ToF32 as exact).  Sign, 5-bit exponent biased by 15, 10-bit fraction;
@@ -143,6 +154,24 @@ static void decode_row(int fmt, const uint8_t *raw, const float *row_scale, int6
                 }
             }
         }
+    } else if (fmt == OR_Q6_K) {
+        int64_t nsb = cols / 256;
+        const uint8_t *row = raw + r * nsb * 210;
+        for (int64_t b = 0; b < nsb; b++) {
+            const uint8_t *blk = row + b * 210;
+            const uint8_t *ql = blk;
+            const uint8_t *qh = blk + 128;
+            const int8_t *scales = (const int8_t *)(blk + 192);
+            double d = oracle_f16_to_f64(rd_u16(blk + 208));
+            for (int c = 0; c < 256; c++) {
+                int half = c / 128, j = (c % 128) / 32, l = c % 32;
+                int lo_byte = ql[64 * half + 32 * (j % 2) + l];
+                int lo = (j < 2) ? (lo_byte & 0x0F) : (lo_byte >> 4);
+                int hi = (qh[32 * half + l] >> (2 * j)) & 3;
+                int q = lo | (hi << 4);
+                out[b * 256 + c] = d * (double)scales[c / 16] * (double)(q - 32);
+            }
+        }
     } else { /* OR_I8ROW */
         const int8_t *row = (const int8_t *)raw + r * cols;
         double s = (double)row_scale[r];
@@ -153,20 +182,21 @@ static void decode_row(int fmt, const uint8_t *raw, const float *row_scale, int6
 
 static int check_shape(int fmt, int64_t rows, int64_t cols)
 {
-    if (fmt < OR_Q4_0 || fmt > OR_I8ROW)
+    if (fmt < OR_Q4_0 || fmt > OR_Q6_K)
         return OR_ERR_FORMAT;
     if (rows < 0 || cols < 0)
         return OR_ERR_SHAPE;
     if ((fmt == OR_Q4_0 || fmt == OR_Q8_0) && cols % 32)
         return OR_ERR_SHAPE;
-    if (fmt == OR_Q4_K && cols % 256)
+    if ((fmt == OR_Q4_K || fmt == OR_Q6_K) && cols % 256)
         return OR_ERR_SHAPE;
     return OR_OK;
 }
 
 /* Dequantized weights rounded once (round-to-nearest-even) to binary32.
- * For Q8_0, Q4_0 and Q4_K the binary64 value is exact and the cast is the
- * single rounding; for I8ROW likewise (s*q has at most 32 significant bits). */
+ * For Q8_0, Q4_0, Q4_K and Q6_K the binary64 value is exact and the cast is
+ * the single rounding; for I8ROW likewise (s*q has at most 32 significant
+ * bits). */
 int oracle_dequant(int fmt, const void *raw, const float *row_scale, int64_t rows, int64_t cols,
                    float *w_out)
 {

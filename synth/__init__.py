@@ -15,12 +15,18 @@ block b of a row covering columns [B*b, B*b+B)):
         get_scale_min_k4 in "Building llamini.cpp" unpacks), then 128 bytes;
         byte 32c+l holds element l of sub-block 2c (low nibble) and of
         sub-block 2c+1 (high nibble).
+  Q6_K  210 B / 256 weights: ql[128], qh[64], 16 int8 scales (one per 16
+        columns), f16 d (the GGUF layout of the Q4_K_M files the pages load).
+        Column c = 128h + 32j + l keeps its low four bits in ql[64h + 32(j mod
+        2) + l] (low nibble for j < 2, high for j >= 2) and its top two bits in
+        bits 2j, 2j+1 of qh[32h + l].
   I8ROW int8 [rows][cols] codes plus one fp32 scale per row.
 
 Distributions follow the five workload descriptions (the quantized FFN of a
 stories15M-sized model, a SmolLM2-135M decode layer with a Q8_0 vocab head, a
 TinyLlama-1.1B layer in Q4_K, a SmolLM2-1.7B-sized per-row INT8 FFN and head,
-and a 27B-class dense FFN).  Every tensor has its own stream:
+and a 27B-class dense FFN), plus TinyLlama-1.1B's Q6_K tensors (the down
+projection and the vocab head of a Q4_K_M file).  Every tensor has its own stream:
 numpy.random.default_rng(SeedSequence([seed, cfg_id, tensor_idx])).
 """
 from dataclasses import dataclass, field
@@ -28,7 +34,7 @@ from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
-FMT_BLOCK = {"q4_0": (32, 18), "q8_0": (32, 34), "q4_k": (256, 144)}
+FMT_BLOCK = {"q4_0": (32, 18), "q8_0": (32, 34), "q4_k": (256, 144), "q6_k": (256, 210)}
 
 
 # --------------------------------------------------------------------------
@@ -95,6 +101,26 @@ def pack_q4_k(d, dmin, sc, m, q) -> np.ndarray:
     return raw.reshape(rows, nsb * 144)
 
 
+def pack_q6_k(d, sc, q) -> np.ndarray:
+    """d: float16 [rows][nsb]; sc: int8 [rows][nsb][16]; q: 0..63 [rows][cols]."""
+    rows, cols = q.shape
+    nsb = cols // 256
+    assert cols % 256 == 0 and d.shape == (rows, nsb) and sc.shape == (rows, nsb, 16)
+    c = np.asarray(q, dtype=np.uint8).reshape(rows, nsb, 2, 4, 32)   # [h][j][l]
+    assert int(c.max(initial=0)) < 64
+    lo, hi = c & 0x0F, c >> 4
+    raw = np.empty((rows, nsb, 210), dtype=np.uint8)
+    ql = np.empty((rows, nsb, 2, 2, 32), dtype=np.uint8)             # [h][j mod 2][l]
+    ql[:, :, :, 0, :] = lo[:, :, :, 0, :] | (lo[:, :, :, 2, :] << 4)
+    ql[:, :, :, 1, :] = lo[:, :, :, 1, :] | (lo[:, :, :, 3, :] << 4)
+    raw[:, :, 0:128] = ql.reshape(rows, nsb, 128)
+    qh = hi[:, :, :, 0, :] | (hi[:, :, :, 1, :] << 2) | (hi[:, :, :, 2, :] << 4) | (hi[:, :, :, 3, :] << 6)
+    raw[:, :, 128:192] = qh.reshape(rows, nsb, 64)
+    raw[:, :, 192:208] = np.ascontiguousarray(sc, dtype=np.int8).view(np.uint8)
+    raw[:, :, 208:210] = _f16_bytes(d)
+    return raw.reshape(rows, nsb * 210)
+
+
 # --------------------------------------------------------------------------
 # seeded draws
 # --------------------------------------------------------------------------
@@ -148,6 +174,14 @@ def draw_q4_k(rng, rows, cols, d_lo=1e-4, d_hi=1e-3):
     return d, dmin, sc, m, q
 
 
+def draw_q6_k(rng, rows, cols, d_lo=1e-4, d_hi=1e-3):
+    nsb = cols // 256
+    d = rng.uniform(d_lo, d_hi, (rows, nsb)).astype(np.float16)
+    sc = rng.integers(-128, 128, (rows, nsb, 16), dtype=np.int8)
+    q = rng.integers(0, 64, (rows, cols), dtype=np.uint8)
+    return d, sc, q
+
+
 def draw_i8row(rng, rows, cols, s_lo=1e-4, s_hi=1e-3):
     q = np.clip(np.rint(rng.normal(0.0, 40.0, (rows, cols))), -127, 127).astype(np.int8)
     s = rng.uniform(s_lo, s_hi, rows).astype(np.float32)
@@ -171,6 +205,11 @@ def make_tensor(fmt: str, rows: int, cols: int, rng: np.random.Generator, name: 
         t = QTensor(name, fmt, rows, cols, pack_q4_k(d, dmin, sc, m, q))
         if keep_logical:
             t.logical = {"d": d, "dmin": dmin, "sc": sc, "m": m, "q": q}
+    elif fmt == "q6_k":
+        d, sc, q = draw_q6_k(rng, rows, cols)
+        t = QTensor(name, fmt, rows, cols, pack_q6_k(d, sc, q))
+        if keep_logical:
+            t.logical = {"d": d, "sc": sc, "q": q}
     elif fmt == "i8row":
         q, s = draw_i8row(rng, rows, cols)
         t = QTensor(name, fmt, rows, cols, q, row_scale=s)
@@ -230,6 +269,9 @@ CFG5 = _reg(Workload(5, "dense27b_ffn_q4_0_5120x17408", "ffn",
                      (("gate", "q4_0", 17408, 5120), ("up", "q4_0", 17408, 5120),
                       ("down", "q4_0", 5120, 17408)),
                      n_tok=(1, 8, 128), d_model=5120, ffn=17408))
+CFG6 = _reg(Workload(6, "tinyllama_1.1b_q6_k_down_head", "gemvs",
+                     (("down", "q6_k", 2048, 5632), ("head", "q6_k", 32000, 2048)),
+                     d_model=2048, ffn=5632))
 
 
 def gen_tensor(w: Workload, idx: int, seed: int = 0, keep_logical: bool = False) -> QTensor:

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
+import synth
 from tests import _golden as G
 
 
@@ -273,6 +274,101 @@ def test_q4_k_one_hot_code_locates_column():
     assert np.array_equal(w, 5 * np.eye(256, dtype=np.float32))
 
 
+# ---------------------------------------------------------------- Q6_K -----
+def _q6_k_block(d_bits, scales16, codes256):
+    """One 210-byte super-block assembled byte by byte from 256 six-bit codes
+    (column c = 128h + 32j + l: low bits to ql[64h + 32(j mod 2) + l], nibble
+    j >= 2; top bits to bits 2j of qh[32h + l])."""
+    c = np.asarray(codes256, np.int64)
+    blk = np.zeros(210, np.int64)
+    for col in range(256):
+        h, j, l = col // 128, (col % 128) // 32, col % 32
+        blk[64 * h + 32 * (j % 2) + l] |= (c[col] & 15) << (4 if j >= 2 else 0)
+        blk[128 + 32 * h + l] |= (c[col] >> 4) << (2 * j)
+    blk[192:208] = np.asarray(scales16, np.int64) & 0xFF
+    blk[208], blk[209] = d_bits & 0xFF, d_bits >> 8
+    return blk.astype(np.uint8)
+
+
+def test_q6_k_golden_block():
+    g = G.load("q6_k_block.json")
+    blk = np.zeros(210, np.uint8)
+    blk[192:208] = G.hexbytes(g["scales_hex"])
+    blk[208:210] = G.hexbytes(g["d_hex"])
+    for off, hx in g["bytes_set"].items():
+        blk[int(off)] = int(hx, 16)
+    w = oracle.dequant("q6_k", blk.reshape(1, 210), 1, 256)[0]
+    for col, v in g["expected"].items():
+        assert w[int(col)] == G.num(v), col
+    y, _ = oracle.gemv("q6_k", blk.reshape(1, 210), np.ones(256, np.float32), 1, 256)
+    assert y[0] == G.num(g["y_ones"])
+
+
+def test_q6_k_bits_per_weight_is_the_pages_figure():
+    # 128 + 64 code bytes, 16 scale bytes and a 2-byte f16 per 256 weights:
+    # 6.5625 bits per weight, the "about 6.6" of the pages
+    per, nbytes = synth.FMT_BLOCK["q6_k"]
+    assert (per, nbytes) == (256, 210) and abs(8 * nbytes / per - 6.6) < 0.05
+    # the decoder's super-block and row strides are 210 bytes: a row of three
+    # blocks with d = 1, 2, 4 and every code 33 (w = d * sc)
+    ones = np.ones(16, np.int64)
+    rows = [np.concatenate([_q6_k_block(b, ones, np.full(256, 33)) for b in ds])
+            for ds in ((0x3C00, 0x4000, 0x4400), (0x4400, 0x3800, 0x3C00))]
+    w = oracle.dequant("q6_k", np.stack(rows), 2, 768)
+    assert np.array_equal(w, np.repeat(np.float32([[1, 2, 4], [4, 0.5, 1]]), 256, axis=1))
+
+
+def test_q6_k_closed_forms():
+    rng = np.random.default_rng(16)
+    codes = rng.integers(0, 64, 256)
+    sc = rng.integers(-128, 128, 16)
+    # d = 0, scales 0, or every code at the offset 32: every weight is zero
+    for d_bits, s16, c in ((0, sc, codes), (0x3C00, np.zeros(16, np.int64), codes), (0x3C00, sc, np.full(256, 32))):
+        w = oracle.dequant("q6_k", _q6_k_block(d_bits, s16, c).reshape(1, 210), 1, 256)[0]
+        assert np.all(w == 0)
+    # every code value at every position (scale 1, d = 1): w = q - 32
+    for k in range(4):
+        c = (np.arange(256) * 5 + 17 * k) % 64
+        w = oracle.dequant("q6_k", _q6_k_block(0x3C00, np.ones(16, np.int64), c).reshape(1, 210), 1, 256)[0]
+        assert np.array_equal(w, (c - 32).astype(np.float32))
+
+
+def test_q6_k_scales_are_signed_bytes():
+    # all 256 scale bytes over 16 blocks, code 33, d = 0.25: w = sc / 4 with
+    # sc the two's-complement value of the byte
+    rows = [_q6_k_block(0x3400, np.arange(16 * b, 16 * b + 16), np.full(256, 33)) for b in range(16)]
+    w = oracle.dequant("q6_k", np.stack(rows), 16, 256)
+    sc = np.arange(256).astype(np.uint8).view(np.int8).astype(np.float32)
+    assert np.array_equal(w, 0.25 * np.repeat(sc.reshape(16, 16), 16, axis=1))
+
+
+def test_q6_k_single_bit_locates_column():
+    # every code at 32 (ql 0x00, qh 0xAA): all weights zero; one flipped bit
+    # moves exactly one column, the one the layout names
+    base = np.zeros(210, np.uint8)
+    base[128:192] = 0xAA
+    base[192:208] = 1
+    base[208:210] = (0x00, 0x3C)
+    rows, want = [], []
+    for i in range(192):
+        for bit in range(8):
+            b = base.copy()
+            b[i] ^= 1 << bit
+            rows.append(b)
+            if i < 128:
+                col = 128 * (i // 64) + i % 64 + (64 if bit >= 4 else 0)
+                val = 2 ** (bit % 4)
+            else:
+                k = i - 128
+                col = 128 * (k // 32) + 32 * (bit // 2) + k % 32
+                val = 16 if bit % 2 == 0 else -32
+            want.append((col, val))
+    w = oracle.dequant("q6_k", np.stack(rows), len(rows), 256)
+    for r, (col, val) in enumerate(want):
+        nz = np.flatnonzero(w[r])
+        assert list(nz) == [col] and w[r, col] == val, (r // 8, r % 8)
+
+
 # ---------------------------------------------------------------- I8ROW ----
 def test_i8row_golden():
     g = G.load("i8row_row.json")
@@ -313,7 +409,7 @@ def test_i8row_dequant_rounds_once():
     assert np.array_equal(w, expect)
 
 
-@pytest.mark.parametrize("fmt,cols", [("q4_0", 33), ("q8_0", 48), ("q4_k", 300)])
+@pytest.mark.parametrize("fmt,cols", [("q4_0", 33), ("q8_0", 48), ("q4_k", 300), ("q6_k", 320)])
 def test_shape_refusals(fmt, cols):
     with pytest.raises(ValueError):
         oracle.dequant(fmt, np.zeros(4096, np.uint8), 1, cols)

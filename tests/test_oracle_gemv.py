@@ -38,6 +38,11 @@ def _exact_weights(fmt, L, rows, cols):
                 b, s = j // 256, (j % 256) // 32
                 W[i][j] = (Fraction(float(d[i, b])) * int(sc[i, b, s]) * int(q[i, j])
                            - Fraction(float(dmin[i, b])) * int(m[i, b, s]))
+    elif fmt == "q6_k":
+        d, sc, q = L["d"], L["sc"], L["q"]
+        for i in range(rows):
+            for j in range(cols):
+                W[i][j] = Fraction(float(d[i, j // 256])) * int(sc[i, j // 256, (j % 256) // 16]) * (int(q[i, j]) - 32)
     else:
         qq, s = L["q"], L["s"]
         for i in range(rows):
@@ -47,7 +52,7 @@ def _exact_weights(fmt, L, rows, cols):
 
 
 @pytest.mark.parametrize("fmt,rows,cols", [("q4_0", 32, 32), ("q8_0", 32, 64),
-                                           ("q4_k", 16, 256), ("i8row", 32, 32)])
+                                           ("q4_k", 16, 256), ("q6_k", 16, 512), ("i8row", 32, 32)])
 def test_brute_force_exact(fmt, rows, cols):
     rng = np.random.default_rng(11)
     t = synth.make_tensor(fmt, rows, cols, rng, keep_logical=True)
@@ -68,7 +73,7 @@ def test_brute_force_exact(fmt, rows, cols):
 
 
 @pytest.mark.parametrize("fmt,rows,cols", [("q4_0", 48, 96), ("q8_0", 40, 64),
-                                           ("q4_k", 24, 512), ("i8row", 40, 72)])
+                                           ("q4_k", 24, 512), ("q6_k", 24, 512), ("i8row", 40, 72)])
 def test_one_hot_x_selects_column(fmt, rows, cols):
     rng = np.random.default_rng(12)
     t = synth.make_tensor(fmt, rows, cols, rng)
@@ -84,7 +89,7 @@ def test_one_hot_x_selects_column(fmt, rows, cols):
         assert np.array_equal(S, np.abs(w[:, k]))
 
 
-@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "q4_k", "i8row"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "q4_k", "q6_k", "i8row"])
 def test_power_of_two_linearity_and_batching(fmt):
     rng = np.random.default_rng(13)
     rows, cols = 20, 512

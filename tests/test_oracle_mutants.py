@@ -32,6 +32,15 @@ MUTANTS = {
     "q4_k_min_high_bits_from_wrong_byte": ("((q[j] >> 6) << 4)", "((q[j - 4] >> 6) << 4)"),
     "q4_k_nibble_parity": ("(s % 2 == 0) ? (chunk[l] & 0x0F)", "(s % 2 == 1) ? (chunk[l] & 0x0F)"),
     "q4_k_chunk_stride": ("qs + 32 * (s / 2)", "qs + 16 * s"),
+    "q6_k_offset_31": ("(double)(q - 32)", "(double)(q - 31)"),
+    "q6_k_scale_per_32": ("(double)scales[c / 16]", "(double)scales[c / 32]"),
+    "q6_k_unsigned_scales": ("const int8_t *scales = (const int8_t *)(blk + 192);",
+                             "const uint8_t *scales = (const uint8_t *)(blk + 192);"),
+    "q6_k_qh_shift": ("(qh[32 * half + l] >> (2 * j)) & 3", "(qh[32 * half + l] >> j) & 3"),
+    "q6_k_ql_half_stride": ("ql[64 * half + 32 * (j % 2) + l]", "ql[32 * half + 32 * (j % 2) + l]"),
+    "q6_k_nibble_by_parity": ("(j < 2) ? (lo_byte & 0x0F)", "(j % 2 == 0) ? (lo_byte & 0x0F)"),
+    "q6_k_high_bits_low": ("int q = lo | (hi << 4);", "int q = (lo << 2) | hi;"),
+    "q6_k_d_first": ("rd_u16(blk + 208)", "rd_u16(blk)"),
     "i8row_first_row_scale": ("double s = (double)row_scale[r];", "double s = (double)row_scale[0];"),
     "gemv_output_transposed": ("y[t * nr + (o - row_begin)] = acc;", "y[(o - row_begin) * n_tok + t] = acc;"),
     "gemv_dropped_x": ("double p = row[j] * (double)xt[j];", "double p = row[j];"),

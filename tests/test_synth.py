@@ -48,6 +48,24 @@ def test_q4_k_pack_layout_by_hand():
     assert int(np.count_nonzero(raw[0, 16:])) == 2
 
 
+def test_q6_k_pack_layout_by_hand():
+    # the columns of the hand-worked super-block in tests/golden/q6_k_block.json
+    d = np.array([[0.5]], np.float16)
+    sc = np.array([[[-128, -8, -6, 1, -4, 7, -2, 127, 5, 3, 16, -1, 9, 2, -64, 11]]], np.int8)
+    q = np.zeros((1, 256), np.uint8)                           # every unlisted code is 0
+    for col, v in {0: 1, 32: 19, 64: 34, 96: 52, 31: 16, 63: 58, 95: 0, 127: 41,
+                   128: 63, 160: 39, 192: 21, 224: 0, 159: 32, 191: 12, 223: 32, 255: 19}.items():
+        q[0, col] = v
+    raw = synth.pack_q6_k(d, sc, q)
+    assert raw.shape == (1, 210)
+    want = {0: 0x21, 32: 0x43, 63: 0x9A, 64: 0x5F, 96: 0x07, 127: 0x3C,
+            128: 0xE4, 159: 0x8D, 160: 0x1B, 191: 0x62}
+    for off in range(192):
+        assert raw[0, off] == want.get(off, 0), off
+    assert bytes(raw[0, 192:208]).hex() == "80f8fa01fc07fe7f050310ff0902c00b"
+    assert list(raw[0, 208:210]) == [0x00, 0x38]
+
+
 def test_distributions_in_range():
     t = synth.make_tensor("q4_0", 64, 256, np.random.default_rng(0), keep_logical=True)
     d = t.logical["d"].astype(np.float64)
@@ -57,6 +75,8 @@ def test_distributions_in_range():
     assert 1e-4 <= t.row_scale.min() and t.row_scale.max() <= 1e-3
     t = synth.make_tensor("q4_k", 8, 512, np.random.default_rng(0), keep_logical=True)
     assert t.logical["sc"].max() < 64 and t.logical["q"].max() < 16
+    t = synth.make_tensor("q6_k", 8, 512, np.random.default_rng(0), keep_logical=True)
+    assert t.logical["sc"].min() >= -128 and t.logical["q"].max() < 64
 
 
 def test_algorithmic_bytes_match_block_sizes():
@@ -64,3 +84,4 @@ def test_algorithmic_bytes_match_block_sizes():
     assert synth.algorithmic_bytes("q8_0", 49152, 576) == 30_081_024
     assert synth.algorithmic_bytes("q4_k", 2048, 2048) == 2_359_296
     assert synth.algorithmic_bytes("i8row", 49152, 2048) == 100_859_904
+    assert synth.algorithmic_bytes("q6_k", 32000, 2048) == 53_760_000
