@@ -13,14 +13,14 @@ import torch
 
 __all__ = [
     "FORMATS", "QGemvError", "lib", "packed_bytes", "max_cols", "repack",
-    "qgemv", "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_k", "qgemv_i8row",
+    "qgemv", "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_k", "qgemv_i8row", "qgemv_q6_k",
     "swiglu_gate_up", "swiglu_ffn", "qdequant", "layout_version", "set_launch_override",
     "set_prefill_override", "swiglu_ffn_scratch_elems", "swiglu_ffn_block", "swiglu_ffn_block_scratch_elems",
     "qgemv_argmax", "qgemv_head_argmax",
-    "qgemv_repack_q4_0", "qgemv_repack_q8_0", "qgemv_repack_q4_k", "qgemv_repack_i8row",
+    "qgemv_repack_q4_0", "qgemv_repack_q8_0", "qgemv_repack_q4_k", "qgemv_repack_i8row", "qgemv_repack_q6_k",
 ]
 
-FORMATS = {"q4_0": 0, "q8_0": 1, "q4_k": 2, "i8row": 3}
+FORMATS = {"q4_0": 0, "q8_0": 1, "q4_k": 2, "i8row": 3, "q6_k": 4}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 
@@ -38,12 +38,12 @@ lib.qgemv_status_string.restype = ctypes.c_char_p
 lib.qgemv_max_cols.restype = _I64
 lib.qgemv_packed_bytes.argtypes = [_I, _I64, _I64]
 lib.qgemv_packed_bytes.restype = _I64
-for _n in ("qgemv_repack_q4_0", "qgemv_repack_q8_0", "qgemv_repack_q4_k"):
+for _n in ("qgemv_repack_q4_0", "qgemv_repack_q8_0", "qgemv_repack_q4_k", "qgemv_repack_q6_k"):
     getattr(lib, _n).argtypes = [_P, _P, _I64, _I64, _P]
     getattr(lib, _n).restype = _I
 lib.qgemv_repack_i8row.argtypes = [_P, _P, _P, _I64, _I64, _P]
 lib.qgemv_repack_i8row.restype = _I
-for _n in ("qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_k", "qgemv_i8row"):
+for _n in ("qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_k", "qgemv_i8row", "qgemv_q6_k"):
     getattr(lib, _n).argtypes = [_P, _P, _P, _I64, _I64, _I64, _P]
     getattr(lib, _n).restype = _I
 lib.qgemv.argtypes = [_I, _P, _P, _P, _I64, _I64, _I64, _P]
@@ -158,6 +158,11 @@ def qgemv_repack_q4_k(raw, packed, rows, cols, stream=None):
     _check(lib.qgemv_repack_q4_k(_ptr(raw), _ptr(packed), rows, cols, _stream(stream)), "qgemv_repack_q4_k")
 
 
+def qgemv_repack_q6_k(raw, packed, rows, cols, stream=None):
+    _dev(raw, packed)
+    _check(lib.qgemv_repack_q6_k(_ptr(raw), _ptr(packed), rows, cols, _stream(stream)), "qgemv_repack_q6_k")
+
+
 def qgemv_repack_i8row(q, row_scale, packed, rows, cols, stream=None):
     _dev(q, row_scale, packed)
     _check(lib.qgemv_repack_i8row(_ptr(q), _ptr(row_scale), _ptr(packed), rows, cols, _stream(stream)),
@@ -178,6 +183,8 @@ def repack(fmt, raw, rows, cols, row_scale=None, stream=None) -> torch.Tensor:
         qgemv_repack_q8_0(raw, packed, rows, cols, stream)
     elif f == 2:
         qgemv_repack_q4_k(raw, packed, rows, cols, stream)
+    elif f == 4:
+        qgemv_repack_q6_k(raw, packed, rows, cols, stream)
     else:
         qgemv_repack_i8row(raw, row_scale, packed, rows, cols, stream)
     return packed
@@ -215,6 +222,7 @@ qgemv_q4_0 = _gemv_named("qgemv_q4_0", 0)
 qgemv_q8_0 = _gemv_named("qgemv_q8_0", 1)
 qgemv_q4_k = _gemv_named("qgemv_q4_k", 2)
 qgemv_i8row = _gemv_named("qgemv_i8row", 3)
+qgemv_q6_k = _gemv_named("qgemv_q6_k", 4)
 
 
 def swiglu_gate_up(fmt, wg, wu, x, d_model, ffn, h=None, stream=None) -> torch.Tensor:

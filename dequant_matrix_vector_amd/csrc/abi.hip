@@ -12,7 +12,7 @@ using namespace qg;
 
 namespace {
 
-bool valid_fmt(int fmt) { return fmt >= QG_Q4_0 && fmt <= QG_I8ROW; }
+bool valid_fmt(int fmt) { return fmt >= QG_Q4_0 && fmt <= QG_Q6_K; }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -127,6 +127,7 @@ static int repack_common(int fmt, const void *raw, const float *row_scale, void 
     case QG_Q4_0: raw_bytes = rows * (cols / 32) * 18; break;
     case QG_Q8_0: raw_bytes = rows * (cols / 32) * 34; break;
     case QG_Q4_K: raw_bytes = rows * (cols / 256) * 144; break;
+    case QG_Q6_K: raw_bytes = rows * (cols / 256) * 210; break;
     default: raw_bytes = rows * cols; break;
     }
     if (overlap(raw, raw_bytes, packed, L.total)) return QG_ERR_ALIAS;
@@ -148,6 +149,10 @@ int qgemv_repack_q8_0(const void *raw, void *packed, int64_t rows, int64_t cols,
 int qgemv_repack_q4_k(const void *raw, void *packed, int64_t rows, int64_t cols, void *stream)
 {
     return repack_common(QG_Q4_K, raw, nullptr, packed, rows, cols, stream);
+}
+int qgemv_repack_q6_k(const void *raw, void *packed, int64_t rows, int64_t cols, void *stream)
+{
+    return repack_common(QG_Q6_K, raw, nullptr, packed, rows, cols, stream);
 }
 int qgemv_repack_i8row(const int8_t *q, const float *row_scale, void *packed, int64_t rows, int64_t cols,
                        void *stream)
@@ -194,6 +199,11 @@ int qgemv_i8row(const void *packed, const float *x, float *y, int64_t rows, int6
                 void *stream)
 {
     return qgemv(QG_I8ROW, packed, x, y, rows, cols, n_tok, stream);
+}
+int qgemv_q6_k(const void *packed, const float *x, float *y, int64_t rows, int64_t cols, int64_t n_tok,
+               void *stream)
+{
+    return qgemv(QG_Q6_K, packed, x, y, rows, cols, n_tok, stream);
 }
 
 int swiglu_gate_up(int fmt, const void *wg, const void *wu, const float *x, float *h, int64_t d_model,

@@ -24,6 +24,7 @@ hipError_t dispatch_fmt(int fmt, const GemvParams &p, const GemvCfg &c, hipStrea
         QG_FMT(QG_Q8_0)
         QG_FMT(QG_Q4_K)
         QG_FMT(QG_I8ROW)
+        QG_FMT(QG_Q6_K)
     }
 #undef QG_FMT
     return hipErrorInvalidValue;
@@ -115,6 +116,9 @@ GemvCfg choose_cfg(int fmt, int64_t rows, int64_t cols, int nmat)
         c.r = (nmat == 1 && rows >= 2048) ? 2 : 1;
         // long rows want deeper per-lane prefetch and more waves per workgroup
         c.depth = nchunk >= 256 ? 4 : 2;
+        // a Q6_K group holds more registers (high bits, scales, d): the fused
+        // pair keeps the shallow ring, which does not spill
+        if (fmt == QG_Q6_K && nmat == 2) c.depth = 2;
         c.waves = nmat == 2 ? 2 : (nchunk >= 256 ? 8 : 4);
         c.max_wg = 4 * cus;
     }
@@ -138,6 +142,8 @@ hipError_t launch_gemv(int fmt, const uint8_t *packed, const float *x, float *y,
     p.gamma = nullptr;
     p.eps = 0.0f;
     p.resid = resid;
+    p.hoff = L.hplane_off;
+    p.doff = L.dplane_off;
     return dispatch_fmt<1>(fmt, p, aligned_cfg(fmt, p.nchunk, cfg), s);
 }
 
@@ -159,6 +165,8 @@ hipError_t launch_gate_up(int fmt, const uint8_t *wg, const uint8_t *wu, const f
     p.gamma = gamma;
     p.eps = eps;
     p.resid = nullptr;
+    p.hoff = L.hplane_off;
+    p.doff = L.dplane_off;
     return dispatch_fmt<2>(fmt, p, aligned_cfg(fmt, p.nchunk, cfg), s);
 }
 

@@ -32,6 +32,15 @@
 // staged chunk sum, accumulated in the same order as the codes so that all-8
 // codes cancel exactly.
 //
+// 6-bit decode (Q6_K): the low four bits of each code sit in a word laid out
+// like Q4_0's, the top two bits in a second plane, placed so that one AND
+// moves them next to the nibble they extend (bits 4-5 / 20-21 for the first
+// mask, 8-9 / 24-25 for the second), giving q*2^-24 or q*2^-20 as before.
+// A 32-weight chunk spans two 16-weight sub-blocks with their own int8
+// scales: the first mask's codes (columns 0-15 of the chunk) and the second
+// mask's (16-31) go to two sums, and the offset of 32 is folded in through
+// two staged half-chunk sums.
+//
 // 8-bit decode (Q8_0, I8ROW): each signed byte converts with one SDWA
 // v_cvt_f32_i32 (sign-extending byte select) and feeds one fma.
 //
@@ -62,6 +71,8 @@ struct GemvParams {
     const float *gamma;   // EPI 1: RMSNorm gain [cols]
     float eps;            // EPI 1: RMSNorm epsilon
     const float *resid;   // EPI 2: residual [rows], added to y (may be y itself)
+    int64_t hoff;         // Q6_K: offsets of the high-bit plane and the f16 d plane
+    int64_t doff;
 };
 
 enum { kEpiPlain = 0, kEpiNorm = 1, kEpiResid = 2 };
@@ -125,15 +136,19 @@ __device__ __forceinline__ float dot_i8_chunk(uint4 a, uint4 b, const float4 (&x
     return t;
 }
 
+// kSums: staged sums of x per chunk (0: none, x not prescaled; 1: the chunk
+// sum; 2: the sums of its two 16-element halves).  kWords: 16-byte quant words
+// per chunk.
 template <int FMT> struct Fmt;
-template <> struct Fmt<QG_Q4_0> { static constexpr bool kPrescale = true; static constexpr int kWords = 1; };
-template <> struct Fmt<QG_Q4_K> { static constexpr bool kPrescale = true; static constexpr int kWords = 1; };
-template <> struct Fmt<QG_Q8_0> { static constexpr bool kPrescale = false; static constexpr int kWords = 2; };
-template <> struct Fmt<QG_I8ROW> { static constexpr bool kPrescale = false; static constexpr int kWords = 2; };
+template <> struct Fmt<QG_Q4_0> { static constexpr int kSums = 1; static constexpr int kWords = 1; };
+template <> struct Fmt<QG_Q4_K> { static constexpr int kSums = 1; static constexpr int kWords = 1; };
+template <> struct Fmt<QG_Q6_K> { static constexpr int kSums = 2; static constexpr int kWords = 1; };
+template <> struct Fmt<QG_Q8_0> { static constexpr int kSums = 0; static constexpr int kWords = 2; };
+template <> struct Fmt<QG_I8ROW> { static constexpr int kSums = 0; static constexpr int kWords = 2; };
 
 // ------------------------------------------------------------ x staging --
-// Per chunk: 32 values (scaled by 2^24 / 2^20 for the 4-bit formats) and,
-// for those, the chunk sum in the decode order.  A thread issues the loads of
+// Per chunk: 32 values (scaled by 2^24 / 2^20 for the 4- and 6-bit formats)
+// and, for those, the chunk sum (Q6_K: the two half sums) in the decode order.  A thread issues the loads of
 // its first two chunks before anything else (so they are not queued behind
 // the weight stream) and finishes them after the first weight loads are out.
 template <bool NORM> struct XStage {
@@ -179,13 +194,16 @@ __device__ __forceinline__ float chunk_sumsq(const float4 (&v)[8])
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <bool kPrescale>
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <int SUMS>
 __device__ __forceinline__ void stage_store(float4 (&v)[8], float *xs, int c)
 {
     // stores through a native vector type: a whole-struct float4 copy becomes a
     // memcpy, which keeps the staging registers out of registers (in scratch)
     f32x4 *dst = reinterpret_cast<f32x4 *>(xs + c * kXStride);
-    if (kPrescale) {
+    if constexpr (SUMS == 1) {
+        // in the order the codes are summed (see dot_q4_chunk)
         float sum = 0.0f;
 #pragma unroll
         for (int k = 0; k < 4; k++) {
@@ -198,6 +216,24 @@ __device__ __forceinline__ void stage_store(float4 (&v)[8], float *xs, int c)
             sum = sum + v[4 + k].y;
             sum = sum + v[4 + k].w;
         }
+        xs[c * kXStride + 32] = sum;
+    } else if constexpr (SUMS == 2) {
+        // each half in the order its codes are summed (columns 4k, 4k+2, 4k+1, 4k+3)
+        float a = 0.0f, b = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            a = a + v[k].x;
+            a = a + v[k].z;
+            b = b + v[4 + k].x;
+            b = b + v[4 + k].z;
+            a = a + v[k].y;
+            a = a + v[k].w;
+            b = b + v[4 + k].y;
+            b = b + v[4 + k].w;
+        }
+        *reinterpret_cast<f32x2 *>(xs + c * kXStride + 32) = f32x2{a, b};
+    }
+    if constexpr (SUMS > 0) {
 #pragma unroll
         for (int k = 0; k < 8; k++) {
             const float sc = k < 4 ? 0x1p24f : 0x1p20f;
@@ -206,7 +242,6 @@ __device__ __forceinline__ void stage_store(float4 (&v)[8], float *xs, int c)
             v[k].z *= sc;
             v[k].w *= sc;
         }
-        xs[c * kXStride + 32] = sum;
     }
 #pragma unroll
     for (int k = 0; k < 8; k++) dst[k] = f32x4{v[k].x, v[k].y, v[k].z, v[k].w};
@@ -214,7 +249,7 @@ __device__ __forceinline__ void stage_store(float4 (&v)[8], float *xs, int c)
 
 // x (times the gain, NORM) -> chunk c of the staging area; NORM adds the raw
 // chunk's sum of squares to ss when `count` (false for the clamped duplicate)
-template <bool kPrescale, bool NORM>
+template <int SUMS, bool NORM>
 __device__ __forceinline__ void stage_chunk(float4 (&v)[8], const float4 *gm, float *xs, int c, bool count, float &ss)
 {
     if constexpr (NORM) {
@@ -228,10 +263,10 @@ __device__ __forceinline__ void stage_chunk(float4 (&v)[8], const float4 *gm, fl
             v[k].w *= gm[k].w;
         }
     }
-    stage_store<kPrescale>(v, xs, c);
+    stage_store<SUMS>(v, xs, c);
 }
 
-template <bool kPrescale, bool NORM>
+template <int SUMS, bool NORM>
 __device__ __forceinline__ void stage_finish(float *xs, int nchunk, XStage<NORM> &st, float &ss)
 {
     // Branch-free for the first two chunks of each thread (an out-of-range
@@ -243,13 +278,13 @@ __device__ __forceinline__ void stage_finish(float *xs, int nchunk, XStage<NORM>
         const int c = (int)threadIdx.x + u * (int)blockDim.x;
         const float4 *gm = nullptr;
         if constexpr (NORM) gm = st.gm[u];
-        stage_chunk<kPrescale, NORM>(st.v[u], gm, xs, c < nchunk ? c : nchunk, c < nchunk, ss);
+        stage_chunk<SUMS, NORM>(st.v[u], gm, xs, c < nchunk ? c : nchunk, c < nchunk, ss);
     }
 }
 
 // Chunks beyond the first two per thread (only when nchunk > 2 * threads),
 // staged synchronously before any weight load is issued.
-template <bool kPrescale, bool NORM>
+template <int SUMS, bool NORM>
 __device__ __forceinline__ void stage_rest(const float *__restrict__ x, const float *__restrict__ gamma, float *xs,
                                            int nchunk, float &ss)
 {
@@ -258,8 +293,7 @@ __device__ __forceinline__ void stage_rest(const float *__restrict__ x, const fl
         float4 v[8];
 #pragma unroll
         for (int k = 0; k < 8; k++) v[k] = src[k];
-        stage_chunk<kPrescale, NORM>(v, reinterpret_cast<const float4 *>(gamma + (int64_t)c * kChunk), xs, c, true,
-                                     ss);
+        stage_chunk<SUMS, NORM>(v, reinterpret_cast<const float4 *>(gamma + (int64_t)c * kChunk), xs, c, true, ss);
     }
 }
 
@@ -270,12 +304,21 @@ template <int FMT, int CPL> struct Group;
 template <int CPL> struct Group<QG_Q4_0, CPL> { uint4 q[CPL]; uint32_t d[(CPL + 1) / 2]; };
 template <int CPL> struct Group<QG_Q8_0, CPL> { uint4 q[2 * CPL]; uint32_t d[(CPL + 1) / 2]; };
 template <int CPL> struct Group<QG_Q4_K, CPL> { uint4 q[CPL]; uint4 h; };
+// Q6_K: low nibbles, 8 bytes of high bits and two int8 scales per chunk, and
+// the super-block's f16 d (a group never crosses a super-block: CPL | 8)
+template <int CPL> struct Group<QG_Q6_K, CPL> {
+    uint4 q[CPL];
+    uint32_t h[2 * CPL];
+    uint32_t sc[(2 * CPL + 3) / 4];
+    uint32_t d;
+};
 template <int CPL> struct Group<QG_I8ROW, CPL> { uint4 q[2 * CPL]; };
 
-// Load the group starting at chunk c0 (c0 a multiple of CPL).
+// Load the group starting at chunk c0 (c0 a multiple of CPL).  hrow and drow
+// (the Q6_K high-bit and d planes) are unused by the other formats.
 template <int FMT, int CPL>
-__device__ __forceinline__ void load_group(Group<FMT, CPL> &o, const uint8_t *qrow, const uint8_t *srow, int c0,
-                                           int nchunk)
+__device__ __forceinline__ void load_group(Group<FMT, CPL> &o, const uint8_t *qrow, const uint8_t *srow,
+                                           const uint8_t *hrow, const uint8_t *drow, int c0, int nchunk)
 {
     constexpr int W = Fmt<FMT>::kWords;
     const uint4 *qp = reinterpret_cast<const uint4 *>(qrow + (int64_t)c0 * 16 * W);
@@ -294,6 +337,30 @@ __device__ __forceinline__ void load_group(Group<FMT, CPL> &o, const uint8_t *qr
         }
     } else if constexpr (FMT == QG_Q4_K) {
         o.h = reinterpret_cast<const uint4 *>(srow)[c0 >> 3];
+    } else if constexpr (FMT == QG_Q6_K) {
+        if constexpr (CPL == 1) {
+            const uint2 v = reinterpret_cast<const uint2 *>(hrow)[c0];
+            o.h[0] = v.x;
+            o.h[1] = v.y;
+            o.sc[0] = reinterpret_cast<const uint16_t *>(srow)[c0];
+        } else {
+#pragma unroll
+            for (int j = 0; j < CPL / 2; j++) {
+                const uint4 v = reinterpret_cast<const uint4 *>(hrow)[(c0 >> 1) + j];
+                o.h[4 * j] = v.x;
+                o.h[4 * j + 1] = v.y;
+                o.h[4 * j + 2] = v.z;
+                o.h[4 * j + 3] = v.w;
+            }
+            if constexpr (CPL == 2) {
+                o.sc[0] = reinterpret_cast<const uint32_t *>(srow)[c0 >> 1];
+            } else {
+                const uint2 v = reinterpret_cast<const uint2 *>(srow)[c0 >> 2];
+                o.sc[0] = v.x;
+                o.sc[1] = v.y;
+            }
+        }
+        o.d = reinterpret_cast<const uint16_t *>(drow)[c0 >> 3];
     }
 }
 
@@ -311,16 +378,46 @@ __device__ __forceinline__ Q4KSub q4k_sub(int s)
     return k;
 }
 
-// acc += contribution of chunk j of the group, x chunk in xv (+ its sum).
+// Q6_K: sum over one chunk of q*x for its two 16-column halves (columns 0-15
+// into ta, 16-31 into tb), codes of low word k extended by high word k/2
+// shifted by 2*(k mod 2); the same column order as the staged half sums.
+__device__ __forceinline__ void dot_q6_chunk(uint4 q, const uint32_t *h, const float4 (&xv)[8], float &ta,
+                                             float &tb)
+{
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    ta = 0.0f;
+    tb = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const uint32_t H = h[k >> 1] >> (2 * (k & 1));
+        const uint32_t pa = (w[k] & 0x000F000Fu) | (H & 0x00300030u);
+        const uint32_t pb = (w[k] & 0x00F000F0u) | (H & 0x03000300u);
+        const uint32_t s = w[k] >> 8;
+        const uint32_t pc = (s & 0x000F000Fu) | ((H >> 8) & 0x00300030u);
+        const uint32_t pd = (s & 0x00F000F0u) | ((H << 8) & 0x03000300u);
+        const float4 xl = xv[k], xh = xv[4 + k];
+        ta = __builtin_fmaf(half_lo(pa), xl.x, ta);
+        ta = __builtin_fmaf(half_hi(pa), xl.z, ta);
+        tb = __builtin_fmaf(half_lo(pb), xh.x, tb);
+        tb = __builtin_fmaf(half_hi(pb), xh.z, tb);
+        ta = __builtin_fmaf(half_lo(pc), xl.y, ta);
+        ta = __builtin_fmaf(half_hi(pc), xl.w, ta);
+        tb = __builtin_fmaf(half_lo(pd), xh.y, tb);
+        tb = __builtin_fmaf(half_hi(pd), xh.w, tb);
+    }
+}
+
+// acc += contribution of chunk j of the group, x chunk in xv (+ its staged
+// sums: xsum.x the chunk sum or the first half's, xsum.y the second half's).
 template <int FMT, int CPL, int J>
-__device__ __forceinline__ float consume(const Group<FMT, CPL> &g, const float4 (&xv)[8], float xsum, float acc,
+__device__ __forceinline__ float consume(const Group<FMT, CPL> &g, const float4 (&xv)[8], f32x2 xsum, float acc,
                                          const Q4KSub &ks)
 {
     if constexpr (FMT == QG_Q4_0 || FMT == QG_Q8_0) {
         const float d = (J & 1) ? half_hi(g.d[J >> 1]) : half_lo(g.d[J >> 1]);
         if constexpr (FMT == QG_Q4_0) {
             const float t = dot_q4_chunk(g.q[J], xv);
-            const float u = __builtin_fmaf(-8.0f, xsum, t);  // sum (q-8) x
+            const float u = __builtin_fmaf(-8.0f, xsum.x, t);  // sum (q-8) x
             return __builtin_fmaf(d, u, acc);
         } else {
             const float t = dot_i8_chunk(g.q[2 * J], g.q[2 * J + 1], xv, 0.0f);
@@ -336,7 +433,17 @@ __device__ __forceinline__ float consume(const Group<FMT, CPL> &g, const float4 
         const float D = half_lo(g.h.x) * (float)sc;   // exact
         const float M = half_hi(g.h.x) * (float)m;    // exact
         acc = __builtin_fmaf(D, t, acc);
-        return __builtin_fmaf(-M, xsum, acc);
+        return __builtin_fmaf(-M, xsum.x, acc);
+    } else if constexpr (FMT == QG_Q6_K) {
+        float ta, tb;
+        dot_q6_chunk(g.q[J], &g.h[2 * J], xv, ta, tb);
+        // int8 scales of the chunk's two sub-blocks: bytes 2J and 2J+1 of the group's run
+        const uint32_t sw = g.sc[J >> 1] >> (16 * (J & 1));
+        const float d = half_lo(g.d);
+        const float da = d * (float)(int8_t)(sw & 0xFFu);           // exact: 11-bit x 8-bit
+        const float db = d * (float)(int8_t)((sw >> 8) & 0xFFu);
+        acc = __builtin_fmaf(da, __builtin_fmaf(-32.0f, xsum.x, ta), acc);   // sum (q-32) x
+        return __builtin_fmaf(db, __builtin_fmaf(-32.0f, xsum.y, tb), acc);
     } else {
         return dot_i8_chunk(g.q[2 * J], g.q[2 * J + 1], xv, acc);
     }
@@ -393,6 +500,8 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
 
     const uint8_t *qrow[NMAT][R];
     const uint8_t *srow[NMAT][R];
+    const uint8_t *hrow[NMAT][R];   // Q6_K only
+    const uint8_t *drow[NMAT][R];   // Q6_K only
     Group<FMT, CPL> st[D][NMAT][R];
 
     auto set_rows = [&](int64_t b) {
@@ -405,9 +514,16 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
                 row = row < p.rows ? row : p.rows - 1;   // ragged tail: read a valid row, store nothing
                 qrow[m][r] = p.q[m] + row * p.row_qbytes;
                 const uint8_t *sp = p.q[m] + p.soff;
-                if (FMT == QG_Q4_0 || FMT == QG_Q8_0) srow[m][r] = sp + row * p.nchunk * 2;
+                if (FMT == QG_Q4_0 || FMT == QG_Q8_0 || FMT == QG_Q6_K) srow[m][r] = sp + row * p.nchunk * 2;
                 else if (FMT == QG_Q4_K) srow[m][r] = sp + row * (p.nchunk / 8) * 16;
                 else srow[m][r] = sp + row * 4;
+                if constexpr (FMT == QG_Q6_K) {
+                    hrow[m][r] = p.q[m] + p.hoff + row * p.nchunk * 8;
+                    drow[m][r] = p.q[m] + p.doff + row * (p.nchunk / 8) * 2;
+                } else {
+                    hrow[m][r] = nullptr;
+                    drow[m][r] = nullptr;
+                }
             }
         }
     };
@@ -419,24 +535,27 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
 #pragma unroll
         for (int m = 0; m < NMAT; m++)
 #pragma unroll
-            for (int r = 0; r < R; r++) load_group<FMT, CPL>(st[s][m][r], qrow[m][r], srow[m][r], c0, p.nchunk);
+            for (int r = 0; r < R; r++)
+                load_group<FMT, CPL>(st[s][m][r], qrow[m][r], srow[m][r], hrow[m][r], drow[m][r], c0, p.nchunk);
     };
     auto prologue = [&]() {
         const int last = P > 0 ? P - 1 : 0;
 #pragma unroll
         for (int s = 0; s < D; s++) load_stage(s, s < last ? s : last);
     };
-    auto read_x = [&](int c, float4 (&xv)[8]) -> float {
+    auto read_x = [&](int c, float4 (&xv)[8]) -> f32x2 {
         const float4 *xp = reinterpret_cast<const float4 *>(xs + c * kXStride);
 #pragma unroll
         for (int k = 0; k < 8; k++) xv[k] = xp[k];
-        return Fmt<FMT>::kPrescale ? xs[c * kXStride + 32] : 0.0f;
+        if constexpr (Fmt<FMT>::kSums == 2) return *reinterpret_cast<const f32x2 *>(xs + c * kXStride + 32);
+        else if constexpr (Fmt<FMT>::kSums == 1) return f32x2{xs[c * kXStride + 32], 0.0f};
+        else return f32x2{0.0f, 0.0f};
     };
     auto compute = [&](const Group<FMT, CPL> (&regs)[NMAT][R], int c0, float (&acc)[NMAT][R]) {
         static_for<CPL>([&](auto jj) {
             constexpr int J = decltype(jj)::value;
             float4 xv[8];
-            const float xsum = read_x(c0 + J, xv);
+            const f32x2 xsum = read_x(c0 + J, xv);
 #pragma unroll
             for (int m = 0; m < NMAT; m++)
 #pragma unroll
@@ -451,14 +570,14 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
         float ss = 0.0f;   // NORM: this thread's sum of x^2, chunks in a fixed order
         XStage<NORM> xst;
         stage_issue<NORM>(p.x, p.gamma, p.nchunk, xst);
-        stage_rest<Fmt<FMT>::kPrescale, NORM>(p.x, p.gamma, xs, p.nchunk, ss);
+        stage_rest<Fmt<FMT>::kSums, NORM>(p.x, p.gamma, xs, p.nchunk, ss);
         __builtin_amdgcn_sched_barrier(0);
         set_rows(batch < nbatch ? batch : nbatch - 1);   // idle waves read a valid row
         prologue();
         // x's loads went out first, so finishing the staging waits for them
         // only, not for the weight loads behind them
         __builtin_amdgcn_sched_barrier(0);
-        stage_finish<Fmt<FMT>::kPrescale, NORM>(xs, p.nchunk, xst, ss);
+        stage_finish<Fmt<FMT>::kSums, NORM>(xs, p.nchunk, xst, ss);
         if constexpr (NORM) {
             // wave sums (fixed xor tree) into the slots after the spare chunk
 #pragma unroll
@@ -512,9 +631,10 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
 #pragma unroll
                 for (int m = 0; m < NMAT; m++)
 #pragma unroll
-                    for (int r = 0; r < R; r++) load_group<FMT, 1>(tl[m][r], qrow[m][r], srow[m][r], c, p.nchunk);
+                    for (int r = 0; r < R; r++)
+                        load_group<FMT, 1>(tl[m][r], qrow[m][r], srow[m][r], hrow[m][r], drow[m][r], c, p.nchunk);
                 float4 xv[8];
-                const float xsum = read_x(c, xv);
+                const f32x2 xsum = read_x(c, xv);
                 const Q4KSub kt = q4k_sub(c);
 #pragma unroll
                 for (int m = 0; m < NMAT; m++)

@@ -8,7 +8,8 @@
 
 namespace qg {
 
-constexpr int kChunk = 32;           // weights per lane work item (a Q4_0/Q8_0 block, a Q4_K sub-block)
+constexpr int kChunk = 32;           // weights per lane work item (a Q4_0/Q8_0 block, a Q4_K sub-block,
+                                     // two Q6_K sub-blocks)
 constexpr int kXStride = 36;         // LDS floats per staged x chunk: 32 values + chunk sum + 3 pad
 constexpr int64_t kPlaneAlign = 256; // packed plane alignment
 constexpr int kLayoutVersion = 1;
@@ -25,11 +26,18 @@ inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 //         sub-block; scale plane = the raw 16-byte super-block headers
 //         (d, dmin, scales[12]) [rows][cols/256].
 //   I8ROW quant row = cols bytes; scale plane fp32 [rows].
+//   Q6_K  quant row = cols/2 bytes of low nibbles, 16 B per 32 columns in the
+//         Q4_0 nibble order; then a high-bit plane [rows][cols/4] (8 B per 32
+//         columns, each 32-bit word holding the top two bits of the codes of
+//         two quant words, placed for the kernel's masks); a scale plane of
+//         int8 [rows][cols/16]; a d plane of f16 [rows][cols/256].
 struct Layout {
     int64_t row_qbytes;   // bytes per row in the quant plane
     int64_t qplane_bytes; // rows * row_qbytes
     int64_t splane_off;   // offset of the scale plane
     int64_t splane_bytes;
+    int64_t hplane_off;   // Q6_K: offset of the high-bit plane (0 otherwise)
+    int64_t dplane_off;   // Q6_K: offset of the d plane (0 otherwise)
     int64_t total;
 };
 

@@ -34,10 +34,25 @@ bool layout_for(int fmt, int64_t rows, int64_t cols, Layout *L)
         L->row_qbytes = cols;
         L->splane_bytes = rows * 4;
         break;
+    case QG_Q6_K:
+        if (cols % 256) return false;
+        L->row_qbytes = cols / 2;
+        L->splane_bytes = rows * (cols / 16);
+        break;
     default:
         return false;
     }
     L->qplane_bytes = rows * L->row_qbytes;
+    L->hplane_off = 0;
+    L->dplane_off = 0;
+    if (fmt == QG_Q6_K) {
+        // quant, high-bit, scale and d planes, each at a 256-byte boundary
+        L->hplane_off = align_up(L->qplane_bytes, kPlaneAlign);
+        L->splane_off = align_up(L->hplane_off + rows * (cols / 4), kPlaneAlign);
+        L->dplane_off = align_up(L->splane_off + L->splane_bytes, kPlaneAlign);
+        L->total = align_up(L->dplane_off + rows * (cols / 256) * 2, kPlaneAlign);
+        return true;
+    }
     L->splane_off = align_up(L->qplane_bytes, kPlaneAlign);
     L->total = align_up(L->splane_off + L->splane_bytes, kPlaneAlign);
     return true;
@@ -106,6 +121,70 @@ __global__ void repack_q4_k_kernel(const uint8_t *__restrict__ raw, uint8_t *__r
             q[s * 16 + l] = (uint8_t)(lo | (hi << 4));
         }
     }
+}
+
+// Q6_K, one thread per 256-weight super-block.  Raw: ql[128], qh[64],
+// scales[16] (int8), d (f16); column c = 128h + 32j + l has its low four bits
+// in ql[64h + 32(j mod 2) + l] (high nibble when j >= 2) and its top two bits
+// at bit 2j of qh[32h + l].
+__device__ __forceinline__ uint32_t q6_code(const uint8_t *blk, int c)
+{
+    const int h = c >> 7, j = (c >> 5) & 3, l = c & 31;
+    const uint32_t lo = (blk[64 * h + 32 * (j & 1) + l] >> (j >= 2 ? 4 : 0)) & 0xFu;
+    const uint32_t hi = (blk[128 + 32 * h + l] >> (2 * j)) & 3u;
+    return lo | (hi << 4);
+}
+
+// Bit position, in the high-bit word of a packed quant word, of the top two
+// bits of the code at nibble position n (0..7) of that quant word: the
+// kernel's masks 0x000F000F | 0x00300030, 0x00F000F0 | 0x03000300 and the same
+// after a byte shift (high bits shifted by 8 the same way; the last mask takes
+// them shifted left by 8) read nibbles 0,4 / 1,5 / 2,6 / 3,7 with high bits at
+// 4,20 / 8,24 / 12,28 / 0,16.
+__device__ __forceinline__ int q6_hbit(int n)
+{
+    const int pos[8] = {4, 8, 12, 0, 20, 24, 28, 16};
+    return pos[n];
+}
+
+__global__ void repack_q6_k_kernel(const uint8_t *__restrict__ raw, uint8_t *__restrict__ packed,
+                                   int64_t nsbs, int64_t nsb, int64_t row_qbytes, int64_t hoff, int64_t soff,
+                                   int64_t doff)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nsbs) return;
+    int64_t r = i / nsb, sb = i % nsb;
+    const uint8_t *blk = raw + i * 210;
+    uint8_t *q = packed + r * row_qbytes + sb * 128;
+    uint32_t *hw = reinterpret_cast<uint32_t *>(packed + hoff + (r * nsb + sb) * 64);
+    for (int ch = 0; ch < 8; ch++) {
+        // quant word k of the chunk holds columns 4k..4k+3 (low nibbles) and
+        // 16+4k..16+4k+3 (high nibbles) of the chunk, byte by byte
+        for (int l = 0; l < 16; l++) {
+            const uint32_t a = q6_code(blk, 32 * ch + l) & 0xFu;
+            const uint32_t b = q6_code(blk, 32 * ch + 16 + l) & 0xFu;
+            q[16 * ch + l] = (uint8_t)(a | (b << 4));
+        }
+        // high-bit word m covers quant words 2m (shift 0) and 2m+1 (shift 2)
+        for (int m = 0; m < 2; m++) {
+            uint32_t v = 0;
+            for (int kk = 0; kk < 2; kk++) {
+                const int k = 2 * m + kk;
+                for (int n = 0; n < 8; n++) {
+                    // nibble n of quant word k: byte n/2, low (n even) or high nibble
+                    const int col = (n & 1) ? 16 + 4 * k + (n >> 1) : 4 * k + (n >> 1);
+                    const uint32_t hi = q6_code(blk, 32 * ch + col) >> 4;
+                    v |= hi << (q6_hbit(n) + 2 * kk);
+                }
+            }
+            hw[2 * ch + m] = v;
+        }
+    }
+    uint8_t *sc = packed + soff + (r * nsb + sb) * 16;
+    for (int l = 0; l < 16; l++) sc[l] = blk[192 + l];
+    uint8_t *d = packed + doff + (r * nsb + sb) * 2;
+    d[0] = blk[208];
+    d[1] = blk[209];
 }
 
 __global__ void repack_i8row_kernel(const uint8_t *__restrict__ q, const float *__restrict__ scale,
@@ -182,6 +261,38 @@ __global__ void dequant_q4_k_kernel(const uint8_t *__restrict__ packed, float *_
     }
 }
 
+// Q6_K, one thread per 32-wide chunk, through the same masks as the GEMV
+// kernel; d*sc (11 x 8 significant bits) times q-32 is exact in binary32.
+__global__ void dequant_q6_k_kernel(const uint8_t *__restrict__ packed, float *__restrict__ w, int64_t nchunks,
+                                    int64_t nch, int64_t row_qbytes, int64_t hoff, int64_t soff, int64_t doff)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nchunks) return;
+    int64_t r = i / nch, c = i % nch;
+    const uint32_t *qw = reinterpret_cast<const uint32_t *>(packed + r * row_qbytes + c * 16);
+    const uint32_t *hw = reinterpret_cast<const uint32_t *>(packed + hoff + i * 8);
+    const int8_t *sc = reinterpret_cast<const int8_t *>(packed + soff + i * 2);
+    const float d = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(packed + doff)[r * (nch / 8) + c / 8]);
+    const float da = d * (float)sc[0], db = d * (float)sc[1];
+    float *o = w + i * 32;
+    for (int k = 0; k < 4; k++) {
+        const uint32_t H = hw[k >> 1] >> (2 * (k & 1));
+        const uint32_t pa = (qw[k] & 0x000F000Fu) | (H & 0x00300030u);
+        const uint32_t pb = (qw[k] & 0x00F000F0u) | (H & 0x03000300u);
+        const uint32_t sh = qw[k] >> 8;
+        const uint32_t pc = (sh & 0x000F000Fu) | ((H >> 8) & 0x00300030u);
+        const uint32_t pd = (sh & 0x00F000F0u) | ((H << 8) & 0x03000300u);
+        o[4 * k] = da * (float)((int)(pa & 0x3Fu) - 32);
+        o[4 * k + 2] = da * (float)((int)((pa >> 16) & 0x3Fu) - 32);
+        o[4 * k + 1] = da * (float)((int)(pc & 0x3Fu) - 32);
+        o[4 * k + 3] = da * (float)((int)((pc >> 16) & 0x3Fu) - 32);
+        o[16 + 4 * k] = db * (float)((int)((pb >> 4) & 0x3Fu) - 32);
+        o[16 + 4 * k + 2] = db * (float)((int)((pb >> 20) & 0x3Fu) - 32);
+        o[16 + 4 * k + 1] = db * (float)((int)((pd >> 4) & 0x3Fu) - 32);
+        o[16 + 4 * k + 3] = db * (float)((int)((pd >> 20) & 0x3Fu) - 32);
+    }
+}
+
 __global__ void dequant_i8row_kernel(const uint8_t *__restrict__ packed, float *__restrict__ w,
                                      int64_t rows, int64_t cols, int64_t soff)
 {
@@ -225,6 +336,12 @@ hipError_t launch_repack(int fmt, const void *raw, const float *row_scale, uint8
         repack_i8row_kernel<<<grid_for(n, bs), bs, 0, st>>>(src, row_scale, packed, rows, cols, L.splane_off);
         break;
     }
+    case QG_Q6_K: {
+        int64_t n = rows * (cols / 256);
+        repack_q6_k_kernel<<<grid_for(n, bs), bs, 0, st>>>(src, packed, n, cols / 256, L.row_qbytes, L.hplane_off,
+                                                           L.splane_off, L.dplane_off);
+        break;
+    }
     default:
         return hipErrorInvalidValue;
     }
@@ -256,6 +373,12 @@ hipError_t launch_dequant(int fmt, const uint8_t *packed, float *w, int64_t rows
     case QG_I8ROW: {
         int64_t n = rows * cols;
         dequant_i8row_kernel<<<grid_for(n, bs), bs, 0, st>>>(packed, w, rows, cols, L.splane_off);
+        break;
+    }
+    case QG_Q6_K: {
+        int64_t n = rows * (cols / 32);
+        dequant_q6_k_kernel<<<grid_for(n, bs), bs, 0, st>>>(packed, w, n, cols / 32, L.row_qbytes, L.hplane_off,
+                                                            L.splane_off, L.dplane_off);
         break;
     }
     default:

@@ -27,9 +27,12 @@
  *  - Block formats: Q8_0 (llmoxide blog section 10: f16 scale + 32 int8, 34 B);
  *    Q4_0 (Go "llm" package README, Design points: 18-byte blocks; w=(q-8)*d);
  *    Q4_K (llamini.cpp post, "What I reimplemented": 256-weight super-blocks,
- *    six-bit scale/min pairs unpacked by get_scale_min_k4, 144 B); per-row
- *    symmetric INT8 (minillm-cpp README, Quantization paragraph: one scale per
- *    output row).  The byte layouts of the raw blocks are spelled out below.
+ *    six-bit scale/min pairs unpacked by get_scale_min_k4, 144 B); Q6_K
+ *    (llmoxide blog section 10: the other k-quant, 256-weight super-blocks
+ *    with their own scales at about 6.6 bits per weight; the llamini.cpp post
+ *    names it the second format of a Q4_K_M file; 210 B); per-row symmetric
+ *    INT8 (minillm-cpp README, Quantization paragraph: one scale per output
+ *    row).  The byte layouts of the raw blocks are spelled out below.
  *  - SwiGLU: gate = Wg x, up = Wu x, h = silu(gate) * up, out = Wd h (llmoxide
  *    blog, section 2 "Layers, and the bend between them"; dasLLAMA-00, section
  *    8.7.1.6.3); no residual add and no normalization inside.
@@ -47,10 +50,16 @@
  *         pairs for the eight 32-wide sub-blocks (get_scale_min_k4 packing);
  *         128 code bytes, byte 32c+l holding element l of sub-block 2c (low
  *         nibble) and of sub-block 2c+1 (high nibble); w = d*sc*q - dmin*m.
+ *   Q6_K  B=256, 210 bytes (the GGUF layout of the files the pages load; the
+ *         pages give only the size): ql[128], qh[64], 16 int8 scales (one per
+ *         16 columns), f16 d.  The 6-bit code of column c = 128h + 32j + l
+ *         (h < 2, j < 4, l < 32) has its low four bits in ql[64h + 32(j%2) + l]
+ *         (low nibble for j < 2, high nibble for j >= 2) and its top two bits
+ *         at bits 2j..2j+1 of qh[32h + l]; w = d * scales[c/16] * (q - 32).
  *   I8ROW int8 codes [rows][cols] plus fp32 scales [rows]; w = s_row * q.
  *
  * Shape rules: rows, cols, n_tok >= 1; cols a multiple of 32 (Q4_0, Q8_0,
- * I8ROW) or of 256 (Q4_K); cols <= qgemv_max_cols(); rows, cols < 2^31.
+ * I8ROW) or of 256 (Q4_K, Q6_K); cols <= qgemv_max_cols(); rows, cols < 2^31.
  * Alignment: packed buffers 256 bytes; x, y, h, out and w_out 16 bytes.
  */
 #ifndef QGEMV_H
@@ -75,7 +84,7 @@ typedef enum {
     QG_ERR_DEVICE = -8   /* no usable HIP device / device query failed */
 } qg_status;
 
-typedef enum { QG_Q4_0 = 0, QG_Q8_0 = 1, QG_Q4_K = 2, QG_I8ROW = 3 } qg_format;
+typedef enum { QG_Q4_0 = 0, QG_Q8_0 = 1, QG_Q4_K = 2, QG_I8ROW = 3, QG_Q6_K = 4 } qg_format;
 
 /* Version of the packed (repacked) layout; packed buffers are only valid for
  * the library that wrote them. */
@@ -90,8 +99,9 @@ int64_t qgemv_max_cols(void);
 
 /* Bytes of the packed buffer for a [rows][cols] tensor of format fmt, or a
  * negative qg_status if the shape or format is invalid.  The packed buffer
- * holds exactly the raw format's bytes (quant plane + scale plane), plus
- * padding to 256-byte plane boundaries. */
+ * holds exactly the raw format's bytes (quant plane + scale plane; Q6_K:
+ * low-nibble, high-bit, scale and d planes), plus padding to 256-byte plane
+ * boundaries. */
 int64_t qgemv_packed_bytes(int fmt, int64_t rows, int64_t cols);
 
 /* Load-time repack: raw blocks (device, layout above) -> packed planes
@@ -101,6 +111,7 @@ int64_t qgemv_packed_bytes(int fmt, int64_t rows, int64_t cols);
 int qgemv_repack_q4_0(const void *raw, void *packed, int64_t rows, int64_t cols, void *stream);
 int qgemv_repack_q8_0(const void *raw, void *packed, int64_t rows, int64_t cols, void *stream);
 int qgemv_repack_q4_k(const void *raw, void *packed, int64_t rows, int64_t cols, void *stream);
+int qgemv_repack_q6_k(const void *raw, void *packed, int64_t rows, int64_t cols, void *stream);
 int qgemv_repack_i8row(const int8_t *q, const float *row_scale, void *packed, int64_t rows,
                        int64_t cols, void *stream);
 
@@ -124,8 +135,10 @@ int qgemv_q4_k(const void *packed, const float *x, float *y, int64_t rows, int64
                int64_t n_tok, void *stream);
 int qgemv_i8row(const void *packed, const float *x, float *y, int64_t rows, int64_t cols,
                 int64_t n_tok, void *stream);
+int qgemv_q6_k(const void *packed, const float *x, float *y, int64_t rows, int64_t cols,
+               int64_t n_tok, void *stream);
 
-/* Format-generic form of the four calls above. */
+/* Format-generic form of the five calls above. */
 int qgemv(int fmt, const void *packed, const float *x, float *y, int64_t rows, int64_t cols,
           int64_t n_tok, void *stream);
 

@@ -50,6 +50,10 @@ def test_host_only_queries(lib):
     assert lib.qgemv_packed_bytes(1, 49152, 576) == 49152 * 576 + 49152 * 18 * 2
     assert lib.qgemv_packed_bytes(2, 3, 256) == 512 + 256
     assert lib.qgemv_packed_bytes(3, 5, 32) == 256 + 256
+    # Q6_K: low-nibble, high-bit, scale and d planes; 210 bytes per 256 weights
+    assert lib.qgemv_packed_bytes(4, 32000, 2048) == 32000 * 8 * 210
+    assert lib.qgemv_packed_bytes(4, 3, 256) == 512 + 256 + 256 + 256
+    assert lib.qgemv_packed_bytes(4, 3, 288) == -2
     assert lib.qgemv_packed_bytes(0, 4, 48) == -2     # not a block multiple
     assert lib.qgemv_packed_bytes(9, 4, 64) == -4     # unknown format
     lib.qgemv_status_string.restype = ctypes.c_char_p
@@ -68,6 +72,7 @@ def test_refusals_before_any_device_call(lib):
     assert lib.qgemv(0, fake, fake, fake, 0, 32, 1, None) == -2
     assert lib.qgemv(0, fake, fake, fake, 4, 32, 0, None) == -2
     assert lib.qgemv(2, fake, fake, fake, 4, 300, 1, None) == -2
+    assert lib.qgemv(4, fake, fake, fake, 4, 288, 1, None) == -2
 
 
 def test_prefill_override_validation(lib):

@@ -87,6 +87,13 @@ def test_head_argmax_vocab_heads(wname, idx, n_tok):
     _check_head(t, n_tok, 40 + n_tok)
 
 
+def test_head_argmax_q6_k_head():
+    # TinyLlama's Q6_K vocab head, 32000 rows
+    t = synth.gen_tensor(synth.CFG6, 1)
+    assert (t.fmt, t.rows) == ("q6_k", 32000)
+    _check_head(t, 1, 47)
+
+
 def test_head_argmax_matrix_cores():
     # a Q4_0 head at 8 tokens runs the product on the matrix cores first
     t = synth.make_tensor("q4_0", 4096, 1024, np.random.default_rng(45))

@@ -18,13 +18,14 @@ from tests import _gpu as G
 
 pytestmark = pytest.mark.gpu
 
-FMTS = ["q4_0", "q8_0", "q4_k", "i8row"]
+FMTS = ["q4_0", "q8_0", "q4_k", "i8row", "q6_k"]
 # (rows, cols): ragged rows, cols that pick 8/16/32/64 lanes per row
 SHAPES = {
     "q4_0": [(1, 32), (7, 288), (131, 576), (200, 1536), (97, 5120), (33, 17408)],
     "q8_0": [(1, 32), (45, 576), (130, 2048), (67, 4096)],
     "q4_k": [(1, 256), (37, 2048), (129, 5632), (20, 4096)],
     "i8row": [(1, 32), (70, 2048), (131, 8192), (9, 96)],
+    "q6_k": [(1, 256), (37, 2048), (129, 5632), (20, 4096), (33, 768)],
 }
 
 
@@ -57,7 +58,8 @@ def test_gemv_within_bound(fmt):
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_one_hot_x_gives_exact_column(fmt):
-    rows, cols = {"q4_0": (77, 1536), "q8_0": (77, 576), "q4_k": (77, 2048), "i8row": (77, 2048)}[fmt]
+    rows, cols = {"q4_0": (77, 1536), "q8_0": (77, 576), "q4_k": (77, 2048), "i8row": (77, 2048),
+                  "q6_k": (77, 2048)}[fmt]
     t = _tensor(fmt, rows, cols, 400)
     packed = G.upload(t)
     for k in (0, 1, 15, 16, 17, 31, 32, cols // 2 + 5, cols - 1):
@@ -86,6 +88,13 @@ def _pow2_tensor(fmt, rows, cols, rng):
         dmin = (2.0 ** rng.integers(-10, -8, (rows, nsb))).astype(np.float16)
         return synth.pack_q4_k(d, dmin, rng.integers(0, 64, (rows, nsb, 8)), rng.integers(0, 64, (rows, nsb, 8)),
                                rng.integers(0, 16, (rows, cols)))
+    if fmt == "q6_k":
+        # |d * sc * (q - 32)| <= 2^-9 * 8 * 32: partial sums stay multiples of
+        # 2^-10 far below 2^14
+        nsb = cols // 256
+        d = (2.0 ** rng.integers(-10, -8, (rows, nsb))).astype(np.float16)
+        return synth.pack_q6_k(d, rng.integers(-8, 9, (rows, nsb, 16)).astype(np.int8),
+                               rng.integers(0, 64, (rows, cols)))
     raise ValueError(fmt)
 
 
@@ -110,7 +119,8 @@ def test_integer_inputs_bit_exact(fmt):
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_determinism_and_power_of_two_linearity(fmt):
-    rows, cols = {"q4_0": (300, 5120), "q8_0": (300, 576), "q4_k": (300, 2048), "i8row": (300, 2048)}[fmt]
+    rows, cols = {"q4_0": (300, 5120), "q8_0": (300, 576), "q4_k": (300, 2048), "i8row": (300, 2048),
+                  "q6_k": (300, 5632)}[fmt]
     t = _tensor(fmt, rows, cols, 600)
     packed = G.upload(t)
     x = np.random.default_rng(601).standard_normal(cols).astype(np.float32)
@@ -123,7 +133,8 @@ def test_determinism_and_power_of_two_linearity(fmt):
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_batched_tokens_match_single(fmt):
-    rows, cols = {"q4_0": (96, 576), "q8_0": (96, 576), "q4_k": (96, 2048), "i8row": (96, 2048)}[fmt]
+    rows, cols = {"q4_0": (96, 576), "q8_0": (96, 576), "q4_k": (96, 2048), "i8row": (96, 2048),
+                  "q6_k": (96, 2048)}[fmt]
     t = _tensor(fmt, rows, cols, 700)
     packed = G.upload(t)
     x = np.random.default_rng(701).standard_normal((5, cols)).astype(np.float32)
@@ -145,7 +156,7 @@ def test_batched_tokens_match_single(fmt):
 def test_every_launch_shape(fmt):
     # every lanes-per-row / rows-per-group / waves / prefetch-depth choice the
     # tuning hook allows, with and without a grid-stride workgroup cap
-    rows, cols = 203, {"q4_0": 1536, "q8_0": 1536, "q4_k": 2048, "i8row": 1536}[fmt]
+    rows, cols = 203, {"q4_0": 1536, "q8_0": 1536, "q4_k": 2048, "i8row": 1536, "q6_k": 2048}[fmt]
     t = _tensor(fmt, rows, cols, 800)
     packed = G.upload(t)
     x = np.random.default_rng(801).standard_normal(cols).astype(np.float32)
@@ -167,7 +178,7 @@ def test_every_launch_shape(fmt):
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_gate_up_every_launch_shape(fmt):
-    d_model, ffn = (2048, 203) if fmt == "q4_k" else (1536, 203)   # ragged ffn rows
+    d_model, ffn = (2048, 203) if fmt in ("q4_k", "q6_k") else (1536, 203)   # ragged ffn rows
     rng = np.random.default_rng(850)
     g = synth.make_tensor(fmt, ffn, d_model, rng)
     u = synth.make_tensor(fmt, ffn, d_model, rng)
@@ -211,6 +222,25 @@ def test_grouped_scales_with_odd_chunk_rows(fmt):
         G.qg().set_launch_override(0)
 
 
+def test_q6_k_neutral_codes_give_exact_zero():
+    # every code 32: w = 0 whatever d and the scales; the offset is folded in
+    # through the staged half-chunk sums, summed in the codes' own order, so
+    # the products cancel exactly for any x (under every launch shape)
+    rows, cols = 75, 2048
+    rng = np.random.default_rng(880)
+    d, sc, _ = synth.draw_q6_k(rng, rows, cols)
+    t = synth.QTensor("w", "q6_k", rows, cols, synth.pack_q6_k(d, sc, np.full((rows, cols), 32)))
+    packed = G.upload(t)
+    x = (100.0 * rng.standard_normal(cols)).astype(np.float32)
+    assert np.all(G.gemv_gpu(t, packed, x) == 0)
+    try:
+        for lpr, cpl in ((8, 1), (16, 2), (32, 2), (64, 1)):
+            G.qg().set_launch_override(lpr, 2, 4, 2, 0, cpl)
+            assert np.all(G.gemv_gpu(t, packed, x) == 0), (lpr, cpl)
+    finally:
+        G.qg().set_launch_override(0)
+
+
 # ----------------------------------------------------------------- SwiGLU --
 def _ffn_tensors(fmt, d_model, ffn, seed):
     rng = np.random.default_rng(seed)
@@ -220,7 +250,7 @@ def _ffn_tensors(fmt, d_model, ffn, seed):
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_swiglu_small(fmt):
-    d_model, ffn = (256, 768) if fmt == "q4_k" else (288, 768)
+    d_model, ffn = (256, 768) if fmt in ("q4_k", "q6_k") else (288, 768)
     tens = _ffn_tensors(fmt, d_model, ffn, 900)
     x = np.random.default_rng(901).standard_normal((1, d_model)).astype(np.float32)
     out, h, r, hb = G.check_ffn(fmt, tens, x, d_model, ffn, f"ffn {fmt}")
