@@ -26,12 +26,23 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
+def _headers():
+    return glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(INCLUDE, "*.h"))
+
+
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source and link the library.  incremental=True skips a
+    source whose object is newer than it and every header (a development
+    convenience; the default always recompiles)."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
+    newest_header = max((os.path.getmtime(h) for h in _headers()), default=0.0)
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        if incremental and os.path.exists(obj) and \
+                os.path.getmtime(obj) > max(os.path.getmtime(src), newest_header):
+            return obj
         cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
@@ -52,4 +63,5 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    print(build(verbose=True, incremental="--incremental" in sys.argv))

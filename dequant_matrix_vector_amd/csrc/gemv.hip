@@ -105,6 +105,26 @@ GemvCfg choose_cfg(int fmt, int64_t rows, int64_t cols, int nmat)
         }
     }
     const int cus = cu_count();
+    if (fmt == QG_Q6_K) {
+        // Q6_K (sweeps over the TinyLlama Q6_K vocab head [32000][2048] and
+        // down projection [2048][5632]): short rows take narrow lane groups
+        // with many rows in flight; long rows take 32 lanes with two chunks
+        // each and a deep ring (shallow for the fused pair, which would spill)
+        c.r = 1;
+        c.max_wg = 4 * cus;
+        if (nchunk < 128) {
+            c.lpr = 8;
+            c.cpl = 1;
+            c.waves = 2;
+            c.depth = 2;
+        } else {
+            c.lpr = 32;
+            c.cpl = 2;
+            c.waves = 4;
+            c.depth = nmat == 2 ? 2 : 4;
+        }
+        return c;
+    }
     if (eight_bit) {
         c.r = rows >= 2048 ? 2 : 1;
         c.depth = nmat == 2 ? 2 : 4;
@@ -116,9 +136,6 @@ GemvCfg choose_cfg(int fmt, int64_t rows, int64_t cols, int nmat)
         c.r = (nmat == 1 && rows >= 2048) ? 2 : 1;
         // long rows want deeper per-lane prefetch and more waves per workgroup
         c.depth = nchunk >= 256 ? 4 : 2;
-        // a Q6_K group holds more registers (high bits, scales, d): the fused
-        // pair keeps the shallow ring, which does not spill
-        if (fmt == QG_Q6_K && nmat == 2) c.depth = 2;
         c.waves = nmat == 2 ? 2 : (nchunk >= 256 ? 8 : 4);
         c.max_wg = 4 * cus;
     }
