@@ -64,6 +64,12 @@ def _load():
     lib.oracle_ffn_block.restype = ctypes.c_int
     lib.oracle_argmax.argtypes = [P, I64]
     lib.oracle_argmax.restype = I64
+    lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+    lib.oracle_quantize_q8_0.argtypes = [P, I64, I64, P, P]
+    lib.oracle_quantize_q8_0.restype = ctypes.c_int
+    lib.oracle_gemv_q8act.argtypes = [ctypes.c_int, P, P, I64, I64, I64, P, P]
+    lib.oracle_gemv_q8act.restype = ctypes.c_int
     lib.oracle_silu.argtypes = [ctypes.c_double]
     lib.oracle_silu.restype = ctypes.c_double
     lib.oracle_swiglu.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, I64, I64, I64,
@@ -209,3 +215,35 @@ def argmax(v) -> int:
     if r < 0:
         raise ValueError(f"oracle argmax: status {r}")
     return int(r)
+
+
+def f32_to_f16(f) -> int:
+    """binary16 bits of a binary32 value, round to nearest even."""
+    return int(_load().oracle_f32_to_f16(float(np.float32(f))))
+
+
+def quantize_q8_0(x):
+    """Q8_0 blocks of activation rows: (d_bits uint16 [n_tok][n/32], q int8 [n_tok][n])
+    for float32 x [n_tok][n] (or [n])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    squeeze = x.ndim == 1
+    n = x.shape[-1]
+    x2 = x.reshape(-1, n)
+    d = np.empty((x2.shape[0], n // 32), dtype=np.uint16)
+    q = np.empty(x2.shape, dtype=np.int8)
+    _check(_load().oracle_quantize_q8_0(_ptr(x2), n, x2.shape[0], _ptr(d), _ptr(q)), "quantize_q8_0")
+    return (d[0], q[0]) if squeeze else (d, q)
+
+
+def gemv_q8act(fmt, raw, x, rows, cols):
+    """(y, S) float64 [n_tok][rows] of W times the Q8_0 representation of x."""
+    raw = _raw(raw)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    squeeze = x.ndim == 1
+    x2 = x.reshape(-1, cols)
+    n_tok = x2.shape[0]
+    y = np.empty((n_tok, rows), dtype=np.float64)
+    S = np.empty((n_tok, rows), dtype=np.float64)
+    _check(_load().oracle_gemv_q8act(_fmt(fmt), _ptr(raw), _ptr(x2), rows, cols, n_tok, _ptr(y), _ptr(S)),
+           "gemv_q8act")
+    return (y[0], S[0]) if squeeze else (y, S)

@@ -57,6 +57,14 @@
  * first index on ties): start from index 0 and move to a later index only
  * when its logit is strictly greater.
  *
+ * Q8_0 activations (the Go "llm" package's ExactGGML mode: activations are
+ * quantised to Q8_0 before every quantised matrix product).  Reading: per
+ * 32-element block, d = max|x| / 127, q = round(x * (1/d)) with halves away
+ * from zero (q = 0 when d = 0), all in binary32; the block stores d rounded
+ * to binary16 (nearest even, the package's F32ToF16), so the product sees
+ * x replaced by f16(d) * q.  The oracle's product is then the plain one on
+ * that representation, in binary64.
+ *
  * Parity pins for every function live in tests/test_oracle_*.py.
  */
 #include <math.h>
@@ -90,6 +98,38 @@ double oracle_f16_to_f64(uint16_t h)
 }
 
 static uint16_t rd_u16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* binary32 -> binary16 bits, round to nearest even (the Go "llm" package's
+ * F32ToF16).  The magnitude is divided, exactly, by the binary16 spacing of
+ * its binade (2^-24 below 2^-14) and rounded by nearbyint in the default
+ * nearest-even mode; past the largest finite value (65504) it is infinite. */
+uint16_t oracle_f32_to_f16(float f)
+{
+    const uint16_t sign = signbit(f) ? 0x8000 : 0;
+    if (isnan(f))
+        return sign | 0x7E00;
+    double a = fabs((double)f);
+    if (isinf(f))
+        return sign | 0x7C00;
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);   /* a in [2^(e-1), 2^e) */
+    int ue = e - 1;
+    if (ue < -14)
+        ue = -14;
+    const double spacing = ldexp(1.0, ue - 10);
+    const double r = nearbyint(a / spacing);
+    const double v = r * spacing;
+    if (v > 65504.0)
+        return sign | 0x7C00;
+    if (v < ldexp(1.0, -14))
+        return sign | (uint16_t)r;   /* subnormal: v = r * 2^-24 */
+    frexp(v, &e);
+    ue = e - 1;
+    const uint16_t frac = (uint16_t)(ldexp(v, 10 - ue) - 1024.0);
+    return sign | (uint16_t)((ue + 15) << 10) | frac;
+}
 
 /* Q4_K scale/min unpack for sub-block j (0..7) from the 12-byte field q, as
  * the llamini.cpp post describes it: sub-blocks 0-3 keep their 6-bit scale and
@@ -348,6 +388,62 @@ int oracle_ffn_block(int fmt, const void *wg, const float *sg, const void *wu, c
     for (int64_t i = 0; i < n_tok * d_model; i++)
         out[i] = (double)x[i] + d[i];
     return OR_OK;
+}
+
+/* Q8_0 quantization of activation rows: n a multiple of 32, x [n_tok][n];
+ * d_bits [n_tok][n/32] binary16 scales, q [n_tok][n] codes. */
+int oracle_quantize_q8_0(const float *x, int64_t n, int64_t n_tok, uint16_t *d_bits, int8_t *q)
+{
+    if (n < 0 || n % 32 || n_tok < 0)
+        return OR_ERR_SHAPE;
+    for (int64_t b = 0; b < n_tok * (n / 32); b++) {
+        const float *xb = x + 32 * b;
+        float amax = 0.0f;
+        for (int l = 0; l < 32; l++) {
+            const float a = fabsf(xb[l]);
+            if (a > amax)
+                amax = a;
+        }
+        const float d = amax / 127.0f;
+        const float id = d != 0.0f ? 1.0f / d : 0.0f;
+        for (int l = 0; l < 32; l++)
+            q[32 * b + l] = (int8_t)roundf(xb[l] * id);
+        d_bits[b] = oracle_f32_to_f16(d);
+    }
+    return OR_OK;
+}
+
+/* y = Wdeq xq with xq the Q8_0 representation of x (f16(d) * q per block),
+ * binary64; S = sum_j |w_ij * xq_tj|.  Q4_0 and Q8_0 weights (the formats of
+ * the model the mode was written for). */
+int oracle_gemv_q8act(int fmt, const void *raw, const float *x, int64_t rows, int64_t cols, int64_t n_tok,
+                      double *y, double *S)
+{
+    if (fmt != OR_Q4_0 && fmt != OR_Q8_0)
+        return OR_ERR_FORMAT;
+    int st = check_shape(fmt, rows, cols);
+    if (st)
+        return st;
+    if (n_tok < 0)
+        return OR_ERR_SHAPE;
+    const int64_t nx = n_tok * cols;
+    uint16_t *d_bits = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(nx / 32 + 1));
+    int8_t *q = (int8_t *)malloc((size_t)(nx + 1));
+    double *xq = (double *)malloc(sizeof(double) * (size_t)(nx + 1));
+    if (!d_bits || !q || !xq) {
+        free(d_bits);
+        free(q);
+        free(xq);
+        return OR_ERR_NOMEM;
+    }
+    oracle_quantize_q8_0(x, cols, n_tok, d_bits, q);
+    for (int64_t j = 0; j < nx; j++)
+        xq[j] = oracle_f16_to_f64(d_bits[j / 32]) * (double)q[j];
+    st = oracle_gemv_f64x(fmt, raw, NULL, xq, rows, cols, n_tok, y, S);
+    free(d_bits);
+    free(q);
+    free(xq);
+    return st;
 }
 
 /* Index of the largest of v[0..n), scanning in order and replacing the best

@@ -15,7 +15,7 @@ from oracle import build as obuild
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_FILES = ["tests/test_oracle_decode.py", "tests/test_oracle_gemv.py", "tests/test_oracle_swiglu.py",
-             "tests/test_oracle_norm.py", "tests/test_oracle_argmax.py"]
+             "tests/test_oracle_norm.py", "tests/test_oracle_argmax.py", "tests/test_oracle_q8act.py"]
 
 MUTANTS = {
     "f16_exponent_bias": ("ldexp((double)(1024 + m), e - 25)", "ldexp((double)(1024 + m), e - 24)"),
@@ -41,6 +41,13 @@ MUTANTS = {
     "q6_k_nibble_by_parity": ("(j < 2) ? (lo_byte & 0x0F)", "(j % 2 == 0) ? (lo_byte & 0x0F)"),
     "q6_k_high_bits_low": ("int q = lo | (hi << 4);", "int q = (lo << 2) | hi;"),
     "q6_k_d_first": ("rd_u16(blk + 208)", "rd_u16(blk)"),
+    "f16_round_down": ("const double r = nearbyint(a / spacing);", "const double r = floor(a / spacing);"),
+    "f16_spacing": ("const double spacing = ldexp(1.0, ue - 10);", "const double spacing = ldexp(1.0, ue - 11);"),
+    "q8act_scale_128": ("const float d = amax / 127.0f;", "const float d = amax / 128.0f;"),
+    "q8act_truncated_codes": ("(int8_t)roundf(xb[l] * id)", "(int8_t)(xb[l] * id)"),
+    "q8act_ties_to_even": ("(int8_t)roundf(xb[l] * id)", "(int8_t)rintf(xb[l] * id)"),
+    "q8act_signed_max": ("const float a = fabsf(xb[l]);", "const float a = xb[l];"),
+    "q8act_block_scale_index": ("oracle_f16_to_f64(d_bits[j / 32])", "oracle_f16_to_f64(d_bits[j / 64])"),
     "i8row_first_row_scale": ("double s = (double)row_scale[r];", "double s = (double)row_scale[0];"),
     "gemv_output_transposed": ("y[t * nr + (o - row_begin)] = acc;", "y[(o - row_begin) * n_tok + t] = acc;"),
     "gemv_dropped_x": ("double p = row[j] * (double)xt[j];", "double p = row[j];"),
