@@ -16,7 +16,7 @@ __all__ = [
     "qgemv", "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_k", "qgemv_i8row", "qgemv_q6_k",
     "swiglu_gate_up", "swiglu_ffn", "qdequant", "layout_version", "set_launch_override",
     "set_prefill_override", "swiglu_ffn_scratch_elems", "swiglu_ffn_block", "swiglu_ffn_block_scratch_elems",
-    "qgemv_argmax", "qgemv_head_argmax",
+    "qgemv_argmax", "qgemv_head_argmax", "qgemv_q8act", "swiglu_ffn_q8act", "qquantize_q8_0",
     "qgemv_repack_q4_0", "qgemv_repack_q8_0", "qgemv_repack_q4_k", "qgemv_repack_i8row", "qgemv_repack_q6_k",
 ]
 
@@ -64,6 +64,12 @@ lib.qgemv_head_argmax.argtypes = [_I, _P, _P, _P, _P, _I64, _I64, _I64, _P]
 lib.qgemv_head_argmax.restype = _I
 lib.qdequant.argtypes = [_I, _P, _P, _I64, _I64, _P]
 lib.qdequant.restype = _I
+lib.qgemv_q8act.argtypes = [_I, _P, _P, _P, _I64, _I64, _I64, _P]
+lib.qgemv_q8act.restype = _I
+lib.swiglu_ffn_q8act.argtypes = [_I, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
+lib.swiglu_ffn_q8act.restype = _I
+lib.qquantize_q8_0.argtypes = [_P, _P, _I64, _I64, _P]
+lib.qquantize_q8_0.restype = _I
 lib.qgemv_set_launch_override.argtypes = [_I, _I, _I, _I, _I, _I]
 lib.qgemv_set_launch_override.restype = _I
 lib.qgemv_set_prefill_override.argtypes = [_I, _I, _I, _I, _I]
@@ -252,6 +258,38 @@ def swiglu_ffn(fmt, wg, wu, wd, x, d_model, ffn, out=None, h_scratch=None, strea
     _check(lib.swiglu_ffn(_fmt(fmt), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(x), _ptr(out), _ptr(h_scratch),
                           h_scratch.numel(), d_model, ffn, n_tok, _stream(stream)), "swiglu_ffn")
     return out, h_scratch.view(-1)[:n_tok * ffn].view(n_tok, ffn)
+
+
+def qgemv_q8act(fmt, packed, x, rows, cols, y=None, stream=None) -> torch.Tensor:
+    """y [n_tok][rows] = W xq, xq the Q8_0 representation of x (Q4_0, Q8_0 weights)."""
+    n_tok = x.numel() // cols
+    y = _y(y, (rows,) if x.dim() == 1 else (n_tok, rows), x.device)
+    _dev(packed, x, y)
+    _check(lib.qgemv_q8act(_fmt(fmt), _ptr(packed), _ptr(x), _ptr(y), rows, cols, n_tok, _stream(stream)),
+           "qgemv_q8act")
+    return y
+
+
+def swiglu_ffn_q8act(fmt, wg, wu, wd, x, d_model, ffn, out=None, h_scratch=None, stream=None):
+    """(out, h): the SwiGLU FFN with x and h quantized to Q8_0 before their products."""
+    n_tok = x.numel() // d_model
+    out = _y(out, (n_tok, d_model), x.device)
+    if h_scratch is None:
+        h_scratch = torch.empty(n_tok * ffn, dtype=torch.float32, device=x.device)
+    _dev(wg, wu, wd, x, out, h_scratch)
+    _check(lib.swiglu_ffn_q8act(_fmt(fmt), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(x), _ptr(out), _ptr(h_scratch),
+                                h_scratch.numel(), d_model, ffn, n_tok, _stream(stream)), "swiglu_ffn_q8act")
+    return out, h_scratch.view(-1)[:n_tok * ffn].view(n_tok, ffn)
+
+
+def qquantize_q8_0(x, n, blocks=None, stream=None) -> torch.Tensor:
+    """Raw Q8_0 blocks (uint8 [n_tok][n/32 * 34]) of activation rows x [n_tok][n]."""
+    n_tok = x.numel() // n
+    if blocks is None:
+        blocks = torch.empty((n_tok, n // 32 * 34), dtype=torch.uint8, device=x.device)
+    _dev(x, blocks)
+    _check(lib.qquantize_q8_0(_ptr(x), _ptr(blocks), n, n_tok, _stream(stream)), "qquantize_q8_0")
+    return blocks
 
 
 def qdequant(fmt, packed, rows, cols, w_out=None, stream=None) -> torch.Tensor:

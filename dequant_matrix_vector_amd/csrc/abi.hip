@@ -251,9 +251,10 @@ int64_t swiglu_ffn_scratch_elems(int fmt, int64_t d_model, int64_t ffn, int64_t 
     return part > 0 ? ffn_part_offset(d_model, ffn, n_tok) + part : n_tok * ffn;
 }
 
-int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const float *x, float *out,
-               float *h_scratch, int64_t h_scratch_elems, int64_t d_model, int64_t ffn, int64_t n_tok,
-               void *stream)
+// Checks shared by swiglu_ffn and swiglu_ffn_q8act.
+static int check_ffn(int fmt, const void *wg, const void *wu, const void *wd, const float *x, const float *out,
+                     const float *h_scratch, int64_t h_scratch_elems, int64_t d_model, int64_t ffn, int64_t n_tok,
+                     Layout *Lg_out, Layout *Ld_out)
 {
     if (!valid_fmt(fmt)) return QG_ERR_FORMAT;
     if (!wg || !wu || !wd || !x || !out || !h_scratch) return QG_ERR_NULL;
@@ -274,6 +275,18 @@ int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const fl
         overlap(wd, Ld.total, h_scratch, hb) || overlap(wg, Lg.total, out, xb) || overlap(wu, Lg.total, out, xb) ||
         overlap(wd, Ld.total, out, xb))
         return QG_ERR_ALIAS;
+    *Lg_out = Lg;
+    *Ld_out = Ld;
+    return QG_OK;
+}
+
+int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const float *x, float *out,
+               float *h_scratch, int64_t h_scratch_elems, int64_t d_model, int64_t ffn, int64_t n_tok,
+               void *stream)
+{
+    Layout Lg, Ld;
+    const int st = check_ffn(fmt, wg, wu, wd, x, out, h_scratch, h_scratch_elems, d_model, ffn, n_tok, &Lg, &Ld);
+    if (st) return st;
     hipStream_t s = (hipStream_t)stream;
     if (fmt == QG_Q4_0 && n_tok > 1 && prefill_enabled()) {
         // partial sums of a K split go behind h, when the caller's scratch has room
@@ -407,6 +420,61 @@ int qgemv_head_argmax(int fmt, const void *packed, const float *x, float *logits
     st = qgemv(fmt, packed, x, logits, rows, cols, n_tok, stream);
     if (st) return st;
     return launch_argmax(logits, token, rows, n_tok, (hipStream_t)stream) == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+// ------------------------------------------------------ Q8_0 activations --
+static bool q8act_fmt(int fmt) { return fmt == QG_Q4_0 || fmt == QG_Q8_0; }
+
+int qgemv_q8act(int fmt, const void *packed, const float *x, float *y, int64_t rows, int64_t cols, int64_t n_tok,
+                void *stream)
+{
+    if (!q8act_fmt(fmt)) return QG_ERR_FORMAT;
+    Layout L;
+    int st = check_product(fmt, packed, x, y, rows, cols, n_tok, &L);
+    if (st) return st;
+    const GemvCfg cfg = choose_cfg(fmt, rows, cols, 1);
+    for (int64_t t = 0; t < n_tok; t++) {
+        if (launch_gemv(fmt | kQ8Act, static_cast<const uint8_t *>(packed), x + t * cols, y + t * rows, rows, cols,
+                        (hipStream_t)stream, cfg) != hipSuccess)
+            return QG_ERR_LAUNCH;
+    }
+    return QG_OK;
+}
+
+int swiglu_ffn_q8act(int fmt, const void *wg, const void *wu, const void *wd, const float *x, float *out,
+                     float *h_scratch, int64_t h_scratch_elems, int64_t d_model, int64_t ffn, int64_t n_tok,
+                     void *stream)
+{
+    if (!q8act_fmt(fmt)) return QG_ERR_FORMAT;
+    Layout Lg, Ld;
+    const int st = check_ffn(fmt, wg, wu, wd, x, out, h_scratch, h_scratch_elems, d_model, ffn, n_tok, &Lg, &Ld);
+    if (st) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const GemvCfg cg = choose_cfg(fmt, ffn, d_model, 2);
+    const GemvCfg cd = choose_cfg(fmt, d_model, ffn, 1);
+    for (int64_t t = 0; t < n_tok; t++) {
+        if (launch_gate_up(fmt | kQ8Act, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu),
+                           x + t * d_model, h_scratch + t * ffn, ffn, d_model, s, cg) != hipSuccess)
+            return QG_ERR_LAUNCH;
+    }
+    for (int64_t t = 0; t < n_tok; t++) {
+        if (launch_gemv(fmt | kQ8Act, static_cast<const uint8_t *>(wd), h_scratch + t * ffn, out + t * d_model,
+                        d_model, ffn, s, cd) != hipSuccess)
+            return QG_ERR_LAUNCH;
+    }
+    return QG_OK;
+}
+
+int qquantize_q8_0(const float *x, void *blocks, int64_t n, int64_t n_tok, void *stream)
+{
+    if (!x || !blocks) return QG_ERR_NULL;
+    if (n < 32 || n % 32 || n >= (int64_t(1) << 31) || n_tok < 1 || n_tok >= (int64_t(1) << 31))
+        return QG_ERR_SHAPE;
+    if (!aligned(x, 16)) return QG_ERR_ALIGN;
+    if (overlap(x, n * n_tok * 4, blocks, n_tok * (n / 32) * 34)) return QG_ERR_ALIAS;
+    return launch_quantize_q8_0(x, static_cast<uint8_t *>(blocks), n, n_tok, (hipStream_t)stream) == hipSuccess
+               ? QG_OK
+               : QG_ERR_LAUNCH;
 }
 
 int qdequant(int fmt, const void *packed, float *w_out, int64_t rows, int64_t cols, void *stream)

@@ -25,6 +25,11 @@ hipError_t dispatch_fmt(int fmt, const GemvParams &p, const GemvCfg &c, hipStrea
         QG_FMT(QG_Q4_K)
         QG_FMT(QG_I8ROW)
         QG_FMT(QG_Q6_K)
+    // Q8_0 activations: plain epilogue only
+    case QG_Q4_0 | kQ8Act:
+        return epi == 0 ? gemv_dispatch<QG_Q4_0 | kQ8Act, NMAT, 0>(p, c, s) : hipErrorInvalidValue;
+    case QG_Q8_0 | kQ8Act:
+        return epi == 0 ? gemv_dispatch<QG_Q8_0 | kQ8Act, NMAT, 0>(p, c, s) : hipErrorInvalidValue;
     }
 #undef QG_FMT
     return hipErrorInvalidValue;
@@ -146,7 +151,7 @@ hipError_t launch_gemv(int fmt, const uint8_t *packed, const float *x, float *y,
                        int64_t cols, hipStream_t s, const GemvCfg &cfg, const float *resid)
 {
     Layout L;
-    if (!layout_for(fmt, rows, cols, &L)) return hipErrorInvalidValue;
+    if (!layout_for(fmt & ~kQ8Act, rows, cols, &L)) return hipErrorInvalidValue;
     GemvParams p;
     p.q[0] = packed;
     p.q[1] = packed;
@@ -169,7 +174,7 @@ hipError_t launch_gate_up(int fmt, const uint8_t *wg, const uint8_t *wu, const f
                           float eps)
 {
     Layout L;
-    if (!layout_for(fmt, ffn, d_model, &L)) return hipErrorInvalidValue;
+    if (!layout_for(fmt & ~kQ8Act, ffn, d_model, &L)) return hipErrorInvalidValue;
     GemvParams p;
     p.q[0] = wg;
     p.q[1] = wu;

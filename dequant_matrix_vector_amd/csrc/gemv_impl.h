@@ -44,6 +44,13 @@
 // 8-bit decode (Q8_0, I8ROW): each signed byte converts with one SDWA
 // v_cvt_f32_i32 (sign-extending byte select) and feeds one fma.
 //
+// Q8_0 activations (format code + kQ8Act, Q4_0 and Q8_0 weights): the
+// workgroup quantizes each staged chunk of x to Q8_0 (q8act.h) and stores its
+// 32 codes, its binary16 scale and its code sum; a chunk's dot product is then
+// exact integer arithmetic (v_dot4_i32_i8 on the codes; Q4_0 nibbles are
+// 0..15 bytes, the offset of 8 folded in through the code sum), scaled once
+// by d_w * d_x (exact in binary32) into the fp32 accumulator.
+//
 // Epilogue variants (EPI): 0 plain; 1 (gate/up) the input is RMS-normalized
 // with a per-element gain (llmoxide blog, section 4 "Keeping the numbers in
 // range"): the workgroup stages x*gamma and sums x^2 while staging, and the
@@ -54,6 +61,7 @@
 #include <atomic>
 #include <type_traits>
 
+#include "q8act.h"
 #include "qg_internal.h"
 
 namespace qg {
@@ -145,6 +153,9 @@ template <> struct Fmt<QG_Q4_K> { static constexpr int kSums = 1; static constex
 template <> struct Fmt<QG_Q6_K> { static constexpr int kSums = 2; static constexpr int kWords = 1; };
 template <> struct Fmt<QG_Q8_0> { static constexpr int kSums = 0; static constexpr int kWords = 2; };
 template <> struct Fmt<QG_I8ROW> { static constexpr int kSums = 0; static constexpr int kWords = 2; };
+// kSums = -1: x staged as Q8_0 codes (8 words), the binary16 scale and the code sum
+template <> struct Fmt<QG_Q4_0 | kQ8Act> { static constexpr int kSums = -1; static constexpr int kWords = 1; };
+template <> struct Fmt<QG_Q8_0 | kQ8Act> { static constexpr int kSums = -1; static constexpr int kWords = 2; };
 
 // ------------------------------------------------------------ x staging --
 // Per chunk: 32 values (scaled by 2^24 / 2^20 for the 4- and 6-bit formats)
@@ -195,10 +206,20 @@ __device__ __forceinline__ float chunk_sumsq(const float4 (&v)[8])
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int SUMS>
 __device__ __forceinline__ void stage_store(float4 (&v)[8], float *xs, int c)
 {
+    if constexpr (SUMS < 0) {
+        Q8Chunk qc;
+        quantize_chunk_q8_0(v, qc);
+        u32x4 *dq = reinterpret_cast<u32x4 *>(xs + c * kXStride);
+        dq[0] = u32x4{qc.q[0], qc.q[1], qc.q[2], qc.q[3]};
+        dq[1] = u32x4{qc.q[4], qc.q[5], qc.q[6], qc.q[7]};
+        *reinterpret_cast<f32x2 *>(xs + c * kXStride + 8) = f32x2{qc.d, (float)qc.qsum};
+        return;
+    }
     // stores through a native vector type: a whole-struct float4 copy becomes a
     // memcpy, which keeps the staging registers out of registers (in scratch)
     f32x4 *dst = reinterpret_cast<f32x4 *>(xs + c * kXStride);
@@ -407,13 +428,47 @@ __device__ __forceinline__ void dot_q6_chunk(uint4 q, const uint32_t *h, const f
     }
 }
 
-// acc += contribution of chunk j of the group, x chunk in xv (+ its staged
-// sums: xsum.x the chunk sum or the first half's, xsum.y the second half's).
-template <int FMT, int CPL, int J>
-__device__ __forceinline__ float consume(const Group<FMT, CPL> &g, const float4 (&xv)[8], f32x2 xsum, float acc,
-                                         const Q4KSub &ks)
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c)
 {
-    if constexpr (FMT == QG_Q4_0 || FMT == QG_Q8_0) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// acc += contribution of chunk j of the group, x chunk in xv (+ its staged
+// sums: xsum.x the chunk sum or the first half's, xsum.y the second half's;
+// Q8_0 activations: xv[0..1] the codes, xsum = (d_x, code sum)).
+template <int FMT, int CPL, int J>
+__device__ __forceinline__ float consume(const Group<(FMT & 7), CPL> &g, const float4 (&xv)[8], f32x2 xsum,
+                                         float acc, const Q4KSub &ks)
+{
+    if constexpr ((FMT & kQ8Act) != 0) {
+        const uint32_t qx[8] = {__builtin_bit_cast(uint32_t, xv[0].x), __builtin_bit_cast(uint32_t, xv[0].y),
+                                __builtin_bit_cast(uint32_t, xv[0].z), __builtin_bit_cast(uint32_t, xv[0].w),
+                                __builtin_bit_cast(uint32_t, xv[1].x), __builtin_bit_cast(uint32_t, xv[1].y),
+                                __builtin_bit_cast(uint32_t, xv[1].z), __builtin_bit_cast(uint32_t, xv[1].w)};
+        int isum = 0;
+        if constexpr ((FMT & 7) == QG_Q4_0) {
+            // word k: low nibbles are columns 4k..4k+3, high nibbles 16+4k..16+4k+3
+            const uint32_t w[4] = {g.q[J].x, g.q[J].y, g.q[J].z, g.q[J].w};
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                isum = dot4(w[k] & 0x0F0F0F0Fu, qx[k], isum);
+                isum = dot4((w[k] >> 4) & 0x0F0F0F0Fu, qx[4 + k], isum);
+            }
+            isum -= 8 * (int)xsum.y;   // sum (q - 8) q_x
+        } else {
+            const uint4 a = g.q[2 * J], b = g.q[2 * J + 1];
+            isum = dot4(a.x, qx[0], isum);
+            isum = dot4(a.y, qx[1], isum);
+            isum = dot4(a.z, qx[2], isum);
+            isum = dot4(a.w, qx[3], isum);
+            isum = dot4(b.x, qx[4], isum);
+            isum = dot4(b.y, qx[5], isum);
+            isum = dot4(b.z, qx[6], isum);
+            isum = dot4(b.w, qx[7], isum);
+        }
+        const float dw = (J & 1) ? half_hi(g.d[J >> 1]) : half_lo(g.d[J >> 1]);
+        return __builtin_fmaf(dw * xsum.x, (float)isum, acc);   // dw * d_x exact: two binary16 significands
+    } else if constexpr (FMT == QG_Q4_0 || FMT == QG_Q8_0) {
         const float d = (J & 1) ? half_hi(g.d[J >> 1]) : half_lo(g.d[J >> 1]);
         if constexpr (FMT == QG_Q4_0) {
             const float t = dot_q4_chunk(g.q[J], xv);
@@ -481,6 +536,8 @@ template <int FMT, int LPR, int R, int NMAT, int D, int CPL, int EPI>
 __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
 {
     constexpr bool NORM = EPI == kEpiNorm;
+    constexpr int BF = FMT & 7;   // the weight format (FMT may carry kQ8Act)
+    static_assert((FMT & kQ8Act) == 0 || EPI == kEpiPlain, "Q8_0 activations: plain epilogue only");
     extern __shared__ float4 qg_lds[];
     float *xs = reinterpret_cast<float *>(qg_lds);
 
@@ -502,7 +559,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
     const uint8_t *srow[NMAT][R];
     const uint8_t *hrow[NMAT][R];   // Q6_K only
     const uint8_t *drow[NMAT][R];   // Q6_K only
-    Group<FMT, CPL> st[D][NMAT][R];
+    Group<BF, CPL> st[D][NMAT][R];
 
     auto set_rows = [&](int64_t b) {
         const int64_t row0 = b * (G * R) + (int64_t)g * R;
@@ -514,10 +571,10 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
                 row = row < p.rows ? row : p.rows - 1;   // ragged tail: read a valid row, store nothing
                 qrow[m][r] = p.q[m] + row * p.row_qbytes;
                 const uint8_t *sp = p.q[m] + p.soff;
-                if (FMT == QG_Q4_0 || FMT == QG_Q8_0 || FMT == QG_Q6_K) srow[m][r] = sp + row * p.nchunk * 2;
-                else if (FMT == QG_Q4_K) srow[m][r] = sp + row * (p.nchunk / 8) * 16;
+                if (BF == QG_Q4_0 || BF == QG_Q8_0 || BF == QG_Q6_K) srow[m][r] = sp + row * p.nchunk * 2;
+                else if (BF == QG_Q4_K) srow[m][r] = sp + row * (p.nchunk / 8) * 16;
                 else srow[m][r] = sp + row * 4;
-                if constexpr (FMT == QG_Q6_K) {
+                if constexpr (BF == QG_Q6_K) {
                     hrow[m][r] = p.q[m] + p.hoff + row * p.nchunk * 8;
                     drow[m][r] = p.q[m] + p.doff + row * (p.nchunk / 8) * 2;
                 } else {
@@ -536,7 +593,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
         for (int m = 0; m < NMAT; m++)
 #pragma unroll
             for (int r = 0; r < R; r++)
-                load_group<FMT, CPL>(st[s][m][r], qrow[m][r], srow[m][r], hrow[m][r], drow[m][r], c0, p.nchunk);
+                load_group<BF, CPL>(st[s][m][r], qrow[m][r], srow[m][r], hrow[m][r], drow[m][r], c0, p.nchunk);
     };
     auto prologue = [&]() {
         const int last = P > 0 ? P - 1 : 0;
@@ -545,13 +602,19 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
     };
     auto read_x = [&](int c, float4 (&xv)[8]) -> f32x2 {
         const float4 *xp = reinterpret_cast<const float4 *>(xs + c * kXStride);
+        if constexpr (Fmt<FMT>::kSums < 0) {
+            xv[0] = xp[0];   // the 32 codes; xv[2..7] unused
+            xv[1] = xp[1];
+            return *reinterpret_cast<const f32x2 *>(xs + c * kXStride + 8);
+        } else {
 #pragma unroll
-        for (int k = 0; k < 8; k++) xv[k] = xp[k];
-        if constexpr (Fmt<FMT>::kSums == 2) return *reinterpret_cast<const f32x2 *>(xs + c * kXStride + 32);
-        else if constexpr (Fmt<FMT>::kSums == 1) return f32x2{xs[c * kXStride + 32], 0.0f};
-        else return f32x2{0.0f, 0.0f};
+            for (int k = 0; k < 8; k++) xv[k] = xp[k];
+            if constexpr (Fmt<FMT>::kSums == 2) return *reinterpret_cast<const f32x2 *>(xs + c * kXStride + 32);
+            else if constexpr (Fmt<FMT>::kSums == 1) return f32x2{xs[c * kXStride + 32], 0.0f};
+            else return f32x2{0.0f, 0.0f};
+        }
     };
-    auto compute = [&](const Group<FMT, CPL> (&regs)[NMAT][R], int c0, float (&acc)[NMAT][R]) {
+    auto compute = [&](const Group<BF, CPL> (&regs)[NMAT][R], int c0, float (&acc)[NMAT][R]) {
         static_for<CPL>([&](auto jj) {
             constexpr int J = decltype(jj)::value;
             float4 xv[8];
@@ -627,12 +690,12 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
         for (int j = 0; j < CPL; j++) {
             const int c = (sl + P * LPR) * CPL + j;
             if (c < p.nchunk) {
-                Group<FMT, 1> tl[NMAT][R];
+                Group<BF, 1> tl[NMAT][R];
 #pragma unroll
                 for (int m = 0; m < NMAT; m++)
 #pragma unroll
                     for (int r = 0; r < R; r++)
-                        load_group<FMT, 1>(tl[m][r], qrow[m][r], srow[m][r], hrow[m][r], drow[m][r], c, p.nchunk);
+                        load_group<BF, 1>(tl[m][r], qrow[m][r], srow[m][r], hrow[m][r], drow[m][r], c, p.nchunk);
                 float4 xv[8];
                 const f32x2 xsum = read_x(c, xv);
                 const Q4KSub kt = q4k_sub(c);
@@ -648,7 +711,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
         for (int m = 0; m < NMAT; m++)
 #pragma unroll
             for (int r = 0; r < R; r++)
-                scale[m][r] = FMT == QG_I8ROW ? *reinterpret_cast<const float *>(srow[m][r]) : 1.0f;
+                scale[m][r] = BF == QG_I8ROW ? *reinterpret_cast<const float *>(srow[m][r]) : 1.0f;
         const int64_t row0 = batch * (G * R) + (int64_t)g * R;
         const int64_t nb = batch + bstride;
         if (nb < nbatch) {               // next batch starts streaming before this one is reduced

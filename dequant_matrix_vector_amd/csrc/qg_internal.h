@@ -13,6 +13,9 @@ constexpr int kChunk = 32;           // weights per lane work item (a Q4_0/Q8_0 
 constexpr int kXStride = 36;         // LDS floats per staged x chunk: 32 values + chunk sum + 3 pad
 constexpr int64_t kPlaneAlign = 256; // packed plane alignment
 constexpr int kLayoutVersion = 1;
+// Added to a format code (Q4_0, Q8_0) inside the library: the GEMV quantizes
+// its activation row to Q8_0 while staging it and takes integer dot products.
+constexpr int kQ8Act = 8;
 
 inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
@@ -96,6 +99,8 @@ int64_t prefill_part_elems(int nmat, int64_t rows, int64_t cols, int64_t n_tok);
 hipError_t launch_prefill(int nmat, const uint8_t *w0, const uint8_t *w1, const float *x, float *y,
                           int64_t rows, int64_t cols, int64_t n_tok, float *part, int64_t part_elems,
                           hipStream_t s, const float *resid = nullptr);
+// Raw Q8_0 blocks (f16 d, 32 int8) of activation rows x [n_tok][n], n a multiple of 32.
+hipError_t launch_quantize_q8_0(const float *x, uint8_t *blocks, int64_t n, int64_t n_tok, hipStream_t s);
 // token[t] = first index of the largest of logits[t][0..n) (NaN never chosen, unless at index 0).
 hipError_t launch_argmax(const float *logits, int32_t *token, int64_t n, int64_t n_tok, hipStream_t s);
 // xn[t][j] = x[t][j] * gamma[j] / sqrt(mean_j x[t][j]^2 + eps), fp32, one workgroup per token.

@@ -214,6 +214,32 @@ int qgemv_argmax(const float *logits, int32_t *token, int64_t n, int64_t n_tok, 
 int qgemv_head_argmax(int fmt, const void *packed, const float *x, float *logits, int32_t *token,
                       int64_t rows, int64_t cols, int64_t n_tok, void *stream);
 
+/* Q8_0 activations: the products as the Go "llm" package's ExactGGML mode
+ * computes them (its CPU type: activations are quantised to Q8_0 before every
+ * quantised matrix product).  Each 32-element block of the activation row is
+ * quantized -- d = max|x|/127, q = round(x * (1/d)) with halves away from
+ * zero (q = 0 when d = 0), binary32 with correctly rounded divisions, d kept
+ * as binary16 nearest even -- and y is the product with x replaced by
+ * f16(d) * q: per block an exact integer dot product (Q4_0 codes minus 8, or
+ * Q8_0 codes, times the activation codes) scaled by d_w * d_x, accumulated in
+ * fp32 (|y - exact| <= 2e-5 * sum_j |w_ij xq_j| + 1e-7 for xq the quantized
+ * activations).  Q4_0 and Q8_0 weights only (QG_ERR_FORMAT otherwise); same
+ * arguments, layouts and checks as qgemv and swiglu_ffn.  swiglu_ffn_q8act
+ * quantizes x before the gate/up pair and h before the down product (h,
+ * fp32, is left in the scratch as in swiglu_ffn; n_tok * ffn floats
+ * suffice).  One launch per product and token. */
+int qgemv_q8act(int fmt, const void *packed, const float *x, float *y, int64_t rows, int64_t cols,
+                int64_t n_tok, void *stream);
+int swiglu_ffn_q8act(int fmt, const void *wg, const void *wu, const void *wd, const float *x,
+                     float *out, float *h_scratch, int64_t h_scratch_elems, int64_t d_model,
+                     int64_t ffn, int64_t n_tok, void *stream);
+
+/* Test export: the activation quantizer above on its own.  x: fp32
+ * [n_tok][n] (16-byte aligned), n a multiple of 32; blocks: n_tok * n/32 raw
+ * Q8_0 blocks of 34 bytes (f16 d, then 32 int8 codes in column order), any
+ * alignment, not overlapping x.  Not used on the hot path. */
+int qquantize_q8_0(const float *x, void *blocks, int64_t n, int64_t n_tok, void *stream);
+
 /* Test export: the packed tensor decoded to fp32 [rows][cols] (each weight its
  * exact value rounded once to binary32).  Not used on the hot path. */
 int qdequant(int fmt, const void *packed, float *w_out, int64_t rows, int64_t cols, void *stream);

@@ -73,6 +73,14 @@ def test_refusals_before_any_device_call(lib):
     assert lib.qgemv(0, fake, fake, fake, 4, 32, 0, None) == -2
     assert lib.qgemv(2, fake, fake, fake, 4, 300, 1, None) == -2
     assert lib.qgemv(4, fake, fake, fake, 4, 288, 1, None) == -2
+    # Q8_0 activations: Q4_0 and Q8_0 weights only; the quantizer's shape rules
+    lib.qgemv_q8act.argtypes = [ctypes.c_int, P, P, P, I64, I64, I64, P]
+    assert lib.qgemv_q8act(2, fake, fake, fake, 4, 256, 1, None) == -4
+    assert lib.qgemv_q8act(4, fake, fake, fake, 4, 256, 1, None) == -4
+    lib.qquantize_q8_0.argtypes = [P, P, I64, I64, P]
+    assert lib.qquantize_q8_0(fake, fake, 48, 1, None) == -2
+    assert lib.qquantize_q8_0(fake, fake, 64, 0, None) == -2
+    assert lib.qquantize_q8_0(None, fake, 64, 1, None) == -1
 
 
 def test_prefill_override_validation(lib):

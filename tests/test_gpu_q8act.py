@@ -1,0 +1,191 @@
+"""GPU parity of the Q8_0-activation mode (the Go "llm" package's ExactGGML:
+activations quantised to Q8_0 before each quantised product) through the C ABI.
+
+Bars:
+  * the quantized activation blocks (binary16 scale and the 32 codes) are
+    byte-identical to the oracle's: the same decisions in the same binary32
+    precision, ties included;
+  * y: |y_gpu - y_ref| <= 2e-5 * sum_j |w_ij xq_j| + 1e-7, y_ref the oracle's
+    binary64 product with the quantized activations xq (the block products are
+    exact integers on the device; only the per-block scaling and the fp32
+    accumulation round);
+  * weights with power-of-two scales and activations on the Q8_0 grid: every
+    partial sum is exact, so y is bit-identical to the oracle;
+  * the FFN stage by stage: h against silu(g) u of the oracle's products, out
+    against the oracle's down product of the device's own h (quantized again).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ["q4_0", "q8_0"]
+
+
+def _oracle_blocks(x, n):
+    d, q = oracle.quantize_q8_0(x.reshape(-1, n))
+    nb = n // 32
+    out = np.empty((d.shape[0], nb, 34), np.uint8)
+    out[:, :, 0:2] = d.astype("<u2").view(np.uint8).reshape(d.shape[0], nb, 2)
+    out[:, :, 2:] = q.view(np.uint8).reshape(d.shape[0], nb, 32)
+    return out.reshape(d.shape[0], nb * 34)
+
+
+def _gpu_blocks(x, n):
+    xd = G.torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(G.dev())
+    b = G.qg().qquantize_q8_0(xd, n)
+    G.torch.cuda.synchronize()
+    return b.cpu().numpy()
+
+
+def test_quantize_matches_oracle_bytes():
+    rng = np.random.default_rng(3000)
+    for n, n_tok in ((32, 1), (576, 3), (5120, 2), (17408, 1)):
+        x = (rng.standard_normal((n_tok, n)) * 2.0 ** rng.integers(-14, 14, (n_tok, n // 32)).repeat(32, 1))
+        x = x.astype(np.float32)
+        x[:, 64:96] = 0.0 if n > 96 else x[:, 64:96]                       # a zero block
+        assert np.array_equal(_gpu_blocks(x, n), _oracle_blocks(x, n)), (n, n_tok)
+
+
+def test_quantize_ties_and_edges():
+    # halves on an exact grid (away from zero), a negative maximum, tiny
+    # scales (binary16 subnormal d) and large ones
+    rows = []
+    b = np.zeros(32, np.float32)
+    b[:8] = [127, 2.5, -2.5, 0.5, -0.5, 1.5, -1.49, 126.5]
+    rows.append(b)
+    rows.append(np.float32([-254, 3, 1, -5] + [0] * 28))
+    rng = np.random.default_rng(3001)
+    for s in (1e-6, 3e-5, 1e3, 4e6):
+        rows.append((rng.standard_normal(32) * s).astype(np.float32))
+    k = rng.integers(-127, 128, 32).astype(np.float32)
+    k[5] = 127
+    rows.append((k + 0.5 * np.sign(k)) * np.float32(2.0 ** -3))       # on-grid halves
+    x = np.concatenate(rows).reshape(1, -1)
+    assert np.array_equal(_gpu_blocks(x, x.size), _oracle_blocks(x, x.size))
+
+
+SHAPES = {"q4_0": [(1, 32), (131, 576), (200, 1536), (97, 5120), (33, 17408)],
+          "q8_0": [(1, 32), (45, 576), (130, 2048), (67, 4096)]}
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_q8act_within_bound(fmt):
+    for k, (rows, cols) in enumerate(SHAPES[fmt]):
+        rng = np.random.default_rng(3100 + k)
+        t = synth.make_tensor(fmt, rows, cols, rng)
+        x = rng.standard_normal((2, cols)).astype(np.float32)
+        xd = G.torch.from_numpy(x).to(G.dev())
+        y = G.qg().qgemv_q8act(fmt, G.upload(t), xd, rows, cols)
+        G.torch.cuda.synchronize()
+        yr, S = oracle.gemv_q8act(fmt, t.raw, x, rows, cols)
+        G.check_bound(y.cpu().numpy(), yr, S, what=f"q8act {fmt} {rows}x{cols}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_q8act_exact_inputs_bit_exact(fmt):
+    # power-of-two weight scales, activations k * 2^-4 with a code of 127 in
+    # every block (so d_x = 2^-4 and the codes are k): every sum is exact
+    rng = np.random.default_rng(3200)
+    rows, cols = 150, 1024
+    if fmt == "q4_0":
+        d = (2.0 ** rng.integers(-6, -2, (rows, cols // 32))).astype(np.float16)
+        raw = synth.pack_q4_0(d, rng.integers(0, 16, (rows, cols)))
+    else:
+        d = (2.0 ** rng.integers(-8, -4, (rows, cols // 32))).astype(np.float16)
+        raw = synth.pack_q8_0(d, rng.integers(-127, 128, (rows, cols)).astype(np.int8))
+    t = synth.QTensor("w", fmt, rows, cols, raw)
+    kx = rng.integers(-127, 128, cols)
+    kx[::32] = 127
+    x = (kx * 2.0 ** -4).astype(np.float32)
+    xd = G.torch.from_numpy(x).to(G.dev())
+    y = G.qg().qgemv_q8act(fmt, G.upload(t), xd, rows, cols)
+    G.torch.cuda.synchronize()
+    yr, _ = oracle.gemv_q8act(fmt, t.raw, x, rows, cols)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), yr)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_q8act_every_launch_shape(fmt):
+    rows, cols = 203, 1536
+    rng = np.random.default_rng(3300)
+    t = synth.make_tensor(fmt, rows, cols, rng)
+    pk = G.upload(t)
+    x = rng.standard_normal(cols).astype(np.float32)
+    xd = G.torch.from_numpy(x).to(G.dev())
+    yr, S = oracle.gemv_q8act(fmt, t.raw, x, rows, cols)
+    ref = None
+    try:
+        for lpr in (8, 16, 32, 64):
+            for r in (1, 2):
+                for waves, depth, max_wg in ((1, 2, 0), (4, 4, 3), (8, 2, 0)):
+                    for cpl in (1, 2, 4):
+                        G.qg().set_launch_override(lpr, r, waves, depth, max_wg, cpl)
+                        y = G.qg().qgemv_q8act(fmt, pk, xd, rows, cols)
+                        G.torch.cuda.synchronize()
+                        G.check_bound(y.cpu().numpy(), yr, S, what=f"q8act {fmt} {lpr} {r} {waves} {depth} {cpl}")
+    finally:
+        G.qg().set_launch_override(0)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_q8act_deterministic_and_scale_invariant(fmt):
+    # scaling x by 2 doubles every d_x exactly and leaves the codes: y doubles exactly
+    rows, cols = 300, 2048
+    rng = np.random.default_rng(3400)
+    t = synth.make_tensor(fmt, rows, cols, rng)
+    pk = G.upload(t)
+    x = rng.standard_normal(cols).astype(np.float32)
+    run = lambda v: G.qg().qgemv_q8act(fmt, pk, G.torch.from_numpy(v).to(G.dev()), rows, cols).cpu().numpy()
+    y1, y2, y4 = run(x), run(x), run(x * np.float32(4))
+    assert np.array_equal(y1, y2) and np.array_equal(y4, np.float32(4) * y1)
+
+
+def _check_ffn_q8act(fmt, tens, x, d_model, ffn, what):
+    pk = [G.upload(t) for t in tens]
+    xd = G.torch.from_numpy(x).to(G.dev())
+    out, h = G.qg().swiglu_ffn_q8act(fmt, pk[0], pk[1], pk[2], xd, d_model, ffn)
+    G.torch.cuda.synchronize()
+    out, h = out.cpu().numpy(), h.cpu().numpy()
+    r = {}
+    r["g"], r["Sg"] = oracle.gemv_q8act(fmt, tens[0].raw, x, ffn, d_model)
+    r["u"], r["Su"] = oracle.gemv_q8act(fmt, tens[1].raw, x, ffn, d_model)
+    r["h"] = G.silu64(r["g"]) * r["u"]
+    assert np.all(np.abs(h - r["h"]) <= G.h_bound(r)), f"{what}: h outside its bound"
+    yr, S = oracle.gemv_q8act(fmt, tens[2].raw, h, d_model, ffn)
+    G.check_bound(out, yr, S, what=f"{what} down")
+
+
+@pytest.mark.parametrize("fmt,n_tok", [("q4_0", 1), ("q8_0", 1), ("q4_0", 3)])
+def test_swiglu_ffn_q8act(fmt, n_tok):
+    d_model, ffn = 576, 1536
+    rng = np.random.default_rng(3500 + n_tok)
+    tens = [synth.make_tensor(fmt, ffn, d_model, rng), synth.make_tensor(fmt, ffn, d_model, rng),
+            synth.make_tensor(fmt, d_model, ffn, rng)]
+    x = rng.standard_normal((n_tok, d_model)).astype(np.float32)
+    _check_ffn_q8act(fmt, tens, x, d_model, ffn, f"ffn q8act {fmt} n_tok={n_tok}")
+
+
+@pytest.mark.parametrize("idx", range(8))
+def test_fullsize_smollm2_layer_and_head_q8act(idx):
+    # the SmolLM2-135M-shaped Q4_0 layer and its Q8_0 vocab head (the model the
+    # mode was written for), every matrix at full size
+    w = synth.CFG2
+    t = synth.gen_tensor(w, idx)
+    x = synth.gen_x(w, t.cols, 1, which=idx)
+    xd = G.torch.from_numpy(x).to(G.dev())
+    y = G.qg().qgemv_q8act(t.fmt, G.upload(t), xd, t.rows, t.cols)
+    G.torch.cuda.synchronize()
+    yr, S = oracle.gemv_q8act(t.fmt, t.raw, x, t.rows, t.cols)
+    G.check_bound(y.cpu().numpy(), yr, S, what=f"cfg2 {t.name} q8act")
+
+
+def test_fullsize_27b_ffn_q8act():
+    w = synth.CFG5
+    tens = synth.gen_workload(w)
+    x = synth.gen_x(w, w.d_model, 1)
+    _check_ffn_q8act("q4_0", tens, x, w.d_model, w.ffn, "27B-class FFN q8act")
