@@ -9,9 +9,15 @@ working set is >= 1 GiB (over 4x the 256 MB Infinity Cache), so each step
 streams its weights from HBM.
 
 value = algorithmic weight bytes per step (150,405,120 B: 18 B per 32 weights)
-        / wall time per step (K steps between two device synchronizations).
+        / wall time per step (K steps between two device synchronizations,
+        launched through the C ABI with nothing else between the kernels).
 roofline: the dominant kernel (fused gate/up, 100,270,080 B per launch) timed
-with HIP events on the stream it runs on, against 8 TB/s HBM.
+with HIP events on the stream it runs on, against 8 TB/s HBM: the same K steps
+run a second time with each launch carrying its own start/stop events
+(qgemv_time_next_launch: the library launches it with hipExtLaunchKernel), so
+the events hold the dispatch's own start and end -- the duration rocprofv3's
+kernel trace reports.  Timed launches leave gaps between the kernels (as
+hipEventRecord pairs do), hence a pass of their own.
 cpu_baseline: the CPU oracle (scalar C, binary64) on the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
@@ -46,10 +52,9 @@ def parse():
 
 
 class TimingEvents:
-    """HIP events created for timing only (hipEventDisableSystemFence): recording
-    them adds no system-scope cache writeback between the kernels they bracket.
-    Uses the HIP runtime torch already loaded (same soname)."""
-    DISABLE_SYSTEM_FENCE = 0x20000000
+    """HIP events for kernel timing, handed to the library's launch hook (the
+    dispatch records them).  Uses the HIP runtime torch already loaded (same
+    soname)."""
 
     def __init__(self, n):
         self.lib = ctypes.CDLL("libamdhip64.so.7")
@@ -60,7 +65,7 @@ class TimingEvents:
         self.ev = []
         for _ in range(n):
             e = ctypes.c_void_p()
-            if self.lib.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+            if self.lib.hipEventCreateWithFlags(ctypes.byref(e), 0) != 0:
                 raise RuntimeError("hipEventCreateWithFlags failed")
             self.ev.append(e)
 
@@ -253,6 +258,17 @@ def extra_report(qg, synth, torch, np, dev, graph_iters=20):
         rep[f"cfg5_block_n{n_tok}"] = {"workload": w.name + " + RMSNorm in, residual out", "n_tok": n_tok,
                                        "us_per_step": round(ub, 2), "ffn_alone_us_per_step": round(uf, 2),
                                        "GBs": round(wbytes / ub / 1e3, 1)}
+        if n_tok == 1:
+            hq = torch.empty(w.ffn, device=dev)
+
+            def q8act(i):
+                c = copies[i % ncopy]
+                qg.swiglu_ffn_q8act("q4_0", c[0], c[1], c[2], x, w.d_model, w.ffn, out=out, h_scratch=hq)
+
+            uq = _graph_us(torch, q8act, graph_iters)
+            rep["cfg5_ffn_q8act"] = {"workload": w.name + ", x and h quantized to Q8_0 (integer dot products)",
+                                     "n_tok": 1, "us_per_step": round(uq, 2), "ffn_f32_us_per_step": round(uf, 2),
+                                     "GBs": round(wbytes / uq / 1e3, 1)}
     del copies
     torch.cuda.empty_cache()
     for w, idx in ((synth.CFG2, 7), (synth.CFG4, 3)):
@@ -314,29 +330,45 @@ def main():
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
 
-    def step(i, ev=None):
-        g, u, dn = copies[i % ncopy]
-        if ev is not None:
-            ev.record(3 * i, sptr)
-        qg.swiglu_gate_up("q4_0", g, u, xd, d_model, ffn, h=h, stream=sptr)
-        if ev is not None:
-            ev.record(3 * i + 1, sptr)
-        qg.qgemv("q4_0", dn, h, d_model, ffn, y=out, stream=sptr)
-        if ev is not None:
-            ev.record(3 * i + 2, sptr)
+    # The timed loop calls the C ABI directly with its arguments marshalled
+    # beforehand (the binding's per-call checks cost more host time than a
+    # step's kernels take, which would leave the GPU idle between launches).
+    fq = qg.FORMATS["q4_0"]
+    gu_args = [(fq, g.data_ptr(), u.data_ptr(), xd.data_ptr(), h.data_ptr(), d_model, ffn, 1, sptr)
+               for g, u, _ in copies]
+    dn_args = [(fq, dn.data_ptr(), h.data_ptr(), out.data_ptr(), d_model, ffn, 1, sptr) for _, _, dn in copies]
+    gate_up_call, down_call = qg.lib.swiglu_gate_up, qg.lib.qgemv
+    evs = TimingEvents(4 * a.steps)
+    time_next, ev_handles = qg.lib.qgemv_time_next_launch, evs.ev
+
+    def step(i, timed=False):
+        if timed and time_next(ev_handles[4 * i], ev_handles[4 * i + 1]) != 0:
+            raise RuntimeError("qgemv_time_next_launch failed")
+        if gate_up_call(*gu_args[i % ncopy]) != 0:
+            raise RuntimeError("swiglu_gate_up failed")
+        if timed and time_next(ev_handles[4 * i + 2], ev_handles[4 * i + 3]) != 0:
+            raise RuntimeError("qgemv_time_next_launch failed")
+        if down_call(*dn_args[i % ncopy]) != 0:
+            raise RuntimeError("qgemv failed")
 
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = TimingEvents(3 * a.steps)
-    torch.cuda.synchronize()
+    # value: the K steps with nothing but their launches (no events between the
+    # kernels, which run back to back)
     t0 = time.perf_counter()
     for i in range(a.steps):
-        step(i, evs)
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gu_ms = [evs.ms(3 * i, 3 * i + 1) for i in range(a.steps)]
-    dn_ms = [evs.ms(3 * i + 1, 3 * i + 2) for i in range(a.steps)]
+    # roofline: the same K steps again, each launch carrying its own events
+    # (the timed launch path leaves the GPU idle between kernels, so this pass
+    # gives kernel durations, not the step rate)
+    for i in range(a.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    gu_ms = [evs.ms(4 * i, 4 * i + 1) for i in range(a.steps)]
+    dn_ms = [evs.ms(4 * i + 2, 4 * i + 3) for i in range(a.steps)]
     evs.close()
     ms_per_step = wall * 1e3 / a.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9

@@ -74,6 +74,8 @@ lib.qgemv_set_launch_override.argtypes = [_I, _I, _I, _I, _I, _I]
 lib.qgemv_set_launch_override.restype = _I
 lib.qgemv_set_prefill_override.argtypes = [_I, _I, _I, _I, _I]
 lib.qgemv_set_prefill_override.restype = _I
+lib.qgemv_time_next_launch.argtypes = [_P, _P]
+lib.qgemv_time_next_launch.restype = _I
 
 
 class QGemvError(RuntimeError):

@@ -50,6 +50,27 @@ GemvCfg aligned_cfg(int fmt, int nchunk, GemvCfg c)
 
 } // namespace
 
+namespace {
+thread_local hipEvent_t t_start = nullptr, t_stop = nullptr;
+} // namespace
+
+bool take_launch_timing(hipEvent_t *start, hipEvent_t *stop)
+{
+    if (!t_start) return false;
+    *start = t_start;
+    *stop = t_stop;
+    t_start = t_stop = nullptr;
+    return true;
+}
+
+extern "C" int qgemv_time_next_launch(void *start_event, void *stop_event)
+{
+    if ((start_event == nullptr) != (stop_event == nullptr)) return QG_ERR_NULL;
+    t_start = static_cast<hipEvent_t>(start_event);
+    t_stop = static_cast<hipEvent_t>(stop_event);
+    return QG_OK;
+}
+
 extern "C" int qgemv_set_launch_override(int lpr, int r, int waves, int depth, int max_wg, int cpl)
 {
     if (lpr == 0) {

@@ -61,6 +61,8 @@
 #include <atomic>
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "q8act.h"
 #include "qg_internal.h"
 
@@ -770,6 +772,14 @@ hipError_t go(const GemvParams &p, const GemvCfg &c, hipStream_t s)
             if (e != hipSuccess) return e;
             configured_lds[dev].store((int)lds, std::memory_order_relaxed);
         }
+    }
+    hipEvent_t t0 = nullptr, t1 = nullptr;
+    if (take_launch_timing(&t0, &t1)) {
+        // the events take this dispatch's own start and end (no extra packets)
+        GemvParams arg = p;
+        void *args[] = {&arg};
+        return hipExtLaunchKernel((const void *)kern, dim3((unsigned)nwg), dim3(64 * c.waves), args, lds, s, t0, t1,
+                                  0);
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(64 * c.waves), lds, s, p);
     return hipGetLastError();

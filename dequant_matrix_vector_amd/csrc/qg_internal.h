@@ -58,6 +58,10 @@ struct GemvCfg {
 
 GemvCfg choose_cfg(int fmt, int64_t rows, int64_t cols, int nmat);
 
+// Measurement hook (qgemv_time_next_launch): true, with the calling thread's
+// pending start/stop events, once; the GEMV launcher then launches with them.
+bool take_launch_timing(hipEvent_t *start, hipEvent_t *stop);
+
 // Compute units of the current device (cached per device; 256 if the query fails).
 int cu_count();
 

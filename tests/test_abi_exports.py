@@ -81,6 +81,10 @@ def test_refusals_before_any_device_call(lib):
     assert lib.qquantize_q8_0(fake, fake, 48, 1, None) == -2
     assert lib.qquantize_q8_0(fake, fake, 64, 0, None) == -2
     assert lib.qquantize_q8_0(None, fake, 64, 1, None) == -1
+    # the timing hook wants both events or neither
+    lib.qgemv_time_next_launch.argtypes = [P, P]
+    assert lib.qgemv_time_next_launch(fake, None) == -1
+    assert lib.qgemv_time_next_launch(None, None) == 0
 
 
 def test_prefill_override_validation(lib):
