@@ -22,6 +22,8 @@
 //     raw partial sums when K is split over workgroups.
 // Every weight is decoded once per token group (once per kernel when the
 // group spans all tokens), and x never needs a staging buffer in HBM.
+#include <hip/hip_ext.h>
+
 #include "qg_internal.h"
 
 namespace qg {
@@ -31,8 +33,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kKStep = 128;   // columns per K step: four Q4_0 blocks, one per 16-lane group
 
 struct PrefillParams {
     const uint8_t *q[2];
@@ -394,19 +394,38 @@ hipError_t go_prefill(PrefillParams p, float *y, hipStream_t s)
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * W), lds, s, p);
-    hipError_t e = hipGetLastError();
+    // measurement hook: the start event rides on this launch, the stop event
+    // on the last launch of the product (this one, or the reduce)
+    hipEvent_t t0 = nullptr, t1 = nullptr;
+    const bool timed = take_launch_timing(&t0, &t1);
+    hipError_t e;
+    if (timed) {
+        void *args[] = {&p};
+        e = hipExtLaunchKernel((const void *)kern, dim3((unsigned)grid), dim3(64 * W), args, lds, s, t0,
+                               p.ksplit == 1 ? t1 : nullptr, 0);
+    } else {
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * W), lds, s, p);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess || p.ksplit == 1) return e;
-    const int64_t n = (int64_t)p.n_tok * p.rows;
+    int64_t n = (int64_t)p.n_tok * p.rows;
     const uintptr_t al = reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(p.y) |
                          reinterpret_cast<uintptr_t>(p.resid);
-    if (n % 4 == 0 && (al & 15) == 0)
-        hipLaunchKernelGGL((prefill_reduce_kernel<NMAT, 4>), dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
-                           (const float *)p.y, y, n, p.ksplit, p.resid);
-    else
-        hipLaunchKernelGGL((prefill_reduce_kernel<NMAT, 1>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                           (const float *)p.y, y, n, p.ksplit, p.resid);
-    return hipGetLastError();
+    const float *part = p.y;
+    const float *resid = p.resid;
+    int ksplit = p.ksplit;
+    const void *red;
+    int64_t blocks;
+    if (n % 4 == 0 && (al & 15) == 0) {
+        red = (const void *)prefill_reduce_kernel<NMAT, 4>;
+        blocks = (n / 4 + 255) / 256;
+    } else {
+        red = (const void *)prefill_reduce_kernel<NMAT, 1>;
+        blocks = (n + 255) / 256;
+    }
+    void *rargs[] = {&part, &y, &n, &ksplit, &resid};
+    if (timed) return hipExtLaunchKernel(red, dim3((unsigned)blocks), dim3(256), rargs, 0, s, nullptr, t1, 0);
+    return hipLaunchKernel(red, dim3((unsigned)blocks), dim3(256), rargs, 0, s);
 }
 
 PrefillCfg g_pf_override = {0, 0, 0, 0, 0};
@@ -435,23 +454,30 @@ constexpr bool pf_fits(int nmat, int mtr, int ntw, int waves, int run)
     return false;
 }
 
-// The built-in tile choice (from sweeps on the 27B-class FFN at 8 and 128
-// tokens): one 16-row tile per matrix and wave; up to 4 token tiles per
-// workgroup (64 tokens share each decoded weight) with 4 waves and runs of one
-// step, or, for a single token tile, 8 waves sharing it and runs of two steps;
-// then K ranges until the grid has about four workgroups per CU (if the caller
-// gave room for the partials).
+// The built-in tile choice (from kernel-trace sweeps of every built shape on
+// the 27B-class FFN at 8 to 128 tokens): one 16-row tile per matrix and wave;
+// one token tile: 4 waves, runs of two steps; more: 2 or 4 token tiles per
+// workgroup, 4 waves for the fused gate/up pair (8 waves and 8 token tiles,
+// 128 tokens sharing each decoded weight, from 8 tiles on) and 8 waves for a
+// single matrix; then K ranges until the grid has about four workgroups per
+// CU (if the caller gave room for the partials), as long as the partial sums
+// (written, then read back) stay within half the weight bytes.
 PrefillCfg choose(int nmat, int64_t rows, int64_t cols, int64_t n_tok, int64_t part_elems)
 {
     PrefillCfg c = g_pf_override;
     const int64_t n_tiles = (n_tok + 15) / 16;
     if (c.mtr <= 0) {
         c.mtr = 1;
-        c.ntw = n_tiles >= 4 ? 4 : (n_tiles >= 2 ? 2 : 1);
-        c.waves = 4;
-        c.run = 1;
-        if (c.ntw == 1) c.waves = 8, c.run = 2;   // one token tile: 8 waves share each x tile
         c.ksplit = 0;
+        if (n_tiles == 1) {
+            c.ntw = 1, c.waves = 4, c.run = 2;
+        } else if (nmat == 2 && n_tiles >= 8) {
+            c.ntw = 8, c.waves = 8, c.run = 1;
+        } else {
+            c.ntw = n_tiles >= 4 ? 4 : 2;
+            c.waves = nmat == 2 ? 4 : 8;
+            c.run = 1;
+        }
     }
     // a shape that is not built falls back to the nearest one that is: fewer
     // token tiles last, then one row tile per matrix, the other wave count,
@@ -478,6 +504,12 @@ PrefillCfg choose(int nmat, int64_t rows, int64_t cols, int64_t n_tok, int64_t p
         const int64_t by_len = ssteps / 4;   // keep each range a few ring turns long
         ks = ks < by_len ? ks : (by_len > 1 ? by_len : 1);
         ks = ks < 16 ? ks : 16;
+        // partial-sum traffic: 8 bytes per partial (written, read back) against
+        // 18 bytes per 32 weights of the nmat matrices
+        const int64_t per_range = 8 * (int64_t)nmat * n_tok * rows;
+        const int64_t weights = (int64_t)nmat * rows * (cols / 32) * 18;
+        const int64_t by_traffic = weights / 2 / per_range;
+        ks = ks < by_traffic ? ks : (by_traffic > 1 ? by_traffic : 1);
     }
     ks = ks < ssteps ? ks : ssteps;
     while (ks > 1 && ks * nmat * n_tok * rows > part_elems) ks--;

@@ -255,15 +255,16 @@ int qdequant(int fmt, const void *packed, float *w_out, int64_t rows, int64_t co
  * enqueueing work.  Returns QG_ERR_SHAPE for values outside these sets. */
 int qgemv_set_launch_override(int lpr, int r, int waves, int depth, int max_wg, int cpl);
 
-/* Measurement hook: the next GEMV kernel that the calling thread launches
- * (the kernels of every n_tok == 1 product: qgemv, swiglu_gate_up, swiglu_ffn
- * and the rest) is launched with hipExtLaunchKernel and these two events
+/* Measurement hook: the next product kernel that the calling thread
+ * launches (a GEMV kernel of any call, or a matrix-core product with its
+ * split-K reduce) is launched with hipExtLaunchKernel and these two events
  * (hipEvent_t passed as void*), which then hold that dispatch's own start and
- * end: hipEventElapsedTime gives the kernel's device time with no marker
- * packets between launches (a hipEventRecord pair costs a pipeline drain of a
- * few microseconds on each side).  Both events or neither (NULL, NULL clears
- * a pending pair); consumed by that one launch; thread-local.  Returns
- * QG_ERR_NULL if only one event is given. */
+ * end (a matrix-core product: the start of its main kernel, the end of its
+ * reduce when K is split): hipEventElapsedTime gives the device time with no
+ * marker packets between launches (a hipEventRecord pair costs a pipeline
+ * drain of a few microseconds on each side).  Both events or neither (NULL,
+ * NULL clears a pending pair); consumed by that one product; thread-local.
+ * Returns QG_ERR_NULL if only one event is given. */
 int qgemv_time_next_launch(void *start_event, void *stop_event);
 
 /* Tuning hook for the matrix-core path (Q4_0, n_tok > 1): force 16-row tiles
