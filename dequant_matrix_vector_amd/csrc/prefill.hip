@@ -442,6 +442,7 @@ constexpr int kBuiltShapes[] = {
     21142, 21144, 21181, 21182, 21184, 21241, 21242, 21244, 21281,
     21282, 21441, 21442, 21481, 21482, 21841, 21881, 22141, 22142,
     22182, 22241, 22242, 22281, 22441, 22481, 22841,
+    11561, 11961,   // 16 waves (waves * 10 = 160), one matrix only: two spill
 };
 
 constexpr bool pf_fits(int nmat, int mtr, int ntw, int waves, int run)
@@ -459,7 +460,8 @@ constexpr bool pf_fits(int nmat, int mtr, int ntw, int waves, int run)
 // one token tile: 4 waves, runs of two steps; more: 2 or 4 token tiles per
 // workgroup, 4 waves for the fused gate/up pair (8 waves and 8 token tiles,
 // 128 tokens sharing each decoded weight, from 8 tiles on) and 8 waves for a
-// single matrix; then K ranges until the grid has about four workgroups per
+// single matrix (16 from 4 tiles on: 256 rows share each staged x tile);
+// then K ranges until the grid has about four workgroups per
 // CU (if the caller gave room for the partials), as long as the partial sums
 // (written, then read back) stay within half the weight bytes.
 PrefillCfg choose(int nmat, int64_t rows, int64_t cols, int64_t n_tok, int64_t part_elems)
@@ -475,7 +477,7 @@ PrefillCfg choose(int nmat, int64_t rows, int64_t cols, int64_t n_tok, int64_t p
             c.ntw = 8, c.waves = 8, c.run = 1;
         } else {
             c.ntw = n_tiles >= 4 ? 4 : 2;
-            c.waves = nmat == 2 ? 4 : 8;
+            c.waves = nmat == 2 ? 4 : (n_tiles >= 4 ? 16 : 8);
             c.run = 1;
         }
     }
@@ -486,7 +488,7 @@ PrefillCfg choose(int nmat, int64_t rows, int64_t cols, int64_t n_tok, int64_t p
         bool found = false;
         for (int nt = c.ntw; nt >= 1 && !found; nt /= 2)
             for (int mr : {c.mtr, 1})
-                for (int wv : {c.waves, 12 - c.waves})
+                for (int wv : {c.waves, c.waves == 8 ? 4 : 8})
                     for (int rn = c.run; rn >= 1 && !found; rn /= 2)
                         if (pf_fits(nmat, mr, nt, wv, rn)) {
                             c.mtr = mr, c.ntw = nt, c.waves = wv, c.run = rn;
@@ -526,7 +528,7 @@ extern "C" int qgemv_set_prefill_override(int mtr, int ntw, int waves, int run, 
         g_pf_override = {mtr, 0, 0, 0, 0};
         return QG_OK;
     }
-    if ((mtr != 1 && mtr != 2) || (ntw != 1 && ntw != 2 && ntw != 4 && ntw != 8) || (waves != 4 && waves != 8) ||
+    if ((mtr != 1 && mtr != 2) || (ntw != 1 && ntw != 2 && ntw != 4 && ntw != 8) || (waves != 4 && waves != 8 && waves != 16) ||
         (run != 1 && run != 2 && run != 4) || ksplit < 0 || ksplit > 64)
         return QG_ERR_SHAPE;
     g_pf_override = {mtr, ntw, waves, run, ksplit};
@@ -579,6 +581,7 @@ hipError_t launch_prefill(int nmat, const uint8_t *w0, const uint8_t *w1, const 
             return go_prefill<NM, MR, NT, WV, RN>(p, y, s);
 #define QG_PF_R(NM, MR, NT, WV) QG_PF(NM, MR, NT, WV, 1) QG_PF(NM, MR, NT, WV, 2) QG_PF(NM, MR, NT, WV, 4)
 #define QG_PF_W(NM, MR) QG_PF_R(NM, MR, 1, 4) QG_PF_R(NM, MR, 2, 4) QG_PF_R(NM, MR, 4, 4) QG_PF_R(NM, MR, 8, 4) \
+    QG_PF(NM, MR, 4, 16, 1) QG_PF(NM, MR, 8, 16, 1) \
     QG_PF_R(NM, MR, 1, 8) QG_PF_R(NM, MR, 2, 8) QG_PF_R(NM, MR, 4, 8) QG_PF_R(NM, MR, 8, 8)
     QG_PF_W(1, 1) QG_PF_W(1, 2) QG_PF_W(2, 1) QG_PF_W(2, 2)
 #undef QG_PF_W

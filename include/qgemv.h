@@ -269,7 +269,7 @@ int qgemv_time_next_launch(void *start_event, void *stop_event);
 
 /* Tuning hook for the matrix-core path (Q4_0, n_tok > 1): force 16-row tiles
  * per wave and matrix (mtr 1 or 2), 16-token tiles per workgroup (ntw 1, 2, 4
- * or 8), waves per workgroup (4 or 8), consecutive 32-weight blocks a lane
+ * or 8), waves per workgroup (4, 8 or 16), consecutive 32-weight blocks a lane
  * reads from a row per pass (run 1, 2 or 4) and the number of K ranges
  * (ksplit 1..64, 0 = built-in; honoured as far as the caller's scratch holds
  * the partial sums, and never more than the passes over K).  A shape the

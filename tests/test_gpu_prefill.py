@@ -30,7 +30,7 @@ SHAPES = [(1, 32, 2), (5, 96, 3), (150, 288, 17), (131, 576, 16), (64, 1536, 40)
           (300, 2048, 130), (40, 17408, 9)]
 # (mtr, ntw, waves, run): every shape the override accepts (shapes the library
 # does not build run as the nearest built one)
-TILES = list(itertools.product((1, 2), (1, 2, 4, 8), (4, 8), (1, 2, 4)))
+TILES = list(itertools.product((1, 2), (1, 2, 4, 8), (4, 8, 16), (1, 2, 4)))
 
 
 def _pow2_q4_0(rows, cols, rng, lo=-4, hi=3):
