@@ -301,7 +301,7 @@ def main():
     a = parse()
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported "
-              "(the path shards by rows across GPUs, but this build runs and reports one GPU only)",
+              "(the path shards by rows across GPUs; the benchmark runs and reports one GPU)",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np
