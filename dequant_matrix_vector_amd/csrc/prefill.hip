@@ -174,12 +174,14 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_0_kernel(PrefillParams p)
             constexpr int k = decltype(kc)::value;
             const int piece = threadIdx.x + k * NT;
             const int t = piece / (SCOLS / 4), c4 = piece % (SCOLS / 4);
-            int tok = tok_base + t;
-            int col = ss * SCOLS + 4 * c4;
-            lv |= (tok < p.n_tok && col < p.cols) ? (1u << k) : 0u;
-            tok = tok < p.n_tok ? tok : p.n_tok - 1;   // dead pieces read a valid address, stored as 0
-            col = col < p.cols ? col : 0;
-            xv[J][k] = *reinterpret_cast<const f32x4 *>(p.x + (int64_t)tok * p.cols + col);
+            const int tok = tok_base + t;
+            const int col = ss * SCOLS + 4 * c4;
+            const bool alive = tok < p.n_tok && col < p.cols;
+            lv |= alive ? (1u << k) : 0u;
+            // dead pieces (tokens past n_tok, columns past the row) all read
+            // the first 16 bytes of x: one cache line per wave, stored as 0
+            const int64_t off = alive ? (int64_t)tok * p.cols + col : 0;
+            xv[J][k] = *reinterpret_cast<const f32x4 *>(p.x + off);
         });
         int blk = ss * SB + lblk;
         lv |= blk < p.nb ? (1u << 31) : 0u;
