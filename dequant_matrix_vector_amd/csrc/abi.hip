@@ -166,8 +166,8 @@ int qgemv(int fmt, const void *packed, const float *x, float *y, int64_t rows, i
     Layout L;
     int st = check_product(fmt, packed, x, y, rows, cols, n_tok, &L);
     if (st) return st;
-    if (fmt == QG_Q4_0 && n_tok > 1 && prefill_enabled())
-        return launch_prefill(1, static_cast<const uint8_t *>(packed), nullptr, x, y, rows, cols, n_tok, nullptr, 0,
+    if (prefill_format(fmt) && n_tok > 1 && prefill_enabled())
+        return launch_prefill(fmt, 1, static_cast<const uint8_t *>(packed), nullptr, x, y, rows, cols, n_tok, nullptr, 0,
                               (hipStream_t)stream) == hipSuccess
                    ? QG_OK
                    : QG_ERR_LAUNCH;
@@ -215,8 +215,8 @@ int swiglu_gate_up(int fmt, const void *wg, const void *wu, const float *x, floa
     if (!wu) return QG_ERR_NULL;
     if (!aligned(wu, kPlaneAlign)) return QG_ERR_ALIGN;
     if (overlap(wu, L.total, h, n_tok * ffn * 4)) return QG_ERR_ALIAS;
-    if (fmt == QG_Q4_0 && n_tok > 1 && prefill_enabled())
-        return launch_prefill(2, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), x, h, ffn,
+    if (prefill_format(fmt) && n_tok > 1 && prefill_enabled())
+        return launch_prefill(fmt, 2, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), x, h, ffn,
                               d_model, n_tok, nullptr, 0, (hipStream_t)stream) == hipSuccess
                    ? QG_OK
                    : QG_ERR_LAUNCH;
@@ -231,7 +231,7 @@ int swiglu_gate_up(int fmt, const void *wg, const void *wu, const float *x, floa
 
 // Scratch of swiglu_ffn, in floats: h [n_tok][ffn], then, from the next
 // 256-byte boundary, room for the partial sums of a K split on the matrix-core
-// path (Q4_0, n_tok > 1) -- the most that the gate/up or the down product uses.
+// path (Q4_0 or Q4_K, n_tok > 1) -- the most that the gate/up or the down product uses.
 static int64_t ffn_part_offset(int64_t d_model, int64_t ffn, int64_t n_tok)
 {
     (void)d_model;
@@ -245,8 +245,8 @@ int64_t swiglu_ffn_scratch_elems(int fmt, int64_t d_model, int64_t ffn, int64_t 
     if (n_tok < 1 || n_tok >= (int64_t(1) << 31) || !layout_for(fmt, ffn, d_model, &La) ||
         !layout_for(fmt, d_model, ffn, &Lb))
         return QG_ERR_SHAPE;
-    if (fmt != QG_Q4_0 || n_tok == 1 || !prefill_enabled()) return n_tok * ffn;
-    const int64_t a = prefill_part_elems(2, ffn, d_model, n_tok), b = prefill_part_elems(1, d_model, ffn, n_tok);
+    if (!prefill_format(fmt) || n_tok == 1 || !prefill_enabled()) return n_tok * ffn;
+    const int64_t a = prefill_part_elems(fmt, 2, ffn, d_model, n_tok), b = prefill_part_elems(fmt, 1, d_model, ffn, n_tok);
     const int64_t part = a > b ? a : b;
     return part > 0 ? ffn_part_offset(d_model, ffn, n_tok) + part : n_tok * ffn;
 }
@@ -288,14 +288,14 @@ int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const fl
     const int st = check_ffn(fmt, wg, wu, wd, x, out, h_scratch, h_scratch_elems, d_model, ffn, n_tok, &Lg, &Ld);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    if (fmt == QG_Q4_0 && n_tok > 1 && prefill_enabled()) {
+    if (prefill_format(fmt) && n_tok > 1 && prefill_enabled()) {
         // partial sums of a K split go behind h, when the caller's scratch has room
         const int64_t po = ffn_part_offset(d_model, ffn, n_tok);
         float *part = h_scratch_elems > po ? h_scratch + po : nullptr;
         const int64_t pe = part ? h_scratch_elems - po : 0;
-        if (launch_prefill(2, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), x, h_scratch, ffn,
+        if (launch_prefill(fmt, 2, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), x, h_scratch, ffn,
                            d_model, n_tok, part, pe, s) != hipSuccess ||
-            launch_prefill(1, static_cast<const uint8_t *>(wd), nullptr, h_scratch, out, d_model, ffn, n_tok, part,
+            launch_prefill(fmt, 1, static_cast<const uint8_t *>(wd), nullptr, h_scratch, out, d_model, ffn, n_tok, part,
                            pe, s) != hipSuccess)
             return QG_ERR_LAUNCH;
         return QG_OK;
@@ -316,9 +316,9 @@ int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const fl
 }
 
 // Scratch of swiglu_ffn_block, in floats: h [n_tok][ffn]; on the matrix-core
-// path (Q4_0, n_tok > 1) then the normalized input [n_tok][d_model] and room
+// path (Q4_0 or Q4_K, n_tok > 1) then the normalized input [n_tok][d_model] and room
 // for split-K partial sums, each from a 256-byte boundary.
-static bool block_on_matrix_cores(int fmt, int64_t n_tok) { return fmt == QG_Q4_0 && n_tok > 1 && prefill_enabled(); }
+static bool block_on_matrix_cores(int fmt, int64_t n_tok) { return prefill_format(fmt) && n_tok > 1 && prefill_enabled(); }
 
 static int64_t block_xn_offset(int64_t ffn, int64_t n_tok) { return align_up(n_tok * ffn, kPlaneAlign / 4); }
 
@@ -335,7 +335,7 @@ int64_t swiglu_ffn_block_scratch_elems(int fmt, int64_t d_model, int64_t ffn, in
         !layout_for(fmt, d_model, ffn, &Lb))
         return QG_ERR_SHAPE;
     if (!block_on_matrix_cores(fmt, n_tok)) return n_tok * ffn;
-    const int64_t a = prefill_part_elems(2, ffn, d_model, n_tok), b = prefill_part_elems(1, d_model, ffn, n_tok);
+    const int64_t a = prefill_part_elems(fmt, 2, ffn, d_model, n_tok), b = prefill_part_elems(fmt, 1, d_model, ffn, n_tok);
     const int64_t part = a > b ? a : b;
     return part > 0 ? block_part_offset(d_model, ffn, n_tok) + part : block_xn_offset(ffn, n_tok) + n_tok * d_model;
 }
@@ -374,9 +374,9 @@ int swiglu_ffn_block(int fmt, const void *wg, const void *wu, const void *wd, co
         float *part = h_scratch_elems > po ? h_scratch + po : nullptr;
         const int64_t pe = part ? h_scratch_elems - po : 0;
         if (launch_rmsnorm(x, gamma, eps, xn, d_model, n_tok, s) != hipSuccess ||
-            launch_prefill(2, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), xn, h_scratch, ffn,
+            launch_prefill(fmt, 2, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), xn, h_scratch, ffn,
                            d_model, n_tok, part, pe, s) != hipSuccess ||
-            launch_prefill(1, static_cast<const uint8_t *>(wd), nullptr, h_scratch, out, d_model, ffn, n_tok, part,
+            launch_prefill(fmt, 1, static_cast<const uint8_t *>(wd), nullptr, h_scratch, out, d_model, ffn, n_tok, part,
                            pe, s, x) != hipSuccess)
             return QG_ERR_LAUNCH;
         return QG_OK;

@@ -1,6 +1,6 @@
 // Batched-token (prefill) product on the matrix cores: y[t][i] = sum_j W[i][j] x[t][j]
-// for n_tok > 1 with W in Q4_0, and the fused first half of the SwiGLU block,
-// h = silu(Wg x) * (Wu x).
+// for n_tok > 1 with W in Q4_0 or Q4_K, and the fused first half of the SwiGLU
+// block, h = silu(Wg x) * (Wu x).
 //
 // With several tokens every weight read is shared by all of them, so the work
 // is a dense contraction and belongs on the matrix units (llmoxide blog,
@@ -12,8 +12,10 @@
 //     one run per row and super-step) into registers, then transposed through
 //     a per-wave LDS area into the v_mfma_f32_16x16x32_bf16 A layout (lane l:
 //     row l%16, k-group l/16), where each lane dequantizes its block exactly in
-//     fp32 ((q-8)*d via the binary16-subnormal trick and v_fma_mix_f32, as in
-//     the GEMV) and rounds to bf16 (nearest even);
+//     fp32 (q*D - M via the binary16-subnormal trick and v_fma_mix_f32, as in
+//     the GEMV: Q4_0 D = d, M = 8d; Q4_K, whose repacked sub-blocks have the
+//     Q4_0 nibble order, D = d*sc and M = dmin*m of the sub-block, both exact)
+//     and rounds to bf16 (nearest even);
 //   * the workgroup stages the x tile of the super-step in LDS as bf16 (nearest
 //     even), in natural column order: the decode emits 8 consecutive columns
 //     per operand, so A and B agree on k without any shuffle;
@@ -42,7 +44,7 @@ struct PrefillParams {
     int64_t row_qbytes;
     int64_t soff;
     int64_t row_groups;
-    int nb;          // Q4_0 blocks per row (cols / 32)
+    int nb;          // 32-weight blocks per row (cols / 32): Q4_0 blocks or Q4_K sub-blocks
     int cols;
     int ssteps;      // super-steps (Q K steps each) covering the row
     int n_tok;
@@ -77,12 +79,14 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// Columns 8c .. 8c+7 of a Q4_0 block as 8 bf16 weights (q-8)*d, c = 0..3.
+// Columns 8c .. 8c+7 of a block as 8 bf16 weights q*D - M, c = 0..3.
 // Column j < 16 is the low nibble of byte j, column j >= 16 the high nibble of
 // byte j-16; so c = 0, 1 take the low nibbles of words (2c, 2c+1) and c = 2, 3
 // the high nibbles of words (2c-4, 2c-3).  A masked nibble pair read as two
-// binary16 subnormals is q*2^-24 (low) or q*2^-20 (high); with ds = d*2^24 or
-// d*2^20 and n8 = -8*d, fma(that, ds, n8) is (q-8)*d exactly in fp32.
+// binary16 subnormals is q*2^-24 (low) or q*2^-20 (high); with ds = D*2^24 or
+// D*2^20 and n8 = -M, fma(that, ds, n8) is q*D - M exactly in fp32 (for Q4_0
+// (q-8)*d; for Q4_K d*sc*q - dmin*m, whose two products are exact and whose
+// difference rounds once, as the format's own fp32 value does).
 __device__ __forceinline__ bf16x8 decode8(uint32_t wa, uint32_t wb, uint32_t mask, float ds, float n8)
 {
     const uint32_t ea = wa & mask, oa = (wa >> 8) & mask;   // bytes (0, 2) and (1, 3)
@@ -95,14 +99,28 @@ __device__ __forceinline__ bf16x8 decode8(uint32_t wa, uint32_t wb, uint32_t mas
     return __builtin_bit_cast(bf16x8, u);
 }
 
+// Q4_K: (D, M) = (d*sc, dmin*m) of sub-block s (0..7) from a super-block
+// header (d, dmin as binary16 in h.x; the 12-byte six-bit scale/min field in
+// h.y, h.z, h.w, unpacked as the llamini.cpp post's get_scale_min_k4 does).
+__device__ __forceinline__ f32x2 q4k_dm(u32x4 h, int s)
+{
+    const uint32_t sh = 8u * (uint32_t)(s & 3);
+    const uint32_t a = h.y >> sh, b = h.z >> sh, c = h.w >> sh;
+    const bool upper = s >= 4;
+    const uint32_t sc = upper ? ((c & 0xFu) | ((a >> 2) & 0x30u)) : (a & 63u);
+    const uint32_t m = upper ? (((c >> 4) & 0xFu) | ((b >> 2) & 0x30u)) : (b & 63u);
+    return f32x2{half_lo(h.x) * (float)sc, half_hi(h.x) * (float)m};
+}
+
 // One workgroup: W waves, each with MTR 16-row tiles of every matrix (NMAT),
 // over NTW 16-token tiles and the K range [k0, k1) of super-steps of 4Q
 // blocks.  Super-step S's weight runs and x pieces travel together in ring
 // slot S % 2: the loads of the next super-step are in flight while this one
 // is computed.
-template <int NMAT, int MTR, int NTW, int W, int Q>
-__global__ __launch_bounds__(W * 64) void prefill_q4_0_kernel(PrefillParams p)
+template <int FMT, int NMAT, int MTR, int NTW, int W, int Q>
+__global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
 {
+    constexpr bool KQ = FMT == QG_Q4_K;
     constexpr int MT = MTR * NMAT;          // 16-row tiles per wave
     constexpr int NT = W * 64;              // threads
     constexpr int SB = 4 * Q;               // blocks per super-step
@@ -114,7 +132,7 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_0_kernel(PrefillParams p)
     constexpr int XROW = SCOLS * 2 + 16;
     constexpr int XTILE = NTW * 16 * XROW;
     constexpr int AROW = SB * 16 + 16;
-    constexpr int SROW = SB * 2 + 4;
+    constexpr int SROW = KQ ? SB * 8 + 8 : SB * 2 + 4;   // Q4_0: f16 d; Q4_K: (D, M) as two floats
     constexpr int AWAVE = MT * 16 * (AROW + SROW);
     constexpr int XF4 = NTW * 16 * SCOLS / 4;   // float4 pieces of x per super-step
     constexpr int PT = XF4 / NT;
@@ -163,7 +181,9 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_0_kernel(PrefillParams p)
     // the ring: weight runs, scales, x pieces and liveness (bit k: x piece k
     // inside x; bit 31: the lane's weight block inside the row)
     u32x4 qa[2][MT][Q];
-    uint32_t da[2][MT][Q];
+    uint32_t da[2][MT][Q];                        // Q4_0: the block's f16 scale
+    u32x4 ha[2][KQ ? MT : 1][KQ ? Q : 1];         // Q4_K: the super-block header
+    int sub[2];                                   // Q4_K: the lane's sub-block (0..7)
     f32x4 xv[2][PT];
     uint32_t live[2];
 
@@ -193,10 +213,14 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_0_kernel(PrefillParams p)
                 const int64_t row = arow(m, i);
                 const uint8_t *base = p.q[m / MTR];
                 qa[J][m][i] = reinterpret_cast<const u32x4 *>(base + row * p.row_qbytes)[blk];
-                da[J][m][i] = (reinterpret_cast<const uint16_t *>(base + p.soff) + row * p.nb)[blk];
+                if constexpr (KQ)
+                    ha[J][m][i] = reinterpret_cast<const u32x4 *>(base + p.soff)[row * (p.nb / 8) + blk / 8];
+                else
+                    da[J][m][i] = (reinterpret_cast<const uint16_t *>(base + p.soff) + row * p.nb)[blk];
             });
         });
         live[J] = lv;
+        sub[J] = blk & 7;
     };
 
     auto consume = [&](auto jc, int nxt, bool refill) __attribute__((always_inline)) {
@@ -220,8 +244,14 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_0_kernel(PrefillParams p)
                 constexpr int i = decltype(ic)::value;
                 const int row = i * RPI + lrow;
                 *reinterpret_cast<u32x4 *>(aw + (m * 16 + row) * AROW + lblk * 16) = qa[J][m][i];
-                *reinterpret_cast<uint16_t *>(sw + (m * 16 + row) * SROW + lblk * 2) =
-                    (lv >> 31) ? (uint16_t)da[J][m][i] : (uint16_t)0;
+                if constexpr (KQ) {
+                    const f32x2 dm = q4k_dm(ha[J][m][i], sub[J]);
+                    *reinterpret_cast<f32x2 *>(sw + (m * 16 + row) * SROW + lblk * 8) =
+                        (lv >> 31) ? dm : f32x2{0.0f, 0.0f};
+                } else {
+                    *reinterpret_cast<uint16_t *>(sw + (m * 16 + row) * SROW + lblk * 2) =
+                        (lv >> 31) ? (uint16_t)da[J][m][i] : (uint16_t)0;
+                }
             });
         });
         __syncthreads();
@@ -234,8 +264,16 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_0_kernel(PrefillParams p)
             static_for<MT>([&](auto mc) __attribute__((always_inline)) {
                 constexpr int m = decltype(mc)::value;
                 const u32x4 w = *reinterpret_cast<const u32x4 *>(aw + (m * 16 + r16) * AROW + b * 16);
-                const float d = half_lo(*reinterpret_cast<const uint16_t *>(sw + (m * 16 + r16) * SROW + b * 2));
-                const float d24 = d * 0x1p24f, d20 = d * 0x1p20f, n8 = -8.0f * d;
+                float d, n8;
+                if constexpr (KQ) {
+                    const f32x2 dm = *reinterpret_cast<const f32x2 *>(sw + (m * 16 + r16) * SROW + b * 8);
+                    d = dm.x;
+                    n8 = -dm.y;
+                } else {
+                    d = half_lo(*reinterpret_cast<const uint16_t *>(sw + (m * 16 + r16) * SROW + b * 2));
+                    n8 = -8.0f * d;
+                }
+                const float d24 = d * 0x1p24f, d20 = d * 0x1p20f;
                 af[m][0] = decode8(w.x, w.y, 0x000F000Fu, d24, n8);
                 af[m][1] = decode8(w.z, w.w, 0x000F000Fu, d24, n8);
                 af[m][2] = decode8(w.x, w.y, 0x00F000F0u, d20, n8);
@@ -378,20 +416,21 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ 
     for (int j = threadIdx.x; j < n; j += 256) o[j] = xt[j] * sc * gamma[j];
 }
 
-// LDS of a workgroup: two bf16 x tiles plus one weight area per wave
-constexpr size_t pf_lds_bytes(int nmat, int mtr, int ntw, int waves, int run)
+// LDS of a workgroup: two bf16 x tiles plus one weight area per wave (codes
+// and per-block scales: f16 d for Q4_0, the (D, M) pair for Q4_K)
+constexpr size_t pf_lds_bytes(int fmt, int nmat, int mtr, int ntw, int waves, int run)
 {
-    return 2 * (size_t)ntw * 16 * (run * 256 + 16) +
-           (size_t)waves * nmat * mtr * 16 * ((run * 64 + 16) + (run * 8 + 4));
+    const size_t srow = fmt == QG_Q4_K ? (size_t)run * 32 + 8 : (size_t)run * 8 + 4;
+    return 2 * (size_t)ntw * 16 * (run * 256 + 16) + (size_t)waves * nmat * mtr * 16 * ((run * 64 + 16) + srow);
 }
 
-template <int NMAT, int MTR, int NTW, int W, int Q>
+template <int FMT, int NMAT, int MTR, int NTW, int W, int Q>
 hipError_t go_prefill(PrefillParams p, float *y, hipStream_t s)
 {
-    const size_t lds = pf_lds_bytes(NMAT, MTR, NTW, W, Q);
+    const size_t lds = pf_lds_bytes(FMT, NMAT, MTR, NTW, W, Q);
     const int64_t grid = p.row_groups * p.tok_groups * p.ksplit;
     if (grid >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-    auto kern = prefill_q4_0_kernel<NMAT, MTR, NTW, W, Q>;
+    auto kern = prefill_q4_kernel<FMT, NMAT, MTR, NTW, W, Q>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -432,10 +471,10 @@ hipError_t go_prefill(PrefillParams p, float *y, hipStream_t s)
 
 PrefillCfg g_pf_override = {0, 0, 0, 0, 0};
 
-// Tile shapes that are built: those whose ring, operands and accumulators
-// fit the register file without spilling (checked in the compiled code),
-// whose x pieces split evenly over the threads and whose LDS fits a CU.
-// Code: nmat*10000 + mtr*1000 + ntw*100 + waves*10 + run.
+// Tile shapes that are built, per format: those whose ring, operands and
+// accumulators fit the register file without spilling (checked in the
+// compiled code), whose x pieces split evenly over the threads and whose LDS
+// fits a CU.  Code: nmat*10000 + mtr*1000 + ntw*100 + waves*10 + run.
 constexpr int kBuiltShapes[] = {
     11141, 11142, 11144, 11181, 11182, 11184, 11241, 11242, 11244,
     11281, 11282, 11284, 11441, 11442, 11481, 11482, 11841, 11881,
@@ -447,13 +486,34 @@ constexpr int kBuiltShapes[] = {
     11561, 11961,   // 16 waves (waves * 10 = 160), one matrix only: two spill
 };
 
-constexpr bool pf_fits(int nmat, int mtr, int ntw, int waves, int run)
+#ifndef QG_PF_CENSUS_K
+constexpr int kBuiltShapesK[] = {
+    11141, 11142, 11144, 11181, 11182, 11184, 11241, 11242, 11244,
+    11281, 11282, 11284, 11441, 11442, 11481, 11482, 11561, 11841,
+    11881, 11961, 12141, 12142, 12144, 12181, 12182, 12241, 12242,
+    12281, 12282, 12441, 12442, 12481, 12482, 12841, 12881, 21141,
+    21142, 21144, 21181, 21182, 21241, 21242, 21281, 21282, 21441,
+    21442, 21481, 21482, 21841, 21881, 22141, 22142, 22181, 22241,
+    22242, 22281, 22441, 22442, 22841,
+};
+#endif
+
+constexpr bool pf_fits(int fmt, int nmat, int mtr, int ntw, int waves, int run)
 {
     const int code = nmat * 10000 + mtr * 1000 + ntw * 100 + waves * 10 + run;
+    const bool geometry = pf_lds_bytes(fmt, nmat, mtr, ntw, waves, run) <= 160 * 1024 &&
+                          ntw * 512 * run >= waves * 64 && ntw * 512 * run <= 16 * waves * 64;
+    if (fmt == QG_Q4_K) {
+#ifdef QG_PF_CENSUS_K
+        return geometry && (waves != 16 || nmat == 1);
+#else
+        for (int c : kBuiltShapesK)
+            if (c == code) return geometry;
+        return false;
+#endif
+    }
     for (int c : kBuiltShapes)
-        if (c == code)
-            return pf_lds_bytes(nmat, mtr, ntw, waves, run) <= 160 * 1024 && ntw * 512 * run >= waves * 64 &&
-                   ntw * 512 * run <= 16 * waves * 64;
+        if (c == code) return geometry;
     return false;
 }
 
@@ -463,36 +523,66 @@ constexpr bool pf_fits(int nmat, int mtr, int ntw, int waves, int run)
 // workgroup, 4 waves for the fused gate/up pair (8 waves and 8 token tiles,
 // 128 tokens sharing each decoded weight, from 8 tiles on) and 8 waves for a
 // single matrix (16 from 4 tiles on: 256 rows share each staged x tile);
-// then K ranges until the grid has about four workgroups per
-// CU (if the caller gave room for the partials), as long as the partial sums
-// (written, then read back) stay within half the weight bytes.
-PrefillCfg choose(int nmat, int64_t rows, int64_t cols, int64_t n_tok, int64_t part_elems)
+// then K ranges until the grid has about four workgroups per CU (if the
+// caller gave room for the partials), as long as the partial sums (written,
+// then read back) stay within half the weight bytes or 16 MB, whichever is
+// more.  A matrix too small for its shape (fewer workgroups than half the CUs
+// even with the K split that budget allows) takes the shape for fewer token
+// tiles, i.e. more token groups.
+static void default_tile(PrefillCfg &c, int nmat, int64_t n_tiles)
+{
+    c.mtr = 1;
+    c.ksplit = 0;
+    if (n_tiles == 1) {
+        c.ntw = 1, c.waves = 4, c.run = 2;
+    } else if (nmat == 2 && n_tiles >= 8) {
+        c.ntw = 8, c.waves = 8, c.run = 1;
+    } else {
+        c.ntw = n_tiles >= 4 ? 4 : 2;
+        c.waves = nmat == 2 ? 4 : (n_tiles >= 4 ? 16 : 8);
+        c.run = 1;
+    }
+}
+
+// Most K ranges the shape may take: a few ring turns each, at most 16, and
+// the partial-sum traffic budget above.
+static int64_t max_ksplit(const PrefillCfg &c, int nmat, int64_t rows, int64_t cols, int64_t n_tok)
+{
+    const int64_t ssteps = (cols / 32 + 4 * c.run - 1) / (4 * c.run);
+    int64_t ks = ssteps / 4 > 1 ? ssteps / 4 : 1;
+    ks = ks < 16 ? ks : 16;
+    // 8 bytes per partial (written, read back) against 18 bytes per 32 weights
+    const int64_t per_range = 8 * (int64_t)nmat * n_tok * rows;
+    const int64_t weights = (int64_t)nmat * rows * (cols / 32) * 18;
+    const int64_t budget = weights / 2 > (int64_t(16) << 20) ? weights / 2 : (int64_t(16) << 20);
+    const int64_t by_traffic = budget / per_range;
+    return ks < by_traffic ? ks : (by_traffic > 1 ? by_traffic : 1);
+}
+
+PrefillCfg choose(int fmt, int nmat, int64_t rows, int64_t cols, int64_t n_tok, int64_t part_elems)
 {
     PrefillCfg c = g_pf_override;
     const int64_t n_tiles = (n_tok + 15) / 16;
     if (c.mtr <= 0) {
-        c.mtr = 1;
-        c.ksplit = 0;
-        if (n_tiles == 1) {
-            c.ntw = 1, c.waves = 4, c.run = 2;
-        } else if (nmat == 2 && n_tiles >= 8) {
-            c.ntw = 8, c.waves = 8, c.run = 1;
-        } else {
-            c.ntw = n_tiles >= 4 ? 4 : 2;
-            c.waves = nmat == 2 ? 4 : (n_tiles >= 4 ? 16 : 8);
-            c.run = 1;
+        int64_t eff = n_tiles;
+        default_tile(c, nmat, eff);
+        while (eff > 1) {
+            const int64_t grid = ((rows + c.waves * 16 - 1) / (c.waves * 16)) * ((n_tok + c.ntw * 16 - 1) / (c.ntw * 16));
+            if (2 * grid * max_ksplit(c, nmat, rows, cols, n_tok) >= (int64_t)cu_count()) break;
+            eff = eff >= 8 ? 4 : (eff >= 4 ? 2 : 1);
+            default_tile(c, nmat, eff);
         }
     }
     // a shape that is not built falls back to the nearest one that is: fewer
     // token tiles last, then one row tile per matrix, the other wave count,
     // shorter runs (every nmat has 1, 1, 4, 1)
-    if (!pf_fits(nmat, c.mtr, c.ntw, c.waves, c.run)) {
+    if (!pf_fits(fmt, nmat, c.mtr, c.ntw, c.waves, c.run)) {
         bool found = false;
         for (int nt = c.ntw; nt >= 1 && !found; nt /= 2)
             for (int mr : {c.mtr, 1})
                 for (int wv : {c.waves, c.waves == 8 ? 4 : 8})
                     for (int rn = c.run; rn >= 1 && !found; rn /= 2)
-                        if (pf_fits(nmat, mr, nt, wv, rn)) {
+                        if (pf_fits(fmt, nmat, mr, nt, wv, rn)) {
                             c.mtr = mr, c.ntw = nt, c.waves = wv, c.run = rn;
                             found = true;
                         }
@@ -505,15 +595,8 @@ PrefillCfg choose(int nmat, int64_t rows, int64_t cols, int64_t n_tok, int64_t p
         const int64_t want = 4 * (int64_t)cu_count();
         const int64_t base = row_groups * tok_groups;
         ks = base >= want ? 1 : (want + base - 1) / base;
-        const int64_t by_len = ssteps / 4;   // keep each range a few ring turns long
-        ks = ks < by_len ? ks : (by_len > 1 ? by_len : 1);
-        ks = ks < 16 ? ks : 16;
-        // partial-sum traffic: 8 bytes per partial (written, read back) against
-        // 18 bytes per 32 weights of the nmat matrices
-        const int64_t per_range = 8 * (int64_t)nmat * n_tok * rows;
-        const int64_t weights = (int64_t)nmat * rows * (cols / 32) * 18;
-        const int64_t by_traffic = weights / 2 / per_range;
-        ks = ks < by_traffic ? ks : (by_traffic > 1 ? by_traffic : 1);
+        const int64_t most = max_ksplit(c, nmat, rows, cols, n_tok);
+        ks = ks < most ? ks : most;
     }
     ks = ks < ssteps ? ks : ssteps;
     while (ks > 1 && ks * nmat * n_tok * rows > part_elems) ks--;
@@ -539,9 +622,11 @@ extern "C" int qgemv_set_prefill_override(int mtr, int ntw, int waves, int run, 
 
 bool prefill_enabled() { return g_pf_override.mtr >= 0; }
 
-int64_t prefill_part_elems(int nmat, int64_t rows, int64_t cols, int64_t n_tok)
+bool prefill_format(int fmt) { return fmt == QG_Q4_0 || fmt == QG_Q4_K; }
+
+int64_t prefill_part_elems(int fmt, int nmat, int64_t rows, int64_t cols, int64_t n_tok)
 {
-    const PrefillCfg c = choose(nmat, rows, cols, n_tok, INT64_MAX);
+    const PrefillCfg c = choose(fmt, nmat, rows, cols, n_tok, INT64_MAX);
     return c.ksplit > 1 ? (int64_t)c.ksplit * nmat * n_tok * rows : 0;
 }
 
@@ -553,13 +638,14 @@ hipError_t launch_rmsnorm(const float *x, const float *gamma, float eps, float *
     return hipGetLastError();
 }
 
-hipError_t launch_prefill(int nmat, const uint8_t *w0, const uint8_t *w1, const float *x, float *y, int64_t rows,
-                          int64_t cols, int64_t n_tok, float *part, int64_t part_elems, hipStream_t s,
+hipError_t launch_prefill(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, const float *x, float *y,
+                          int64_t rows, int64_t cols, int64_t n_tok, float *part, int64_t part_elems, hipStream_t s,
                           const float *resid)
 {
     Layout L;
-    if (!layout_for(QG_Q4_0, rows, cols, &L) || n_tok < 1 || n_tok >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-    const PrefillCfg c = choose(nmat, rows, cols, n_tok, part ? part_elems : 0);
+    if (!prefill_format(fmt) || !layout_for(fmt, rows, cols, &L) || n_tok < 1 || n_tok >= (int64_t(1) << 31))
+        return hipErrorInvalidValue;
+    const PrefillCfg c = choose(fmt, nmat, rows, cols, n_tok, part ? part_elems : 0);
     PrefillParams p;
     p.q[0] = w0;
     p.q[1] = w1 ? w1 : w0;
@@ -578,9 +664,12 @@ hipError_t launch_prefill(int nmat, const uint8_t *w0, const uint8_t *w1, const 
     p.spk = (p.ssteps + c.ksplit - 1) / c.ksplit;
     p.resid = nmat == 1 ? resid : nullptr;
 #define QG_PF(NM, MR, NT, WV, RN)                                                                  \
-    if constexpr (pf_fits(NM, MR, NT, WV, RN))                                                     \
-        if (nmat == NM && c.mtr == MR && c.ntw == NT && c.waves == WV && c.run == RN)             \
-            return go_prefill<NM, MR, NT, WV, RN>(p, y, s);
+    if constexpr (pf_fits(QG_Q4_0, NM, MR, NT, WV, RN))                                            \
+        if (fmt == QG_Q4_0 && nmat == NM && c.mtr == MR && c.ntw == NT && c.waves == WV && c.run == RN) \
+            return go_prefill<QG_Q4_0, NM, MR, NT, WV, RN>(p, y, s);                               \
+    if constexpr (pf_fits(QG_Q4_K, NM, MR, NT, WV, RN))                                            \
+        if (fmt == QG_Q4_K && nmat == NM && c.mtr == MR && c.ntw == NT && c.waves == WV && c.run == RN) \
+            return go_prefill<QG_Q4_K, NM, MR, NT, WV, RN>(p, y, s);
 #define QG_PF_R(NM, MR, NT, WV) QG_PF(NM, MR, NT, WV, 1) QG_PF(NM, MR, NT, WV, 2) QG_PF(NM, MR, NT, WV, 4)
 #define QG_PF_W(NM, MR) QG_PF_R(NM, MR, 1, 4) QG_PF_R(NM, MR, 2, 4) QG_PF_R(NM, MR, 4, 4) QG_PF_R(NM, MR, 8, 4) \
     QG_PF(NM, MR, 4, 16, 1) QG_PF(NM, MR, 8, 16, 1) \

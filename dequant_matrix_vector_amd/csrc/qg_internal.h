@@ -84,7 +84,7 @@ hipError_t launch_dequant(int fmt, const uint8_t *packed, float *w, int64_t rows
 
 size_t gemv_lds_bytes(int64_t cols);
 
-// Batched-token path on the matrix cores (Q4_0, n_tok > 1).
+// Batched-token path on the matrix cores (Q4_0 and Q4_K, n_tok > 1).
 struct PrefillCfg {
     int mtr;     // 16-row tiles per wave and matrix (1, 2); 0 = built-in choice, -1 = path off
     int ntw;     // 16-token tiles per workgroup (1, 2, 4, 8)
@@ -94,13 +94,14 @@ struct PrefillCfg {
 };
 extern "C" int qgemv_set_prefill_override(int mtr, int ntw, int waves, int run, int ksplit);
 bool prefill_enabled();   // false after qgemv_set_prefill_override(-1, ...): per-token GEMV loop instead
+bool prefill_format(int fmt);   // formats the matrix-core path takes
 // Floats of partial sums the built-in choice splits K into (0: no split).
-int64_t prefill_part_elems(int nmat, int64_t rows, int64_t cols, int64_t n_tok);
+int64_t prefill_part_elems(int fmt, int nmat, int64_t rows, int64_t cols, int64_t n_tok);
 // nmat == 1: y = W0 x (+ resid, which may equal y).  nmat == 2: y = silu(W0 x) * (W1 x).
 // x fp32 [n_tok][cols].  part (part_elems floats, may be null) lets the K
 // dimension split over workgroups; the partial sums are then added in a
 // second, small launch.
-hipError_t launch_prefill(int nmat, const uint8_t *w0, const uint8_t *w1, const float *x, float *y,
+hipError_t launch_prefill(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, const float *x, float *y,
                           int64_t rows, int64_t cols, int64_t n_tok, float *part, int64_t part_elems,
                           hipStream_t s, const float *resid = nullptr);
 // Raw Q8_0 blocks (f16 d, 32 int8) of activation rows x [n_tok][n], n a multiple of 32.

@@ -8,14 +8,14 @@ import oracle
 REL = 2e-5      # fp32 GEMV bound: |dy| <= REL * sum|w x| + ABS
 ABS = 1e-7
 SILU_REL = 1e-6  # budget for the device exp and divide in h = silu(g) * u
-# matrix-core path (Q4_0, n_tok > 1): weights and x rounded to bf16 (nearest
+# matrix-core path (Q4_0 and Q4_K, n_tok > 1): weights and x rounded to bf16 (nearest
 # even) before fp32 accumulation, each term off by at most about 2 * 2^-9
 PF_REL = 8e-3
 
 
 def rel_for(fmt, n_tok):
     """The bound's relative factor for a product of this format and batch."""
-    return PF_REL if (fmt == "q4_0" and n_tok > 1) else REL
+    return PF_REL if (fmt in ("q4_0", "q4_k") and n_tok > 1) else REL
 
 
 def bf16_rne(a):

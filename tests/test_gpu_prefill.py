@@ -1,4 +1,4 @@
-"""GPU parity of the matrix-core path (Q4_0, n_tok > 1) through the C ABI.
+"""GPU parity of the matrix-core path (Q4_0 and Q4_K, n_tok > 1) through the C ABI.
 
 Bars (per element), with S = sum_j |w_ij x_tj| from the oracle:
   * y and the gate/up products: |y_gpu - y_ref| <= 8e-3 * S + 1e-7 (weights
@@ -40,6 +40,73 @@ def _pow2_q4_0(rows, cols, rng, lo=-4, hi=3):
 
 def _run(t, pk, x):
     return G.gemv_gpu(t, pk, x)
+
+
+# Q4_K shapes: cols a multiple of 256 (ragged rows, partial K steps, partial token tiles)
+SHAPES_K = [(1, 256, 2), (150, 768, 17), (64, 2048, 40), (97, 5632, 33), (300, 2048, 130), (40, 17408, 9)]
+
+
+def _pow2_q4_k(rows, cols, rng):
+    # d, dmin powers of two, sc a power of two, m = 0: every weight d*sc*q has
+    # at most 4 significant bits (exact in bf16)
+    nsb = cols // 256
+    d = (2.0 ** rng.integers(-8, -5, (rows, nsb))).astype(np.float16)
+    dmin = (2.0 ** rng.integers(-8, -5, (rows, nsb))).astype(np.float16)
+    sc = (2 ** rng.integers(0, 6, (rows, nsb, 8))).astype(np.uint8)
+    m = np.zeros((rows, nsb, 8), np.uint8)
+    return synth.QTensor("w", "q4_k", rows, cols, synth.pack_q4_k(d, dmin, sc, m, rng.integers(0, 16, (rows, cols))))
+
+
+@pytest.mark.parametrize("rows,cols,n_tok", SHAPES_K)
+def test_prefill_q4_k_within_bound(rows, cols, n_tok):
+    rng = np.random.default_rng(rows * 11 + cols + n_tok)
+    t = synth.make_tensor("q4_k", rows, cols, rng)
+    x = rng.standard_normal((n_tok, cols)).astype(np.float32)
+    y = _run(t, G.upload(t), x)
+    yr, S = oracle.gemv("q4_k", t.raw, x, rows, cols)
+    G.check_bound(y, yr, S, rel=G.PF_REL, what=f"prefill q4_k {rows}x{cols} n_tok={n_tok}")
+
+
+def test_prefill_q4_k_exact_inputs_bit_exact_every_tile():
+    # weights exact in bf16 (see _pow2_q4_k: the minimum term is 0), small-integer
+    # x: every partial sum is exact in fp32, under every tile shape
+    rng = np.random.default_rng(1150)
+    rows, cols, n_tok = 150, 1280, 37     # 40 sub-blocks: a partial K step for runs of 2 and 4
+    t = _pow2_q4_k(rows, cols, rng)
+    pk = G.upload(t)
+    x = rng.integers(-3, 4, (n_tok, cols)).astype(np.float32)
+    yr, _ = oracle.gemv("q4_k", t.raw, x, rows, cols)
+    try:
+        for tile in TILES:
+            G.qg().set_prefill_override(*tile)
+            y = _run(t, pk, x)
+            assert np.array_equal(y.astype(np.float64), yr), f"q4_k tile (mtr, ntw, waves, run) = {tile}"
+    finally:
+        G.qg().set_prefill_override(0)
+
+
+def test_prefill_q4_k_one_hot_tokens_give_bf16_weights():
+    rng = np.random.default_rng(1350)
+    rows, cols = 70, 2048
+    t = synth.make_tensor("q4_k", rows, cols, rng)
+    nb = cols // 32
+    cs = np.array([32 * ((5 * k) % nb) + k for k in range(32)])
+    x = np.zeros((32, cols), np.float32)
+    x[np.arange(32), cs] = 1.0
+    y = _run(t, G.upload(t), x)
+    w32 = oracle.dequant("q4_k", t.raw, rows, cols)
+    assert np.array_equal(y, G.bf16_rne(w32[:, cs]).T)
+
+
+def test_prefill_q4_k_swiglu_ffn():
+    # the TinyLlama-shaped Q4_K FFN at 24 tokens through swiglu_ffn, both
+    # products on the matrix cores
+    d_model, ffn = 2048, 5632
+    rng = np.random.default_rng(1550)
+    tens = [synth.make_tensor("q4_k", ffn, d_model, rng), synth.make_tensor("q4_k", ffn, d_model, rng),
+            synth.make_tensor("q4_k", d_model, ffn, rng)]
+    x = rng.standard_normal((24, d_model)).astype(np.float32)
+    G.check_ffn("q4_k", tens, x, d_model, ffn, "ffn q4_k n_tok=24")
 
 
 @pytest.mark.parametrize("rows,cols,n_tok", SHAPES)
