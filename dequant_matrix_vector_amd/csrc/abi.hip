@@ -381,8 +381,16 @@ int swiglu_ffn_block(int fmt, const void *wg, const void *wu, const void *wd, co
             return QG_ERR_LAUNCH;
         return QG_OK;
     }
-    const GemvCfg cg = choose_cfg(fmt, ffn, d_model, 2);
+    GemvCfg cg = choose_cfg(fmt, ffn, d_model, 2);
     const GemvCfg cd = choose_cfg(fmt, d_model, ffn, 1);
+    // Every workgroup stages the whole normalized input, x and the gain: twice
+    // the plain staging, from every workgroup at once.  Twice the waves in half
+    // as many workgroups keep the waves and halve that traffic.
+    GemvCfg forced;
+    if (!launch_override(&forced) && cg.max_wg >= 2 && cg.waves <= 4) {
+        cg.waves *= 2;
+        cg.max_wg /= 2;
+    }
     // every token's gate/up (which read x) before any down (which may overwrite x)
     for (int64_t t = 0; t < n_tok; t++) {
         if (launch_gate_up(fmt, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), x + t * d_model,

@@ -305,19 +305,27 @@ __device__ __forceinline__ void stage_finish(float *xs, int nchunk, XStage<NORM>
     }
 }
 
-// Chunks beyond the first two per thread (only when nchunk > 2 * threads),
-// staged synchronously before any weight load is issued.
+// Chunks from the thread's first + `from` blocks of the workgroup on, staged
+// synchronously before any weight load is issued.
 template <int SUMS, bool NORM>
-__device__ __forceinline__ void stage_rest(const float *__restrict__ x, const float *__restrict__ gamma, float *xs,
-                                           int nchunk, float &ss)
+__device__ __forceinline__ void stage_rest_from(const float *__restrict__ x, const float *__restrict__ gamma,
+                                                float *xs, int nchunk, float &ss, int from)
 {
-    for (int c = (int)threadIdx.x + 2 * (int)blockDim.x; c < nchunk; c += blockDim.x) {
+    for (int c = (int)threadIdx.x + from * (int)blockDim.x; c < nchunk; c += blockDim.x) {
         const float4 *src = reinterpret_cast<const float4 *>(x + (int64_t)c * kChunk);
         float4 v[8];
 #pragma unroll
         for (int k = 0; k < 8; k++) v[k] = src[k];
         stage_chunk<SUMS, NORM>(v, reinterpret_cast<const float4 *>(gamma + (int64_t)c * kChunk), xs, c, true, ss);
     }
+}
+
+// Chunks beyond the first two per thread (only when nchunk > 2 * threads).
+template <int SUMS, bool NORM>
+__device__ __forceinline__ void stage_rest(const float *__restrict__ x, const float *__restrict__ gamma, float *xs,
+                                           int nchunk, float &ss)
+{
+    stage_rest_from<SUMS, NORM>(x, gamma, xs, nchunk, ss, 2);
 }
 
 // ------------------------------------------------------- weight groups --
@@ -633,16 +641,23 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
         // No branches until the barrier: a join here would make the compiler
         // wait for every load in flight, the weight stream included.
         float ss = 0.0f;   // NORM: this thread's sum of x^2, chunks in a fixed order
-        XStage<NORM> xst;
-        stage_issue<NORM>(p.x, p.gamma, p.nchunk, xst);
-        stage_rest<Fmt<FMT>::kSums, NORM>(p.x, p.gamma, xs, p.nchunk, ss);
+        XStage<false> xst;
+        if constexpr (NORM) {
+            // the gain doubles the staging registers, and holding them under
+            // the weight ring would halve the waves a SIMD can hold; so the
+            // normalized staging runs chunk by chunk before the weight stream
+            stage_rest_from<Fmt<FMT>::kSums, true>(p.x, p.gamma, xs, p.nchunk, ss, 0);
+        } else {
+            stage_issue<false>(p.x, p.gamma, p.nchunk, xst);
+            stage_rest<Fmt<FMT>::kSums, false>(p.x, p.gamma, xs, p.nchunk, ss);
+        }
         __builtin_amdgcn_sched_barrier(0);
         set_rows(batch < nbatch ? batch : nbatch - 1);   // idle waves read a valid row
         prologue();
         // x's loads went out first, so finishing the staging waits for them
         // only, not for the weight loads behind them
         __builtin_amdgcn_sched_barrier(0);
-        stage_finish<Fmt<FMT>::kSums, NORM>(xs, p.nchunk, xst, ss);
+        if constexpr (!NORM) stage_finish<Fmt<FMT>::kSums, false>(xs, p.nchunk, xst, ss);
         if constexpr (NORM) {
             // wave sums (fixed xor tree) into the slots after the spare chunk
 #pragma unroll
