@@ -82,12 +82,91 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(const float *__r
     }
 }
 
+// Rows of whole 16-byte pieces that fit U pieces per thread (n % 4 == 0,
+// 16-byte aligned, n <= 4096 U): all loads in one round trip, values kept in
+// registers.  First the maximum M of the non-NaN values (fmaxf drops NaN;
+// -0 and +0 compare equal below, whichever fmaxf returns), agreed by the
+// whole workgroup; then the threads holding M scan their values in index
+// order for the first equal one, and the smallest such index wins.  The
+// result is the closed description above, with a few VALU operations per
+// element instead of a (value, index) update.
+template <int U>
+__global__ __launch_bounds__(kArgmaxThreads) void argmax4_kernel(const float *__restrict__ logits,
+                                                                 int32_t *__restrict__ token, int n)
+{
+    __shared__ float wmax[kArgmaxThreads / 64];
+    __shared__ int widx[kArgmaxThreads / 64];
+    const float *row = logits + (int64_t)blockIdx.x * n;
+    const float4 *rv = reinterpret_cast<const float4 *>(row);
+    const int nv = n / 4;
+    float4 v[U];
+#pragma unroll
+    for (int k = 0; k < U; k++) {
+        const int pc = k * kArgmaxThreads + (int)threadIdx.x;
+        v[k] = rv[pc < nv ? pc : nv - 1];
+    }
+    float tm = -__builtin_inff();   // this thread's maximum
+#pragma unroll
+    for (int k = 0; k < U; k++) {
+        const float m4 = fmaxf(fmaxf(v[k].x, v[k].y), fmaxf(v[k].z, v[k].w));
+        tm = fmaxf(tm, k * kArgmaxThreads + (int)threadIdx.x < nv ? m4 : -__builtin_inff());
+    }
+    float m = tm;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) wmax[wave] = m;
+    __syncthreads();
+    float M = wmax[0];
+#pragma unroll
+    for (int w = 1; w < kArgmaxThreads / 64; w++) M = fmaxf(M, wmax[w]);
+    int bi = 0x7FFFFFFF;
+    if (tm == M) {   // the few threads holding the maximum
+#pragma unroll
+        for (int k = U - 1; k >= 0; k--) {   // downwards: the last match written is the first index
+            const int pc = k * kArgmaxThreads + (int)threadIdx.x;
+            if (pc < nv) {
+                if (v[k].w == M) bi = pc * 4 + 3;
+                if (v[k].z == M) bi = pc * 4 + 2;
+                if (v[k].y == M) bi = pc * 4 + 1;
+                if (v[k].x == M) bi = pc * 4;
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) bi = min(bi, __shfl_xor(bi, off, 64));
+    if ((threadIdx.x & 63) == 0) widx[wave] = bi;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int i = widx[0];
+#pragma unroll
+        for (int w = 1; w < kArgmaxThreads / 64; w++) i = min(i, widx[w]);
+        const float first = row[0];
+        token[blockIdx.x] = (first != first) ? 0 : i;   // a NaN at index 0 is never replaced
+    }
+}
+
 } // namespace
 
 hipError_t launch_argmax(const float *logits, int32_t *token, int64_t n, int64_t n_tok, hipStream_t s)
 {
     if (n < 1 || n >= (int64_t(1) << 31) || n_tok < 1 || n_tok >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-    if (n % 4 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0)
+    const bool v4 = n % 4 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
+    const int64_t per = (n / 4 + kArgmaxThreads - 1) / kArgmaxThreads;   // pieces per thread
+    const dim3 grid((unsigned)n_tok), block(kArgmaxThreads);
+    if (v4 && per <= 1)
+        hipLaunchKernelGGL(argmax4_kernel<1>, grid, block, 0, s, logits, token, (int)n);
+    else if (v4 && per <= 2)
+        hipLaunchKernelGGL(argmax4_kernel<2>, grid, block, 0, s, logits, token, (int)n);
+    else if (v4 && per <= 4)
+        hipLaunchKernelGGL(argmax4_kernel<4>, grid, block, 0, s, logits, token, (int)n);
+    else if (v4 && per <= 8)
+        hipLaunchKernelGGL(argmax4_kernel<8>, grid, block, 0, s, logits, token, (int)n);
+    else if (v4 && per <= 12)
+        hipLaunchKernelGGL(argmax4_kernel<12>, grid, block, 0, s, logits, token, (int)n);
+    else if (v4 && per <= 16)
+        hipLaunchKernelGGL(argmax4_kernel<16>, grid, block, 0, s, logits, token, (int)n);
+    else if (v4)
         hipLaunchKernelGGL(argmax_kernel<4>, dim3((unsigned)n_tok), dim3(kArgmaxThreads), 0, s, logits, token, (int)n);
     else
         hipLaunchKernelGGL(argmax_kernel<1>, dim3((unsigned)n_tok), dim3(kArgmaxThreads), 0, s, logits, token, (int)n);
