@@ -26,7 +26,10 @@ def _gpu_argmax(v):
     return t.cpu().numpy()
 
 
-@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 255, 256, 257, 1000, 4097, 49152, 151936])
+# sizes for every per-thread piece count of the one-round kernel (1, 2, 4, 6-8, 9-12, 13-16 pieces of
+# 4 floats per thread), the unaligned path (n % 4 != 0) and the multi-round path (> 65536)
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 255, 256, 257, 1000, 4097, 4100, 8192, 12000, 32000, 40000,
+                               49152, 65536, 65540, 151936])
 def test_argmax_random_rows_with_ties(n):
     rng = np.random.default_rng(n)
     v = rng.standard_normal((5, n)).astype(np.float32)
@@ -37,7 +40,8 @@ def test_argmax_random_rows_with_ties(n):
     assert [int(a) for a in got] == [oracle.argmax(row) for row in v]
 
 
-def test_argmax_special_values():
+@pytest.mark.parametrize("n", [3000, 40000, 65536])
+def test_argmax_special_values(n):
     inf, nan = np.inf, np.nan
     rows = [
         [1.0, 3.0, 3.0, 2.0], [-inf, -inf, -inf, -inf], [-inf, -3e38, -inf, -inf], [1.0, inf, inf, 0.0],
@@ -46,11 +50,10 @@ def test_argmax_special_values():
     ]
     v = np.array(rows, np.float32)
     assert [int(a) for a in _gpu_argmax(v)] == [oracle.argmax(r) for r in v]
-    # the same patterns spread over a long row: specials in different lanes and waves
-    n = 3000
+    # the same patterns spread over a long row: specials in different lanes, waves and pieces
     rng = np.random.default_rng(7)
     long = rng.uniform(-1, 1, (6, n)).astype(np.float32)
-    long[0, [17, 1200, 2999]] = 5.0                       # three-way tie
+    long[0, [17, 1200, n - 1]] = 5.0                      # three-way tie
     long[1, ::7] = np.nan                                   # NaNs everywhere except index 0
     long[2, 0] = np.nan                                     # NaN at index 0
     long[3, [100, 900]] = np.inf

@@ -121,3 +121,16 @@ def test_block_fullsize_27b_sampled():
             want = x[:, r0:r0 + 128].astype(np.float64) + yr
             bound = rel * S + G.ABS + np.abs(want) * 2.0 ** -24
             assert np.all(np.abs(out[:, r0:r0 + 128] - want) <= bound), f"27B block out n_tok={n_tok} rows {r0}.."
+
+
+@pytest.mark.parametrize("d_model,ffn", [(2048, 512), (5120, 512), (8192, 256), (8224, 256)])
+def test_block_matrix_cores_rmsnorm_widths(d_model, ffn):
+    # several tokens on the matrix cores: the RMSNorm launch keeps 2, 6 or 8
+    # float4 pieces of x per thread in registers; 8224 columns take the
+    # strided fallback
+    n_tok = 4
+    tens = _tensors("q4_0", d_model, ffn, 2300 + d_model)
+    rng = np.random.default_rng(2400 + d_model)
+    x = (3.0 * rng.standard_normal((n_tok, d_model))).astype(np.float32)
+    gamma = rng.uniform(0.2, 2.0, d_model).astype(np.float32)
+    check_block("q4_0", tens, x, gamma, d_model, ffn, f"block q4_0 n_tok={n_tok} d_model={d_model}")
