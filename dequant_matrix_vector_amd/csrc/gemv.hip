@@ -157,13 +157,24 @@ GemvCfg choose_cfg(int fmt, int64_t rows, int64_t cols, int nmat)
         c.waves = (nmat == 1 && rows >= 32768) ? 4 : 2;
         c.max_wg = rows >= 32768 ? cus : 4 * cus;
     } else {
-        // two rows per lane group for tall single matrices (x reuse from LDS);
-        // the fused gate/up kernel already reads two rows per staged x chunk
-        c.r = (nmat == 1 && rows >= 2048) ? 2 : 1;
-        // long rows want deeper per-lane prefetch and more waves per workgroup
+        // long rows want deeper per-lane prefetch
         c.depth = nchunk >= 256 ? 4 : 2;
-        c.waves = nmat == 2 ? 2 : (nchunk >= 256 ? 8 : 4);
         c.max_wg = 4 * cus;
+        if (nmat == 2) {
+            // the fused gate/up kernel already reads two rows per staged x chunk
+            c.r = 1;
+            c.waves = 2;
+        } else {
+            // a single matrix: about one workgroup per CU (each stages all of
+            // x, so more would repeat the staging; fewer leave CUs idle), two
+            // rows per lane group only where rows are plentiful (x reuse from
+            // LDS)
+            const int64_t g = 64 / c.lpr;
+            c.r = rows / g >= 8 * (int64_t)cus ? 2 : 1;
+            const int64_t batches = (rows + g * c.r - 1) / (g * c.r);
+            const int64_t w = (batches + cus / 2) / cus;
+            c.waves = (int)(w < 2 ? 2 : (w > 8 ? 8 : w));
+        }
     }
     return c;
 }
