@@ -205,7 +205,7 @@ def workload_report(qg, synth, torch, np, dev, graph_iters=20):
                 qg.swiglu_ffn(tens[gi].fmt, pk[gi], pk[ui], pk[di], xs[w.d_model], w.d_model, w.ffn,
                               out=outs["down"], h_scratch=scratch)
             for j, t in enumerate(tens):
-                if t.name in ffn_names:
+                if is_ffn and t.name in ffn_names:   # already run by swiglu_ffn
                     continue
                 qg.qgemv(t.fmt, pk[j], xs[t.cols], t.rows, t.cols, y=outs[t.name])
 
