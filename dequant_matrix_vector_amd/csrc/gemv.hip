@@ -152,10 +152,18 @@ GemvCfg choose_cfg(int fmt, int64_t rows, int64_t cols, int nmat)
         return c;
     }
     if (eight_bit) {
-        c.r = rows >= 2048 ? 2 : 1;
-        c.depth = nmat == 2 ? 2 : 4;
-        c.waves = (nmat == 1 && rows >= 32768) ? 4 : 2;
-        c.max_wg = rows >= 32768 ? cus : 4 * cus;
+        c.max_wg = 4 * cus;
+        if (nmat == 1 && rows >= 32768) {
+            // vocab heads (sweep over the SmolLM2-shaped Q8_0 [49152][576] and
+            // INT8 [49152][2048] heads): one row per lane group, 4 waves
+            c.r = 1;
+            c.depth = 2;
+            c.waves = 4;
+        } else {
+            c.r = rows >= 2048 ? 2 : 1;
+            c.depth = nmat == 2 ? 2 : 4;
+            c.waves = 2;
+        }
     } else {
         // long rows want deeper per-lane prefetch
         c.depth = nchunk >= 256 ? 4 : 2;
