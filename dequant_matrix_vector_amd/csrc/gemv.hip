@@ -152,18 +152,14 @@ GemvCfg choose_cfg(int fmt, int64_t rows, int64_t cols, int nmat)
         return c;
     }
     if (eight_bit) {
+        // one row per lane group and 4 waves (sweeps over the SmolLM2-shaped
+        // Q8_0 [49152][576] and INT8 [49152][2048] heads and the INT8 FFN
+        // [8192][2048] pair and [2048][8192] down); a 4-deep ring for a single
+        // matrix, 2 for the pair and the tall heads
         c.max_wg = 4 * cus;
-        if (nmat == 1 && rows >= 32768) {
-            // vocab heads (sweep over the SmolLM2-shaped Q8_0 [49152][576] and
-            // INT8 [49152][2048] heads): one row per lane group, 4 waves
-            c.r = 1;
-            c.depth = 2;
-            c.waves = 4;
-        } else {
-            c.r = rows >= 2048 ? 2 : 1;
-            c.depth = nmat == 2 ? 2 : 4;
-            c.waves = 2;
-        }
+        c.r = 1;
+        c.waves = 4;
+        c.depth = (nmat == 2 || rows >= 32768) ? 2 : 4;
     } else {
         // long rows want deeper per-lane prefetch
         c.depth = nchunk >= 256 ? 4 : 2;
