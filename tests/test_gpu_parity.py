@@ -164,7 +164,7 @@ def test_every_launch_shape(fmt):
     try:
         for lpr in (8, 16, 32, 64):
             for r in (1, 2):
-                for waves in (1, 4, 8):
+                for waves in (1, 3, 4, 5, 8):
                     for depth in (2, 4):
                         for max_wg in (0, 3):
                             for cpl in (1, 2, 4):
@@ -193,7 +193,7 @@ def test_gate_up_every_launch_shape(fmt):
     try:
         for lpr in (8, 16, 32, 64):
             for rr in (1, 2):
-                for waves in (1, 4, 8):
+                for waves in (1, 3, 4, 5, 8):
                     for depth in (2, 4):
                         for max_wg in (0, 3):
                             for cpl in (1, 2, 4):
