@@ -176,7 +176,7 @@ def workload_report(qg, synth, torch, np, dev, graph_iters=20):
     ("hbm"), otherwise they may sit in the 256 MB Infinity Cache ("cache")."""
     rep = {}
     plans = [(synth.CFG1, 1), (synth.CFG2, 1), (synth.CFG3, 1), (synth.CFG4, 1),
-             (synth.CFG5, 8), (synth.CFG5, 128), (synth.CFG6, 1), (synth.CFG3, 128)]
+             (synth.CFG5, 8), (synth.CFG5, 128), (synth.CFG6, 1), (synth.CFG3, 128), (synth.CFG6, 128)]
     for w, n_tok in plans:
         tens = synth.gen_workload(w)
         wbytes = sum(t.weight_bytes for t in tens)
@@ -231,7 +231,7 @@ def workload_report(qg, synth, torch, np, dev, graph_iters=20):
                     "weight_bytes": wbytes, "GBs": round(wbytes / us / 1e3, 1),
                     "pct_hbm_peak": round(100 * wbytes / us / 1e3 / HBM_PEAK_GBS, 1),
                     "resident": "hbm" if ncopy * wbytes >= ROTATE_BYTES else "cache",
-                    "path": "matrix cores (bf16 MFMA)" if (n_tok > 1 and tens[0].fmt in ("q4_0", "q4_k")) else "GEMV"}
+                    "path": "matrix cores (bf16 MFMA)" if (n_tok > 1 and tens[0].fmt in ("q4_0", "q4_k", "q6_k")) else "GEMV"}
         if n_tok > 1:
             flops = 2 * n_tok * sum(t.rows * t.cols for t in tens)
             rep[key]["TFLOPs"] = round(flops / us / 1e6, 2)

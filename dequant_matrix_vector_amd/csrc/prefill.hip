@@ -1,6 +1,6 @@
 // Batched-token (prefill) product on the matrix cores: y[t][i] = sum_j W[i][j] x[t][j]
-// for n_tok > 1 with W in Q4_0 or Q4_K, and the fused first half of the SwiGLU
-// block, h = silu(Wg x) * (Wu x).
+// for n_tok > 1 with W in Q4_0, Q4_K or Q6_K, and the fused first half of the
+// SwiGLU block, h = silu(Wg x) * (Wu x).
 //
 // With several tokens every weight read is shared by all of them, so the work
 // is a dense contraction and belongs on the matrix units (llmoxide blog,
@@ -14,7 +14,9 @@
 //     row l%16, k-group l/16), where each lane dequantizes its block exactly in
 //     fp32 (q*D - M via the binary16-subnormal trick and v_fma_mix_f32, as in
 //     the GEMV: Q4_0 D = d, M = 8d; Q4_K, whose repacked sub-blocks have the
-//     Q4_0 nibble order, D = d*sc and M = dmin*m of the sub-block, both exact)
+//     Q4_0 nibble order, D = d*sc and M = dmin*m of the sub-block, both exact;
+//     Q6_K, the same nibble order with the two high bits of each code OR-ed
+//     in from the high-bit plane, D = d*sc of each 16-column half and M = 32D)
 //     and rounds to bf16 (nearest even);
 //   * the workgroup stages the x tile of the super-step in LDS as bf16 (nearest
 //     even), in natural column order: the decode emits 8 consecutive columns
@@ -52,6 +54,8 @@ struct PrefillParams {
     int ksplit;      // K ranges, one per workgroup of a (row group, token group)
     int spk;         // super-steps per K range; every range is non-empty
     const float *resid;  // NMAT 1: residual [n_tok][rows] added to y (may be y itself), or null
+    int64_t hoff;    // Q6_K: offsets of the high-bit plane and the f16 d plane
+    int64_t doff;
 };
 
 template <int N, typename F>
@@ -99,6 +103,34 @@ __device__ __forceinline__ bf16x8 decode8(uint32_t wa, uint32_t wb, uint32_t mas
     return __builtin_bit_cast(bf16x8, u);
 }
 
+// Q6_K: as decode8, the codes' two high bits OR-ed in from the high-bit words
+// of the two code words (ha for wa, hb for wb; each already shifted by 2 for
+// an odd code word), at bit 4 of each half for the low nibbles (the code is
+// q*2^-24) or at bit 8 for the high nibbles (q*2^-20); ds = D*2^24 or D*2^20,
+// n8 = -32D.
+__device__ __forceinline__ bf16x8 decode8_q6(uint32_t wa, uint32_t wb, uint32_t ha, uint32_t hb, bool high, float ds,
+                                            float n8)
+{
+    uint32_t ea, oa, eb, ob;
+    if (high) {
+        ea = (wa & 0x00F000F0u) | (ha & 0x03000300u);
+        oa = ((wa >> 8) & 0x00F000F0u) | ((ha << 8) & 0x03000300u);
+        eb = (wb & 0x00F000F0u) | (hb & 0x03000300u);
+        ob = ((wb >> 8) & 0x00F000F0u) | ((hb << 8) & 0x03000300u);
+    } else {
+        ea = (wa & 0x000F000Fu) | (ha & 0x00300030u);
+        oa = ((wa >> 8) & 0x000F000Fu) | ((ha >> 8) & 0x00300030u);
+        eb = (wb & 0x000F000Fu) | (hb & 0x00300030u);
+        ob = ((wb >> 8) & 0x000F000Fu) | ((hb >> 8) & 0x00300030u);
+    }
+    uint4 u;
+    u.x = pack_bf16(__builtin_fmaf(half_lo(ea), ds, n8), __builtin_fmaf(half_lo(oa), ds, n8));
+    u.y = pack_bf16(__builtin_fmaf(half_hi(ea), ds, n8), __builtin_fmaf(half_hi(oa), ds, n8));
+    u.z = pack_bf16(__builtin_fmaf(half_lo(eb), ds, n8), __builtin_fmaf(half_lo(ob), ds, n8));
+    u.w = pack_bf16(__builtin_fmaf(half_hi(eb), ds, n8), __builtin_fmaf(half_hi(ob), ds, n8));
+    return __builtin_bit_cast(bf16x8, u);
+}
+
 // Q4_K: (D, M) = (d*sc, dmin*m) of sub-block s (0..7) from a super-block
 // header (d, dmin as binary16 in h.x; the 12-byte six-bit scale/min field in
 // h.y, h.z, h.w, unpacked as the llamini.cpp post's get_scale_min_k4 does).
@@ -121,6 +153,7 @@ template <int FMT, int NMAT, int MTR, int NTW, int W, int Q>
 __global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
 {
     constexpr bool KQ = FMT == QG_Q4_K;
+    constexpr bool K6 = FMT == QG_Q6_K;
     constexpr int MT = MTR * NMAT;          // 16-row tiles per wave
     constexpr int NT = W * 64;              // threads
     constexpr int SB = 4 * Q;               // blocks per super-step
@@ -132,8 +165,10 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
     constexpr int XROW = SCOLS * 2 + 16;
     constexpr int XTILE = NTW * 16 * XROW;
     constexpr int AROW = SB * 16 + 16;
-    constexpr int SROW = KQ ? SB * 8 + 8 : SB * 2 + 4;   // Q4_0: f16 d; Q4_K: (D, M) as two floats
-    constexpr int AWAVE = MT * 16 * (AROW + SROW);
+    // Q4_0: f16 d; Q4_K: (D, M) as two floats; Q6_K: the two halves' D
+    constexpr int SROW = (KQ || K6) ? SB * 8 + 8 : SB * 2 + 4;
+    constexpr int HROW = K6 ? SB * 8 + 8 : 0;           // Q6_K: 8 bytes of high bits per block
+    constexpr int AWAVE = MT * 16 * (AROW + SROW + HROW);
     constexpr int XF4 = NTW * 16 * SCOLS / 4;   // float4 pieces of x per super-step
     constexpr int PT = XF4 / NT;
     static_assert(XF4 % NT == 0 && PT >= 1 && PT <= 16, "x pieces must split evenly over the threads");
@@ -144,6 +179,7 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
     const int r16 = lane & 15, g = lane >> 4;
     uint8_t *aw = lds + 2 * XTILE + wave * AWAVE;           // this wave's weight area
     uint8_t *sw = aw + MT * 16 * AROW;
+    uint8_t *hw = sw + MT * 16 * SROW;                      // Q6_K: high bits
 
     // work item (row group, K range, token group), token group fastest;
     // consecutive items share an XCD, so the token groups of one row group
@@ -183,6 +219,8 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
     u32x4 qa[2][MT][Q];
     uint32_t da[2][MT][Q];                        // Q4_0: the block's f16 scale
     u32x4 ha[2][KQ ? MT : 1][KQ ? Q : 1];         // Q4_K: the super-block header
+    uint2 h6[2][K6 ? MT : 1][K6 ? Q : 1];         // Q6_K: the block's high bits
+    uint32_t d6[2][K6 ? MT : 1][K6 ? Q : 1];      // Q6_K: the super-block's f16 d (da: the two int8 scales)
     int sub[2];                                   // Q4_K: the lane's sub-block (0..7)
     f32x4 xv[2][PT];
     uint32_t live[2];
@@ -213,10 +251,15 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
                 const int64_t row = arow(m, i);
                 const uint8_t *base = p.q[m / MTR];
                 qa[J][m][i] = reinterpret_cast<const u32x4 *>(base + row * p.row_qbytes)[blk];
-                if constexpr (KQ)
+                if constexpr (KQ) {
                     ha[J][m][i] = reinterpret_cast<const u32x4 *>(base + p.soff)[row * (p.nb / 8) + blk / 8];
-                else
+                } else {
                     da[J][m][i] = (reinterpret_cast<const uint16_t *>(base + p.soff) + row * p.nb)[blk];
+                    if constexpr (K6) {
+                        h6[J][m][i] = reinterpret_cast<const uint2 *>(base + p.hoff)[row * p.nb + blk];
+                        d6[J][m][i] = (reinterpret_cast<const uint16_t *>(base + p.doff) + row * (p.nb / 8))[blk / 8];
+                    }
+                }
             });
         });
         live[J] = lv;
@@ -248,6 +291,14 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
                     const f32x2 dm = q4k_dm(ha[J][m][i], sub[J]);
                     *reinterpret_cast<f32x2 *>(sw + (m * 16 + row) * SROW + lblk * 8) =
                         (lv >> 31) ? dm : f32x2{0.0f, 0.0f};
+                } else if constexpr (K6) {
+                    // the two 16-column halves' D = d * sc (exact: 11-bit by 8-bit)
+                    const float d = half_lo(d6[J][m][i]);
+                    const uint32_t sc = da[J][m][i];
+                    const f32x2 dd{d * (float)(int8_t)(sc & 0xFFu), d * (float)(int8_t)((sc >> 8) & 0xFFu)};
+                    *reinterpret_cast<f32x2 *>(sw + (m * 16 + row) * SROW + lblk * 8) =
+                        (lv >> 31) ? dd : f32x2{0.0f, 0.0f};
+                    *reinterpret_cast<uint2 *>(hw + (m * 16 + row) * HROW + lblk * 8) = h6[J][m][i];
                 } else {
                     *reinterpret_cast<uint16_t *>(sw + (m * 16 + row) * SROW + lblk * 2) =
                         (lv >> 31) ? (uint16_t)da[J][m][i] : (uint16_t)0;
@@ -264,6 +315,18 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
             static_for<MT>([&](auto mc) __attribute__((always_inline)) {
                 constexpr int m = decltype(mc)::value;
                 const u32x4 w = *reinterpret_cast<const u32x4 *>(aw + (m * 16 + r16) * AROW + b * 16);
+                if constexpr (K6) {
+                    // code words 0, 1 take high-bit word 0 (shifted 0, 2), words 2, 3 word 1
+                    const uint2 hv = *reinterpret_cast<const uint2 *>(hw + (m * 16 + r16) * HROW + b * 8);
+                    const f32x2 dd = *reinterpret_cast<const f32x2 *>(sw + (m * 16 + r16) * SROW + b * 8);
+                    const float a24 = dd.x * 0x1p24f, na = -32.0f * dd.x;
+                    const float b20 = dd.y * 0x1p20f, nb = -32.0f * dd.y;
+                    af[m][0] = decode8_q6(w.x, w.y, hv.x, hv.x >> 2, false, a24, na);
+                    af[m][1] = decode8_q6(w.z, w.w, hv.y, hv.y >> 2, false, a24, na);
+                    af[m][2] = decode8_q6(w.x, w.y, hv.x, hv.x >> 2, true, b20, nb);
+                    af[m][3] = decode8_q6(w.z, w.w, hv.y, hv.y >> 2, true, b20, nb);
+                    return;
+                }
                 float d, n8;
                 if constexpr (KQ) {
                     const f32x2 dm = *reinterpret_cast<const f32x2 *>(sw + (m * 16 + r16) * SROW + b * 8);
@@ -463,11 +526,14 @@ __global__ __launch_bounds__(256) void rmsnorm4_kernel(const float *__restrict__
 }
 
 // LDS of a workgroup: two bf16 x tiles plus one weight area per wave (codes
-// and per-block scales: f16 d for Q4_0, the (D, M) pair for Q4_K)
+// and per-block scales: f16 d for Q4_0, the (D, M) pair for Q4_K, the two
+// halves' D for Q6_K, which also stages 8 bytes of high bits per block)
 constexpr size_t pf_lds_bytes(int fmt, int nmat, int mtr, int ntw, int waves, int run)
 {
-    const size_t srow = fmt == QG_Q4_K ? (size_t)run * 32 + 8 : (size_t)run * 8 + 4;
-    return 2 * (size_t)ntw * 16 * (run * 256 + 16) + (size_t)waves * nmat * mtr * 16 * ((run * 64 + 16) + srow);
+    const size_t srow = (fmt == QG_Q4_K || fmt == QG_Q6_K) ? (size_t)run * 32 + 8 : (size_t)run * 8 + 4;
+    const size_t hrow = fmt == QG_Q6_K ? (size_t)run * 32 + 8 : 0;
+    return 2 * (size_t)ntw * 16 * (run * 256 + 16) +
+           (size_t)waves * nmat * mtr * 16 * ((run * 64 + 16) + srow + hrow);
 }
 
 template <int FMT, int NMAT, int MTR, int NTW, int W, int Q>
@@ -544,11 +610,32 @@ constexpr int kBuiltShapesK[] = {
 };
 #endif
 
+#ifndef QG_PF_CENSUS_6
+constexpr int kBuiltShapes6[] = {
+    11141, 11142, 11144, 11181, 11182, 11184, 11241, 11242, 11244,
+    11281, 11282, 11284, 11441, 11442, 11481, 11482, 11561, 11841,
+    11881, 11961, 12141, 12142, 12144, 12181, 12182, 12241, 12242,
+    12244, 12281, 12282, 12441, 12442, 12481, 12841, 12881, 21141,
+    21142, 21144, 21181, 21182, 21241, 21242, 21244, 21281, 21282,
+    21441, 21442, 21481, 21841, 21881, 22141, 22142, 22181, 22241,
+    22242, 22281, 22441, 22841,
+};
+#endif
+
 constexpr bool pf_fits(int fmt, int nmat, int mtr, int ntw, int waves, int run)
 {
     const int code = nmat * 10000 + mtr * 1000 + ntw * 100 + waves * 10 + run;
     const bool geometry = pf_lds_bytes(fmt, nmat, mtr, ntw, waves, run) <= 160 * 1024 &&
                           ntw * 512 * run >= waves * 64 && ntw * 512 * run <= 16 * waves * 64;
+    if (fmt == QG_Q6_K) {
+#ifdef QG_PF_CENSUS_6
+        return geometry && (waves != 16 || nmat == 1);
+#else
+        for (int c : kBuiltShapes6)
+            if (c == code) return geometry;
+        return false;
+#endif
+    }
     if (fmt == QG_Q4_K) {
 #ifdef QG_PF_CENSUS_K
         return geometry && (waves != 16 || nmat == 1);
@@ -668,7 +755,7 @@ extern "C" int qgemv_set_prefill_override(int mtr, int ntw, int waves, int run, 
 
 bool prefill_enabled() { return g_pf_override.mtr >= 0; }
 
-bool prefill_format(int fmt) { return fmt == QG_Q4_0 || fmt == QG_Q4_K; }
+bool prefill_format(int fmt) { return fmt == QG_Q4_0 || fmt == QG_Q4_K || fmt == QG_Q6_K; }
 
 int64_t prefill_part_elems(int fmt, int nmat, int64_t rows, int64_t cols, int64_t n_tok)
 {
@@ -721,13 +808,18 @@ hipError_t launch_prefill(int fmt, int nmat, const uint8_t *w0, const uint8_t *w
     p.ksplit = c.ksplit;
     p.spk = (p.ssteps + c.ksplit - 1) / c.ksplit;
     p.resid = nmat == 1 ? resid : nullptr;
+    p.hoff = L.hplane_off;
+    p.doff = L.dplane_off;
 #define QG_PF(NM, MR, NT, WV, RN)                                                                  \
     if constexpr (pf_fits(QG_Q4_0, NM, MR, NT, WV, RN))                                            \
         if (fmt == QG_Q4_0 && nmat == NM && c.mtr == MR && c.ntw == NT && c.waves == WV && c.run == RN) \
             return go_prefill<QG_Q4_0, NM, MR, NT, WV, RN>(p, y, s);                               \
     if constexpr (pf_fits(QG_Q4_K, NM, MR, NT, WV, RN))                                            \
         if (fmt == QG_Q4_K && nmat == NM && c.mtr == MR && c.ntw == NT && c.waves == WV && c.run == RN) \
-            return go_prefill<QG_Q4_K, NM, MR, NT, WV, RN>(p, y, s);
+            return go_prefill<QG_Q4_K, NM, MR, NT, WV, RN>(p, y, s);                               \
+    if constexpr (pf_fits(QG_Q6_K, NM, MR, NT, WV, RN))                                            \
+        if (fmt == QG_Q6_K && nmat == NM && c.mtr == MR && c.ntw == NT && c.waves == WV && c.run == RN) \
+            return go_prefill<QG_Q6_K, NM, MR, NT, WV, RN>(p, y, s);
 #define QG_PF_R(NM, MR, NT, WV) QG_PF(NM, MR, NT, WV, 1) QG_PF(NM, MR, NT, WV, 2) QG_PF(NM, MR, NT, WV, 4)
 #define QG_PF_W(NM, MR) QG_PF_R(NM, MR, 1, 4) QG_PF_R(NM, MR, 2, 4) QG_PF_R(NM, MR, 4, 4) QG_PF_R(NM, MR, 8, 4) \
     QG_PF(NM, MR, 4, 16, 1) QG_PF(NM, MR, 8, 16, 1) \

@@ -1,4 +1,4 @@
-"""GPU parity of the matrix-core path (Q4_0 and Q4_K, n_tok > 1) through the C ABI.
+"""GPU parity of the matrix-core path (Q4_0, Q4_K and Q6_K, n_tok > 1) through the C ABI.
 
 Bars (per element), with S = sum_j |w_ij x_tj| from the oracle:
   * y and the gate/up products: |y_gpu - y_ref| <= 8e-3 * S + 1e-7 (weights
@@ -249,3 +249,71 @@ def test_prefill_override_rejects_bad_shapes():
                 (1, 1, 4, 8, 0), (1, 1, 4, 2, -1), (1, 1, 4, 2, 65)):
         assert G.qg().lib.qgemv_set_prefill_override(*bad) == -2, bad
     G.qg().set_prefill_override(0)
+
+
+
+# Q6_K shapes: cols a multiple of 256 (ragged rows, partial K steps, partial token tiles)
+SHAPES_6 = [(1, 256, 2), (150, 768, 17), (97, 5632, 33), (300, 2048, 130), (40, 5632, 9)]
+
+
+def _pow2_q6_k(rows, cols, rng):
+    # d and |sc| powers of two, codes 0..63: every weight d*sc*(q-32) has at
+    # most 6 significant bits (exact in bf16); with x in -3..3 and at most
+    # 1280 columns every partial sum stays below 2^14 in steps of 2^-8 (exact
+    # in fp32)
+    nsb = cols // 256
+    d = (2.0 ** rng.integers(-8, -5, (rows, nsb))).astype(np.float16)
+    sc = ((2 ** rng.integers(0, 4, (rows, nsb, 16))) * rng.choice([-1, 1], (rows, nsb, 16))).astype(np.int8)
+    q = rng.integers(0, 64, (rows, cols))
+    return synth.QTensor("w", "q6_k", rows, cols, synth.pack_q6_k(d, sc, q))
+
+
+@pytest.mark.parametrize("rows,cols,n_tok", SHAPES_6)
+def test_prefill_q6_k_within_bound(rows, cols, n_tok):
+    rng = np.random.default_rng(rows * 13 + cols + n_tok)
+    t = synth.make_tensor("q6_k", rows, cols, rng)
+    x = rng.standard_normal((n_tok, cols)).astype(np.float32)
+    y = _run(t, G.upload(t), x)
+    yr, S = oracle.gemv("q6_k", t.raw, x, rows, cols)
+    G.check_bound(y, yr, S, rel=G.PF_REL, what=f"prefill q6_k {rows}x{cols} n_tok={n_tok}")
+
+
+def test_prefill_q6_k_exact_inputs_bit_exact_every_tile():
+    rng = np.random.default_rng(1170)
+    rows, cols, n_tok = 150, 1280, 37     # 40 blocks: a partial K step for runs of 2 and 4
+    t = _pow2_q6_k(rows, cols, rng)
+    pk = G.upload(t)
+    x = rng.integers(-3, 4, (n_tok, cols)).astype(np.float32)
+    yr, _ = oracle.gemv("q6_k", t.raw, x, rows, cols)
+    try:
+        for tile in TILES:
+            G.qg().set_prefill_override(*tile)
+            y = _run(t, pk, x)
+            assert np.array_equal(y.astype(np.float64), yr), f"q6_k tile (mtr, ntw, waves, run) = {tile}"
+    finally:
+        G.qg().set_prefill_override(0)
+
+
+def test_prefill_q6_k_one_hot_tokens_give_bf16_weights():
+    # all 32 positions of a block (both halves, low and high nibbles, every
+    # code word and high-bit shift)
+    rng = np.random.default_rng(1370)
+    rows, cols = 70, 2048
+    t = synth.make_tensor("q6_k", rows, cols, rng)
+    nb = cols // 32
+    cs = np.array([32 * ((5 * k) % nb) + k for k in range(32)])
+    x = np.zeros((32, cols), np.float32)
+    x[np.arange(32), cs] = 1.0
+    y = _run(t, G.upload(t), x)
+    w32 = oracle.dequant("q6_k", t.raw, rows, cols).astype(np.float32)
+    assert np.array_equal(y, G.bf16_rne(w32[:, cs]).T)
+
+
+def test_prefill_q6_k_swiglu_ffn():
+    # a Q6_K FFN at 24 tokens through swiglu_ffn, both products on the matrix cores
+    d_model, ffn = 1024, 2816
+    rng = np.random.default_rng(1570)
+    tens = [synth.make_tensor("q6_k", ffn, d_model, rng), synth.make_tensor("q6_k", ffn, d_model, rng),
+            synth.make_tensor("q6_k", d_model, ffn, rng)]
+    x = rng.standard_normal((24, d_model)).astype(np.float32)
+    G.check_ffn("q6_k", tens, x, d_model, ffn, "ffn q6_k n_tok=24")
