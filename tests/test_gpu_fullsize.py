@@ -121,3 +121,18 @@ def test_fullsize_cfg5_ffn_batched_sampled_rows(n_tok):
     for r0 in _row_samples(w.d_model):
         yr, S = oracle.gemv(tens[2].fmt, tens[2].raw, h, w.d_model, w.ffn, row_begin=r0, row_end=r0 + 128)
         G.check_bound(out[:, r0:r0 + 128], yr, S, rel=G.PF_REL, what=f"cfg5 down n_tok={n_tok} rows {r0}..")
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_fullsize_cfg6_q6_k_batched_sampled_rows(idx):
+    # the TinyLlama-shaped Q6_K down [2048][5632] and vocab head [32000][2048]
+    # at n_tok = 8 and 128 (matrix-core path), sampled rows against the oracle
+    w = synth.CFG6
+    t = synth.gen_tensor(w, idx)
+    pk = G.upload(t)
+    for n in (8, 128):
+        x = synth.gen_x(w, t.cols, n, which=30 + n + idx)
+        y = G.gemv_gpu(t, pk, x)
+        for r0 in _row_samples(t.rows):
+            yr, S = oracle.gemv(t.fmt, t.raw, x, t.rows, t.cols, row_begin=r0, row_end=r0 + 128)
+            G.check_bound(y[:, r0:r0 + 128], yr, S, rel=G.PF_REL, what=f"cfg6 {t.name} n_tok={n} rows {r0}..")
