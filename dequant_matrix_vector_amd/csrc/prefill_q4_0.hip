@@ -1,0 +1,11 @@
+// Matrix-core product instantiated for Q4_0 weights (prefill_impl.h).
+#include "prefill_impl.h"
+
+namespace qg {
+
+hipError_t prefill_dispatch_q4_0(const PrefillCfg &c, int nmat, const PrefillParams &p, float *y, hipStream_t s)
+{
+    return prefill_dispatch<QG_Q4_0>(c, nmat, p, y, s);
+}
+
+} // namespace qg
