@@ -231,7 +231,7 @@ def workload_report(qg, synth, torch, np, dev, graph_iters=20):
                     "weight_bytes": wbytes, "GBs": round(wbytes / us / 1e3, 1),
                     "pct_hbm_peak": round(100 * wbytes / us / 1e3 / HBM_PEAK_GBS, 1),
                     "resident": "hbm" if ncopy * wbytes >= ROTATE_BYTES else "cache",
-                    "path": "matrix cores (bf16 MFMA)" if (n_tok > 1 and tens[0].fmt in ("q4_0", "q4_k", "q6_k")) else "GEMV"}
+                    "path": "matrix cores (bf16 MFMA)" if n_tok > 1 else "GEMV"}
         if n_tok > 1:
             flops = 2 * n_tok * sum(t.rows * t.cols for t in tens)
             rep[key]["TFLOPs"] = round(flops / us / 1e6, 2)

@@ -143,7 +143,7 @@ def set_launch_override(lpr=0, r=0, waves=0, depth=2, max_wg=0, cpl=1):
 
 
 def set_prefill_override(mtr=0, ntw=0, waves=0, run=0, ksplit=0):
-    """Force the matrix-core tile shape (Q4_0, Q4_K, Q6_K; n_tok > 1); mtr=0 restores the
+    """Force the matrix-core tile shape (n_tok > 1); mtr=0 restores the
     built-in choice, mtr=-1 turns the matrix-core path off (per-token GEMV)."""
     if mtr > 0 and run == 0:
         run = 1

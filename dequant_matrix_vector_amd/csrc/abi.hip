@@ -231,7 +231,7 @@ int swiglu_gate_up(int fmt, const void *wg, const void *wu, const float *x, floa
 
 // Scratch of swiglu_ffn, in floats: h [n_tok][ffn], then, from the next
 // 256-byte boundary, room for the partial sums of a K split on the matrix-core
-// path (Q4_0 or Q4_K, n_tok > 1) -- the most that the gate/up or the down product uses.
+// path (n_tok > 1) -- the most that the gate/up or the down product uses.
 static int64_t ffn_part_offset(int64_t d_model, int64_t ffn, int64_t n_tok)
 {
     (void)d_model;
@@ -316,7 +316,7 @@ int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const fl
 }
 
 // Scratch of swiglu_ffn_block, in floats: h [n_tok][ffn]; on the matrix-core
-// path (Q4_0 or Q4_K, n_tok > 1) then the normalized input [n_tok][d_model] and room
+// path (n_tok > 1) then the normalized input [n_tok][d_model] and room
 // for split-K partial sums, each from a 256-byte boundary.
 static bool block_on_matrix_cores(int fmt, int64_t n_tok) { return prefill_format(fmt) && n_tok > 1 && prefill_enabled(); }
 

@@ -236,7 +236,10 @@ extern "C" int qgemv_set_prefill_override(int mtr, int ntw, int waves, int run, 
 
 bool prefill_enabled() { return g_pf_override.mtr >= 0; }
 
-bool prefill_format(int fmt) { return fmt == QG_Q4_0 || fmt == QG_Q4_K || fmt == QG_Q6_K; }
+bool prefill_format(int fmt)
+{
+    return fmt == QG_Q4_0 || fmt == QG_Q4_K || fmt == QG_Q6_K || fmt == QG_Q8_0 || fmt == QG_I8ROW;
+}
 
 int64_t prefill_part_elems(int fmt, int nmat, int64_t rows, int64_t cols, int64_t n_tok)
 {
@@ -295,6 +298,8 @@ hipError_t launch_prefill(int fmt, int nmat, const uint8_t *w0, const uint8_t *w
     case QG_Q4_0: return prefill_dispatch_q4_0(c, nmat, p, y, s);
     case QG_Q4_K: return prefill_dispatch_q4_k(c, nmat, p, y, s);
     case QG_Q6_K: return prefill_dispatch_q6_k(c, nmat, p, y, s);
+    case QG_Q8_0: return prefill_dispatch_q8_0(c, nmat, p, y, s);
+    case QG_I8ROW: return prefill_dispatch_i8row(c, nmat, p, y, s);
     default: return hipErrorInvalidValue;
     }
 }

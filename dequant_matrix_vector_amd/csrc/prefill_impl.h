@@ -1,6 +1,6 @@
 // Batched-token (prefill) product on the matrix cores: y[t][i] = sum_j W[i][j] x[t][j]
-// for n_tok > 1 with W in Q4_0, Q4_K or Q6_K, and the fused first half of the
-// SwiGLU block, h = silu(Wg x) * (Wu x).
+// for n_tok > 1 with W in any of the five formats, and the fused first half of
+// the SwiGLU block, h = silu(Wg x) * (Wu x).
 //
 // With several tokens every weight read is shared by all of them, so the work
 // is a dense contraction and belongs on the matrix units (llmoxide blog,
@@ -8,16 +8,19 @@
 // run as a real GEMM).  Here:
 //   * each wave owns MTR 16-row tiles of every matrix (NMAT of them) and the
 //     workgroup NTW 16-token tiles; K advances by super-steps of 4Q blocks;
-//   * weights are read row by row in runs of 64Q bytes (whole cache lines,
-//     one run per row and super-step) into registers, then transposed through
-//     a per-wave LDS area into the v_mfma_f32_16x16x32_bf16 A layout (lane l:
+//   * weights are read row by row in runs of 64Q bytes (128Q for the 8-bit
+//     formats; whole cache lines, one run per row and super-step) into
+//     registers, then transposed through a per-wave LDS area into the
+//     v_mfma_f32_16x16x32_bf16 A layout (lane l:
 //     row l%16, k-group l/16), where each lane dequantizes its block exactly in
 //     fp32 (q*D - M via the binary16-subnormal trick and v_fma_mix_f32, as in
 //     the GEMV: Q4_0 D = d, M = 8d; Q4_K, whose repacked sub-blocks have the
 //     Q4_0 nibble order, D = d*sc and M = dmin*m of the sub-block, both exact;
 //     Q6_K, the same nibble order with the two high bits of each code OR-ed
-//     in from the high-bit plane, D = d*sc of each 16-column half and M = 32D)
-//     and rounds to bf16 (nearest even);
+//     in from the high-bit plane, D = d*sc of each 16-column half and M = 32D;
+//     Q8_0 and per-row INT8, 32-byte blocks whose signed bytes xor 0x80 are
+//     q + 128, D = d or 1 and M = 128D, the INT8 row scale multiplying the
+//     fp32 sums) and rounds to bf16 (nearest even);
 //   * the workgroup stages the x tile of the super-step in LDS as bf16 (nearest
 //     even), in natural column order: the decode emits 8 consecutive columns
 //     per operand, so A and B agree on k without any shuffle;
@@ -70,6 +73,8 @@ hipError_t launch_prefill_reduce(int nmat, const float *part, float *y, int64_t 
 hipError_t prefill_dispatch_q4_0(const PrefillCfg &c, int nmat, const PrefillParams &p, float *y, hipStream_t s);
 hipError_t prefill_dispatch_q4_k(const PrefillCfg &c, int nmat, const PrefillParams &p, float *y, hipStream_t s);
 hipError_t prefill_dispatch_q6_k(const PrefillCfg &c, int nmat, const PrefillParams &p, float *y, hipStream_t s);
+hipError_t prefill_dispatch_q8_0(const PrefillCfg &c, int nmat, const PrefillParams &p, float *y, hipStream_t s);
+hipError_t prefill_dispatch_i8row(const PrefillCfg &c, int nmat, const PrefillParams &p, float *y, hipStream_t s);
 
 namespace {
 
@@ -174,6 +179,9 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
 {
     constexpr bool KQ = FMT == QG_Q4_K;
     constexpr bool K6 = FMT == QG_Q6_K;
+    constexpr bool K8 = FMT == QG_Q8_0 || FMT == QG_I8ROW;   // 32 code bytes per block
+    constexpr bool KR = FMT == QG_I8ROW;    // one fp32 scale per row, applied to the sums
+    constexpr int BB = K8 ? 32 : 16;        // code bytes per block
     constexpr int MT = MTR * NMAT;          // 16-row tiles per wave
     constexpr int NT = W * 64;              // threads
     constexpr int SB = 4 * Q;               // blocks per super-step
@@ -184,9 +192,10 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
     // rows padded so that the 16 rows of a read fall in different banks)
     constexpr int XROW = SCOLS * 2 + 16;
     constexpr int XTILE = NTW * 16 * XROW;
-    constexpr int AROW = SB * 16 + 16;
-    // Q4_0: f16 d; Q4_K: (D, M) as two floats; Q6_K: the two halves' D
-    constexpr int SROW = (KQ || K6) ? SB * 8 + 8 : SB * 2 + 4;
+    constexpr int AROW = SB * BB + 16;
+    // Q4_0, Q8_0: f16 d; Q4_K: (D, M) as two floats; Q6_K: the two halves' D;
+    // I8ROW: none
+    constexpr int SROW = (KQ || K6) ? SB * 8 + 8 : (KR ? 0 : SB * 2 + 4);
     constexpr int HROW = K6 ? SB * 8 + 8 : 0;           // Q6_K: 8 bytes of high bits per block
     constexpr int AWAVE = MT * 16 * (AROW + SROW + HROW);
     constexpr int XF4 = NTW * 16 * SCOLS / 4;   // float4 pieces of x per super-step
@@ -237,6 +246,7 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
     // the ring: weight runs, scales, x pieces and liveness (bit k: x piece k
     // inside x; bit 31: the lane's weight block inside the row)
     u32x4 qa[2][MT][Q];
+    u32x4 qb[2][K8 ? MT : 1][K8 ? Q : 1];         // 8-bit: the second 16-byte piece
     uint32_t da[2][MT][Q];                        // Q4_0: the block's f16 scale
     u32x4 ha[2][KQ ? MT : 1][KQ ? Q : 1];         // Q4_K: the super-block header
     uint2 h6[2][K6 ? MT : 1][K6 ? Q : 1];         // Q6_K: the block's high bits
@@ -270,8 +280,21 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
                 constexpr int i = decltype(ic)::value;
                 const int64_t row = arow(m, i);
                 const uint8_t *base = p.q[m / MTR];
-                qa[J][m][i] = reinterpret_cast<const u32x4 *>(base + row * p.row_qbytes)[blk];
-                if constexpr (KQ) {
+                if constexpr (K8) {
+                    // 8-bit: the row's 2SB 16-byte pieces of the super-step,
+                    // pieces lblk and lblk + 4Q (each instruction reads 64Q
+                    // consecutive bytes of the row); pieces past the row read
+                    // the last one and meet x = 0
+                    const u32x4 *rp = reinterpret_cast<const u32x4 *>(base + row * p.row_qbytes);
+                    const int pa = ss * 2 * SB + lblk, pb = pa + 4 * Q;
+                    qa[J][m][i] = rp[pa < 2 * p.nb ? pa : 2 * p.nb - 1];
+                    qb[J][m][i] = rp[pb < 2 * p.nb ? pb : 2 * p.nb - 1];
+                } else {
+                    qa[J][m][i] = reinterpret_cast<const u32x4 *>(base + row * p.row_qbytes)[blk];
+                }
+                if constexpr (KR) {
+                    // the row scale is applied to the sums
+                } else if constexpr (KQ) {
                     ha[J][m][i] = reinterpret_cast<const u32x4 *>(base + p.soff)[row * (p.nb / 8) + blk / 8];
                 } else {
                     da[J][m][i] = (reinterpret_cast<const uint16_t *>(base + p.soff) + row * p.nb)[blk];
@@ -307,7 +330,10 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
                 constexpr int i = decltype(ic)::value;
                 const int row = i * RPI + lrow;
                 *reinterpret_cast<u32x4 *>(aw + (m * 16 + row) * AROW + lblk * 16) = qa[J][m][i];
-                if constexpr (KQ) {
+                if constexpr (K8)
+                    *reinterpret_cast<u32x4 *>(aw + (m * 16 + row) * AROW + (lblk + 4 * Q) * 16) = qb[J][m][i];
+                if constexpr (KR) {
+                } else if constexpr (KQ) {
                     const f32x2 dm = q4k_dm(ha[J][m][i], sub[J]);
                     *reinterpret_cast<f32x2 *>(sw + (m * 16 + row) * SROW + lblk * 8) =
                         (lv >> 31) ? dm : f32x2{0.0f, 0.0f};
@@ -334,6 +360,24 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
             bf16x8 af[MT][4];
             static_for<MT>([&](auto mc) __attribute__((always_inline)) {
                 constexpr int m = decltype(mc)::value;
+                if constexpr (K8) {
+                    // q + 128 (the byte xor 0x80) as a binary16 subnormal is
+                    // (q + 128)*2^-24; fma with D*2^24 and -128D gives q*D,
+                    // exact in fp32 for Q8_0 (an 8-bit code by an 11-bit d)
+                    // and for I8ROW (D = 1: the code itself)
+                    const uint8_t *ap = aw + (m * 16 + r16) * AROW + b * 32;
+                    const u32x4 w0 = *reinterpret_cast<const u32x4 *>(ap);
+                    const u32x4 w1 = *reinterpret_cast<const u32x4 *>(ap + 16);
+                    float d = 1.0f;
+                    if constexpr (!KR) d = half_lo(*reinterpret_cast<const uint16_t *>(sw + (m * 16 + r16) * SROW + b * 2));
+                    const float d24 = d * 0x1p24f, nd = -128.0f * d;
+                    constexpr uint32_t F = 0x80808080u, M8 = 0x00FF00FFu;
+                    af[m][0] = decode8(w0.x ^ F, w0.y ^ F, M8, d24, nd);
+                    af[m][1] = decode8(w0.z ^ F, w0.w ^ F, M8, d24, nd);
+                    af[m][2] = decode8(w1.x ^ F, w1.y ^ F, M8, d24, nd);
+                    af[m][3] = decode8(w1.z ^ F, w1.w ^ F, M8, d24, nd);
+                    return;
+                }
                 const u32x4 w = *reinterpret_cast<const u32x4 *>(aw + (m * 16 + r16) * AROW + b * 16);
                 if constexpr (K6) {
                     // code words 0, 1 take high-bit word 0 (shifted 0, 2), words 2, 3 word 1
@@ -408,6 +452,15 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
             if (row + 3 < p.rows) dst[3] = v3;
         }
     };
+    // I8ROW: the sums of matrix mo's rows row .. row+3 times their row scales
+    auto rscale = [&](int mo, int64_t row, f32x4 a) __attribute__((always_inline)) -> f32x4 {
+        if constexpr (KR) {
+            const float *sp = reinterpret_cast<const float *>(p.q[mo] + p.soff);
+#pragma unroll
+            for (int i = 0; i < 4; i++) a[i] *= sp[row + i < p.rows ? row + i : p.rows - 1];
+        }
+        return a;
+    };
     static_for<NTW>([&](auto nc) __attribute__((always_inline)) {
         constexpr int n = decltype(nc)::value;
         const int tok = tok_base + n * 16 + r16;
@@ -419,12 +472,12 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
                     // raw sums of this K range: [ks][matrix][token][row]
                     static_for<NMAT>([&](auto oc) __attribute__((always_inline)) {
                         constexpr int mo = decltype(oc)::value;
-                        const f32x4 a = acc[mo * MTR + mr][n];
+                        const f32x4 a = rscale(mo, row, acc[mo * MTR + mr][n]);
                         store4(p.y + (((int64_t)(ks * NMAT + mo) * p.n_tok + tok) * p.rows + row), row, a[0], a[1],
                                a[2], a[3]);
                     });
                 } else if (NMAT == 1) {
-                    f32x4 a = acc[mr][n];
+                    f32x4 a = rscale(0, row, acc[mr][n]);
                     if (p.resid) {   // the residual stream: read before this thread overwrites it
                         const float *rp = p.resid + (int64_t)tok * p.rows + row;
 #pragma unroll
@@ -432,7 +485,7 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
                     }
                     store4(p.y + (int64_t)tok * p.rows + row, row, a[0], a[1], a[2], a[3]);
                 } else {
-                    const f32x4 gg = acc[mr][n], uu = acc[(NMAT - 1) * MTR + mr][n];
+                    const f32x4 gg = rscale(0, row, acc[mr][n]), uu = rscale(NMAT - 1, row, acc[(NMAT - 1) * MTR + mr][n]);
                     float v[4];
                     for (int i = 0; i < 4; i++) v[i] = gg[i] / (1.0f + expf(-gg[i])) * uu[i];
                     store4(p.y + (int64_t)tok * p.rows + row, row, v[0], v[1], v[2], v[3]);
@@ -442,15 +495,19 @@ __global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
     });
 }
 
-// LDS of a workgroup: two bf16 x tiles plus one weight area per wave (codes
-// and per-block scales: f16 d for Q4_0, the (D, M) pair for Q4_K, the two
-// halves' D for Q6_K, which also stages 8 bytes of high bits per block)
+// LDS of a workgroup: two bf16 x tiles plus one weight area per wave (codes,
+// 16 bytes per block or 32 for the 8-bit formats, and per-block scales: f16
+// d for Q4_0 and Q8_0, the (D, M) pair for Q4_K, the two halves' D for Q6_K,
+// which also stages 8 bytes of high bits per block; none for I8ROW)
 constexpr size_t pf_lds_bytes(int fmt, int nmat, int mtr, int ntw, int waves, int run)
 {
-    const size_t srow = (fmt == QG_Q4_K || fmt == QG_Q6_K) ? (size_t)run * 32 + 8 : (size_t)run * 8 + 4;
+    const size_t bb = (fmt == QG_Q8_0 || fmt == QG_I8ROW) ? 32 : 16;
+    const size_t srow = (fmt == QG_Q4_K || fmt == QG_Q6_K) ? (size_t)run * 32 + 8
+                        : fmt == QG_I8ROW                  ? 0
+                                                           : (size_t)run * 8 + 4;
     const size_t hrow = fmt == QG_Q6_K ? (size_t)run * 32 + 8 : 0;
     return 2 * (size_t)ntw * 16 * (run * 256 + 16) +
-           (size_t)waves * nmat * mtr * 16 * ((run * 64 + 16) + srow + hrow);
+           (size_t)waves * nmat * mtr * 16 * ((run * 4 * bb + 16) + srow + hrow);
 }
 
 template <int FMT, int NMAT, int MTR, int NTW, int W, int Q>
@@ -520,11 +577,54 @@ constexpr int kBuiltShapes6[] = {
 };
 #endif
 
+#ifndef QG_PF_CENSUS_8
+constexpr int kBuiltShapes8[] = {
+    11141, 11142, 11144, 11181, 11182, 11184, 11241, 11242, 11244,
+    11281, 11282, 11284, 11441, 11442, 11481, 11482, 11561, 11841,
+    11881, 11961, 12141, 12142, 12144, 12181, 12182, 12241, 12242,
+    12244, 12281, 12282, 12441, 12442, 12481, 12841, 12881, 21141,
+    21142, 21144, 21181, 21182, 21241, 21242, 21244, 21281, 21282,
+    21441, 21442, 21481, 21841, 21881, 22141, 22142, 22181, 22241,
+    22242, 22281, 22441, 22841,
+};
+#endif
+
+#ifndef QG_PF_CENSUS_R
+constexpr int kBuiltShapesR[] = {
+    11141, 11142, 11144, 11181, 11182, 11184, 11241, 11242, 11244,
+    11281, 11282, 11284, 11441, 11442, 11481, 11482, 11561, 11841,
+    11881, 11961, 12141, 12142, 12144, 12181, 12182, 12241, 12242,
+    12244, 12281, 12282, 12441, 12442, 12481, 12482, 12561, 12841,
+    12881, 21141, 21142, 21144, 21181, 21182, 21241, 21242, 21244,
+    21281, 21282, 21441, 21442, 21481, 21482, 21841, 21881, 22141,
+    22142, 22181, 22182, 22241, 22242, 22281, 22441, 22442, 22481,
+    22841,
+};
+#endif
+
 constexpr bool pf_fits(int fmt, int nmat, int mtr, int ntw, int waves, int run)
 {
     const int code = nmat * 10000 + mtr * 1000 + ntw * 100 + waves * 10 + run;
     const bool geometry = pf_lds_bytes(fmt, nmat, mtr, ntw, waves, run) <= 160 * 1024 &&
                           ntw * 512 * run >= waves * 64 && ntw * 512 * run <= 16 * waves * 64;
+    if (fmt == QG_Q8_0) {
+#ifdef QG_PF_CENSUS_8
+        return geometry && (waves != 16 || nmat == 1);
+#else
+        for (int c : kBuiltShapes8)
+            if (c == code) return geometry;
+        return false;
+#endif
+    }
+    if (fmt == QG_I8ROW) {
+#ifdef QG_PF_CENSUS_R
+        return geometry && (waves != 16 || nmat == 1);
+#else
+        for (int c : kBuiltShapesR)
+            if (c == code) return geometry;
+        return false;
+#endif
+    }
     if (fmt == QG_Q6_K) {
 #ifdef QG_PF_CENSUS_6
         return geometry && (waves != 16 || nmat == 1);

@@ -84,7 +84,7 @@ hipError_t launch_dequant(int fmt, const uint8_t *packed, float *w, int64_t rows
 
 size_t gemv_lds_bytes(int64_t cols);
 
-// Batched-token path on the matrix cores (Q4_0 and Q4_K, n_tok > 1).
+// Batched-token path on the matrix cores (every format, n_tok > 1).
 struct PrefillCfg {
     int mtr;     // 16-row tiles per wave and matrix (1, 2); 0 = built-in choice, -1 = path off
     int ntw;     // 16-token tiles per workgroup (1, 2, 4, 8)

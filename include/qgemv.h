@@ -120,13 +120,14 @@ int qgemv_repack_i8row(const int8_t *q, const float *row_scale, void *packed, in
  * y: fp32 [n_tok][rows], overwritten.  x must not overlap y.
  * n_tok == 1 runs the fused dequant-dot GEMV kernels: exact weights, fp32 x,
  * fp32 accumulation.  n_tok > 1:
- *  - Q4_0, Q4_K and Q6_K run on the matrix cores (llmoxide blog, section 11 "Prefill and
- *    decode": with several tokens the product is a real GEMM, each weight
- *    tile dequantized once for all tokens).  Weights and x are rounded to
- *    bf16 (nearest even) and multiplied by v_mfma_f32_16x16x32_bf16 with fp32
- *    accumulation: |y - exact| <= 8e-3 * sum_j |w_ij x_tj| + 1e-7.  One launch,
- *    no workspace.
- *  - the other formats loop the GEMV over the tokens (fp32 accuracy). */
+ *  every format runs on the matrix cores (llmoxide blog, section 11 "Prefill
+ *  and decode": with several tokens the product is a real GEMM, each weight
+ *  tile dequantized once for all tokens).  Weights and x are rounded to bf16
+ *  (nearest even; per-row INT8 codes are exact in bf16 and their row scale
+ *  multiplies the fp32 sums) and multiplied by v_mfma_f32_16x16x32_bf16 with
+ *  fp32 accumulation: |y - exact| <= 8e-3 * sum_j |w_ij x_tj| + 1e-7.  One
+ *  launch, no workspace.  qgemv_set_prefill_override(-1, ...) turns this off:
+ *  the GEMV then loops over the tokens (fp32 accuracy). */
 int qgemv_q4_0(const void *packed, const float *x, float *y, int64_t rows, int64_t cols,
                int64_t n_tok, void *stream);
 int qgemv_q8_0(const void *packed, const float *x, float *y, int64_t rows, int64_t cols,
@@ -145,8 +146,8 @@ int qgemv(int fmt, const void *packed, const float *x, float *y, int64_t rows, i
 /* First half of the SwiGLU block: h[t][i] = silu(Wg x)[t][i] * (Wu x)[t][i],
  * silu(g) = g / (1 + exp(-g)).  wg, wu: packed [ffn][d_model] of format fmt;
  * x: fp32 [n_tok][d_model]; h: fp32 [n_tok][ffn], overwritten, must not
- * overlap x.  Q4_0, Q4_K and Q6_K with n_tok > 1 run on the matrix cores as qgemv does,
- * with silu(g) * u applied in the same kernel. */
+ * overlap x.  With n_tok > 1 the products run on the matrix cores as qgemv's
+ * do, with silu(g) * u applied in the same kernel. */
 int swiglu_gate_up(int fmt, const void *wg, const void *wu, const float *x, float *h,
                    int64_t d_model, int64_t ffn, int64_t n_tok, void *stream);
 
@@ -155,7 +156,7 @@ int swiglu_gate_up(int fmt, const void *wg, const void *wu, const float *x, floa
  * [n_tok][d_model], overwritten; h_scratch: caller-owned fp32 scratch of
  * h_scratch_elems >= n_tok*ffn elements, whose first n_tok*ffn elements hold
  * h ([n_tok][ffn]) on return (so the caller can inspect the intermediate).
- * On the matrix-core path (Q4_0, Q4_K, Q6_K; n_tok > 1) a scratch of
+ * On the matrix-core path (n_tok > 1) a scratch of
  * swiglu_ffn_scratch_elems() elements (16-byte aligned) also holds the partial
  * sums that let both products split their K dimension over more workgroups
  * (deterministic: fixed summation order); with less, the products run
@@ -176,11 +177,11 @@ int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const fl
  * [n_tok][d_model]; out may be x itself (the stream updated in place) or must
  * not overlap it.  h_scratch: >= swiglu_ffn_block_scratch_elems() floats
  * (QG_ERR_SCRATCH below the minimum that query's comment states), first
- * n_tok*ffn of them hold h on return.  With n_tok == 1, or formats without
- * the matrix-core path, the norm is fused into the gate/up GEMV (the per-token scale factors
+ * n_tok*ffn of them hold h on return.  With n_tok == 1, or with the
+ * matrix-core path turned off, the norm is fused into the gate/up GEMV (the per-token scale factors
  * out of every dot product; the workgroup sums x^2 while staging x*gamma) and
- * the residual into the down GEMV's epilogue: two launches per token.  The
- * matrix-core formats with n_tok > 1 run a small RMSNorm launch into the scratch, then the
+ * the residual into the down GEMV's epilogue: two launches per token.  With
+ * n_tok > 1 the matrix-core path runs a small RMSNorm launch into the scratch, then the
  * matrix-core products (residual added in the down product's epilogue or in
  * its split-K reduce). */
 int swiglu_ffn_block(int fmt, const void *wg, const void *wu, const void *wd, const float *gamma,
@@ -188,7 +189,7 @@ int swiglu_ffn_block(int fmt, const void *wg, const void *wu, const void *wd, co
                      int64_t d_model, int64_t ffn, int64_t n_tok, void *stream);
 
 /* Scratch elements (fp32) for which swiglu_ffn_block runs its fastest form:
- * n_tok*ffn on the GEMV path; on the matrix-core path (Q4_0, Q4_K, Q6_K; n_tok > 1) h,
+ * n_tok*ffn on the GEMV path; on the matrix-core path (n_tok > 1) h,
  * the normalized input (required: together the minimum) and room for
  * split-K partial sums (optional).  Negative qg_status for an invalid shape
  * or format. */
@@ -267,7 +268,7 @@ int qgemv_set_launch_override(int lpr, int r, int waves, int depth, int max_wg, 
  * Returns QG_ERR_NULL if only one event is given. */
 int qgemv_time_next_launch(void *start_event, void *stop_event);
 
-/* Tuning hook for the matrix-core path (Q4_0, Q4_K, Q6_K; n_tok > 1): force 16-row tiles
+/* Tuning hook for the matrix-core path (n_tok > 1): force 16-row tiles
  * per wave and matrix (mtr 1 or 2), 16-token tiles per workgroup (ntw 1, 2, 4
  * or 8), waves per workgroup (4, 8 or 16), consecutive 32-weight blocks a lane
  * reads from a row per pass (run 1, 2 or 4) and the number of K ranges

@@ -15,7 +15,7 @@ PF_REL = 8e-3
 
 def rel_for(fmt, n_tok):
     """The bound's relative factor for a product of this format and batch."""
-    return PF_REL if (fmt in ("q4_0", "q4_k", "q6_k") and n_tok > 1) else REL
+    return PF_REL if (fmt in ("q4_0", "q4_k", "q6_k", "q8_0", "i8row") and n_tok > 1) else REL
 
 
 def bf16_rne(a):

@@ -1,4 +1,4 @@
-"""GPU parity of the matrix-core path (Q4_0, Q4_K and Q6_K, n_tok > 1) through the C ABI.
+"""GPU parity of the matrix-core path (every weight format, n_tok > 1) through the C ABI.
 
 Bars (per element), with S = sum_j |w_ij x_tj| from the oracle:
   * y and the gate/up products: |y_gpu - y_ref| <= 8e-3 * S + 1e-7 (weights
@@ -317,3 +317,82 @@ def test_prefill_q6_k_swiglu_ffn():
             synth.make_tensor("q6_k", d_model, ffn, rng)]
     x = rng.standard_normal((24, d_model)).astype(np.float32)
     G.check_ffn("q6_k", tens, x, d_model, ffn, "ffn q6_k n_tok=24")
+
+
+# ---------------------------------------------------------------- 8-bit --
+# Q8_0 and per-row INT8 on the matrix cores: the byte xor 0x80 read as a
+# binary16 subnormal, then one fma, gives q*D exactly in fp32 (Q8_0: D = d;
+# INT8: D = 1, the row scale multiplies the fp32 sums).
+EIGHT = ("q8_0", "i8row")
+
+
+def _pow2_8bit(fmt, rows, cols, rng):
+    # every code -128..127 (the xor's edge included); Q8_0 d and INT8 row
+    # scales powers of two: q*D has at most 8 significant bits (exact in bf16)
+    q = rng.integers(-128, 128, (rows, cols)).astype(np.int8)
+    if fmt == "q8_0":
+        d = (2.0 ** rng.integers(-6, -2, (rows, cols // 32))).astype(np.float16)
+        return synth.QTensor("w", "q8_0", rows, cols, synth.pack_q8_0(d, q))
+    s = (2.0 ** rng.integers(-6, -2, rows)).astype(np.float32)
+    return synth.QTensor("w", "i8row", rows, cols, q, row_scale=s)
+
+
+@pytest.mark.parametrize("fmt", EIGHT)
+@pytest.mark.parametrize("rows,cols,n_tok", SHAPES)
+def test_prefill_8bit_within_bound(fmt, rows, cols, n_tok):
+    rng = np.random.default_rng(rows * 7 + cols + n_tok + (5 if fmt == "i8row" else 0))
+    t = synth.make_tensor(fmt, rows, cols, rng)
+    x = rng.standard_normal((n_tok, cols)).astype(np.float32)
+    y = _run(t, G.upload(t), x)
+    yr, S = oracle.gemv(fmt, t.raw, x, rows, cols, row_scale=t.row_scale)
+    G.check_bound(y, yr, S, rel=G.PF_REL, what=f"prefill {fmt} {rows}x{cols} n_tok={n_tok}")
+
+
+@pytest.mark.parametrize("fmt", EIGHT)
+def test_prefill_8bit_exact_inputs_bit_exact_every_tile(fmt):
+    # |q*D*x| <= 128 * 2^-3 * 3 in steps of 2^-6: with 1312 columns every
+    # partial sum is exact in fp32; 41 blocks leave a partial K step for
+    # runs of 2 and 4
+    rng = np.random.default_rng(1710 if fmt == "q8_0" else 1711)
+    rows, cols, n_tok = 150, 1312, 37
+    t = _pow2_8bit(fmt, rows, cols, rng)
+    pk = G.upload(t)
+    x = rng.integers(-3, 4, (n_tok, cols)).astype(np.float32)
+    yr, _ = oracle.gemv(fmt, t.raw, x, rows, cols, row_scale=t.row_scale)
+    try:
+        for tile in TILES:
+            G.qg().set_prefill_override(*tile)
+            y = _run(t, pk, x)
+            assert np.array_equal(y.astype(np.float64), yr), f"{fmt} tile (mtr, ntw, waves, run) = {tile}"
+    finally:
+        G.qg().set_prefill_override(0)
+
+
+@pytest.mark.parametrize("fmt", EIGHT)
+def test_prefill_8bit_one_hot_tokens(fmt):
+    # all 32 positions of a block: Q8_0 gives the weight q*d rounded to bf16;
+    # INT8 the fp32 weight q*s itself (the code is exact in bf16 and the
+    # scale multiplies the fp32 sum)
+    rng = np.random.default_rng(1720 if fmt == "q8_0" else 1721)
+    rows, cols = 70, 2048
+    t = synth.make_tensor(fmt, rows, cols, rng)
+    nb = cols // 32
+    cs = np.array([32 * ((5 * k) % nb) + k for k in range(32)])
+    x = np.zeros((32, cols), np.float32)
+    x[np.arange(32), cs] = 1.0
+    y = _run(t, G.upload(t), x)
+    w32 = oracle.dequant(fmt, t.raw, rows, cols, row_scale=t.row_scale).astype(np.float32)
+    want = G.bf16_rne(w32[:, cs]).T if fmt == "q8_0" else w32[:, cs].T
+    assert np.array_equal(y, want)
+
+
+@pytest.mark.parametrize("fmt", EIGHT)
+def test_prefill_8bit_swiglu_ffn(fmt):
+    # a SmolLM2-135M-shaped FFN at 24 tokens through swiglu_ffn, both products
+    # on the matrix cores
+    d_model, ffn = 576, 1536
+    rng = np.random.default_rng(1730 if fmt == "q8_0" else 1731)
+    tens = [synth.make_tensor(fmt, ffn, d_model, rng), synth.make_tensor(fmt, ffn, d_model, rng),
+            synth.make_tensor(fmt, d_model, ffn, rng)]
+    x = rng.standard_normal((24, d_model)).astype(np.float32)
+    G.check_ffn(fmt, tens, x, d_model, ffn, f"ffn {fmt} n_tok=24")
