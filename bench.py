@@ -176,7 +176,8 @@ def workload_report(qg, synth, torch, np, dev, graph_iters=20):
     ("hbm"), otherwise they may sit in the 256 MB Infinity Cache ("cache")."""
     rep = {}
     plans = [(synth.CFG1, 1), (synth.CFG2, 1), (synth.CFG3, 1), (synth.CFG4, 1),
-             (synth.CFG5, 8), (synth.CFG5, 128), (synth.CFG6, 1), (synth.CFG3, 128), (synth.CFG6, 128)]
+             (synth.CFG5, 8), (synth.CFG5, 128), (synth.CFG6, 1), (synth.CFG3, 128), (synth.CFG6, 128),
+             (synth.CFG2, 128), (synth.CFG4, 128)]
     for w, n_tok in plans:
         tens = synth.gen_workload(w)
         wbytes = sum(t.weight_bytes for t in tens)

@@ -132,29 +132,31 @@ namespace {
 PrefillCfg g_pf_override = {0, 0, 0, 0, 0};
 
 // The built-in tile choice (from kernel-trace sweeps of every built shape on
-// the 27B-class FFN at 8 to 128 tokens): one 16-row tile per matrix and wave;
-// one token tile: 4 waves, runs of two steps; more: 2 or 4 token tiles per
-// workgroup, 4 waves for the fused gate/up pair (8 waves and 8 token tiles,
-// 128 tokens sharing each decoded weight, from 8 tiles on) and 8 waves for a
-// single matrix (16 from 4 tiles on: 256 rows share each staged x tile);
-// then K ranges until the grid has about four workgroups per CU (if the
-// caller gave room for the partials), as long as the partial sums (written,
-// then read back) stay within half the weight bytes or 16 MB, whichever is
-// more.  A matrix too small for its shape (fewer workgroups than half the CUs
-// even with the K split that budget allows) takes the shape for fewer token
-// tiles, i.e. more token groups.
+// the 27B-class FFN at 8 to 128 tokens and the SmolLM2-1.7B-shaped FFN and
+// head at 128 tokens, all five formats): one 16-row tile per matrix and wave;
+// one token tile: 4 waves, runs of two steps; 8 token tiles (128 tokens
+// sharing each decoded weight): 8 waves for the fused gate/up pair, 16 for a
+// single matrix (256 rows share each staged x tile); 4 token tiles: 4 waves
+// for the pair, 16 for a single matrix; 2: 4 waves for the pair, and for a
+// single matrix 4 waves with runs of two steps; then K ranges until the grid
+// has about four workgroups per CU (if the caller gave room for the
+// partials), as long as the partial sums (written, then read back) stay
+// within half the weight bytes or 16 MB, whichever is more.  A matrix too
+// small for its shape (fewer workgroups than half the CUs even with the K
+// split that budget and the caller's room allow) takes the shape for fewer
+// token tiles, i.e. more token groups.
 static void default_tile(PrefillCfg &c, int nmat, int64_t n_tiles)
 {
     c.mtr = 1;
     c.ksplit = 0;
     if (n_tiles == 1) {
         c.ntw = 1, c.waves = 4, c.run = 2;
-    } else if (nmat == 2 && n_tiles >= 8) {
-        c.ntw = 8, c.waves = 8, c.run = 1;
+    } else if (n_tiles >= 8) {
+        c.ntw = 8, c.waves = nmat == 2 ? 8 : 16, c.run = 1;
+    } else if (n_tiles >= 4) {
+        c.ntw = 4, c.waves = nmat == 2 ? 4 : 16, c.run = 1;
     } else {
-        c.ntw = n_tiles >= 4 ? 4 : 2;
-        c.waves = nmat == 2 ? 4 : (n_tiles >= 4 ? 16 : 8);
-        c.run = 1;
+        c.ntw = 2, c.waves = 4, c.run = nmat == 2 ? 1 : 2;
     }
 }
 
@@ -178,11 +180,15 @@ PrefillCfg choose(int fmt, int nmat, int64_t rows, int64_t cols, int64_t n_tok, 
     PrefillCfg c = g_pf_override;
     const int64_t n_tiles = (n_tok + 15) / 16;
     if (c.mtr <= 0) {
+        // K ranges the caller's room for partial sums allows (1: none)
+        const int64_t room = part_elems / ((int64_t)nmat * n_tok * rows);
         int64_t eff = n_tiles;
         default_tile(c, nmat, eff);
         while (eff > 1) {
             const int64_t grid = ((rows + c.waves * 16 - 1) / (c.waves * 16)) * ((n_tok + c.ntw * 16 - 1) / (c.ntw * 16));
-            if (2 * grid * max_ksplit(c, nmat, rows, cols, n_tok) >= (int64_t)cu_count()) break;
+            int64_t ks = max_ksplit(c, nmat, rows, cols, n_tok);
+            ks = ks < room ? ks : (room > 1 ? room : 1);
+            if (2 * grid * ks >= (int64_t)cu_count()) break;
             eff = eff >= 8 ? 4 : (eff >= 4 ? 2 : 1);
             default_tile(c, nmat, eff);
         }
