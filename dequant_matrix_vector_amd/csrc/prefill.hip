@@ -142,9 +142,9 @@ PrefillCfg g_pf_override = {0, 0, 0, 0, 0};
 // has about four workgroups per CU (if the caller gave room for the
 // partials), as long as the partial sums (written, then read back) stay
 // within half the weight bytes or 16 MB, whichever is more.  A matrix too
-// small for its shape (fewer workgroups than half the CUs even with the K
-// split that budget and the caller's room allow) takes the shape for fewer
-// token tiles, i.e. more token groups.
+// small for its shape (even with the K split that budget and the caller's
+// room allow: fewer workgroups than half the CUs, or fewer waves than one per
+// SIMD) takes the shape for fewer token tiles, i.e. more token groups.
 static void default_tile(PrefillCfg &c, int nmat, int64_t n_tiles)
 {
     c.mtr = 1;
@@ -188,7 +188,8 @@ PrefillCfg choose(int fmt, int nmat, int64_t rows, int64_t cols, int64_t n_tok, 
             const int64_t grid = ((rows + c.waves * 16 - 1) / (c.waves * 16)) * ((n_tok + c.ntw * 16 - 1) / (c.ntw * 16));
             int64_t ks = max_ksplit(c, nmat, rows, cols, n_tok);
             ks = ks < room ? ks : (room > 1 ? room : 1);
-            if (2 * grid * ks >= (int64_t)cu_count()) break;
+            const int64_t cus = cu_count();
+            if (2 * grid * ks >= cus && grid * ks * c.waves >= 4 * cus) break;
             eff = eff >= 8 ? 4 : (eff >= 4 ? 2 : 1);
             default_tile(c, nmat, eff);
         }
