@@ -136,3 +136,60 @@ def test_fullsize_cfg6_q6_k_batched_sampled_rows(idx):
         for r0 in _row_samples(t.rows):
             yr, S = oracle.gemv(t.fmt, t.raw, x, t.rows, t.cols, row_begin=r0, row_end=r0 + 128)
             G.check_bound(y[:, r0:r0 + 128], yr, S, rel=G.PF_REL, what=f"cfg6 {t.name} n_tok={n} rows {r0}..")
+
+
+def _check_ffn_sampled(w, tens, x, what):
+    # swiglu_ffn (the scratch swiglu_ffn_scratch_elems asks for, as bench.py
+    # runs it): h on sampled rows against silu(g) u of the oracle, out on
+    # sampled rows against the oracle's down projection of the device's own h
+    names = [t.name for t in tens]
+    g, u, d = (tens[names.index(n)] for n in ("gate", "up", "down"))
+    pk = [G.upload(t) for t in (g, u, d)]
+    xd = G.torch.from_numpy(x).to(G.dev())
+    out, h = G.qg().swiglu_ffn(g.fmt, pk[0], pk[1], pk[2], xd, w.d_model, w.ffn)
+    G.torch.cuda.synchronize()
+    out, h = out.cpu().numpy(), h.cpu().numpy()
+    for r0 in _row_samples(w.ffn):
+        r = {}
+        r["g"], r["Sg"] = oracle.gemv(g.fmt, g.raw, x, w.ffn, w.d_model, row_scale=g.row_scale, row_begin=r0,
+                                      row_end=r0 + 128)
+        r["u"], r["Su"] = oracle.gemv(u.fmt, u.raw, x, w.ffn, w.d_model, row_scale=u.row_scale, row_begin=r0,
+                                      row_end=r0 + 128)
+        r["h"] = G.silu64(r["g"]) * r["u"]
+        assert np.all(np.abs(h[:, r0:r0 + 128] - r["h"]) <= G.h_bound(r, G.PF_REL)), f"{what} h rows {r0}.."
+    for r0 in _row_samples(w.d_model):
+        yr, S = oracle.gemv(d.fmt, d.raw, h, w.d_model, w.ffn, row_scale=d.row_scale, row_begin=r0, row_end=r0 + 128)
+        G.check_bound(out[:, r0:r0 + 128], yr, S, rel=G.PF_REL, what=f"{what} down rows {r0}..")
+
+
+def test_fullsize_cfg4_int8_ffn_head_128_tokens_sampled_rows():
+    # the SmolLM2-1.7B-shaped INT8 FFN (2048/8192) and vocab head [49152][2048]
+    # at 128 tokens on the matrix cores, as bench.py times them
+    w = synth.CFG4
+    tens = synth.gen_workload(w)
+    x = synth.gen_x(w, w.d_model, 128, which=40)
+    _check_ffn_sampled(w, tens, x, "cfg4 n_tok=128")
+    t = tens[[t.name for t in tens].index("head")]
+    y = G.gemv_gpu(t, G.upload(t), x)
+    for r0 in _row_samples(t.rows):
+        yr, S = oracle.gemv(t.fmt, t.raw, x, t.rows, t.cols, row_scale=t.row_scale, row_begin=r0, row_end=r0 + 128)
+        G.check_bound(y[:, r0:r0 + 128], yr, S, rel=G.PF_REL, what=f"cfg4 head n_tok=128 rows {r0}..")
+
+
+def test_fullsize_cfg2_layer_q8_0_head_128_tokens():
+    # the SmolLM2-135M-shaped Q4_0 layer (q, o, k, v, FFN) and its Q8_0 vocab
+    # head [49152][576] at 128 tokens on the matrix cores, as bench.py times
+    # them: every row of the attention products, sampled rows of the rest
+    w = synth.CFG2
+    tens = synth.gen_workload(w)
+    x = synth.gen_x(w, w.d_model, 128, which=41)
+    _check_ffn_sampled(w, tens, x, "cfg2 n_tok=128")
+    for t in tens:
+        if t.name in ("gate", "up", "down"):
+            continue
+        y = G.gemv_gpu(t, G.upload(t), x)
+        starts = _row_samples(t.rows) if t.rows > 1024 else (0,)
+        for r0 in starts:
+            r1 = min(t.rows, r0 + 128) if t.rows > 1024 else t.rows
+            yr, S = oracle.gemv(t.fmt, t.raw, x, t.rows, t.cols, row_begin=r0, row_end=r1)
+            G.check_bound(y[:, r0:r1], yr, S, rel=G.PF_REL, what=f"cfg2 {t.name} n_tok=128 rows {r0}..")
