@@ -59,7 +59,8 @@ def check_block(fmt, tens, x, gamma, d_model, ffn, what):
 
 
 @pytest.mark.parametrize("fmt,n_tok", [("q4_0", 1), ("q8_0", 1), ("q4_k", 1), ("i8row", 1), ("q6_k", 1), ("q8_0", 3),
-                                       ("q4_0", 3), ("q4_0", 40), ("q6_k", 2), ("q4_k", 3), ("q4_k", 20)])
+                                       ("q4_0", 3), ("q4_0", 40), ("q6_k", 2), ("q4_k", 3), ("q4_k", 20),
+                                       ("q8_0", 20), ("i8row", 3), ("i8row", 20), ("q6_k", 20)])
 def test_block_matches_oracle(fmt, n_tok):
     d_model, ffn = (256, 768) if fmt in ("q4_k", "q6_k") else (288, 768)
     tens = _tensors(fmt, d_model, ffn, 2000 + n_tok)

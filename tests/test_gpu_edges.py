@@ -63,6 +63,20 @@ def test_widest_rows_batched_and_normalized():
     assert np.all(np.abs(h.cpu().numpy() - r["h"]) <= hb + 1e-30)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_widest_rows_batched_every_format(fmt):
+    # the matrix-core path at the widest row the GEMV takes (the matrix-core
+    # kernel streams K, so its LDS does not grow with cols): ragged rows,
+    # a partial token tile
+    mc = G.qg().max_cols()
+    rng = np.random.default_rng(5150)
+    t = synth.make_tensor(fmt, 37, mc, rng)
+    x = rng.standard_normal((5, mc)).astype(np.float32)
+    y = G.gemv_gpu(t, G.upload(t), x)
+    yr, S = oracle.gemv(fmt, t.raw, x, 37, mc, row_scale=t.row_scale)
+    G.check_bound(y, yr, S, rel=G.PF_REL, what=f"{fmt} n_tok=5 37x{mc}")
+
+
 def _bufs(rows, cols, n_tok=1):
     t = synth.make_tensor("q4_0", rows, cols, np.random.default_rng(5200))
     pk = G.upload(t)
