@@ -175,7 +175,7 @@ __device__ __forceinline__ f32x2 q4k_dm(u32x4 h, int s)
 // slot S % 2: the loads of the next super-step are in flight while this one
 // is computed.
 template <int FMT, int NMAT, int MTR, int NTW, int W, int Q>
-__global__ __launch_bounds__(W * 64) void prefill_q4_kernel(PrefillParams p)
+__global__ __launch_bounds__(W * 64) void prefill_mfma_kernel(PrefillParams p)
 {
     constexpr bool KQ = FMT == QG_Q4_K;
     constexpr bool K6 = FMT == QG_Q6_K;
@@ -516,7 +516,7 @@ hipError_t go_prefill(PrefillParams p, float *y, hipStream_t s)
     const size_t lds = pf_lds_bytes(FMT, NMAT, MTR, NTW, W, Q);
     const int64_t grid = p.row_groups * p.tok_groups * p.ksplit;
     if (grid >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-    auto kern = prefill_q4_kernel<FMT, NMAT, MTR, NTW, W, Q>;
+    auto kern = prefill_mfma_kernel<FMT, NMAT, MTR, NTW, W, Q>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
