@@ -238,6 +238,35 @@ static int64_t ffn_part_offset(int64_t d_model, int64_t ffn, int64_t n_tok)
     return align_up(n_tok * ffn, kPlaneAlign / 4);
 }
 
+// From this many tokens on, and for matrices of at least this many weights,
+// swiglu_ffn's matrix-core products read bf16 copies of x and h (made by one
+// conversion launch each, when the scratch holds them): each workgroup
+// re-reads its x tile from L2 for every super-step, so halving those bytes
+// outweighs the two extra launches (about 2 us each) only on large matrices
+// (27B-class FFN at 128 tokens: 184.9 to 173.8 us; a 576 x 1536 FFN: 72 to 76).
+static const int64_t kFfnBf16MinTok = 32;
+static const int64_t kFfnBf16MinWeights = int64_t(1) << 24;
+
+static bool ffn_bf16_copies(int64_t d_model, int64_t ffn, int64_t n_tok)
+{
+    return n_tok >= kFfnBf16MinTok && d_model * ffn >= kFfnBf16MinWeights;
+}
+
+// Floats of scratch behind the partial sums for the bf16 copies of x
+// [n_tok][d_model] and h [n_tok][ffn], each from a 256-byte boundary.
+static int64_t ffn_bf16_elems(int64_t d_model, int64_t ffn, int64_t n_tok)
+{
+    return align_up(n_tok * d_model / 2, kPlaneAlign / 4) + align_up(n_tok * ffn / 2, kPlaneAlign / 4);
+}
+
+// Floats of partial sums the built-in tile choice asks for (the larger of
+// the gate/up and the down product's).
+static int64_t ffn_part_elems(int fmt, int64_t d_model, int64_t ffn, int64_t n_tok)
+{
+    const int64_t a = prefill_part_elems(fmt, 2, ffn, d_model, n_tok), b = prefill_part_elems(fmt, 1, d_model, ffn, n_tok);
+    return a > b ? a : b;
+}
+
 int64_t swiglu_ffn_scratch_elems(int fmt, int64_t d_model, int64_t ffn, int64_t n_tok)
 {
     if (!valid_fmt(fmt)) return QG_ERR_FORMAT;
@@ -246,8 +275,9 @@ int64_t swiglu_ffn_scratch_elems(int fmt, int64_t d_model, int64_t ffn, int64_t 
         !layout_for(fmt, d_model, ffn, &Lb))
         return QG_ERR_SHAPE;
     if (!prefill_format(fmt) || n_tok == 1 || !prefill_enabled()) return n_tok * ffn;
-    const int64_t a = prefill_part_elems(fmt, 2, ffn, d_model, n_tok), b = prefill_part_elems(fmt, 1, d_model, ffn, n_tok);
-    const int64_t part = a > b ? a : b;
+    const int64_t part = ffn_part_elems(fmt, d_model, ffn, n_tok);
+    if (ffn_bf16_copies(d_model, ffn, n_tok))
+        return align_up(ffn_part_offset(d_model, ffn, n_tok) + part, kPlaneAlign / 4) + ffn_bf16_elems(d_model, ffn, n_tok);
     return part > 0 ? ffn_part_offset(d_model, ffn, n_tok) + part : n_tok * ffn;
 }
 
@@ -289,14 +319,29 @@ int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const fl
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
     if (prefill_format(fmt) && n_tok > 1 && prefill_enabled()) {
-        // partial sums of a K split go behind h, when the caller's scratch has room
+        // partial sums of a K split go behind h, when the caller's scratch has
+        // room; for large matrices from kFfnBf16MinTok tokens on, and with
+        // room for them behind the partials, the bf16 copies of x and h too
         const int64_t po = ffn_part_offset(d_model, ffn, n_tok);
         float *part = h_scratch_elems > po ? h_scratch + po : nullptr;
-        const int64_t pe = part ? h_scratch_elems - po : 0;
-        if (launch_prefill(fmt, 2, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), x, h_scratch, ffn,
-                           d_model, n_tok, part, pe, s) != hipSuccess ||
+        int64_t pe = part ? h_scratch_elems - po : 0;
+        uint16_t *xb = nullptr, *hb = nullptr;
+        if (ffn_bf16_copies(d_model, ffn, n_tok)) {
+            const int64_t pn = ffn_part_elems(fmt, d_model, ffn, n_tok);
+            const int64_t xo = align_up(po + pn, kPlaneAlign / 4);
+            if (h_scratch_elems >= xo + ffn_bf16_elems(d_model, ffn, n_tok)) {
+                part = pn > 0 ? h_scratch + po : nullptr;
+                pe = pn;
+                xb = reinterpret_cast<uint16_t *>(h_scratch + xo);
+                hb = reinterpret_cast<uint16_t *>(h_scratch + xo + align_up(n_tok * d_model / 2, kPlaneAlign / 4));
+            }
+        }
+        if ((xb && launch_to_bf16(x, xb, n_tok * d_model, s) != hipSuccess) ||
+            launch_prefill(fmt, 2, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), x, h_scratch, ffn,
+                           d_model, n_tok, part, pe, s, nullptr, xb) != hipSuccess ||
+            (hb && launch_to_bf16(h_scratch, hb, n_tok * ffn, s) != hipSuccess) ||
             launch_prefill(fmt, 1, static_cast<const uint8_t *>(wd), nullptr, h_scratch, out, d_model, ffn, n_tok, part,
-                           pe, s) != hipSuccess)
+                           pe, s, nullptr, hb) != hipSuccess)
             return QG_ERR_LAUNCH;
         return QG_OK;
     }

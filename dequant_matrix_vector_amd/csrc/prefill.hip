@@ -110,6 +110,15 @@ __global__ __launch_bounds__(256) void rmsnorm4_kernel(const float *__restrict__
     }
 }
 
+// x -> bf16 (nearest even, the kernel's own rounding of x), 4 values per thread
+__global__ void to_bf16_kernel(const float4 *__restrict__ x, uint2 *__restrict__ xb, int64_t n4)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n4) return;
+    const float4 a = x[i];
+    xb[i] = make_uint2(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w));
+}
+
 } // namespace
 
 hipError_t launch_prefill_reduce(int nmat, const float *part, float *y, int64_t n, int ksplit, const float *resid,
@@ -274,9 +283,18 @@ hipError_t launch_rmsnorm(const float *x, const float *gamma, float eps, float *
     return hipGetLastError();
 }
 
+hipError_t launch_to_bf16(const float *x, uint16_t *xb, int64_t n, hipStream_t s)
+{
+    if (n < 4 || n % 4 || n / 4 >= (int64_t(1) << 38)) return hipErrorInvalidValue;
+    const int64_t n4 = n / 4;
+    hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                       reinterpret_cast<const float4 *>(x), reinterpret_cast<uint2 *>(xb), n4);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, const float *x, float *y,
                           int64_t rows, int64_t cols, int64_t n_tok, float *part, int64_t part_elems, hipStream_t s,
-                          const float *resid)
+                          const float *resid, const uint16_t *xb)
 {
     Layout L;
     if (!prefill_format(fmt) || !layout_for(fmt, rows, cols, &L) || n_tok < 1 || n_tok >= (int64_t(1) << 31))
@@ -301,6 +319,7 @@ hipError_t launch_prefill(int fmt, int nmat, const uint8_t *w0, const uint8_t *w
     p.resid = nmat == 1 ? resid : nullptr;
     p.hoff = L.hplane_off;
     p.doff = L.dplane_off;
+    p.xb = xb;
     switch (fmt) {
     case QG_Q4_0: return prefill_dispatch_q4_0(c, nmat, p, y, s);
     case QG_Q4_K: return prefill_dispatch_q4_k(c, nmat, p, y, s);

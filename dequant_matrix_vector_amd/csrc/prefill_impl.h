@@ -62,6 +62,7 @@ struct PrefillParams {
     const float *resid;  // NMAT 1: residual [n_tok][rows] added to y (may be y itself), or null
     int64_t hoff;    // Q6_K: offsets of the high-bit plane and the f16 d plane
     int64_t doff;
+    const uint16_t *xb;  // null, or x already rounded to bf16 (nearest even) [n_tok][cols]: read instead of x
 };
 
 // Split-K sum of the partials (prefill.hip): y = sum over the ksplit ranges
@@ -174,7 +175,7 @@ __device__ __forceinline__ f32x2 q4k_dm(u32x4 h, int s)
 // blocks.  Super-step S's weight runs and x pieces travel together in ring
 // slot S % 2: the loads of the next super-step are in flight while this one
 // is computed.
-template <int FMT, int NMAT, int MTR, int NTW, int W, int Q>
+template <int FMT, int NMAT, int MTR, int NTW, int W, int Q, int XB>
 __global__ __launch_bounds__(W * 64) void prefill_mfma_kernel(PrefillParams p)
 {
     constexpr bool KQ = FMT == QG_Q4_K;
@@ -255,22 +256,41 @@ __global__ __launch_bounds__(W * 64) void prefill_mfma_kernel(PrefillParams p)
     f32x4 xv[2][PT];
     uint32_t live[2];
 
+    // x pieces of 16 bytes: 4 fp32 values, or (XB) 8 bf16 values from the
+    // bf16 copy (half as many pieces: those of k < PT/2, the last one partly)
+    constexpr bool xb16 = XB != 0;
     auto issue = [&](auto jc, int ss) __attribute__((always_inline)) {
         constexpr int J = decltype(jc)::value;
         uint32_t lv = 0;
-        static_for<PT>([&](auto kc) __attribute__((always_inline)) {
-            constexpr int k = decltype(kc)::value;
-            const int piece = threadIdx.x + k * NT;
-            const int t = piece / (SCOLS / 4), c4 = piece % (SCOLS / 4);
-            const int tok = tok_base + t;
-            const int col = ss * SCOLS + 4 * c4;
-            const bool alive = tok < p.n_tok && col < p.cols;
-            lv |= alive ? (1u << k) : 0u;
-            // dead pieces (tokens past n_tok, columns past the row) all read
-            // the first 16 bytes of x: one cache line per wave, stored as 0
-            const int64_t off = alive ? (int64_t)tok * p.cols + col : 0;
-            xv[J][k] = *reinterpret_cast<const f32x4 *>(p.x + off);
-        });
+        if constexpr (xb16) {
+            static_for<PT>([&](auto kc) __attribute__((always_inline)) {
+                constexpr int k = decltype(kc)::value;
+                if constexpr (2 * k < PT) {
+                    const int piece = threadIdx.x + k * NT;
+                    const int t = piece / (SCOLS / 8), c8 = piece % (SCOLS / 8);
+                    const int tok = tok_base + t;
+                    const int col = ss * SCOLS + 8 * c8;
+                    const bool alive = piece < XF4 / 2 && tok < p.n_tok && col < p.cols;
+                    lv |= alive ? (1u << k) : 0u;
+                    const int64_t off = alive ? (int64_t)tok * p.cols + col : 0;
+                    xv[J][k] = __builtin_bit_cast(f32x4, *reinterpret_cast<const u32x4 *>(p.xb + off));
+                }
+            });
+        } else {
+            static_for<PT>([&](auto kc) __attribute__((always_inline)) {
+                constexpr int k = decltype(kc)::value;
+                const int piece = threadIdx.x + k * NT;
+                const int t = piece / (SCOLS / 4), c4 = piece % (SCOLS / 4);
+                const int tok = tok_base + t;
+                const int col = ss * SCOLS + 4 * c4;
+                const bool alive = tok < p.n_tok && col < p.cols;
+                lv |= alive ? (1u << k) : 0u;
+                // dead pieces (tokens past n_tok, columns past the row) all read
+                // the first 16 bytes of x: one cache line per wave, stored as 0
+                const int64_t off = alive ? (int64_t)tok * p.cols + col : 0;
+                xv[J][k] = *reinterpret_cast<const f32x4 *>(p.x + off);
+            });
+        }
         int blk = ss * SB + lblk;
         lv |= blk < p.nb ? (1u << 31) : 0u;
         blk = blk < p.nb ? blk : p.nb - 1;   // past the row: a valid block, weighted 0
@@ -314,15 +334,28 @@ __global__ __launch_bounds__(W * 64) void prefill_mfma_kernel(PrefillParams p)
         const uint32_t lv = live[J];
         uint8_t *xt = lds + J * XTILE;
         // x of this super-step -> bf16 tile, natural column order
-        static_for<PT>([&](auto kc) __attribute__((always_inline)) {
-            constexpr int k = decltype(kc)::value;
-            const int piece = threadIdx.x + k * NT;
-            const int t = piece / (SCOLS / 4), c4 = piece % (SCOLS / 4);
-            const f32x4 a = xv[J][k];
-            uint2 v = make_uint2(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w));
-            if (!((lv >> k) & 1u)) v = make_uint2(0u, 0u);
-            *reinterpret_cast<uint2 *>(xt + t * XROW + c4 * 8) = v;
-        });
+        if constexpr (xb16) {
+            static_for<PT>([&](auto kc) __attribute__((always_inline)) {
+                constexpr int k = decltype(kc)::value;
+                if constexpr (2 * k < PT) {
+                    const int piece = threadIdx.x + k * NT;
+                    const int t = piece / (SCOLS / 8), c8 = piece % (SCOLS / 8);
+                    u32x4 v = __builtin_bit_cast(u32x4, xv[J][k]);
+                    if (!((lv >> k) & 1u)) v = u32x4{0u, 0u, 0u, 0u};
+                    if (piece < XF4 / 2) *reinterpret_cast<u32x4 *>(xt + t * XROW + c8 * 16) = v;
+                }
+            });
+        } else {
+            static_for<PT>([&](auto kc) __attribute__((always_inline)) {
+                constexpr int k = decltype(kc)::value;
+                const int piece = threadIdx.x + k * NT;
+                const int t = piece / (SCOLS / 4), c4 = piece % (SCOLS / 4);
+                const f32x4 a = xv[J][k];
+                uint2 v = make_uint2(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w));
+                if (!((lv >> k) & 1u)) v = make_uint2(0u, 0u);
+                *reinterpret_cast<uint2 *>(xt + t * XROW + c4 * 8) = v;
+            });
+        }
         // this wave's weight runs -> its LDS area (a block past the row gets scale 0)
         static_for<MT>([&](auto mc) __attribute__((always_inline)) {
             constexpr int m = decltype(mc)::value;
@@ -510,13 +543,13 @@ constexpr size_t pf_lds_bytes(int fmt, int nmat, int mtr, int ntw, int waves, in
            (size_t)waves * nmat * mtr * 16 * ((run * 4 * bb + 16) + srow + hrow);
 }
 
-template <int FMT, int NMAT, int MTR, int NTW, int W, int Q>
+template <int FMT, int NMAT, int MTR, int NTW, int W, int Q, int XB>
 hipError_t go_prefill(PrefillParams p, float *y, hipStream_t s)
 {
     const size_t lds = pf_lds_bytes(FMT, NMAT, MTR, NTW, W, Q);
     const int64_t grid = p.row_groups * p.tok_groups * p.ksplit;
     if (grid >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-    auto kern = prefill_mfma_kernel<FMT, NMAT, MTR, NTW, W, Q>;
+    auto kern = prefill_mfma_kernel<FMT, NMAT, MTR, NTW, W, Q, XB>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -570,8 +603,8 @@ constexpr int kBuiltShapes6[] = {
     11141, 11142, 11144, 11181, 11182, 11184, 11241, 11242, 11244,
     11281, 11282, 11284, 11441, 11442, 11481, 11482, 11561, 11841,
     11881, 11961, 12141, 12142, 12144, 12181, 12182, 12241, 12242,
-    12244, 12281, 12282, 12441, 12442, 12481, 12841, 12881, 21141,
-    21142, 21144, 21181, 21182, 21241, 21242, 21244, 21281, 21282,
+    12281, 12282, 12441, 12442, 12481, 12841, 12881, 21141,
+    21142, 21144, 21181, 21182, 21241, 21242, 21281, 21282,
     21441, 21442, 21481, 21841, 21881, 22141, 22142, 22181, 22241,
     22242, 22281, 22441, 22841,
 };
@@ -648,6 +681,17 @@ constexpr bool pf_fits(int fmt, int nmat, int mtr, int ntw, int waves, int run)
     return false;
 }
 
+// The bf16-x variant is built for shapes with several token tiles (the
+// copies exist from 32 tokens on); a shape with one token tile reads fp32 x,
+// which is always given as well.
+template <int FMT, int NM, int MR, int NT, int WV, int RN>
+hipError_t go_prefill_x(const PrefillParams &p, float *y, hipStream_t s)
+{
+    if constexpr (NT >= 2)
+        if (p.xb) return go_prefill<FMT, NM, MR, NT, WV, RN, 1>(p, y, s);
+    return go_prefill<FMT, NM, MR, NT, WV, RN, 0>(p, y, s);
+}
+
 // The built shapes of one format, dispatched on the chosen tile.
 template <int FMT>
 hipError_t prefill_dispatch(const PrefillCfg &c, int nmat, const PrefillParams &p, float *y, hipStream_t s)
@@ -655,7 +699,7 @@ hipError_t prefill_dispatch(const PrefillCfg &c, int nmat, const PrefillParams &
 #define QG_PF(NM, MR, NT, WV, RN)                                                                  \
     if constexpr (pf_fits(FMT, NM, MR, NT, WV, RN))                                                \
         if (nmat == NM && c.mtr == MR && c.ntw == NT && c.waves == WV && c.run == RN)              \
-            return go_prefill<FMT, NM, MR, NT, WV, RN>(p, y, s);
+            return go_prefill_x<FMT, NM, MR, NT, WV, RN>(p, y, s);
 #define QG_PF_R(NM, MR, NT, WV) QG_PF(NM, MR, NT, WV, 1) QG_PF(NM, MR, NT, WV, 2) QG_PF(NM, MR, NT, WV, 4)
 #define QG_PF_W(NM, MR) QG_PF_R(NM, MR, 1, 4) QG_PF_R(NM, MR, 2, 4) QG_PF_R(NM, MR, 4, 4) QG_PF_R(NM, MR, 8, 4) \
     QG_PF(NM, MR, 4, 16, 1) QG_PF(NM, MR, 8, 16, 1) \

@@ -101,9 +101,14 @@ int64_t prefill_part_elems(int fmt, int nmat, int64_t rows, int64_t cols, int64_
 // x fp32 [n_tok][cols].  part (part_elems floats, may be null) lets the K
 // dimension split over workgroups; the partial sums are then added in a
 // second, small launch.
+// xb (may be null): x already rounded to bf16 (nearest even, as the kernel
+// rounds it), 16-byte aligned; the kernel then reads it instead of x
+// (half the bytes, the same result).
 hipError_t launch_prefill(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, const float *x, float *y,
                           int64_t rows, int64_t cols, int64_t n_tok, float *part, int64_t part_elems,
-                          hipStream_t s, const float *resid = nullptr);
+                          hipStream_t s, const float *resid = nullptr, const uint16_t *xb = nullptr);
+// xb[i] = bf16(x[i]) (nearest even), n % 4 == 0, both 16-byte aligned.
+hipError_t launch_to_bf16(const float *x, uint16_t *xb, int64_t n, hipStream_t s);
 // Raw Q8_0 blocks (f16 d, 32 int8) of activation rows x [n_tok][n], n a multiple of 32.
 hipError_t launch_quantize_q8_0(const float *x, uint8_t *blocks, int64_t n, int64_t n_tok, hipStream_t s);
 // token[t] = first index of the largest of logits[t][0..n) (NaN never chosen, unless at index 0).

@@ -159,10 +159,13 @@ int swiglu_gate_up(int fmt, const void *wg, const void *wu, const float *x, floa
  * On the matrix-core path (n_tok > 1) a scratch of
  * swiglu_ffn_scratch_elems() elements (16-byte aligned) also holds the partial
  * sums that let both products split their K dimension over more workgroups
- * (deterministic: fixed summation order); with less, the products run
- * unsplit, with the same accuracy bound.  x, out and the whole declared
+ * (deterministic: fixed summation order) and, from 32 tokens on with
+ * d_model * ffn >= 2^24, bf16 copies of x and h (rounded to nearest even as the matrix cores take them, so the
+ * results are bit-identical; the products then read half the bytes of x and
+ * h, for one short conversion launch each); with less, the products run
+ * unsplit and on fp32 x and h, with the same accuracy bound.  x, out and the whole declared
  * scratch must be pairwise disjoint.  Two launches on `stream` for n_tok == 1,
- * up to four on the matrix-core path, else two per token; no host
+ * up to six on the matrix-core path, else two per token; no host
  * synchronization. */
 int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const float *x,
                float *out, float *h_scratch, int64_t h_scratch_elems, int64_t d_model,

@@ -396,3 +396,32 @@ def test_prefill_8bit_swiglu_ffn(fmt):
             synth.make_tensor(fmt, d_model, ffn, rng)]
     x = rng.standard_normal((24, d_model)).astype(np.float32)
     G.check_ffn(fmt, tens, x, d_model, ffn, f"ffn {fmt} n_tok=24")
+
+
+@pytest.mark.parametrize("fmt,n_tok", [("q4_0", 40), ("q4_0", 128), ("q6_k", 33), ("i8row", 64), ("q4_k", 32),
+                                       ("q8_0", 35)])
+def test_swiglu_ffn_bf16_copies_bit_identical(fmt, n_tok):
+    # from 32 tokens on with d_model * ffn >= 2^24, and the scratch
+    # swiglu_ffn_scratch_elems asks for, both products read bf16 copies of x
+    # and h made by a conversion launch; one float less of scratch keeps the
+    # fp32 inputs. The copies round as the kernel does, so h and out are
+    # bit-identical either way. (4096 x 4096: ragged token tiles, both copies)
+    d_model, ffn = 4096, 4096
+    rng = np.random.default_rng(1800 + n_tok)
+    tens = [synth.make_tensor(fmt, ffn, d_model, rng), synth.make_tensor(fmt, ffn, d_model, rng),
+            synth.make_tensor(fmt, d_model, ffn, rng)]
+    pk = [G.upload(t) for t in tens]
+    x = G.torch.from_numpy(rng.standard_normal((n_tok, d_model)).astype(np.float32)).to(G.dev())
+    full = G.qg().swiglu_ffn_scratch_elems(fmt, d_model, ffn, n_tok)
+    assert full > n_tok * ffn
+    res = []
+    for elems in (full, full - 1):
+        sc = G.torch.full((elems,), float("nan"), device=G.dev())
+        out, h = G.qg().swiglu_ffn(fmt, pk[0], pk[1], pk[2], x, d_model, ffn, h_scratch=sc)
+        G.torch.cuda.synchronize()
+        res.append((out.cpu().numpy(), h.cpu().numpy()))
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+    # and the bf16-copy path (the default scratch) against the oracle (the
+    # smaller batches: the oracle's time grows with the tokens)
+    if n_tok <= 40:
+        G.check_ffn(fmt, tens, x.cpu().numpy(), d_model, ffn, f"ffn {fmt} n_tok={n_tok} bf16 copies")
