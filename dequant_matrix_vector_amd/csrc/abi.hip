@@ -239,11 +239,12 @@ static int64_t ffn_part_offset(int64_t d_model, int64_t ffn, int64_t n_tok)
 }
 
 // From this many tokens on, and for matrices of at least this many weights,
-// swiglu_ffn's matrix-core products read bf16 copies of x and h (made by one
-// conversion launch each, when the scratch holds them): each workgroup
-// re-reads its x tile from L2 for every super-step, so halving those bytes
-// outweighs the two extra launches (about 2 us each) only on large matrices
-// (27B-class FFN at 128 tokens: 184.9 to 173.8 us; a 576 x 1536 FFN: 72 to 76).
+// swiglu_ffn's matrix-core products read bf16 copies of x and h (x's made by
+// a conversion launch, h's by the gate/up product itself, when the scratch
+// holds them): each workgroup re-reads its x tile from L2 for every
+// super-step, so halving those bytes outweighs the extra launch (about 2 us)
+// only on large matrices (27B-class FFN at 128 tokens: 184.9 to about 174 us
+// with two conversion launches; a 576 x 1536 FFN: 72 to 76).
 static const int64_t kFfnBf16MinTok = 32;
 static const int64_t kFfnBf16MinWeights = int64_t(1) << 24;
 
@@ -336,10 +337,11 @@ int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const fl
                 hb = reinterpret_cast<uint16_t *>(h_scratch + xo + align_up(n_tok * d_model / 2, kPlaneAlign / 4));
             }
         }
+        // the gate/up product writes h's bf16 copy itself (its epilogue or
+        // its split-K sum)
         if ((xb && launch_to_bf16(x, xb, n_tok * d_model, s) != hipSuccess) ||
             launch_prefill(fmt, 2, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), x, h_scratch, ffn,
-                           d_model, n_tok, part, pe, s, nullptr, xb) != hipSuccess ||
-            (hb && launch_to_bf16(h_scratch, hb, n_tok * ffn, s) != hipSuccess) ||
+                           d_model, n_tok, part, pe, s, nullptr, xb, hb) != hipSuccess ||
             launch_prefill(fmt, 1, static_cast<const uint8_t *>(wd), nullptr, h_scratch, out, d_model, ffn, n_tok, part,
                            pe, s, nullptr, hb) != hipSuccess)
             return QG_ERR_LAUNCH;

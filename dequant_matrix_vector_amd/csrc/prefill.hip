@@ -9,11 +9,11 @@ namespace {
 
 // y[t][i] = sum over K ranges of the partials, in range order (NMAT = 1, plus
 // the residual when given), or silu(g) * u of the two summed products
-// (NMAT = 2).  V outputs per thread (4 when the element count allows 16-byte
-// accesses).
+// (NMAT = 2; yb, if not null, also gets it rounded to bf16).  V outputs per
+// thread (4 when the element count allows 16-byte accesses).
 template <int NMAT, int V>
 __global__ void prefill_reduce_kernel(const float *__restrict__ part, float *y, int64_t n, int ksplit,
-                                      const float *resid)
+                                      const float *resid, uint16_t *yb)
 {
     typedef float fv __attribute__((ext_vector_type(V)));
     const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * V;
@@ -41,6 +41,10 @@ __global__ void prefill_reduce_kernel(const float *__restrict__ part, float *y, 
     for (int e = 0; e < V; e++) r[e] = NMAT == 1 ? s[0][e] : s[0][e] / (1.0f + expf(-s[0][e])) * s[NMAT - 1][e];
     if (NMAT == 1 && resid) r += *reinterpret_cast<const fv *>(resid + i);
     *reinterpret_cast<fv *>(y + i) = r;
+    if (NMAT == 2 && yb) {
+        if constexpr (V == 4) *reinterpret_cast<uint2 *>(yb + i) = make_uint2(pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3]));
+        else yb[i] = (uint16_t)(pack_bf16(r[0], 0.0f) & 0xFFFFu);
+    }
 }
 
 // RMSNorm of one token row per workgroup (llmoxide blog, section 4 "Keeping
@@ -122,16 +126,16 @@ __global__ void to_bf16_kernel(const float4 *__restrict__ x, uint2 *__restrict__
 } // namespace
 
 hipError_t launch_prefill_reduce(int nmat, const float *part, float *y, int64_t n, int ksplit, const float *resid,
-                                 hipStream_t s, hipEvent_t stop)
+                                 hipStream_t s, hipEvent_t stop, uint16_t *yb)
 {
     const uintptr_t al = reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(part) |
-                         reinterpret_cast<uintptr_t>(resid);
+                         reinterpret_cast<uintptr_t>(resid) | reinterpret_cast<uintptr_t>(yb);
     const bool v4 = n % 4 == 0 && (al & 15) == 0;
     const void *red;
     if (nmat == 2) red = v4 ? (const void *)prefill_reduce_kernel<2, 4> : (const void *)prefill_reduce_kernel<2, 1>;
     else red = v4 ? (const void *)prefill_reduce_kernel<1, 4> : (const void *)prefill_reduce_kernel<1, 1>;
     const int64_t blocks = ((v4 ? n / 4 : n) + 255) / 256;
-    void *rargs[] = {&part, &y, &n, &ksplit, &resid};
+    void *rargs[] = {&part, &y, &n, &ksplit, &resid, &yb};
     if (stop) return hipExtLaunchKernel(red, dim3((unsigned)blocks), dim3(256), rargs, 0, s, nullptr, stop, 0);
     return hipLaunchKernel(red, dim3((unsigned)blocks), dim3(256), rargs, 0, s);
 }
@@ -294,7 +298,7 @@ hipError_t launch_to_bf16(const float *x, uint16_t *xb, int64_t n, hipStream_t s
 
 hipError_t launch_prefill(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, const float *x, float *y,
                           int64_t rows, int64_t cols, int64_t n_tok, float *part, int64_t part_elems, hipStream_t s,
-                          const float *resid, const uint16_t *xb)
+                          const float *resid, const uint16_t *xb, uint16_t *yb)
 {
     Layout L;
     if (!prefill_format(fmt) || !layout_for(fmt, rows, cols, &L) || n_tok < 1 || n_tok >= (int64_t(1) << 31))
@@ -320,6 +324,7 @@ hipError_t launch_prefill(int fmt, int nmat, const uint8_t *w0, const uint8_t *w
     p.hoff = L.hplane_off;
     p.doff = L.dplane_off;
     p.xb = xb;
+    p.yb = nmat == 2 ? yb : nullptr;
     switch (fmt) {
     case QG_Q4_0: return prefill_dispatch_q4_0(c, nmat, p, y, s);
     case QG_Q4_K: return prefill_dispatch_q4_k(c, nmat, p, y, s);

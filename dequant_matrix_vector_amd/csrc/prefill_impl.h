@@ -63,13 +63,14 @@ struct PrefillParams {
     int64_t hoff;    // Q6_K: offsets of the high-bit plane and the f16 d plane
     int64_t doff;
     const uint16_t *xb;  // null, or x already rounded to bf16 (nearest even) [n_tok][cols]: read instead of x
+    uint16_t *yb;        // NMAT 2 without a K split: null, or where y is also written rounded to bf16
 };
 
 // Split-K sum of the partials (prefill.hip): y = sum over the ksplit ranges
 // (range order) of part, plus resid for one matrix, or silu(g) * u for the
 // pair; n = n_tok * rows; stop (may be null) is recorded when it ends.
 hipError_t launch_prefill_reduce(int nmat, const float *part, float *y, int64_t n, int ksplit, const float *resid,
-                                 hipStream_t s, hipEvent_t stop);
+                                 hipStream_t s, hipEvent_t stop, uint16_t *yb = nullptr);
 // One format's built shapes (prefill_<format>.hip).
 hipError_t prefill_dispatch_q4_0(const PrefillCfg &c, int nmat, const PrefillParams &p, float *y, hipStream_t s);
 hipError_t prefill_dispatch_q4_k(const PrefillCfg &c, int nmat, const PrefillParams &p, float *y, hipStream_t s);
@@ -522,6 +523,15 @@ __global__ __launch_bounds__(W * 64) void prefill_mfma_kernel(PrefillParams p)
                     float v[4];
                     for (int i = 0; i < 4; i++) v[i] = gg[i] / (1.0f + expf(-gg[i])) * uu[i];
                     store4(p.y + (int64_t)tok * p.rows + row, row, v[0], v[1], v[2], v[3]);
+                    if (p.yb) {   // the bf16 copy of h for the next product, the kernel's own rounding
+                        uint16_t *yb = p.yb + (int64_t)tok * p.rows + row;
+                        if ((p.rows & 3) == 0 && row + 3 < p.rows) {
+                            *reinterpret_cast<uint2 *>(yb) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+                        } else {
+                            for (int i = 0; i < 4; i++)
+                                if (row + i < p.rows) yb[i] = (uint16_t)(pack_bf16(v[i], 0.0f) & 0xFFFFu);
+                        }
+                    }
                 }
             });
         }
@@ -568,7 +578,8 @@ hipError_t go_prefill(PrefillParams p, float *y, hipStream_t s)
         e = hipGetLastError();
     }
     if (e != hipSuccess || p.ksplit == 1) return e;
-    return launch_prefill_reduce(NMAT, p.y, y, (int64_t)p.n_tok * p.rows, p.ksplit, p.resid, s, timed ? t1 : nullptr);
+    return launch_prefill_reduce(NMAT, p.y, y, (int64_t)p.n_tok * p.rows, p.ksplit, p.resid, s, timed ? t1 : nullptr,
+                                 p.yb);
 }
 
 // Tile shapes that are built, per format: those whose ring, operands and

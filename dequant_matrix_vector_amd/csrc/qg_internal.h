@@ -103,10 +103,12 @@ int64_t prefill_part_elems(int fmt, int nmat, int64_t rows, int64_t cols, int64_
 // second, small launch.
 // xb (may be null): x already rounded to bf16 (nearest even, as the kernel
 // rounds it), 16-byte aligned; the kernel then reads it instead of x
-// (half the bytes, the same result).
+// (half the bytes, the same result).  yb (nmat == 2, may be null): y is also
+// written there rounded to bf16 (16-byte aligned), the next product's xb.
 hipError_t launch_prefill(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, const float *x, float *y,
                           int64_t rows, int64_t cols, int64_t n_tok, float *part, int64_t part_elems,
-                          hipStream_t s, const float *resid = nullptr, const uint16_t *xb = nullptr);
+                          hipStream_t s, const float *resid = nullptr, const uint16_t *xb = nullptr,
+                          uint16_t *yb = nullptr);
 // xb[i] = bf16(x[i]) (nearest even), n % 4 == 0, both 16-byte aligned.
 hipError_t launch_to_bf16(const float *x, uint16_t *xb, int64_t n, hipStream_t s);
 // Raw Q8_0 blocks (f16 d, 32 int8) of activation rows x [n_tok][n], n a multiple of 32.
