@@ -243,9 +243,10 @@ static int64_t ffn_part_offset(int64_t d_model, int64_t ffn, int64_t n_tok)
 // a conversion launch, h's by the gate/up product itself, when the scratch
 // holds them): each workgroup re-reads its x tile from L2 for every
 // super-step, so halving those bytes outweighs the extra launch (about 2 us)
-// only on large matrices (27B-class FFN at 128 tokens: 184.9 to about 174 us
-// with two conversion launches; a 576 x 1536 FFN: 72 to 76).
-static const int64_t kFfnBf16MinTok = 32;
+// only on large matrices (27B-class FFN: 62.9 to 61.9 us at 8 tokens, 69.7 to
+// 64.8 at 16, 184.9 to 171 at 128; a 576 x 1536 FFN at 128 tokens with two
+// conversion launches: 72 to 76).
+static const int64_t kFfnBf16MinTok = 8;
 static const int64_t kFfnBf16MinWeights = int64_t(1) << 24;
 
 static bool ffn_bf16_copies(int64_t d_model, int64_t ffn, int64_t n_tok)

@@ -692,14 +692,11 @@ constexpr bool pf_fits(int fmt, int nmat, int mtr, int ntw, int waves, int run)
     return false;
 }
 
-// The bf16-x variant is built for shapes with several token tiles (the
-// copies exist from 32 tokens on); a shape with one token tile reads fp32 x,
-// which is always given as well.
+// Every built shape has both x variants: fp32 x, or its bf16 copy when given.
 template <int FMT, int NM, int MR, int NT, int WV, int RN>
 hipError_t go_prefill_x(const PrefillParams &p, float *y, hipStream_t s)
 {
-    if constexpr (NT >= 2)
-        if (p.xb) return go_prefill<FMT, NM, MR, NT, WV, RN, 1>(p, y, s);
+    if (p.xb) return go_prefill<FMT, NM, MR, NT, WV, RN, 1>(p, y, s);
     return go_prefill<FMT, NM, MR, NT, WV, RN, 0>(p, y, s);
 }
 

@@ -159,7 +159,7 @@ int swiglu_gate_up(int fmt, const void *wg, const void *wu, const float *x, floa
  * On the matrix-core path (n_tok > 1) a scratch of
  * swiglu_ffn_scratch_elems() elements (16-byte aligned) also holds the partial
  * sums that let both products split their K dimension over more workgroups
- * (deterministic: fixed summation order) and, from 32 tokens on with
+ * (deterministic: fixed summation order) and, from 8 tokens on with
  * d_model * ffn >= 2^24, bf16 copies of x and h (rounded to nearest even as the matrix cores take them, so the
  * results are bit-identical; the products then read half the bytes of x and
  * h, for one short conversion launch each); with less, the products run

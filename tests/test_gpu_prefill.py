@@ -399,9 +399,9 @@ def test_prefill_8bit_swiglu_ffn(fmt):
 
 
 @pytest.mark.parametrize("fmt,n_tok", [("q4_0", 40), ("q4_0", 128), ("q6_k", 33), ("i8row", 64), ("q4_k", 32),
-                                       ("q8_0", 35)])
+                                       ("q8_0", 35), ("q4_0", 8), ("q4_k", 13), ("i8row", 9)])
 def test_swiglu_ffn_bf16_copies_bit_identical(fmt, n_tok):
-    # from 32 tokens on with d_model * ffn >= 2^24, and the scratch
+    # from 8 tokens on with d_model * ffn >= 2^24, and the scratch
     # swiglu_ffn_scratch_elems asks for, both products read bf16 copies of x
     # and h made by a conversion launch; one float less of scratch keeps the
     # fp32 inputs. The copies round as the kernel does, so h and out are
