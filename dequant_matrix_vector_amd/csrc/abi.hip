@@ -383,8 +383,9 @@ int64_t swiglu_ffn_block_scratch_elems(int fmt, int64_t d_model, int64_t ffn, in
         !layout_for(fmt, d_model, ffn, &Lb))
         return QG_ERR_SHAPE;
     if (!block_on_matrix_cores(fmt, n_tok)) return n_tok * ffn;
-    const int64_t a = prefill_part_elems(fmt, 2, ffn, d_model, n_tok), b = prefill_part_elems(fmt, 1, d_model, ffn, n_tok);
-    const int64_t part = a > b ? a : b;
+    const int64_t part = ffn_part_elems(fmt, d_model, ffn, n_tok);
+    if (ffn_bf16_copies(d_model, ffn, n_tok))
+        return align_up(block_part_offset(d_model, ffn, n_tok) + part, kPlaneAlign / 4) + ffn_bf16_elems(d_model, ffn, n_tok);
     return part > 0 ? block_part_offset(d_model, ffn, n_tok) + part : block_xn_offset(ffn, n_tok) + n_tok * d_model;
 }
 
@@ -416,16 +417,30 @@ int swiglu_ffn_block(int fmt, const void *wg, const void *wu, const void *wd, co
         return QG_ERR_ALIAS;
     hipStream_t s = (hipStream_t)stream;
     if (mfma) {
-        // normalized input and partial sums behind h in the scratch
+        // normalized input and partial sums behind h in the scratch; with room
+        // behind those (large matrices), the bf16 copies of the normalized
+        // input (written by the RMSNorm launch) and of h (by the gate/up
+        // product), as in swiglu_ffn
         float *xn = h_scratch + block_xn_offset(ffn, n_tok);
         const int64_t po = block_part_offset(d_model, ffn, n_tok);
         float *part = h_scratch_elems > po ? h_scratch + po : nullptr;
-        const int64_t pe = part ? h_scratch_elems - po : 0;
-        if (launch_rmsnorm(x, gamma, eps, xn, d_model, n_tok, s) != hipSuccess ||
+        int64_t pe = part ? h_scratch_elems - po : 0;
+        uint16_t *xnb = nullptr, *hb = nullptr;
+        if (ffn_bf16_copies(d_model, ffn, n_tok)) {
+            const int64_t pn = ffn_part_elems(fmt, d_model, ffn, n_tok);
+            const int64_t xo = align_up(po + pn, kPlaneAlign / 4);
+            if (h_scratch_elems >= xo + ffn_bf16_elems(d_model, ffn, n_tok)) {
+                part = pn > 0 ? h_scratch + po : nullptr;
+                pe = pn;
+                xnb = reinterpret_cast<uint16_t *>(h_scratch + xo);
+                hb = reinterpret_cast<uint16_t *>(h_scratch + xo + align_up(n_tok * d_model / 2, kPlaneAlign / 4));
+            }
+        }
+        if (launch_rmsnorm(x, gamma, eps, xn, d_model, n_tok, s, xnb) != hipSuccess ||
             launch_prefill(fmt, 2, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), xn, h_scratch, ffn,
-                           d_model, n_tok, part, pe, s) != hipSuccess ||
+                           d_model, n_tok, part, pe, s, nullptr, xnb, hb) != hipSuccess ||
             launch_prefill(fmt, 1, static_cast<const uint8_t *>(wd), nullptr, h_scratch, out, d_model, ffn, n_tok, part,
-                           pe, s, x) != hipSuccess)
+                           pe, s, x, hb) != hipSuccess)
             return QG_ERR_LAUNCH;
         return QG_OK;
     }

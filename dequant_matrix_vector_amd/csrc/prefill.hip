@@ -52,7 +52,7 @@ __global__ void prefill_reduce_kernel(const float *__restrict__ part, float *y, 
 // sum of squares runs in a fixed order (thread stride, xor tree, waves in
 // order), so every call gives the same scale.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ x, const float *__restrict__ gamma,
-                                                      float eps, float *__restrict__ xn, int n)
+                                                      float eps, float *__restrict__ xn, int n, uint16_t *xnb)
 {
     __shared__ float wsum[4];
     const float *xt = x + (int64_t)blockIdx.x * n;
@@ -65,17 +65,22 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ 
     const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
     const float sc = 1.0f / sqrtf(tot / (float)n + eps);
     float *o = xn + (int64_t)blockIdx.x * n;
-    for (int j = threadIdx.x; j < n; j += 256) o[j] = xt[j] * sc * gamma[j];
+    uint16_t *ob = xnb ? xnb + (int64_t)blockIdx.x * n : nullptr;
+    for (int j = threadIdx.x; j < n; j += 256) {
+        const float v = xt[j] * sc * gamma[j];
+        o[j] = v;
+        if (ob) ob[j] = (uint16_t)(pack_bf16(v, 0.0f) & 0xFFFFu);
+    }
 }
 
 // The same for rows of whole 16-byte pieces that fit P pieces per thread
 // (n % 4 == 0, 16-byte aligned, n <= 1024 P): x and the gain are loaded once,
 // together, and stay in registers between the sum of squares (each thread
 // over its pieces in index order, then the xor tree and the waves in order)
-// and the scaling.
+// and the scaling.  xnb (may be null) also gets xn rounded to bf16.
 template <int P>
 __global__ __launch_bounds__(256) void rmsnorm4_kernel(const float *__restrict__ x, const float *__restrict__ gamma,
-                                                       float eps, float *__restrict__ xn, int n)
+                                                       float eps, float *__restrict__ xn, int n, uint16_t *xnb)
 {
     __shared__ float wsum[4];
     const int n4 = n / 4;
@@ -105,12 +110,16 @@ __global__ __launch_bounds__(256) void rmsnorm4_kernel(const float *__restrict__
     const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
     const float sc = 1.0f / sqrtf(tot / (float)n + eps);
     float4 *o = reinterpret_cast<float4 *>(xn + (int64_t)blockIdx.x * n);
+    uint2 *ob = xnb ? reinterpret_cast<uint2 *>(xnb + (int64_t)blockIdx.x * n) : nullptr;
 #pragma unroll
     for (int k = 0; k < P; k++) {
         const int j = (int)threadIdx.x + k * 256;
-        if (j < n4)
-            o[j] = make_float4(v[k].x * sc * gm[k].x, v[k].y * sc * gm[k].y, v[k].z * sc * gm[k].z,
-                               v[k].w * sc * gm[k].w);
+        if (j < n4) {
+            const float4 r = make_float4(v[k].x * sc * gm[k].x, v[k].y * sc * gm[k].y, v[k].z * sc * gm[k].z,
+                                         v[k].w * sc * gm[k].w);
+            o[j] = r;
+            if (ob) ob[j] = make_uint2(pack_bf16(r.x, r.y), pack_bf16(r.z, r.w));
+        }
     }
 }
 
@@ -268,21 +277,21 @@ int64_t prefill_part_elems(int fmt, int nmat, int64_t rows, int64_t cols, int64_
 }
 
 hipError_t launch_rmsnorm(const float *x, const float *gamma, float eps, float *xn, int64_t n, int64_t n_tok,
-                          hipStream_t s)
+                          hipStream_t s, uint16_t *xnb)
 {
     if (n < 1 || n_tok < 1 || n_tok >= (int64_t(1) << 31) || n >= (int64_t(1) << 31)) return hipErrorInvalidValue;
     const uintptr_t al = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(gamma) |
-                         reinterpret_cast<uintptr_t>(xn);
+                         reinterpret_cast<uintptr_t>(xn) | reinterpret_cast<uintptr_t>(xnb);
     const int64_t per = (n / 4 + 255) / 256;   // 16-byte pieces per thread
     const dim3 grid((unsigned)n_tok), block(256);
     if (n % 4 == 0 && (al & 15) == 0 && per <= 8) {
-        if (per <= 1) hipLaunchKernelGGL(rmsnorm4_kernel<1>, grid, block, 0, s, x, gamma, eps, xn, (int)n);
-        else if (per <= 2) hipLaunchKernelGGL(rmsnorm4_kernel<2>, grid, block, 0, s, x, gamma, eps, xn, (int)n);
-        else if (per <= 4) hipLaunchKernelGGL(rmsnorm4_kernel<4>, grid, block, 0, s, x, gamma, eps, xn, (int)n);
-        else if (per <= 6) hipLaunchKernelGGL(rmsnorm4_kernel<6>, grid, block, 0, s, x, gamma, eps, xn, (int)n);
-        else hipLaunchKernelGGL(rmsnorm4_kernel<8>, grid, block, 0, s, x, gamma, eps, xn, (int)n);
+        if (per <= 1) hipLaunchKernelGGL(rmsnorm4_kernel<1>, grid, block, 0, s, x, gamma, eps, xn, (int)n, xnb);
+        else if (per <= 2) hipLaunchKernelGGL(rmsnorm4_kernel<2>, grid, block, 0, s, x, gamma, eps, xn, (int)n, xnb);
+        else if (per <= 4) hipLaunchKernelGGL(rmsnorm4_kernel<4>, grid, block, 0, s, x, gamma, eps, xn, (int)n, xnb);
+        else if (per <= 6) hipLaunchKernelGGL(rmsnorm4_kernel<6>, grid, block, 0, s, x, gamma, eps, xn, (int)n, xnb);
+        else hipLaunchKernelGGL(rmsnorm4_kernel<8>, grid, block, 0, s, x, gamma, eps, xn, (int)n, xnb);
     } else {
-        hipLaunchKernelGGL(rmsnorm_kernel, grid, block, 0, s, x, gamma, eps, xn, (int)n);
+        hipLaunchKernelGGL(rmsnorm_kernel, grid, block, 0, s, x, gamma, eps, xn, (int)n, xnb);
     }
     return hipGetLastError();
 }

@@ -116,7 +116,8 @@ hipError_t launch_quantize_q8_0(const float *x, uint8_t *blocks, int64_t n, int6
 // token[t] = first index of the largest of logits[t][0..n) (NaN never chosen, unless at index 0).
 hipError_t launch_argmax(const float *logits, int32_t *token, int64_t n, int64_t n_tok, hipStream_t s);
 // xn[t][j] = x[t][j] * gamma[j] / sqrt(mean_j x[t][j]^2 + eps), fp32, one workgroup per token.
+// xnb (may be null): xn also written rounded to bf16 (nearest even).
 hipError_t launch_rmsnorm(const float *x, const float *gamma, float eps, float *xn, int64_t n, int64_t n_tok,
-                          hipStream_t s);
+                          hipStream_t s, uint16_t *xnb = nullptr);
 
 } // namespace qg

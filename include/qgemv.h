@@ -193,8 +193,10 @@ int swiglu_ffn_block(int fmt, const void *wg, const void *wu, const void *wd, co
 
 /* Scratch elements (fp32) for which swiglu_ffn_block runs its fastest form:
  * n_tok*ffn on the GEMV path; on the matrix-core path (n_tok > 1) h,
- * the normalized input (required: together the minimum) and room for
- * split-K partial sums (optional).  Negative qg_status for an invalid shape
+ * the normalized input (required: together the minimum), room for split-K
+ * partial sums and, from 8 tokens on with d_model * ffn >= 2^24, bf16 copies
+ * of the normalized input and h as swiglu_ffn keeps them (both optional; the
+ * results are bit-identical with or without the copies).  Negative qg_status for an invalid shape
  * or format. */
 int64_t swiglu_ffn_block_scratch_elems(int fmt, int64_t d_model, int64_t ffn, int64_t n_tok);
 

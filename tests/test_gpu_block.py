@@ -135,3 +135,29 @@ def test_block_matrix_cores_rmsnorm_widths(d_model, ffn):
     x = (3.0 * rng.standard_normal((n_tok, d_model))).astype(np.float32)
     gamma = rng.uniform(0.2, 2.0, d_model).astype(np.float32)
     check_block("q4_0", tens, x, gamma, d_model, ffn, f"block q4_0 n_tok={n_tok} d_model={d_model}")
+
+
+@pytest.mark.parametrize("fmt,n_tok", [("q4_0", 8), ("q4_k", 40), ("i8row", 13)])
+def test_block_bf16_copies_bit_identical(fmt, n_tok):
+    # large matrices from 8 tokens on: the RMSNorm launch also writes the
+    # normalized input rounded to bf16 and the gate/up product h's bf16 copy,
+    # when swiglu_ffn_block_scratch_elems' room is given; one float less keeps
+    # the fp32 inputs. Same rounding, so out and h are bit-identical; the
+    # default scratch is checked against the oracle too.
+    d_model, ffn = 4096, 4096
+    tens = _tensors(fmt, d_model, ffn, 2400 + n_tok)
+    pk = [G.upload(t) for t in tens]
+    rng = np.random.default_rng(2401 + n_tok)
+    x = (2.0 * rng.standard_normal((n_tok, d_model))).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, d_model).astype(np.float32)
+    xd, gd = G.torch.from_numpy(x).to(G.dev()), G.torch.from_numpy(gamma).to(G.dev())
+    full = G.qg().swiglu_ffn_block_scratch_elems(fmt, d_model, ffn, n_tok)
+    res = []
+    for elems in (full, full - 1):
+        sc = G.torch.full((elems,), float("nan"), device=G.dev())
+        out, h = G.qg().swiglu_ffn_block(fmt, pk[0], pk[1], pk[2], gd, 1e-5, xd, d_model, ffn, h_scratch=sc)
+        G.torch.cuda.synchronize()
+        res.append((out.cpu().numpy(), h.cpu().numpy()))
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+    if n_tok <= 13:
+        check_block(fmt, tens, x, gamma, d_model, ffn, f"block {fmt} n_tok={n_tok} bf16 copies")
