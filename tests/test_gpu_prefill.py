@@ -425,3 +425,34 @@ def test_swiglu_ffn_bf16_copies_bit_identical(fmt, n_tok):
     # smaller batches: the oracle's time grows with the tokens)
     if n_tok <= 40:
         G.check_ffn(fmt, tens, x.cpu().numpy(), d_model, ffn, f"ffn {fmt} n_tok={n_tok} bf16 copies")
+
+
+def test_swiglu_ffn_bf16_copies_graph_replays():
+    # the matrix-core FFN with its bf16 copies, K split and conversion launch,
+    # captured in a HIP graph and replayed three times with eager work and a
+    # synchronization between the replays: every replay equals the eager call
+    d_model, ffn, n_tok = 4096, 4096, 16
+    rng = np.random.default_rng(1900)
+    tens = [synth.make_tensor("q4_0", ffn, d_model, rng), synth.make_tensor("q4_0", ffn, d_model, rng),
+            synth.make_tensor("q4_0", d_model, ffn, rng)]
+    pk = [G.upload(t) for t in tens]
+    torch = G.torch
+    x = torch.from_numpy(rng.standard_normal((n_tok, d_model)).astype(np.float32)).to(G.dev())
+    sc = torch.empty(G.qg().swiglu_ffn_scratch_elems("q4_0", d_model, ffn, n_tok), device=G.dev())
+    out = torch.empty((n_tok, d_model), device=G.dev())
+    G.qg().swiglu_ffn("q4_0", pk[0], pk[1], pk[2], x, d_model, ffn, out=out, h_scratch=sc)
+    torch.cuda.synchronize()
+    want = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):   # the binding launches on torch's current stream: the capture stream
+        G.qg().swiglu_ffn("q4_0", pk[0], pk[1], pk[2], x, d_model, ffn, out=out, h_scratch=sc)
+    torch.cuda.synchronize()
+    for k in range(3):
+        out.fill_(float("nan"))
+        sc.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"replay {k}"
+        G.qg().swiglu_ffn("q4_0", pk[0], pk[1], pk[2], x, d_model, ffn, out=torch.empty_like(out),
+                          h_scratch=torch.empty_like(sc))   # eager work between the replays
+        torch.cuda.synchronize()
