@@ -159,7 +159,9 @@ PrefillCfg g_pf_override = {0, 0, 0, 0, 0};
 // one token tile: 4 waves, runs of two steps; 8 token tiles (128 tokens
 // sharing each decoded weight): 8 waves for the fused gate/up pair, 16 for a
 // single matrix (256 rows share each staged x tile); 4 token tiles: 4 waves
-// for the pair, 16 for a single matrix; 2: 4 waves for the pair, and for a
+// for the pair, 8 for a single matrix (a per-kernel trace of the down
+// products at 128 tokens: [2048][8192] 21.7 to 15.1 us against 16 waves,
+// [5120][17408] 62.0 to 60.0); 2: 4 waves for the pair, and for a
 // single matrix 4 waves with runs of two steps; then K ranges until the grid
 // has about four workgroups per CU (if the caller gave room for the
 // partials), as long as the partial sums (written, then read back) stay
@@ -176,7 +178,7 @@ static void default_tile(PrefillCfg &c, int nmat, int64_t n_tiles)
     } else if (n_tiles >= 8) {
         c.ntw = 8, c.waves = nmat == 2 ? 8 : 16, c.run = 1;
     } else if (n_tiles >= 4) {
-        c.ntw = 4, c.waves = nmat == 2 ? 4 : 16, c.run = 1;
+        c.ntw = 4, c.waves = nmat == 2 ? 4 : 8, c.run = 1;
     } else {
         c.ntw = 2, c.waves = 4, c.run = nmat == 2 ? 1 : 2;
     }
