@@ -217,6 +217,11 @@ PrefillCfg choose(int fmt, int nmat, int64_t rows, int64_t cols, int64_t n_tok, 
             eff = eff >= 8 ? 4 : (eff >= 4 ? 2 : 1);
             default_tile(c, nmat, eff);
         }
+        // several token tiles stepped down to one (few rows, no K split):
+        // long rows take runs of four steps (sweeps at 128 tokens: Q6_K
+        // [2048][5632] 31.3 to 27.8 us, Q4_0 [2048][8192] 30.6 to 29.9; rows of
+        // 2048 or fewer columns keep runs of two)
+        if (n_tiles > 1 && eff == 1 && cols >= 4096) c.run = 4;
     }
     // a shape that is not built falls back to the nearest one that is: fewer
     // token tiles last, then one row tile per matrix, the other wave count,
