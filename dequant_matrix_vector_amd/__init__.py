@@ -15,7 +15,7 @@ __all__ = [
     "FORMATS", "QGemvError", "lib", "packed_bytes", "max_cols", "repack",
     "qgemv", "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_k", "qgemv_i8row", "qgemv_q6_k",
     "swiglu_gate_up", "swiglu_ffn", "qdequant", "layout_version", "set_launch_override",
-    "set_prefill_override", "swiglu_ffn_scratch_elems", "swiglu_ffn_block", "swiglu_ffn_block_scratch_elems",
+    "set_prefill_override", "prefill_plan", "swiglu_ffn_scratch_elems", "swiglu_ffn_block", "swiglu_ffn_block_scratch_elems",
     "qgemv_argmax", "qgemv_head_argmax", "qgemv_q8act", "swiglu_ffn_q8act", "qquantize_q8_0",
     "qgemv_repack_q4_0", "qgemv_repack_q8_0", "qgemv_repack_q4_k", "qgemv_repack_i8row", "qgemv_repack_q6_k",
 ]
@@ -47,6 +47,7 @@ for _n in ("qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_k", "qgemv_i8row", "qgemv_q6_k"
     getattr(lib, _n).argtypes = [_P, _P, _P, _I64, _I64, _I64, _P]
     getattr(lib, _n).restype = _I
 lib.qgemv.argtypes = [_I, _P, _P, _P, _I64, _I64, _I64, _P]
+lib.qgemv_prefill_plan.argtypes = [_I, _I, _I64, _I64, _I64, _I64, _I, _P]
 lib.qgemv.restype = _I
 lib.swiglu_gate_up.argtypes = [_I, _P, _P, _P, _P, _I64, _I64, _I64, _P]
 lib.swiglu_gate_up.restype = _I
@@ -140,6 +141,13 @@ def packed_bytes(fmt, rows, cols) -> int:
 def set_launch_override(lpr=0, r=0, waves=0, depth=2, max_wg=0, cpl=1):
     """Force a GEMV launch shape (tuning); lpr=0 restores the built-in choice."""
     _check(lib.qgemv_set_launch_override(lpr, r, waves, depth, max_wg, cpl), "qgemv_set_launch_override")
+
+
+def prefill_plan(fmt, nmat, rows, cols, n_tok, part_elems=0, cus=256):
+    """(mtr, ntw, waves, run, ksplit): the matrix-core tile and K split of one product (host only)."""
+    plan = (ctypes.c_int * 5)()
+    _check(lib.qgemv_prefill_plan(_fmt(fmt), nmat, rows, cols, n_tok, part_elems, cus, plan), "qgemv_prefill_plan")
+    return tuple(plan)
 
 
 def set_prefill_override(mtr=0, ntw=0, waves=0, run=0, ksplit=0):

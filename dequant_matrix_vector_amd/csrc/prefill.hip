@@ -199,7 +199,7 @@ static int64_t max_ksplit(const PrefillCfg &c, int nmat, int64_t rows, int64_t c
     return ks < by_traffic ? ks : (by_traffic > 1 ? by_traffic : 1);
 }
 
-PrefillCfg choose(int fmt, int nmat, int64_t rows, int64_t cols, int64_t n_tok, int64_t part_elems)
+PrefillCfg choose(int fmt, int nmat, int64_t rows, int64_t cols, int64_t n_tok, int64_t part_elems, int64_t cus)
 {
     PrefillCfg c = g_pf_override;
     const int64_t n_tiles = (n_tok + 15) / 16;
@@ -212,7 +212,6 @@ PrefillCfg choose(int fmt, int nmat, int64_t rows, int64_t cols, int64_t n_tok, 
             const int64_t grid = ((rows + c.waves * 16 - 1) / (c.waves * 16)) * ((n_tok + c.ntw * 16 - 1) / (c.ntw * 16));
             int64_t ks = max_ksplit(c, nmat, rows, cols, n_tok);
             ks = ks < room ? ks : (room > 1 ? room : 1);
-            const int64_t cus = cu_count();
             if (2 * grid * ks >= cus && grid * ks * c.waves >= 4 * cus) break;
             eff = eff >= 8 ? 4 : (eff >= 4 ? 2 : 1);
             default_tile(c, nmat, eff);
@@ -242,7 +241,7 @@ PrefillCfg choose(int fmt, int nmat, int64_t rows, int64_t cols, int64_t n_tok, 
     const int64_t tok_groups = (n_tok + c.ntw * 16 - 1) / (c.ntw * 16);
     int64_t ks = c.ksplit;
     if (ks <= 0) {
-        const int64_t want = 4 * (int64_t)cu_count();
+        const int64_t want = 4 * cus;
         const int64_t base = row_groups * tok_groups;
         ks = base >= want ? 1 : (want + base - 1) / base;
         const int64_t most = max_ksplit(c, nmat, rows, cols, n_tok);
@@ -270,6 +269,24 @@ extern "C" int qgemv_set_prefill_override(int mtr, int ntw, int waves, int run, 
     return QG_OK;
 }
 
+extern "C" int qgemv_prefill_plan(int fmt, int nmat, int64_t rows, int64_t cols, int64_t n_tok, int64_t part_elems,
+                                  int cus, int *plan)
+{
+    if (!plan) return QG_ERR_NULL;
+    if (!prefill_format(fmt)) return QG_ERR_FORMAT;
+    Layout L;
+    if ((nmat != 1 && nmat != 2) || n_tok < 2 || n_tok >= (int64_t(1) << 31) || part_elems < 0 || cus < 1 ||
+        !layout_for(fmt, rows, cols, &L))
+        return QG_ERR_SHAPE;
+    const PrefillCfg c = choose(fmt, nmat, rows, cols, n_tok, part_elems, cus);
+    plan[0] = c.mtr;
+    plan[1] = c.ntw;
+    plan[2] = c.waves;
+    plan[3] = c.run;
+    plan[4] = c.ksplit;
+    return QG_OK;
+}
+
 bool prefill_enabled() { return g_pf_override.mtr >= 0; }
 
 bool prefill_format(int fmt)
@@ -279,7 +296,7 @@ bool prefill_format(int fmt)
 
 int64_t prefill_part_elems(int fmt, int nmat, int64_t rows, int64_t cols, int64_t n_tok)
 {
-    const PrefillCfg c = choose(fmt, nmat, rows, cols, n_tok, INT64_MAX);
+    const PrefillCfg c = choose(fmt, nmat, rows, cols, n_tok, INT64_MAX, cu_count());
     return c.ksplit > 1 ? (int64_t)c.ksplit * nmat * n_tok * rows : 0;
 }
 
@@ -319,7 +336,7 @@ hipError_t launch_prefill(int fmt, int nmat, const uint8_t *w0, const uint8_t *w
     Layout L;
     if (!prefill_format(fmt) || !layout_for(fmt, rows, cols, &L) || n_tok < 1 || n_tok >= (int64_t(1) << 31))
         return hipErrorInvalidValue;
-    const PrefillCfg c = choose(fmt, nmat, rows, cols, n_tok, part ? part_elems : 0);
+    const PrefillCfg c = choose(fmt, nmat, rows, cols, n_tok, part ? part_elems : 0, cu_count());
     PrefillParams p;
     p.q[0] = w0;
     p.q[1] = w1 ? w1 : w0;

@@ -286,6 +286,20 @@ int qgemv_time_next_launch(void *start_event, void *stop_event);
  * qgemv_set_launch_override.  Returns QG_ERR_SHAPE for other values. */
 int qgemv_set_prefill_override(int mtr, int ntw, int waves, int run, int ksplit);
 
+/* The tile and K split the matrix-core path picks for one product (tuning and
+ * tests; host only, no device call): nmat 1 (a qgemv product, or the down
+ * product) or 2 (the gate/up pair); n_tok >= 2; part_elems the floats of
+ * room for partial sums the call gives (0 for qgemv and swiglu_gate_up; the
+ * partial-sum share of the swiglu_ffn scratch otherwise); cus the compute
+ * units to plan for (256 on MI355X).  plan (5 ints, caller-owned) receives
+ * the 16-row tiles per wave and matrix, 16-token tiles per workgroup, waves
+ * per workgroup, 32-weight blocks a lane reads per row and pass, and K
+ * ranges, as the product would launch them (the current
+ * qgemv_set_prefill_override applies).  Returns QG_OK, QG_ERR_NULL (plan),
+ * QG_ERR_FORMAT or QG_ERR_SHAPE; plan is untouched on an error. */
+int qgemv_prefill_plan(int fmt, int nmat, int64_t rows, int64_t cols, int64_t n_tok, int64_t part_elems,
+                       int cus, int *plan);
+
 #ifdef __cplusplus
 }
 #endif

@@ -97,3 +97,53 @@ def test_prefill_override_validation(lib):
         assert f(*bad) == -2, bad
     assert f(2, 8, 4, 2, 0) == 0 and f(1, 2, 8, 4, 3) == 0 and f(1, 1, 8, 1, 0) == 0 and f(-1, 0, 0, 0, 0) == 0
     assert f(0, 0, 0, 0, 0) == 0
+
+
+def test_prefill_plan_pins_the_tile_rules(lib):
+    # host only: the tile and K split the matrix-core path picks, for 256 CUs,
+    # on the shapes its rules were measured on (per-kernel traces at 8, 64
+    # and 128 tokens); room = partial-sum floats the call gives
+    I64 = ctypes.c_int64
+    f = lib.qgemv_prefill_plan
+    f.argtypes = [ctypes.c_int, ctypes.c_int, I64, I64, I64, I64, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    f.restype = ctypes.c_int
+    lib.qgemv_set_prefill_override.argtypes = [ctypes.c_int] * 5
+    assert lib.qgemv_set_prefill_override(0, 0, 0, 0, 0) == 0
+
+    def plan(fmt, nmat, rows, cols, n_tok, room):
+        out = (ctypes.c_int * 5)()
+        assert f(fmt, nmat, rows, cols, n_tok, room, 256, out) == 0
+        return tuple(out)
+
+    big = 1 << 40
+    # 27B-class FFN (swiglu_ffn, K split allowed): the pair and the down product
+    assert plan(0, 2, 17408, 5120, 128, big) == (1, 8, 8, 1, 1)
+    assert plan(0, 1, 5120, 17408, 128, big) == (1, 4, 8, 1, 4)
+    assert plan(0, 2, 17408, 5120, 64, big) == (1, 4, 4, 1, 2)
+    assert plan(0, 2, 17408, 5120, 8, big) == (1, 1, 4, 2, 4)
+    assert plan(0, 1, 5120, 17408, 8, big) == (1, 1, 4, 2, 12)
+    assert plan(3, 1, 2048, 8192, 128, big) == (1, 4, 8, 1, 8)
+    # qgemv (no room): 2048-row products fall back to one token tile, long rows
+    # with runs of four; tall heads keep 8 or 4 token tiles
+    assert plan(4, 1, 2048, 5632, 128, 0) == (1, 1, 4, 4, 1)
+    assert plan(2, 1, 2048, 2048, 128, 0) == (1, 1, 4, 2, 1)
+    assert plan(3, 1, 49152, 2048, 128, 0) == (1, 8, 16, 1, 1)
+    assert plan(4, 1, 32000, 2048, 128, 0) == (1, 4, 8, 1, 1)
+    # the K split never exceeds the room given
+    assert plan(0, 1, 5120, 17408, 8, 2 * 8 * 5120) == (1, 1, 4, 2, 2)
+    # an override is honoured, a shape that is not built runs as the nearest built one
+    assert lib.qgemv_set_prefill_override(2, 8, 16, 4, 1) == 0
+    try:
+        p = plan(0, 2, 17408, 5120, 128, big)
+        assert p[1:] != (8, 16, 4, 1) and p[4] == 1
+    finally:
+        assert lib.qgemv_set_prefill_override(0, 0, 0, 0, 0) == 0
+    # refusals
+    out = (ctypes.c_int * 5)(*([7] * 5))
+    assert f(0, 1, 64, 64, 8, 0, 256, None) == -1
+    assert f(9, 1, 64, 64, 8, 0, 256, out) == -4
+    assert f(0, 3, 64, 64, 8, 0, 256, out) == -2
+    assert f(0, 1, 64, 48, 8, 0, 256, out) == -2
+    assert f(0, 1, 64, 64, 1, 0, 256, out) == -2
+    assert f(0, 1, 64, 64, 8, 0, 0, out) == -2
+    assert tuple(out) == (7,) * 5
