@@ -15,7 +15,7 @@ __all__ = [
     "FORMATS", "QGemvError", "lib", "packed_bytes", "max_cols", "repack",
     "qgemv", "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_k", "qgemv_i8row", "qgemv_q6_k",
     "swiglu_gate_up", "swiglu_ffn", "qdequant", "layout_version", "set_launch_override",
-    "set_prefill_override", "prefill_plan", "swiglu_ffn_scratch_elems", "swiglu_ffn_block", "swiglu_ffn_block_scratch_elems",
+    "set_prefill_override", "set_xs_override", "prefill_plan", "swiglu_ffn_scratch_elems", "swiglu_ffn_block", "swiglu_ffn_block_scratch_elems",
     "qgemv_argmax", "qgemv_head_argmax", "qgemv_q8act", "swiglu_ffn_q8act", "qquantize_q8_0",
     "qgemv_repack_q4_0", "qgemv_repack_q8_0", "qgemv_repack_q4_k", "qgemv_repack_i8row", "qgemv_repack_q6_k",
 ]
@@ -75,6 +75,8 @@ lib.qgemv_set_launch_override.argtypes = [_I, _I, _I, _I, _I, _I]
 lib.qgemv_set_launch_override.restype = _I
 lib.qgemv_set_prefill_override.argtypes = [_I, _I, _I, _I, _I]
 lib.qgemv_set_prefill_override.restype = _I
+lib.qgemv_set_xs_override.argtypes = [_I, _I, _I, _I, _I, _I]
+lib.qgemv_set_xs_override.restype = _I
 lib.qgemv_time_next_launch.argtypes = [_P, _P]
 lib.qgemv_time_next_launch.restype = _I
 
@@ -111,13 +113,42 @@ def _stream(stream):
     return int(stream)
 
 
-def _dev(*ts):
+F32, U8, I8, I32 = torch.float32, torch.uint8, torch.int8, torch.int32
+
+
+def _arg(t, name, dtype, min_numel=0):
+    """Refuse, before any C call, a tensor the kernels would misread: not a
+    torch tensor, not on the GPU, not contiguous, of another element type, or
+    with fewer elements than the call reads or writes."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name}: needs at least {min_numel} elements, has {t.numel()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: tensors must be contiguous")
+
+
+def _on_gpu(*ts):
+    """After every argument's type and size checks: all of them on the GPU."""
     for t in ts:
-        if t is not None and isinstance(t, torch.Tensor):
-            if not t.is_cuda:
-                raise ValueError("tensors must live on the GPU")
-            if not t.is_contiguous():
-                raise ValueError("tensors must be contiguous")
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def _ntok(x, cols, name="x"):
+    """Tokens in an activation tensor x [n_tok][cols] (or [cols]); refuses a
+    size that is not a whole number of rows of cols."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(x).__name__}")
+    if cols < 1 or x.numel() < cols or x.numel() % cols:
+        raise ValueError(f"{name}: {x.numel()} elements is not a whole number of rows of {cols}")
+    return x.numel() // cols
+
+
+def _packed(t, fmt, rows, cols, name="packed"):
+    _arg(t, name, U8, packed_bytes(fmt, rows, cols))
 
 
 def layout_version() -> int:
@@ -143,6 +174,12 @@ def set_launch_override(lpr=0, r=0, waves=0, depth=2, max_wg=0, cpl=1):
     _check(lib.qgemv_set_launch_override(lpr, r, waves, depth, max_wg, cpl), "qgemv_set_launch_override")
 
 
+def set_xs_override(mode=0, rs=0, seg=0, depth=0, nrs=0, order=-1):
+    """Row-streaming one-token kernel: mode 0 built-in, -1 off (lane-group
+    kernels), 1 forced with the given fields (0 / -1 = built-in value)."""
+    _check(lib.qgemv_set_xs_override(mode, rs, seg, depth, nrs, order), "qgemv_set_xs_override")
+
+
 def prefill_plan(fmt, nmat, rows, cols, n_tok, part_elems=0, cus=256):
     """(mtr, ntw, waves, run, ksplit): the matrix-core tile and K split of one product (host only)."""
     plan = (ctypes.c_int * 5)()
@@ -159,28 +196,47 @@ def set_prefill_override(mtr=0, ntw=0, waves=0, run=0, ksplit=0):
 
 
 # ------------------------------------------------------------- repack ------
+
+def _raw_bytes(fmt, rows, cols):
+    """Bytes of the raw blocks of a [rows][cols] tensor (the layouts in qgemv.h)."""
+    f = _fmt(fmt)
+    per = {0: (32, 18), 1: (32, 34), 2: (256, 144), 4: (256, 210), 3: (1, 1)}[f]
+    return rows * (cols // per[0]) * per[1]
+
+
 def qgemv_repack_q4_0(raw, packed, rows, cols, stream=None):
-    _dev(raw, packed)
+    _arg(raw, "raw", U8, _raw_bytes(0, rows, cols))
+    _packed(packed, 0, rows, cols)
+    _on_gpu(raw, packed)
     _check(lib.qgemv_repack_q4_0(_ptr(raw), _ptr(packed), rows, cols, _stream(stream)), "qgemv_repack_q4_0")
 
 
 def qgemv_repack_q8_0(raw, packed, rows, cols, stream=None):
-    _dev(raw, packed)
+    _arg(raw, "raw", U8, _raw_bytes(1, rows, cols))
+    _packed(packed, 1, rows, cols)
+    _on_gpu(raw, packed)
     _check(lib.qgemv_repack_q8_0(_ptr(raw), _ptr(packed), rows, cols, _stream(stream)), "qgemv_repack_q8_0")
 
 
 def qgemv_repack_q4_k(raw, packed, rows, cols, stream=None):
-    _dev(raw, packed)
+    _arg(raw, "raw", U8, _raw_bytes(2, rows, cols))
+    _packed(packed, 2, rows, cols)
+    _on_gpu(raw, packed)
     _check(lib.qgemv_repack_q4_k(_ptr(raw), _ptr(packed), rows, cols, _stream(stream)), "qgemv_repack_q4_k")
 
 
 def qgemv_repack_q6_k(raw, packed, rows, cols, stream=None):
-    _dev(raw, packed)
+    _arg(raw, "raw", U8, _raw_bytes(4, rows, cols))
+    _packed(packed, 4, rows, cols)
+    _on_gpu(raw, packed)
     _check(lib.qgemv_repack_q6_k(_ptr(raw), _ptr(packed), rows, cols, _stream(stream)), "qgemv_repack_q6_k")
 
 
 def qgemv_repack_i8row(q, row_scale, packed, rows, cols, stream=None):
-    _dev(q, row_scale, packed)
+    _arg(q, "q", I8, rows * cols)
+    _arg(row_scale, "row_scale", F32, rows)
+    _packed(packed, 3, rows, cols)
+    _on_gpu(q, row_scale, packed)
     _check(lib.qgemv_repack_i8row(_ptr(q), _ptr(row_scale), _ptr(packed), rows, cols, _stream(stream)),
            "qgemv_repack_i8row")
 
@@ -215,9 +271,12 @@ def _y(y, shape, dev):
 
 def qgemv(fmt, packed, x, rows, cols, y=None, stream=None) -> torch.Tensor:
     """y [n_tok][rows] = W x, x fp32 [n_tok][cols] (or [cols])."""
-    n_tok = x.numel() // cols
+    n_tok = _ntok(x, cols)
     y = _y(y, (rows,) if x.dim() == 1 else (n_tok, rows), x.device)
-    _dev(packed, x, y)
+    _packed(packed, fmt, rows, cols)
+    _arg(x, "x", F32)
+    _arg(y, "y", F32, n_tok * rows)
+    _on_gpu(packed, x, y)
     _check(lib.qgemv(_fmt(fmt), _ptr(packed), _ptr(x), _ptr(y), rows, cols, n_tok, _stream(stream)), "qgemv")
     return y
 
@@ -226,7 +285,10 @@ def _gemv_named(name, fmtid):
     cfn = getattr(lib, name)
 
     def f(packed, x, y, rows, cols, n_tok=1, stream=None):
-        _dev(packed, x, y)
+        _packed(packed, fmtid, rows, cols)
+        _arg(x, "x", F32, n_tok * cols)
+        _arg(y, "y", F32, n_tok * rows)
+        _on_gpu(packed, x, y)
         _check(cfn(_ptr(packed), _ptr(x), _ptr(y), rows, cols, n_tok, _stream(stream)), name)
         return y
     f.__name__ = name
@@ -242,12 +304,25 @@ qgemv_q6_k = _gemv_named("qgemv_q6_k", 4)
 
 
 def swiglu_gate_up(fmt, wg, wu, x, d_model, ffn, h=None, stream=None) -> torch.Tensor:
-    n_tok = x.numel() // d_model
+    n_tok = _ntok(x, d_model)
     h = _y(h, (n_tok, ffn), x.device)
-    _dev(wg, wu, x, h)
+    _packed(wg, fmt, ffn, d_model, "wg")
+    _packed(wu, fmt, ffn, d_model, "wu")
+    _arg(x, "x", F32)
+    _arg(h, "h", F32, n_tok * ffn)
+    _on_gpu(wg, wu, x, h)
     _check(lib.swiglu_gate_up(_fmt(fmt), _ptr(wg), _ptr(wu), _ptr(x), _ptr(h), d_model, ffn, n_tok,
                               _stream(stream)), "swiglu_gate_up")
     return h
+
+
+def _ffn_args(fmt, wg, wu, wd, x, out, h_scratch, d_model, ffn, n_tok):
+    _packed(wg, fmt, ffn, d_model, "wg")
+    _packed(wu, fmt, ffn, d_model, "wu")
+    _packed(wd, fmt, d_model, ffn, "wd")
+    _arg(x, "x", F32)
+    _arg(out, "out", F32, n_tok * d_model)
+    _arg(h_scratch, "h_scratch", F32, n_tok * ffn)
 
 
 def swiglu_ffn_scratch_elems(fmt, d_model, ffn, n_tok) -> int:
@@ -259,12 +334,13 @@ def swiglu_ffn_scratch_elems(fmt, d_model, ffn, n_tok) -> int:
 def swiglu_ffn(fmt, wg, wu, wd, x, d_model, ffn, out=None, h_scratch=None, stream=None):
     """(out, h): out [n_tok][d_model] = Wd (silu(Wg x) * (Wu x)); h [n_tok][ffn]
     is a view of the scratch (allocated at swiglu_ffn_scratch_elems if None)."""
-    n_tok = x.numel() // d_model
+    n_tok = _ntok(x, d_model)
     out = _y(out, (n_tok, d_model), x.device)
     if h_scratch is None:
         h_scratch = torch.empty(swiglu_ffn_scratch_elems(fmt, d_model, ffn, n_tok), dtype=torch.float32,
                                 device=x.device)
-    _dev(wg, wu, wd, x, out, h_scratch)
+    _ffn_args(fmt, wg, wu, wd, x, out, h_scratch, d_model, ffn, n_tok)
+    _on_gpu(wg, wu, wd, x, out, h_scratch)
     _check(lib.swiglu_ffn(_fmt(fmt), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(x), _ptr(out), _ptr(h_scratch),
                           h_scratch.numel(), d_model, ffn, n_tok, _stream(stream)), "swiglu_ffn")
     return out, h_scratch.view(-1)[:n_tok * ffn].view(n_tok, ffn)
@@ -272,9 +348,12 @@ def swiglu_ffn(fmt, wg, wu, wd, x, d_model, ffn, out=None, h_scratch=None, strea
 
 def qgemv_q8act(fmt, packed, x, rows, cols, y=None, stream=None) -> torch.Tensor:
     """y [n_tok][rows] = W xq, xq the Q8_0 representation of x (Q4_0, Q8_0 weights)."""
-    n_tok = x.numel() // cols
+    n_tok = _ntok(x, cols)
     y = _y(y, (rows,) if x.dim() == 1 else (n_tok, rows), x.device)
-    _dev(packed, x, y)
+    _packed(packed, fmt, rows, cols)
+    _arg(x, "x", F32)
+    _arg(y, "y", F32, n_tok * rows)
+    _on_gpu(packed, x, y)
     _check(lib.qgemv_q8act(_fmt(fmt), _ptr(packed), _ptr(x), _ptr(y), rows, cols, n_tok, _stream(stream)),
            "qgemv_q8act")
     return y
@@ -282,11 +361,12 @@ def qgemv_q8act(fmt, packed, x, rows, cols, y=None, stream=None) -> torch.Tensor
 
 def swiglu_ffn_q8act(fmt, wg, wu, wd, x, d_model, ffn, out=None, h_scratch=None, stream=None):
     """(out, h): the SwiGLU FFN with x and h quantized to Q8_0 before their products."""
-    n_tok = x.numel() // d_model
+    n_tok = _ntok(x, d_model)
     out = _y(out, (n_tok, d_model), x.device)
     if h_scratch is None:
         h_scratch = torch.empty(n_tok * ffn, dtype=torch.float32, device=x.device)
-    _dev(wg, wu, wd, x, out, h_scratch)
+    _ffn_args(fmt, wg, wu, wd, x, out, h_scratch, d_model, ffn, n_tok)
+    _on_gpu(wg, wu, wd, x, out, h_scratch)
     _check(lib.swiglu_ffn_q8act(_fmt(fmt), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(x), _ptr(out), _ptr(h_scratch),
                                 h_scratch.numel(), d_model, ffn, n_tok, _stream(stream)), "swiglu_ffn_q8act")
     return out, h_scratch.view(-1)[:n_tok * ffn].view(n_tok, ffn)
@@ -294,17 +374,21 @@ def swiglu_ffn_q8act(fmt, wg, wu, wd, x, d_model, ffn, out=None, h_scratch=None,
 
 def qquantize_q8_0(x, n, blocks=None, stream=None) -> torch.Tensor:
     """Raw Q8_0 blocks (uint8 [n_tok][n/32 * 34]) of activation rows x [n_tok][n]."""
-    n_tok = x.numel() // n
+    n_tok = _ntok(x, n)
     if blocks is None:
         blocks = torch.empty((n_tok, n // 32 * 34), dtype=torch.uint8, device=x.device)
-    _dev(x, blocks)
+    _arg(x, "x", F32)
+    _arg(blocks, "blocks", U8, n_tok * (n // 32) * 34)
+    _on_gpu(x, blocks)
     _check(lib.qquantize_q8_0(_ptr(x), _ptr(blocks), n, n_tok, _stream(stream)), "qquantize_q8_0")
     return blocks
 
 
 def qdequant(fmt, packed, rows, cols, w_out=None, stream=None) -> torch.Tensor:
+    _packed(packed, fmt, rows, cols)
     w_out = _y(w_out, (rows, cols), packed.device)
-    _dev(packed, w_out)
+    _arg(w_out, "w_out", F32, rows * cols)
+    _on_gpu(packed, w_out)
     _check(lib.qdequant(_fmt(fmt), _ptr(packed), _ptr(w_out), rows, cols, _stream(stream)), "qdequant")
     return w_out
 
@@ -319,12 +403,14 @@ def swiglu_ffn_block(fmt, wg, wu, wd, gamma, eps, x, d_model, ffn, out=None, h_s
     """(out, h): out = x + Wd (silu(Wg xn) * (Wu xn)), xn = rmsnorm(x) * gamma; out may be x
     (in place).  h [n_tok][ffn] is a view of the scratch (allocated at
     swiglu_ffn_block_scratch_elems if None)."""
-    n_tok = x.numel() // d_model
+    n_tok = _ntok(x, d_model)
     out = _y(out, (n_tok, d_model), x.device)
     if h_scratch is None:
         h_scratch = torch.empty(swiglu_ffn_block_scratch_elems(fmt, d_model, ffn, n_tok), dtype=torch.float32,
                                 device=x.device)
-    _dev(wg, wu, wd, gamma, x, out, h_scratch)
+    _ffn_args(fmt, wg, wu, wd, x, out, h_scratch, d_model, ffn, n_tok)
+    _arg(gamma, "gamma", F32, d_model)
+    _on_gpu(wg, wu, wd, gamma, x, out, h_scratch)
     _check(lib.swiglu_ffn_block(_fmt(fmt), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(gamma), float(eps), _ptr(x), _ptr(out),
                                 _ptr(h_scratch), h_scratch.numel(), d_model, ffn, n_tok, _stream(stream)),
            "swiglu_ffn_block")
@@ -333,21 +419,27 @@ def swiglu_ffn_block(fmt, wg, wu, wd, gamma, eps, x, d_model, ffn, out=None, h_s
 
 def qgemv_argmax(logits, n, token=None, stream=None) -> torch.Tensor:
     """int32 [n_tok]: first index of the largest logit of each row of logits [n_tok][n]."""
-    n_tok = logits.numel() // n
+    n_tok = _ntok(logits, n, "logits")
     if token is None:
         token = torch.empty(n_tok, dtype=torch.int32, device=logits.device)
-    _dev(logits, token)
+    _arg(logits, "logits", F32)
+    _arg(token, "token", I32, n_tok)
+    _on_gpu(logits, token)
     _check(lib.qgemv_argmax(_ptr(logits), _ptr(token), n, n_tok, _stream(stream)), "qgemv_argmax")
     return token
 
 
 def qgemv_head_argmax(fmt, packed, x, rows, cols, logits=None, token=None, stream=None):
     """(token int32 [n_tok], logits [n_tok][rows]): the head product then greedy sampling."""
-    n_tok = x.numel() // cols
+    n_tok = _ntok(x, cols)
     logits = _y(logits, (n_tok, rows), x.device)
     if token is None:
         token = torch.empty(n_tok, dtype=torch.int32, device=x.device)
-    _dev(packed, x, logits, token)
+    _packed(packed, fmt, rows, cols)
+    _arg(x, "x", F32)
+    _arg(logits, "logits", F32, n_tok * rows)
+    _arg(token, "token", I32, n_tok)
+    _on_gpu(packed, x, logits, token)
     _check(lib.qgemv_head_argmax(_fmt(fmt), _ptr(packed), _ptr(x), _ptr(logits), _ptr(token), rows, cols, n_tok,
                                  _stream(stream)), "qgemv_head_argmax")
     return token, logits

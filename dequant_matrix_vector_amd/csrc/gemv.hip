@@ -2,6 +2,7 @@
 // The kernels themselves are in gemv_impl.h (instantiated per format in
 // gemv_<format>.hip).
 #include "gemv_impl.h"
+#include "gemv_xs.h"
 
 namespace qg {
 
@@ -35,7 +36,8 @@ hipError_t dispatch_fmt(int fmt, const GemvParams &p, const GemvCfg &c, hipStrea
     return hipErrorInvalidValue;
 }
 
-GemvCfg g_override = {0, 0, 0, 0, 0, 0};
+// tuning override of the calling thread (qgemv_set_launch_override)
+thread_local GemvCfg g_override = {0, 0, 0, 0, 0, 0};
 
 // CPL must divide the row's chunk count: a group of CPL f16 scales is read
 // with one 2*CPL-byte load, which needs the row's scale run (nchunk * 2
@@ -188,6 +190,10 @@ hipError_t launch_gemv(int fmt, const uint8_t *packed, const float *x, float *y,
 {
     Layout L;
     if (!layout_for(fmt & ~kQ8Act, rows, cols, &L)) return hipErrorInvalidValue;
+    GemvCfg forced;
+    XsCfg xc;
+    if (!launch_override(&forced) && xs_choose(fmt, rows, cols, 1, false, &xc))
+        return launch_xs(fmt, 1, packed, nullptr, x, y, rows, cols, xc, s, nullptr, 0.0f, resid);
     GemvParams p;
     p.q[0] = packed;
     p.q[1] = packed;
@@ -211,6 +217,10 @@ hipError_t launch_gate_up(int fmt, const uint8_t *wg, const uint8_t *wu, const f
 {
     Layout L;
     if (!layout_for(fmt & ~kQ8Act, ffn, d_model, &L)) return hipErrorInvalidValue;
+    GemvCfg forced;
+    XsCfg xc;
+    if (!launch_override(&forced) && xs_choose(fmt, ffn, d_model, 2, gamma != nullptr, &xc))
+        return launch_xs(fmt, 2, wg, wu, x, h, ffn, d_model, xc, s, gamma, eps, nullptr);
     GemvParams p;
     p.q[0] = wg;
     p.q[1] = wu;

@@ -1,0 +1,348 @@
+// Row-streaming GEMV for one token, the activation held in registers.
+//
+// y = W x with W block-quantized, one token (llmoxide blog, section 11
+// "Prefill and decode": every weight is streamed once for one multiply-add, so
+// the product runs at the speed the weight bytes arrive; section 10 "Loading
+// weights": each dot product decodes its row's blocks on the fly).
+//
+// Work decomposition ("x-stationary"):
+//   * A lane owns one 32-weight chunk position c of the rows (a Q4_0 block).
+//     The workgroup stages x once in LDS (coalesced loads issued before the
+//     weight stream, chunks 144 bytes apart so that lanes reading consecutive
+//     chunks use different banks); each lane then reads its chunk once and
+//     keeps it in registers pre-scaled for the
+//     binary16-subnormal decode (2^24 for the low nibbles, 2^20 for the high
+//     ones) together with its sum in the decode order (the Q4_0 offset of 8
+//     folds in through it, and all-8 codes cancel exactly), and then streams
+//     chunk c of row after row.
+//   * The lanes of a row are 32-lane segments: lprow = 32 * segments >= the
+//     chunks of a row (spare lanes read a valid chunk and contribute 0).  A
+//     workgroup of rs * lprow threads covers rs rows per row-step (row
+//     phases), so each load instruction of a wave reads whole 512-byte or
+//     1 KB runs of consecutive chunks of one or two rows.
+//   * A workgroup owns nrs row-steps of rs rows: consecutive ones, or every
+//     grid-th one so that all workgroups sweep one band of rows together (the
+//     order a plain streaming read is fastest in).  Each lane keeps D row-steps
+//     of weight loads in flight in a register ring whose refills are issued
+//     as soon as a slot is consumed, across row boundaries (no per-row
+//     prologue or drain).
+//   * After every D row-steps the lane has D * NMAT chunk products; a
+//     butterfly over the 32 lanes of the segment (DPP and one swizzle, no
+//     atomics) leaves one full segment sum per lane, written to LDS.  After
+//     the last row-step one barrier, then one thread per row adds its
+//     segments' sums in segment order (deterministic) and applies the
+//     epilogue: silu(g) * u for the gate/up pair (NMAT 2), the RMSNorm scale
+//     (EPI 1) or the residual (EPI 2).
+//
+// Compared with the lane-group kernel (gemv_impl.h) this stages nothing in
+// LDS before streaming (a workgroup of the 27B-class down product would
+// otherwise read all 68 KB of its input first), reads x once per lane instead
+// of once per chunk from LDS, and keeps the weight ring running through rows.
+#pragma once
+#include "gemv_impl.h"
+
+namespace qg {
+namespace xs_detail {
+
+using gemv_detail::dot_q4_chunk;
+using gemv_detail::half_lo;
+using gemv_detail::silu_mul;
+using gemv_detail::f32x4;
+
+struct XsParams {
+    const uint8_t *q[2];  // packed tensors (quant plane at offset 0)
+    const float *x;       // [cols]
+    float *y;             // [rows]
+    const float *gamma;   // EPI 1: RMSNorm gain [cols]
+    const float *resid;   // EPI 2: residual [rows] (may be y itself)
+    float eps;            // EPI 1
+    int rows;
+    int nchunk;           // cols / 32
+    uint32_t row_qbytes;  // quant-plane bytes per row
+    uint32_t soff;        // scale-plane offset
+    int lprow;            // lanes per row: 32 * segments >= nchunk
+    int rs;               // rows per row-step
+    int nrs;              // row-steps per workgroup (a multiple of D)
+    int ga, gb;           // global row-step of local step i in workgroup b: i * ga + b * gb
+                          // (ga = 1, gb = nrs: consecutive steps; ga = grid, gb = 1: round robin)
+};
+
+enum { kEpiPlain = 0, kEpiNorm = 1, kEpiResid = 2 };
+
+// One row-step of one matrix in flight: the lane's 16 code bytes and f16 scale.
+struct Slot {
+    uint4 q;
+    uint32_t d;
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Partner value across lane bit k of a 32-lane segment: quad permutations for
+// bits 0 and 1, the 8- and 16-lane mirrors for bits 2 and 3 (each pairs every
+// lane with one whose bit k differs), a swizzle for bit 4.
+template <int K>
+__device__ __forceinline__ float partner(float v)
+{
+    if constexpr (K == 0) return dpp<0xB1>(v);        // quad_perm [1,0,3,2]
+    else if constexpr (K == 1) return dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    else if constexpr (K == 2) return dpp<0x141>(v);  // row_half_mirror
+    else if constexpr (K == 3) return dpp<0x140>(v);  // row_mirror
+    else return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));   // xor 16
+}
+
+// Lane bit taken by step S of the butterfly.  The mirrors pair lanes whose
+// lower bits differ, so they come first, while every lane still holds every
+// value; each later step pairs lanes that agree on the bits already split on.
+__device__ __host__ constexpr int bfly_bit(int S) { return S < 4 ? 3 - S : 4; }
+
+// Butterfly over the 32 lanes of a segment: v[0..V) in every lane -> each lane
+// holds one complete segment sum, of the value seg_index<V>(lane).
+template <int V, int S = 0>
+__device__ __forceinline__ float seg_reduce(float (&v)[V], int lane)
+{
+    if constexpr (S == 5) {
+        return v[0];
+    } else {
+        constexpr int K = bfly_bit(S);
+        if constexpr ((1 << S) < V) {
+            constexpr int H = V >> (S + 1);   // values left after this step
+            const bool up = (lane >> K) & 1;
+#pragma unroll
+            for (int i = 0; i < H; i++) {
+                const float send = up ? v[i] : v[i + H];
+                const float keep = up ? v[i + H] : v[i];
+                v[i] = keep + partner<K>(send);
+            }
+        } else {
+            v[0] += partner<K>(v[0]);
+        }
+        return seg_reduce<V, S + 1>(v, lane);
+    }
+}
+
+// The value a lane holds after seg_reduce, and whether it is the lane of its
+// segment that writes it (the lane whose bits not split on are zero).
+template <int V>
+__device__ __forceinline__ int seg_index(int lane)
+{
+    int idx = 0;
+#pragma unroll
+    for (int s = 0; (1 << s) < V; s++) idx += ((lane >> bfly_bit(s)) & 1) * (V >> (s + 1));
+    return idx;
+}
+template <int V>
+__device__ __forceinline__ bool seg_writer(int lane)
+{
+    int split = 0;
+#pragma unroll
+    for (int s = 0; (1 << s) < V; s++) split |= 1 << bfly_bit(s);
+    return (lane & 31 & ~split) == 0;
+}
+
+// x chunk -> pre-scaled registers; returns the chunk sum in the order
+// dot_q4_chunk adds the codes (so that sum (q - 8) x of all-8 codes is 0).
+__device__ __forceinline__ float prep_q4(float4 (&v)[8])
+{
+    float sum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        sum = sum + v[k].x;
+        sum = sum + v[k].z;
+        sum = sum + v[4 + k].x;
+        sum = sum + v[4 + k].z;
+        sum = sum + v[k].y;
+        sum = sum + v[k].w;
+        sum = sum + v[4 + k].y;
+        sum = sum + v[4 + k].w;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const float sc = k < 4 ? 0x1p24f : 0x1p20f;
+        v[k].x *= sc;
+        v[k].y *= sc;
+        v[k].z *= sc;
+        v[k].w *= sc;
+    }
+    return sum;
+}
+
+template <int FMT, int NMAT, int EPI, int D>
+__global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
+{
+    static_assert(FMT == QG_Q4_0, "x-stationary GEMV: Q4_0");
+    constexpr int V = D * NMAT;   // chunk products per lane between reductions
+    static_assert(V >= 2 && V <= 32 && (V & (V - 1)) == 0, "power-of-two batch");
+    extern __shared__ float4 xs_lds4[];
+    float *xs_part = reinterpret_cast<float *>(xs_lds4);
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int phase = t / p.lprow;
+    const int craw = t - phase * p.lprow;
+    const bool live = craw < p.nchunk;
+    const int c = live ? craw : p.nchunk - 1;   // spare lanes read a valid chunk, contribute 0
+    const int seg = t >> 5;
+    const int nseg = p.lprow >> 5;
+    const int row0 = blockIdx.x * p.gb * p.rs + phase;   // row of local step i: row0 + i * ga * rs
+    const int rstep = p.ga * p.rs;
+    const int last = p.rows - 1;
+
+    // LDS: x staged [nchunk + 1][36] (chunks 144 bytes apart, so the lanes' 16-byte
+    // reads of consecutive chunks fall in different banks), then (EPI 1) the
+    // gain the same way and one sum of squares per chunk, then the partial row
+    // sums [segments][nrs][NMAT]
+    float *xsx = xs_part;
+    float *xsg = xsx + (p.nchunk + 1) * kXStride;   // each staging area has a spare chunk slot
+    float *sq = xsg + (EPI == kEpiNorm ? (p.nchunk + 1) * kXStride : 0);
+    float *part = sq + (EPI == kEpiNorm ? p.nchunk : 0);
+
+    // x (and the gain) in 16-byte pieces, consecutive threads reading
+    // consecutive pieces, at most 8 per thread (threads >= chunks); issued
+    // before the weight stream so that waiting for them waits for nothing else
+    const int npiece = p.nchunk * 8;
+    float4 xp[8], gp[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        int j = t + k * (int)blockDim.x;
+        j = j < npiece ? j : npiece - 1;
+        xp[k] = reinterpret_cast<const float4 *>(p.x)[j];
+        if constexpr (EPI == kEpiNorm) gp[k] = reinterpret_cast<const float4 *>(p.gamma)[j];
+    }
+
+    Slot st[D][NMAT];
+    const uint32_t qcol = (uint32_t)c * 16u, scol = p.soff + (uint32_t)c * 2u;
+    auto load_step = [&](int s, int i) {
+        int row = row0 + i * rstep;
+        row = row < last ? row : last;
+        const uint32_t qo = __umul24((uint32_t)row, p.row_qbytes) + qcol;
+        const uint32_t so = __umul24((uint32_t)row, (uint32_t)p.nchunk) * 2u + scol;
+#pragma unroll
+        for (int m = 0; m < NMAT; m++) {
+            st[s][m].q = *reinterpret_cast<const uint4 *>(p.q[m] + qo);
+            st[s][m].d = *reinterpret_cast<const uint16_t *>(p.q[m] + so);
+        }
+    };
+#pragma unroll
+    for (int s = 0; s < D; s++) load_step(s, s);   // nrs >= D
+    __builtin_amdgcn_sched_barrier(0);
+
+    // branch-free (a divergent branch here would make the compiler wait for
+    // the weight stream too, and keep the pieces in scratch): a piece past the
+    // end goes to the spare slot after the last chunk
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const int j = t + k * (int)blockDim.x;
+        const int at = j < npiece ? (j >> 3) * kXStride + (j & 7) * 4 : p.nchunk * kXStride;
+        *reinterpret_cast<f32x4 *>(xsx + at) = f32x4{xp[k].x, xp[k].y, xp[k].z, xp[k].w};
+        if constexpr (EPI == kEpiNorm)
+            *reinterpret_cast<f32x4 *>(xsg + at) = f32x4{gp[k].x, gp[k].y, gp[k].z, gp[k].w};
+    }
+    __syncthreads();
+    float4 xv[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) xv[k] = *reinterpret_cast<const float4 *>(xsx + c * kXStride + k * 4);
+
+    float ss = 0.0f;   // EPI 1: this chunk's sum of x^2 (raw x, column order)
+    if constexpr (EPI == kEpiNorm) {
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            ss = __builtin_fmaf(xv[k].x, xv[k].x, ss);
+            ss = __builtin_fmaf(xv[k].y, xv[k].y, ss);
+            ss = __builtin_fmaf(xv[k].z, xv[k].z, ss);
+            ss = __builtin_fmaf(xv[k].w, xv[k].w, ss);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const float4 g = *reinterpret_cast<const float4 *>(xsg + c * kXStride + k * 4);
+            xv[k].x *= g.x;
+            xv[k].y *= g.y;
+            xv[k].z *= g.z;
+            xv[k].w *= g.w;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        xv[k].x = live ? xv[k].x : 0.0f;
+        xv[k].y = live ? xv[k].y : 0.0f;
+        xv[k].z = live ? xv[k].z : 0.0f;
+        xv[k].w = live ? xv[k].w : 0.0f;
+    }
+    const float xsum = prep_q4(xv);
+
+    float norm_scale = 1.0f;
+    if constexpr (EPI == kEpiNorm) {
+        // every workgroup adds the same per-chunk sums in chunk order: one scale
+        if (phase == 0 && live) sq[c] = ss;
+        __syncthreads();
+        float tot = 0.0f;
+        for (int k = 0; k < p.nchunk; k++) tot += sq[k];
+        norm_scale = 1.0f / sqrtf(tot / (float)(p.nchunk * kChunk) + p.eps);
+    }
+
+    const bool writer = seg_writer<V>(lane);
+    const int widx = seg_index<V>(lane);
+    for (int i0 = 0; i0 < p.nrs; i0 += D) {
+        float v[V];
+#pragma unroll
+        for (int s = 0; s < D; s++) {
+#pragma unroll
+            for (int m = 0; m < NMAT; m++) {
+                const float tq = dot_q4_chunk(st[s][m].q, xv);
+                const float u = __builtin_fmaf(-8.0f, xsum, tq);   // sum (q - 8) x
+                v[s * NMAT + m] = live ? half_lo(st[s][m].d) * u : 0.0f;   // spare lanes: exactly 0
+            }
+            const int nxt = i0 + s + D;
+            load_step(s, nxt < p.nrs ? nxt : p.nrs - 1);
+            // keep the refill here, right after its slot is consumed
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const float r = seg_reduce<V>(v, lane);
+        if (writer) part[(seg * p.nrs + i0) * NMAT + widx] = r;   // widx = step * NMAT + matrix
+    }
+    __syncthreads();
+
+    // one thread per row: the row phase's segments in order
+    for (int j = t; j < p.rs * p.nrs; j += blockDim.x) {
+        const int ph = j % p.rs, i = j / p.rs;
+        const int row = blockIdx.x * p.gb * p.rs + i * rstep + ph;
+        if (row > last) continue;
+        float a[NMAT];
+#pragma unroll
+        for (int m = 0; m < NMAT; m++) a[m] = 0.0f;
+        for (int sg = ph * nseg; sg < (ph + 1) * nseg; sg++) {
+#pragma unroll
+            for (int m = 0; m < NMAT; m++) a[m] += part[(sg * p.nrs + i) * NMAT + m];
+        }
+        if constexpr (EPI == kEpiNorm) {
+#pragma unroll
+            for (int m = 0; m < NMAT; m++) a[m] *= norm_scale;
+        }
+        if constexpr (EPI == kEpiResid) a[0] += p.resid[row];
+        if constexpr (NMAT == 1) p.y[row] = a[0];
+        else p.y[row] = silu_mul(a[0], a[NMAT - 1]);
+    }
+}
+
+} // namespace xs_detail
+
+// Launch configuration of the x-stationary kernel.
+struct XsCfg {
+    int rs;     // rows per row-step (row phases)
+    int seg;    // 32-lane segments per row (>= chunks / 32)
+    int depth;  // row-steps in flight per lane (ring depth, also the reduction batch)
+    int nrs;    // row-steps per workgroup
+    int rr;     // 1: row-steps dealt to workgroups round robin; 0: consecutive
+};
+
+// Host side (gemv_xs.hip): the configuration for a shape, or false when the
+// x-stationary kernel does not take it.
+bool xs_choose(int fmt, int64_t rows, int64_t cols, int nmat, bool norm, XsCfg *c);
+hipError_t launch_xs(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, const float *x, float *y,
+                     int64_t rows, int64_t cols, const XsCfg &c, hipStream_t s, const float *gamma, float eps,
+                     const float *resid);
+
+} // namespace qg

@@ -1,0 +1,177 @@
+// Host side of the x-stationary GEMV (gemv_xs.h): which shapes it takes, its
+// launch configuration and the per-variant dispatch.
+#include <atomic>
+
+#include "gemv_xs.h"
+
+namespace qg {
+
+using xs_detail::XsParams;
+
+namespace {
+
+// tuning override of the calling thread (qgemv_set_xs_override): mode 0 =
+// built-in, -1 = never take the x-stationary kernel, 1 = take it with the
+// fields below (0 = built-in value)
+thread_local int g_xs_mode = 0;
+thread_local XsCfg g_xs_force = {0, 0, 0, 0, -1};
+
+template <int FMT, int NMAT, int EPI, int D>
+hipError_t go(const XsParams &p, int waves, int64_t nwg, size_t lds, hipStream_t s)
+{
+    auto kern = xs_detail::gemv_xs_kernel<FMT, NMAT, EPI, D>;
+    if (lds > 65536) {
+        static std::atomic<int> configured[64];
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+        if ((int)lds > configured[dev].load(std::memory_order_relaxed)) {
+            hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            configured[dev].store((int)lds, std::memory_order_relaxed);
+        }
+    }
+    hipEvent_t t0 = nullptr, t1 = nullptr;
+    if (take_launch_timing(&t0, &t1)) {
+        XsParams arg = p;
+        void *args[] = {&arg};
+        return hipExtLaunchKernel((const void *)kern, dim3((unsigned)nwg), dim3(64 * waves), args, lds, s, t0, t1, 0);
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(64 * waves), lds, s, p);
+    return hipGetLastError();
+}
+
+template <int FMT, int NMAT, int EPI>
+hipError_t by_depth(const XsParams &p, int depth, int waves, int64_t nwg, size_t lds, hipStream_t s)
+{
+    switch (depth) {
+    case 2: return go<FMT, NMAT, EPI, 2>(p, waves, nwg, lds, s);
+    case 4: return go<FMT, NMAT, EPI, 4>(p, waves, nwg, lds, s);
+    case 8:
+        if constexpr (NMAT == 1) return go<FMT, NMAT, EPI, 8>(p, waves, nwg, lds, s);
+        break;
+    }
+    return hipErrorInvalidValue;
+}
+
+// LDS of a workgroup: the partial row sums of every segment, plus (normalized
+// input) one sum of squares per chunk.
+size_t xs_lds_bytes(const XsCfg &c, int nmat, int64_t nchunk, bool norm)
+{
+    const size_t staged = (size_t)(nchunk + 1) * kXStride * (norm ? 2 : 1) + (norm ? (size_t)nchunk : 0);
+    return (staged + (size_t)c.rs * c.seg * c.nrs * nmat) * sizeof(float);
+}
+
+// a workgroup's LDS may use all of a CU's 160 KB (x of a row of 1024 chunks
+// alone takes 144 KB; with the gain staged too, rows of up to 540 chunks fit)
+constexpr size_t kXsMaxLds = 160 * 1024;
+
+bool valid_cfg(const XsCfg &c, int nmat, int64_t nchunk, bool norm)
+{
+    if (c.rs < 1 || c.rs > 8 || (c.rs & (c.rs - 1))) return false;
+    if (c.seg * 32 < nchunk || c.seg > 32) return false;
+    if ((c.rs * c.seg) % 2 || c.rs * c.seg / 2 > 16) return false;
+    if (!(c.depth == 2 || c.depth == 4 || (c.depth == 8 && nmat == 1))) return false;
+    return c.nrs >= c.depth && c.nrs % c.depth == 0 && xs_lds_bytes(c, nmat, nchunk, norm) <= kXsMaxLds;
+}
+
+} // namespace
+
+extern "C" int qgemv_set_xs_override(int mode, int rs, int seg, int depth, int nrs, int order)
+{
+    if (mode == 0 || mode == -1) {
+        g_xs_mode = mode;
+        g_xs_force = {0, 0, 0, 0, -1};
+        return QG_OK;
+    }
+    if (mode != 1 || rs < 0 || seg < 0 || depth < 0 || nrs < 0 || order < -1 || order > 1) return QG_ERR_SHAPE;
+    g_xs_mode = 1;
+    g_xs_force = {rs, seg, depth, nrs, order};
+    return QG_OK;
+}
+
+// The shapes the kernel takes: Q4_0, a row of at most 1024 chunks (32
+// segments), offsets inside one packed tensor below 2^32 and rows below 2^24
+// (24-bit multiplies form the addresses).
+bool xs_choose(int fmt, int64_t rows, int64_t cols, int nmat, bool norm, XsCfg *out)
+{
+    if (g_xs_mode < 0 || fmt != QG_Q4_0) return false;
+    Layout L;
+    if (!layout_for(fmt, rows, cols, &L) || L.total >= (int64_t(1) << 32) || rows >= (1 << 24) ||
+        L.row_qbytes >= (1 << 24))
+        return false;
+    const int64_t nchunk = cols / kChunk;
+    const int seg0 = (int)((nchunk + 31) / 32);
+    if (seg0 > 32) return false;
+    // The built-in choice: rows per row-step and segments (padded by one when
+    // needed) for a whole number of waves, at most 16; ring depth 4; row-steps
+    // per workgroup for about three workgroups per CU (pair) or one (single
+    // matrix, whose workgroups are wider).
+    XsCfg c = {0, 0, 0, 0, 1};
+    for (int rs : {2, 1, 4, 8}) {
+        for (int seg : {seg0, seg0 + 1}) {
+            if ((rs * seg) % 2 == 0 && rs * seg / 2 <= 16 && rs * seg / 2 >= 2 && c.rs == 0) {
+                c.rs = rs;
+                c.seg = seg;
+            }
+        }
+    }
+    if (c.rs == 0) return false;
+    c.depth = 4;
+    const int64_t steps = (rows + c.rs - 1) / c.rs;
+    const int64_t want_wg = (int64_t)cu_count() * (nmat == 2 ? 3 : 1);
+    int64_t nrs = (steps + want_wg - 1) / want_wg;
+    nrs = (nrs + c.depth - 1) / c.depth * c.depth;
+    // tall matrices: more workgroups rather than more LDS per workgroup
+    const int64_t room = (int64_t)(kXsMaxLds / sizeof(float)) - (nchunk + 1) * (norm ? 2 * kXStride + 1 : kXStride);
+    const int64_t cap = room / ((int64_t)c.rs * c.seg * nmat) / c.depth * c.depth;
+    if (nrs > cap) nrs = cap;
+    c.nrs = (int)(nrs < c.depth ? c.depth : nrs);
+    if (g_xs_mode == 1) {
+        if (g_xs_force.rs) c.rs = g_xs_force.rs;
+        if (g_xs_force.seg) c.seg = g_xs_force.seg;
+        if (g_xs_force.depth) c.depth = g_xs_force.depth;
+        if (g_xs_force.nrs) c.nrs = g_xs_force.nrs;
+        if (g_xs_force.rr >= 0) c.rr = g_xs_force.rr;
+    }
+    if (!valid_cfg(c, nmat, nchunk, norm)) return false;
+    *out = c;
+    return true;
+}
+
+hipError_t launch_xs(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, const float *x, float *y,
+                     int64_t rows, int64_t cols, const XsCfg &c, hipStream_t s, const float *gamma, float eps,
+                     const float *resid)
+{
+    Layout L;
+    if (!layout_for(fmt, rows, cols, &L)) return hipErrorInvalidValue;
+    XsParams p;
+    p.q[0] = w0;
+    p.q[1] = nmat == 2 ? w1 : w0;
+    p.x = x;
+    p.y = y;
+    p.gamma = gamma;
+    p.resid = resid;
+    p.eps = eps;
+    p.rows = (int)rows;
+    p.nchunk = (int)(cols / kChunk);
+    p.row_qbytes = (uint32_t)L.row_qbytes;
+    p.soff = (uint32_t)L.splane_off;
+    p.lprow = 32 * c.seg;
+    p.rs = c.rs;
+    p.nrs = c.nrs;
+    const int waves = c.rs * c.seg / 2;
+    const int64_t nwg = ((rows + c.rs - 1) / c.rs + c.nrs - 1) / c.nrs;
+    p.ga = c.rr ? (int)nwg : 1;
+    p.gb = c.rr ? 1 : c.nrs;
+    const size_t lds = xs_lds_bytes(c, nmat, p.nchunk, gamma != nullptr);
+    const int epi = nmat == 2 ? (gamma ? 1 : 0) : (resid ? 2 : 0);
+    if (fmt != QG_Q4_0) return hipErrorInvalidValue;
+    if (nmat == 1) {
+        if (epi == 2) return by_depth<QG_Q4_0, 1, 2>(p, c.depth, waves, nwg, lds, s);
+        return by_depth<QG_Q4_0, 1, 0>(p, c.depth, waves, nwg, lds, s);
+    }
+    if (epi == 1) return by_depth<QG_Q4_0, 2, 1>(p, c.depth, waves, nwg, lds, s);
+    return by_depth<QG_Q4_0, 2, 0>(p, c.depth, waves, nwg, lds, s);
+}
+
+} // namespace qg

@@ -151,7 +151,8 @@ hipError_t launch_prefill_reduce(int nmat, const float *part, float *y, int64_t 
 
 namespace {
 
-PrefillCfg g_pf_override = {0, 0, 0, 0, 0};
+// tuning override of the calling thread (qgemv_set_prefill_override)
+thread_local PrefillCfg g_pf_override = {0, 0, 0, 0, 0};
 
 // The built-in tile choice (from kernel-trace sweeps of every built shape on
 // the 27B-class FFN at 8 to 128 tokens and the SmolLM2-1.7B-shaped FFN and

@@ -37,6 +37,7 @@
 
 #include <hip/hip_ext.h>
 
+#include <atomic>
 #include <cstdint>
 #include <type_traits>
 
@@ -561,8 +562,15 @@ hipError_t go_prefill(PrefillParams p, float *y, hipStream_t s)
     if (grid >= (int64_t(1) << 31)) return hipErrorInvalidValue;
     auto kern = prefill_mfma_kernel<FMT, NMAT, MTR, NTW, W, Q, XB>;
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
+        // the attribute is per device and per instantiation: set it once
+        static std::atomic<bool> configured[64];
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+        if (!configured[dev].load(std::memory_order_relaxed)) {
+            hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            configured[dev].store(true, std::memory_order_relaxed);
+        }
     }
     // measurement hook: the start event rides on this launch, the stop event
     // on the last launch of the product (this one, or the reduce)
@@ -597,7 +605,6 @@ constexpr int kBuiltShapes[] = {
     11561, 11961,   // 16 waves (waves * 10 = 160), one matrix only: two spill
 };
 
-#ifndef QG_PF_CENSUS_K
 constexpr int kBuiltShapesK[] = {
     11141, 11142, 11144, 11181, 11182, 11184, 11241, 11242, 11244,
     11281, 11282, 11284, 11441, 11442, 11481, 11482, 11561, 11841,
@@ -607,9 +614,7 @@ constexpr int kBuiltShapesK[] = {
     21442, 21481, 21482, 21841, 21881, 22141, 22142, 22181, 22241,
     22242, 22281, 22441, 22442, 22841,
 };
-#endif
 
-#ifndef QG_PF_CENSUS_6
 constexpr int kBuiltShapes6[] = {
     11141, 11142, 11144, 11181, 11182, 11184, 11241, 11242, 11244,
     11281, 11282, 11284, 11441, 11442, 11481, 11482, 11561, 11841,
@@ -619,9 +624,7 @@ constexpr int kBuiltShapes6[] = {
     21441, 21442, 21481, 21841, 21881, 22141, 22142, 22181, 22241,
     22242, 22281, 22441, 22841,
 };
-#endif
 
-#ifndef QG_PF_CENSUS_8
 constexpr int kBuiltShapes8[] = {
     11141, 11142, 11144, 11181, 11182, 11184, 11241, 11242, 11244,
     11281, 11282, 11284, 11441, 11442, 11481, 11482, 11561, 11841,
@@ -631,9 +634,7 @@ constexpr int kBuiltShapes8[] = {
     21441, 21442, 21481, 21841, 21881, 22141, 22142, 22181, 22241,
     22242, 22281, 22441, 22841,
 };
-#endif
 
-#ifndef QG_PF_CENSUS_R
 constexpr int kBuiltShapesR[] = {
     11141, 11142, 11144, 11181, 11182, 11184, 11241, 11242, 11244,
     11281, 11282, 11284, 11441, 11442, 11481, 11482, 11561, 11841,
@@ -644,7 +645,6 @@ constexpr int kBuiltShapesR[] = {
     22142, 22181, 22182, 22241, 22242, 22281, 22441, 22442, 22481,
     22841,
 };
-#endif
 
 constexpr bool pf_fits(int fmt, int nmat, int mtr, int ntw, int waves, int run)
 {
@@ -652,40 +652,24 @@ constexpr bool pf_fits(int fmt, int nmat, int mtr, int ntw, int waves, int run)
     const bool geometry = pf_lds_bytes(fmt, nmat, mtr, ntw, waves, run) <= 160 * 1024 &&
                           ntw * 512 * run >= waves * 64 && ntw * 512 * run <= 16 * waves * 64;
     if (fmt == QG_Q8_0) {
-#ifdef QG_PF_CENSUS_8
-        return geometry && (waves != 16 || nmat == 1);
-#else
         for (int c : kBuiltShapes8)
             if (c == code) return geometry;
         return false;
-#endif
     }
     if (fmt == QG_I8ROW) {
-#ifdef QG_PF_CENSUS_R
-        return geometry && (waves != 16 || nmat == 1);
-#else
         for (int c : kBuiltShapesR)
             if (c == code) return geometry;
         return false;
-#endif
     }
     if (fmt == QG_Q6_K) {
-#ifdef QG_PF_CENSUS_6
-        return geometry && (waves != 16 || nmat == 1);
-#else
         for (int c : kBuiltShapes6)
             if (c == code) return geometry;
         return false;
-#endif
     }
     if (fmt == QG_Q4_K) {
-#ifdef QG_PF_CENSUS_K
-        return geometry && (waves != 16 || nmat == 1);
-#else
         for (int c : kBuiltShapesK)
             if (c == code) return geometry;
         return false;
-#endif
     }
     for (int c : kBuiltShapes)
         if (c == code) return geometry;

@@ -5,8 +5,11 @@
  *
  * C ABI.  Every pointer argument except `stream` is DEVICE memory owned by the
  * caller; the library allocates nothing and keeps no mutable global state
- * beyond a lazily read per-device property cache.  `stream` is a hipStream_t
- * passed as void* (NULL = the legacy null stream).
+ * beyond a lazily read per-device property cache.  The tuning and measurement
+ * hooks (qgemv_set_launch_override, qgemv_set_prefill_override,
+ * qgemv_time_next_launch) keep their setting per calling thread and affect
+ * only that thread's later calls.  `stream` is a hipStream_t passed as void*
+ * (NULL = the legacy null stream).
  *
  * Errors are returned, never thrown: every entry point validates its arguments
  * synchronously and, on any error, returns a negative qg_status and enqueues
@@ -254,12 +257,30 @@ int qdequant(int fmt, const void *packed, float *w_out, int64_t rows, int64_t co
  * (8, 16, 32 or 64), rows per lane group (1 or 2), waves per workgroup (1..8),
  * prefetch depth per lane (2 or 4), a cap on the number of workgroups (0 =
  * none; with a cap, workgroups loop over row batches) and adjacent 32-weight
- * chunks per lane per pass (1, 2 or 4) for subsequent calls in this process;
- * lpr == 0 restores the built-in choice.  Results depend on the shape only
+ * chunks per lane per pass (1, 2 or 4) for the calling thread's subsequent
+ * calls; lpr == 0 restores the built-in choice.  Results depend on the shape only
  * through summation order (every choice stays within the fp32 bound).
- * Process-global and not synchronized: set it only while no other thread is
- * enqueueing work.  Returns QG_ERR_SHAPE for values outside these sets. */
+ * Per calling thread: it applies to that thread's later calls only.  Returns
+ * QG_ERR_SHAPE for values outside these sets. */
 int qgemv_set_launch_override(int lpr, int r, int waves, int depth, int max_wg, int cpl);
+
+/* Tuning hook for the one-token products of Q4_0 matrices whose rows have at
+ * most 1024 blocks: by default these run on a row-streaming kernel in which
+ * each lane keeps one block's activations in registers and streams that
+ * block of consecutive rows.  mode -1 keeps them on the lane-group kernels
+ * (also the effect of any qgemv_set_launch_override shape); mode 1 forces the
+ * row-streaming kernel's rows per row-step (rs 1, 2, 4 or 8), 32-lane
+ * segments per row (seg: 32 * seg >= blocks per row, rs * seg even, at most
+ * 32 waves' worth: rs * seg / 2 <= 16), row-steps in flight per lane (depth
+ * 2 or 4; 8 for a single matrix) and row-steps per workgroup (nrs, a multiple
+ * of depth) and the order in which row-steps are dealt to workgroups (order
+ * 1: round robin, 0: consecutive, -1: built-in); a 0 field keeps the
+ * built-in value, and a combination outside
+ * these rules falls back to the lane-group kernels.  mode 0 restores the
+ * built-in choice.  Results depend on the choice only through summation
+ * order.  Per calling thread.  Returns QG_ERR_SHAPE for other modes or
+ * negative fields. */
+int qgemv_set_xs_override(int mode, int rs, int seg, int depth, int nrs, int order);
 
 /* Measurement hook: the next product kernel that the calling thread
  * launches (a GEMV kernel of any call, or a matrix-core product with its
@@ -282,7 +303,7 @@ int qgemv_time_next_launch(void *start_event, void *stop_event);
  * library does not build (it would spill registers or overflow the LDS) runs
  * as the nearest built one.  mtr == 0 restores the built-in choice; mtr == -1
  * turns the matrix-core path off, so that n_tok > 1 loops the GEMV over the
- * tokens (fp32 accuracy), for comparisons.  Same threading rule as
+ * tokens (fp32 accuracy), for comparisons.  Per calling thread, as
  * qgemv_set_launch_override.  Returns QG_ERR_SHAPE for other values. */
 int qgemv_set_prefill_override(int mtr, int ntw, int waves, int run, int ksplit);
 

@@ -49,6 +49,22 @@ def gemv_gpu(t, packed, x):
     return y.cpu().numpy()
 
 
+def oracle_gemv_rows(fmt, raw, x, rows, cols, row_scale=None, threads=16):
+    """oracle.gemv over every row, the rows split into ranges run on a thread
+    pool (ctypes releases the GIL in the C oracle; each row is summed in the
+    same order as in one call, so the result is identical)."""
+    from concurrent.futures import ThreadPoolExecutor
+    threads = max(1, min(threads, rows // 64 or 1))
+    cuts = np.linspace(0, rows, threads + 1).astype(int)
+    with ThreadPoolExecutor(threads) as pool:
+        parts = list(pool.map(lambda ab: oracle.gemv(fmt, raw, x, rows, cols, row_scale=row_scale,
+                                                     row_begin=int(ab[0]), row_end=int(ab[1])),
+                              zip(cuts[:-1], cuts[1:])))
+    y = np.concatenate([p[0] for p in parts], axis=-1)
+    S = np.concatenate([p[1] for p in parts], axis=-1)
+    return y, S
+
+
 def check_bound(y_gpu, y_ref, S, rel=REL, what=""):
     y_gpu = np.asarray(y_gpu, np.float64)
     err = np.abs(y_gpu - y_ref)

@@ -134,8 +134,9 @@ def test_prefill_plan_pins_the_tile_rules(lib):
     # an override is honoured, a shape that is not built runs as the nearest built one
     assert lib.qgemv_set_prefill_override(2, 8, 16, 4, 1) == 0
     try:
-        p = plan(0, 2, 17408, 5120, 128, big)
-        assert p[1:] != (8, 16, 4, 1) and p[4] == 1
+        # the pair with 2 row tiles, 16 waves and runs of four is not built:
+        # it runs as the nearest built shape, one row tile, 8 waves, runs of one
+        assert plan(0, 2, 17408, 5120, 128, big) == (1, 8, 8, 1, 1)
     finally:
         assert lib.qgemv_set_prefill_override(0, 0, 0, 0, 0) == 0
     # refusals
@@ -147,3 +148,50 @@ def test_prefill_plan_pins_the_tile_rules(lib):
     assert f(0, 1, 64, 64, 1, 0, 256, out) == -2
     assert f(0, 1, 64, 64, 8, 0, 0, out) == -2
     assert tuple(out) == (7,) * 5
+
+
+def test_tuning_overrides_are_per_thread(lib):
+    # a tuning override set on one thread leaves other threads' calls alone
+    import threading
+    I64 = ctypes.c_int64
+    f = lib.qgemv_prefill_plan
+    f.argtypes = [ctypes.c_int, ctypes.c_int, I64, I64, I64, I64, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    f.restype = ctypes.c_int
+    lib.qgemv_set_prefill_override.argtypes = [ctypes.c_int] * 5
+    lib.swiglu_ffn_scratch_elems.argtypes = [ctypes.c_int, I64, I64, I64]
+    lib.swiglu_ffn_scratch_elems.restype = I64
+
+    def plan():
+        out = (ctypes.c_int * 5)()
+        assert f(0, 2, 17408, 5120, 128, 1 << 40, 256, out) == 0
+        return tuple(out)
+
+    seen = {}
+
+    def other():
+        assert lib.qgemv_set_prefill_override(1, 4, 8, 1, 2) == 0
+        seen["forced"] = plan()
+        assert lib.qgemv_set_prefill_override(-1, 0, 0, 0, 0) == 0   # matrix cores off on this thread
+        seen["scratch_off"] = lib.swiglu_ffn_scratch_elems(0, 5120, 17408, 8)
+        assert lib.qgemv_set_prefill_override(0, 0, 0, 0, 0) == 0
+
+    assert lib.qgemv_set_prefill_override(0, 0, 0, 0, 0) == 0
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["forced"] == (1, 4, 8, 1, 2)
+    assert seen["scratch_off"] == 8 * 17408
+    assert plan() == (1, 8, 8, 1, 1)
+    assert lib.swiglu_ffn_scratch_elems(0, 5120, 17408, 8) > 8 * 17408
+
+
+def test_xs_override_refusals(lib):
+    f = lib.qgemv_set_xs_override
+    f.argtypes = [ctypes.c_int] * 6
+    f.restype = ctypes.c_int
+    assert f(2, 0, 0, 0, 0, -1) == -2     # unknown mode
+    assert f(1, -1, 0, 0, 0, -1) == -2    # negative field
+    assert f(1, 0, 0, 0, 0, 2) == -2      # unknown order
+    assert f(1, 2, 5, 2, 12, 1) == 0
+    assert f(-1, 0, 0, 0, 0, 0) == 0
+    assert f(0, 0, 0, 0, 0, 0) == 0

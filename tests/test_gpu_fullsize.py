@@ -80,116 +80,93 @@ def test_fullsize_swiglu_other_formats(wname, ffn_idx):
     G.check_bound(out, yr, S, what=f"{wname} down")
 
 
-def _row_samples(rows, k=128):
-    return (0, rows // 2 - k // 2, rows - k)
-
-
-def test_fullsize_cfg5_batched_tokens_sampled_rows():
-    # n_tok = 8 and 128 on the 27B-class gate matrix (matrix-core path); the
-    # oracle checks a contiguous sample of rows at the start, middle and end
+def test_fullsize_cfg5_batched_tokens_every_row():
+    # n_tok = 8 and 128 on the 27B-class gate matrix (matrix-core path), every
+    # output element against the oracle
     w = synth.CFG5
     t = synth.gen_tensor(w, 0)
     pk = G.upload(t)
     for n in (8, 128):
         x = synth.gen_x(w, w.d_model, n, which=10 + n)
         y = G.gemv_gpu(t, pk, x)
-        for r0 in _row_samples(t.rows):
-            yr, S = oracle.gemv(t.fmt, t.raw, x, t.rows, t.cols, row_begin=r0, row_end=r0 + 128)
-            G.check_bound(y[:, r0:r0 + 128], yr, S, rel=G.PF_REL, what=f"cfg5 gate n_tok={n} rows {r0}..")
+        yr, S = G.oracle_gemv_rows(t.fmt, t.raw, x, t.rows, t.cols)
+        G.check_bound(y, yr, S, rel=G.PF_REL, what=f"cfg5 gate n_tok={n}")
+
+
+def _check_ffn_every_row(fmt, tens, x, d_model, ffn, what):
+    # swiglu_ffn with the scratch swiglu_ffn_scratch_elems asks for (as
+    # bench.py runs it): every element of h against silu(g) u of the oracle,
+    # every element of out against the oracle's down projection of the
+    # device's own h (all of h is an input there)
+    g, u, d = tens
+    pk = [G.upload(t) for t in (g, u, d)]
+    xd = G.torch.from_numpy(np.ascontiguousarray(x)).to(G.dev())
+    out, h = G.qg().swiglu_ffn(fmt, pk[0], pk[1], pk[2], xd, d_model, ffn)
+    G.torch.cuda.synchronize()
+    out, h = out.cpu().numpy(), h.cpu().numpy()
+    r = {}
+    r["g"], r["Sg"] = G.oracle_gemv_rows(g.fmt, g.raw, x, ffn, d_model, row_scale=g.row_scale)
+    r["u"], r["Su"] = G.oracle_gemv_rows(u.fmt, u.raw, x, ffn, d_model, row_scale=u.row_scale)
+    r["h"] = G.silu64(r["g"]) * r["u"]
+    bad = ~(np.abs(h - r["h"]) <= G.h_bound(r, G.PF_REL))
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements of h outside the bound"
+    yr, S = G.oracle_gemv_rows(d.fmt, d.raw, h, d_model, ffn, row_scale=d.row_scale)
+    G.check_bound(out, yr, S, rel=G.PF_REL, what=f"{what} down")
 
 
 @pytest.mark.parametrize("n_tok", [8, 128])
-def test_fullsize_cfg5_ffn_batched_sampled_rows(n_tok):
+def test_fullsize_cfg5_ffn_batched_every_row(n_tok):
     # the whole 27B-class FFN at n_tok = 8 and 128 through swiglu_ffn, in the
-    # launch configuration bench.py times: h on sampled rows against silu(g) u
-    # of the oracle, out on sampled rows against the oracle's down projection
-    # of the device's own h (all of h is an input there)
+    # launch configuration bench.py times
     w = synth.CFG5
     tens = synth.gen_workload(w)
-    pk = [G.upload(t) for t in tens]
     x = synth.gen_x(w, w.d_model, n_tok, which=20 + n_tok)
-    xd = G.torch.from_numpy(x).to(G.dev())
-    out, h = G.qg().swiglu_ffn(tens[0].fmt, pk[0], pk[1], pk[2], xd, w.d_model, w.ffn)
-    G.torch.cuda.synchronize()
-    out, h = out.cpu().numpy(), h.cpu().numpy()
-    for r0 in _row_samples(w.ffn):
-        r = {}
-        r["g"], r["Sg"] = oracle.gemv(tens[0].fmt, tens[0].raw, x, w.ffn, w.d_model, row_begin=r0, row_end=r0 + 128)
-        r["u"], r["Su"] = oracle.gemv(tens[1].fmt, tens[1].raw, x, w.ffn, w.d_model, row_begin=r0, row_end=r0 + 128)
-        r["h"] = G.silu64(r["g"]) * r["u"]
-        assert np.all(np.abs(h[:, r0:r0 + 128] - r["h"]) <= G.h_bound(r, G.PF_REL)), f"h rows {r0}.. outside its bound"
-    for r0 in _row_samples(w.d_model):
-        yr, S = oracle.gemv(tens[2].fmt, tens[2].raw, h, w.d_model, w.ffn, row_begin=r0, row_end=r0 + 128)
-        G.check_bound(out[:, r0:r0 + 128], yr, S, rel=G.PF_REL, what=f"cfg5 down n_tok={n_tok} rows {r0}..")
+    _check_ffn_every_row(tens[0].fmt, tens, x, w.d_model, w.ffn, f"cfg5 n_tok={n_tok}")
 
 
 @pytest.mark.parametrize("idx", [0, 1])
-def test_fullsize_cfg6_q6_k_batched_sampled_rows(idx):
+def test_fullsize_cfg6_q6_k_batched_every_row(idx):
     # the TinyLlama-shaped Q6_K down [2048][5632] and vocab head [32000][2048]
-    # at n_tok = 8 and 128 (matrix-core path), sampled rows against the oracle
+    # at n_tok = 8 and 128 (matrix-core path), every element against the oracle
     w = synth.CFG6
     t = synth.gen_tensor(w, idx)
     pk = G.upload(t)
     for n in (8, 128):
         x = synth.gen_x(w, t.cols, n, which=30 + n + idx)
         y = G.gemv_gpu(t, pk, x)
-        for r0 in _row_samples(t.rows):
-            yr, S = oracle.gemv(t.fmt, t.raw, x, t.rows, t.cols, row_begin=r0, row_end=r0 + 128)
-            G.check_bound(y[:, r0:r0 + 128], yr, S, rel=G.PF_REL, what=f"cfg6 {t.name} n_tok={n} rows {r0}..")
+        yr, S = G.oracle_gemv_rows(t.fmt, t.raw, x, t.rows, t.cols)
+        G.check_bound(y, yr, S, rel=G.PF_REL, what=f"cfg6 {t.name} n_tok={n}")
 
 
-def _check_ffn_sampled(w, tens, x, what):
-    # swiglu_ffn (the scratch swiglu_ffn_scratch_elems asks for, as bench.py
-    # runs it): h on sampled rows against silu(g) u of the oracle, out on
-    # sampled rows against the oracle's down projection of the device's own h
+def _ffn_of(tens):
     names = [t.name for t in tens]
-    g, u, d = (tens[names.index(n)] for n in ("gate", "up", "down"))
-    pk = [G.upload(t) for t in (g, u, d)]
-    xd = G.torch.from_numpy(x).to(G.dev())
-    out, h = G.qg().swiglu_ffn(g.fmt, pk[0], pk[1], pk[2], xd, w.d_model, w.ffn)
-    G.torch.cuda.synchronize()
-    out, h = out.cpu().numpy(), h.cpu().numpy()
-    for r0 in _row_samples(w.ffn):
-        r = {}
-        r["g"], r["Sg"] = oracle.gemv(g.fmt, g.raw, x, w.ffn, w.d_model, row_scale=g.row_scale, row_begin=r0,
-                                      row_end=r0 + 128)
-        r["u"], r["Su"] = oracle.gemv(u.fmt, u.raw, x, w.ffn, w.d_model, row_scale=u.row_scale, row_begin=r0,
-                                      row_end=r0 + 128)
-        r["h"] = G.silu64(r["g"]) * r["u"]
-        assert np.all(np.abs(h[:, r0:r0 + 128] - r["h"]) <= G.h_bound(r, G.PF_REL)), f"{what} h rows {r0}.."
-    for r0 in _row_samples(w.d_model):
-        yr, S = oracle.gemv(d.fmt, d.raw, h, w.d_model, w.ffn, row_scale=d.row_scale, row_begin=r0, row_end=r0 + 128)
-        G.check_bound(out[:, r0:r0 + 128], yr, S, rel=G.PF_REL, what=f"{what} down rows {r0}..")
+    return [tens[names.index(n)] for n in ("gate", "up", "down")]
 
 
-def test_fullsize_cfg4_int8_ffn_head_128_tokens_sampled_rows():
+def test_fullsize_cfg4_int8_ffn_head_128_tokens_every_row():
     # the SmolLM2-1.7B-shaped INT8 FFN (2048/8192) and vocab head [49152][2048]
     # at 128 tokens on the matrix cores, as bench.py times them
     w = synth.CFG4
     tens = synth.gen_workload(w)
     x = synth.gen_x(w, w.d_model, 128, which=40)
-    _check_ffn_sampled(w, tens, x, "cfg4 n_tok=128")
+    _check_ffn_every_row("i8row", _ffn_of(tens), x, w.d_model, w.ffn, "cfg4 n_tok=128")
     t = tens[[t.name for t in tens].index("head")]
     y = G.gemv_gpu(t, G.upload(t), x)
-    for r0 in _row_samples(t.rows):
-        yr, S = oracle.gemv(t.fmt, t.raw, x, t.rows, t.cols, row_scale=t.row_scale, row_begin=r0, row_end=r0 + 128)
-        G.check_bound(y[:, r0:r0 + 128], yr, S, rel=G.PF_REL, what=f"cfg4 head n_tok=128 rows {r0}..")
+    yr, S = G.oracle_gemv_rows(t.fmt, t.raw, x, t.rows, t.cols, row_scale=t.row_scale)
+    G.check_bound(y, yr, S, rel=G.PF_REL, what="cfg4 head n_tok=128")
 
 
-def test_fullsize_cfg2_layer_q8_0_head_128_tokens():
+def test_fullsize_cfg2_layer_q8_0_head_128_tokens_every_row():
     # the SmolLM2-135M-shaped Q4_0 layer (q, o, k, v, FFN) and its Q8_0 vocab
     # head [49152][576] at 128 tokens on the matrix cores, as bench.py times
-    # them: every row of the attention products, sampled rows of the rest
+    # them, every element against the oracle
     w = synth.CFG2
     tens = synth.gen_workload(w)
     x = synth.gen_x(w, w.d_model, 128, which=41)
-    _check_ffn_sampled(w, tens, x, "cfg2 n_tok=128")
+    _check_ffn_every_row("q4_0", _ffn_of(tens), x, w.d_model, w.ffn, "cfg2 n_tok=128")
     for t in tens:
         if t.name in ("gate", "up", "down"):
             continue
         y = G.gemv_gpu(t, G.upload(t), x)
-        starts = _row_samples(t.rows) if t.rows > 1024 else (0,)
-        for r0 in starts:
-            r1 = min(t.rows, r0 + 128) if t.rows > 1024 else t.rows
-            yr, S = oracle.gemv(t.fmt, t.raw, x, t.rows, t.cols, row_begin=r0, row_end=r1)
-            G.check_bound(y[:, r0:r1], yr, S, rel=G.PF_REL, what=f"cfg2 {t.name} n_tok=128 rows {r0}..")
+        yr, S = G.oracle_gemv_rows(t.fmt, t.raw, x, t.rows, t.cols)
+        G.check_bound(y, yr, S, rel=G.PF_REL, what=f"cfg2 {t.name} n_tok=128")
