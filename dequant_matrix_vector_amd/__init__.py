@@ -14,7 +14,7 @@ import torch
 __all__ = [
     "FORMATS", "QGemvError", "lib", "packed_bytes", "max_cols", "repack",
     "qgemv", "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_k", "qgemv_i8row", "qgemv_q6_k",
-    "swiglu_gate_up", "swiglu_ffn", "qdequant", "layout_version", "set_launch_override",
+    "swiglu_gate_up", "swiglu_ffn", "swiglu_ffn_noalloc", "qdequant", "layout_version", "set_launch_override",
     "set_prefill_override", "set_xs_override", "prefill_plan", "swiglu_ffn_scratch_elems", "swiglu_ffn_block", "swiglu_ffn_block_scratch_elems",
     "qgemv_argmax", "qgemv_head_argmax", "qgemv_q8act", "swiglu_ffn_q8act", "qquantize_q8_0",
     "qgemv_repack_q4_0", "qgemv_repack_q8_0", "qgemv_repack_q4_k", "qgemv_repack_i8row", "qgemv_repack_q6_k",
@@ -53,6 +53,9 @@ lib.swiglu_gate_up.argtypes = [_I, _P, _P, _P, _P, _I64, _I64, _I64, _P]
 lib.swiglu_gate_up.restype = _I
 lib.swiglu_ffn.argtypes = [_I, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
 lib.swiglu_ffn.restype = _I
+lib.swiglu_ffn_noalloc.argtypes = [_I, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
+lib.swiglu_ffn_noalloc.restype = _I
+NOALLOC_SCRATCH_ELEMS = 1 << 23   # QG_NOALLOC_SCRATCH_ELEMS of include/qgemv.h
 lib.swiglu_ffn_scratch_elems.argtypes = [_I, _I64, _I64, _I64]
 lib.swiglu_ffn_scratch_elems.restype = _I64
 lib.swiglu_ffn_block.argtypes = [_I, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
@@ -344,6 +347,23 @@ def swiglu_ffn(fmt, wg, wu, wd, x, d_model, ffn, out=None, h_scratch=None, strea
     _check(lib.swiglu_ffn(_fmt(fmt), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(x), _ptr(out), _ptr(h_scratch),
                           h_scratch.numel(), d_model, ffn, n_tok, _stream(stream)), "swiglu_ffn")
     return out, h_scratch.view(-1)[:n_tok * ffn].view(n_tok, ffn)
+
+
+def swiglu_ffn_noalloc(fmt, wg, wu, wd, x, d_model, ffn, out=None, stream=None) -> torch.Tensor:
+    """out [n_tok][d_model] = Wd (silu(Wg x) * (Wu x)) with the library's own
+    per-device scratch (no allocation in the call; calls overlapping on one
+    device race)."""
+    n_tok = _ntok(x, d_model)
+    out = _y(out, (n_tok, d_model), x.device)
+    _packed(wg, fmt, ffn, d_model, "wg")
+    _packed(wu, fmt, ffn, d_model, "wu")
+    _packed(wd, fmt, d_model, ffn, "wd")
+    _arg(x, "x", F32)
+    _arg(out, "out", F32, n_tok * d_model)
+    _on_gpu(wg, wu, wd, x, out)
+    _check(lib.swiglu_ffn_noalloc(_fmt(fmt), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(x), _ptr(out), d_model, ffn, n_tok,
+                                  _stream(stream)), "swiglu_ffn_noalloc")
+    return out
 
 
 def qgemv_q8act(fmt, packed, x, rows, cols, y=None, stream=None) -> torch.Tensor:

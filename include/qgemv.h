@@ -174,6 +174,21 @@ int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const fl
                float *out, float *h_scratch, int64_t h_scratch_elems, int64_t d_model,
                int64_t ffn, int64_t n_tok, void *stream);
 
+/* swiglu_ffn for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same products and results as swiglu_ffn given min(swiglu_ffn_scratch_elems(),
+ * QG_NOALLOC_SCRATCH_ELEMS) floats of scratch, with that scratch in an array
+ * of QG_NOALLOC_SCRATCH_ELEMS floats (32 MiB) that the library keeps on each
+ * device it runs on until the process ends; the call itself allocates
+ * nothing.  Arguments as swiglu_ffn without the scratch (h is not returned).
+ * QG_ERR_SCRATCH when n_tok * ffn > QG_NOALLOC_SCRATCH_ELEMS; QG_ERR_DEVICE if
+ * the array's device address cannot be found.  Every call on one device uses
+ * the same array: calls that overlap in time on one device (other streams,
+ * other threads) race and must be serialized by the caller. */
+#define QG_NOALLOC_SCRATCH_ELEMS (1 << 23)
+int swiglu_ffn_noalloc(int fmt, const void *wg, const void *wu, const void *wd, const float *x, float *out,
+                       int64_t d_model, int64_t ffn, int64_t n_tok, void *stream);
+
 /* The FFN block of the residual stream: out = x + Wd (silu(Wg xn) * (Wu xn)),
  * xn = x * gamma / sqrt(mean(x^2) + eps) per token row -- RMSNorm before the
  * block (llmoxide blog, section 4 "Keeping the numbers in range"; the rmsnorm
