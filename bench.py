@@ -18,6 +18,11 @@ run a second time with each launch carrying its own start/stop events
 the events hold the dispatch's own start and end -- the duration rocprofv3's
 kernel trace reports.  Timed launches leave gaps between the kernels (as
 hipEventRecord pairs do), hence a pass of their own.
+Also reported: the same two kernels back to back (a HIP graph of 32 launches
+of one product over the rotating copies), and the read ceiling -- what a plain
+16-byte grid-stride read kernel (qgemv_read_probe) streams over 1 GiB and,
+back to back, over rotating slices of each product's size -- with each
+kernel's fraction of it.
 cpu_baseline: the CPU oracle (scalar C, binary64) on the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
@@ -48,6 +53,11 @@ def parse():
     ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload report")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with a plain 256 MiB device copy (known bytes, for scaling HBM counters)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the read-ceiling probe and the back-to-back graph passes (short profiled runs)")
+    ap.add_argument("--workloads", default="",
+                    help="comma-separated keys of the per-workload report to run (e.g. cfg5_n8,cfg5_n128); "
+                         "default: all")
     return ap.parse_args()
 
 
@@ -85,8 +95,8 @@ class TimingEvents:
         self.ev = []
 
 
-GEMV_SOURCES = ("dequant_matrix_vector_amd/csrc/gemv_impl.h", "dequant_matrix_vector_amd/csrc/gemv_q4_0.hip",
-                "dequant_matrix_vector_amd/csrc/gemv.hip")
+GEMV_SOURCES = ("dequant_matrix_vector_amd/csrc/gemv_impl.h", "dequant_matrix_vector_amd/csrc/gemv_xs.h",
+                "dequant_matrix_vector_amd/csrc/gemv_xs.hip", "dequant_matrix_vector_amd/csrc/gemv.hip")
 TRAFFIC_PROFILE = "profiles/gemv_q4_0_27b_ffn_hbm_counters.md"
 
 
@@ -112,6 +122,76 @@ def measured_traffic():
         return int(fields["traffic_gate_up_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def read_ceiling(qg, torch, dev, launch_bytes=(100270080, 50135040)):
+    """Streaming-read rate of a plain kernel (qgemv_read_probe: 16-byte loads,
+    grid-stride), best over a few launch shapes: over 1 GiB in one launch, and
+    back to back over rotating slices of each product's size (a launch of the
+    products' length pays the same ramp-up and drain)."""
+    pool = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    pool.random_(0, 255)
+    out = torch.zeros(256 * 64, dtype=torch.int32, device=dev)
+    sptr = torch.cuda.current_stream().cuda_stream
+    probe = qg.lib.qgemv_read_probe
+    res = {}
+
+    def run(nbytes, nslice, wpc, u, iters):
+        def launch(i):
+            if probe(pool.data_ptr() + (i % nslice) * nbytes, nbytes, wpc, u, out.data_ptr(), sptr) != 0:
+                raise RuntimeError("qgemv_read_probe failed")
+        for i in range(3):
+            launch(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(iters):
+            launch(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return nbytes / (e0.elapsed_time(e1) * 1e-3 / iters) / 1e9
+
+    shapes = [(4, 2), (4, 8), (16, 8), (8, 4)]
+    res["GBs_1GiB"] = round(max(run(1 << 30, 1, w, u, 10) for w, u in shapes), 1)
+    for nb in launch_bytes:
+        nslice = (1 << 30) // nb
+        res[f"GBs_{nb}_per_launch"] = round(max(run(nb, nslice, w, u, 60) for w, u in shapes), 1)
+    del pool
+    torch.cuda.empty_cache()
+    return res
+
+
+def back_to_back_us(torch, launch, n=32, reps=5):
+    """Device microseconds per launch of launch(i, stream) when n of them run
+    back to back (a HIP graph of n launches over the rotating copies,
+    replayed)."""
+    s = torch.cuda.current_stream().cuda_stream
+    for i in range(3):
+        launch(i, s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream().cuda_stream
+        for i in range(n):
+            launch(i, cs)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * n)
 
 
 def cpu_baseline(tens, x, w, min_seconds):
@@ -160,13 +240,13 @@ def cpu_baseline(tens, x, w, min_seconds):
                 break
     perm = elm / repm
     return {"value": round(wb / perm / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "value_1_thread": round(wb / per1 / 1e9, 4),
+            "value_1_thread": round(wb / per1 / 1e9, 4), "cpu_model": cpu_model(),
             "sample": f"full FFN (gate, up, down): {repm} runs with the rows of each product split over "
                       f"{threads} threads ({perm * 1e3:.1f} ms per FFN) and {reps} runs on 1 thread "
                       f"({per1 * 1e3:.0f} ms per FFN), binary64 scalar C"}
 
 
-def workload_report(qg, synth, torch, np, dev, graph_iters=20):
+def workload_report(qg, synth, torch, np, dev, graph_iters=20, only=()):
     """Device time per step of every workload, from HIP graph replays.
 
     A step is the workload's whole hot path: the FFN (gate/up + down) for the
@@ -179,6 +259,9 @@ def workload_report(qg, synth, torch, np, dev, graph_iters=20):
              (synth.CFG5, 8), (synth.CFG5, 128), (synth.CFG6, 1), (synth.CFG3, 128), (synth.CFG6, 128),
              (synth.CFG2, 128), (synth.CFG4, 128)]
     for w, n_tok in plans:
+        key = f"cfg{w.cfg_id}" + (f"_n{n_tok}" if (w.n_tok != (1,) or n_tok != 1) else "")
+        if only and key not in only:
+            continue
         tens = synth.gen_workload(w)
         wbytes = sum(t.weight_bytes for t in tens)
         ncopy = int(min(graph_iters, max(1, -(-ROTATE_BYTES // wbytes))))
@@ -227,7 +310,6 @@ def workload_report(qg, synth, torch, np, dev, graph_iters=20):
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / (reps * graph_iters)
-        key = f"cfg{w.cfg_id}" + (f"_n{n_tok}" if (w.n_tok != (1,) or n_tok != 1) else "")
         rep[key] = {"workload": w.name, "n_tok": n_tok, "us_per_step": round(us, 2),
                     "weight_bytes": wbytes, "GBs": round(wbytes / us / 1e3, 1),
                     "pct_hbm_peak": round(100 * wbytes / us / 1e3 / HBM_PEAK_GBS, 1),
@@ -239,7 +321,8 @@ def workload_report(qg, synth, torch, np, dev, graph_iters=20):
             rep[key]["pct_bf16_mfma_peak"] = round(100 * flops / us / 1e6 / BF16_MFMA_PEAK_TFLOPS, 1)
         del copies, g
         torch.cuda.empty_cache()
-    rep.update(extra_report(qg, synth, torch, np, dev, graph_iters))
+    if not only:
+        rep.update(extra_report(qg, synth, torch, np, dev, graph_iters))
     return rep
 
 
@@ -412,8 +495,28 @@ def main():
     dn_avg = float(np.mean(dn_ms))
     achieved = gu_bytes / (gu_avg * 1e-3) / 1e9
 
+    # the same kernels back to back (no events between them): a HIP graph of
+    # 32 launches of one product over the rotating copies
+    def gu_launch(i, s):
+        a = gu_args[i % ncopy]
+        if gate_up_call(*a[:-1], s) != 0:
+            raise RuntimeError("swiglu_gate_up failed")
+
+    def dn_launch(i, s):
+        a = dn_args[i % ncopy]
+        if down_call(*a[:-1], s) != 0:
+            raise RuntimeError("qgemv failed")
+
+    gu_b2b = dn_b2b = float("nan")
+    if not a.no_extras:
+        gu_b2b = back_to_back_us(torch, gu_launch)
+        dn_b2b = back_to_back_us(torch, dn_launch)
+
     detail = {
         "gate_up_us": round(gu_avg * 1e3, 2), "down_us": round(dn_avg * 1e3, 2),
+        "gate_up_us_back_to_back": round(gu_b2b, 2), "down_us_back_to_back": round(dn_b2b, 2),
+        "gate_up_GBs_back_to_back": round(gu_bytes / gu_b2b / 1e3, 1),
+        "down_GBs_back_to_back": round(tens[2].weight_bytes / dn_b2b / 1e3, 1),
         "gate_up_GBs": round(achieved, 1),
         "down_GBs": round(tens[2].weight_bytes / (dn_avg * 1e-3) / 1e9, 1),
         "ffn_device_us": round((gu_avg + dn_avg) * 1e3, 2),
@@ -421,6 +524,10 @@ def main():
         "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
         "rotating_copies": ncopy,
     }
+    if a.no_extras:
+        for k in ("gate_up_us_back_to_back", "down_us_back_to_back", "gate_up_GBs_back_to_back",
+                  "down_GBs_back_to_back"):
+            detail[k] = None
     if a.warm:
         g, u, dn = copies[0]
         for _ in range(10):
@@ -452,10 +559,22 @@ def main():
                    "weight_bytes_per_step": step_bytes, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "fused gate/up GEMV (gemv_kernel<Q4_0, NMAT=2>)",
+                     "kernel": "fused gate/up row-streaming GEMV (gemv_xs_kernel<Q4_0, NMAT=2>)",
                      "bytes_per_launch": gu_bytes},
         "detail": detail,
     }
+    del copies
+    torch.cuda.empty_cache()
+    if not a.no_extras:
+        ceil = read_ceiling(qg, torch, dev, (gu_bytes, tens[2].weight_bytes))
+        rec["read_ceiling"] = dict(ceil, unit="GB/s", kernel="qgemv_read_probe (plain 16-byte grid-stride read)")
+        cg = ceil[f"GBs_{gu_bytes}_per_launch"]
+        rec["roofline"]["read_ceiling_per_launch"] = cg
+        rec["roofline"]["frac_of_read_ceiling"] = round(achieved / cg, 4)
+        detail["gate_up_frac_of_read_ceiling_back_to_back"] = round(gu_bytes / gu_b2b / 1e3 / cg, 4)
+        detail["down_frac_of_read_ceiling_back_to_back"] = round(
+            tens[2].weight_bytes / dn_b2b / 1e3 / ceil[f"GBs_{tens[2].weight_bytes}_per_launch"], 4)
+        detail["step_frac_of_read_ceiling"] = round(value / ceil["GBs_1GiB"], 4)
     if a.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -463,9 +582,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if not a.no_workloads:
-        del copies
-        torch.cuda.empty_cache()
-        rec["workloads"] = workload_report(qg, synth, torch, np, dev)
+        rec["workloads"] = workload_report(qg, synth, torch, np, dev,
+                                           only=tuple(k for k in a.workloads.split(",") if k))
     if not a.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(tens, x, w, a.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -78,8 +78,10 @@ lib.qgemv_set_launch_override.argtypes = [_I, _I, _I, _I, _I, _I]
 lib.qgemv_set_launch_override.restype = _I
 lib.qgemv_set_prefill_override.argtypes = [_I, _I, _I, _I, _I]
 lib.qgemv_set_prefill_override.restype = _I
-lib.qgemv_set_xs_override.argtypes = [_I, _I, _I, _I, _I, _I]
+lib.qgemv_set_xs_override.argtypes = [_I, _I, _I, _I, _I, _I, _I]
 lib.qgemv_set_xs_override.restype = _I
+lib.qgemv_read_probe.argtypes = [_P, _I64, _I, _I, _P, _P]
+lib.qgemv_read_probe.restype = _I
 lib.qgemv_time_next_launch.argtypes = [_P, _P]
 lib.qgemv_time_next_launch.restype = _I
 
@@ -177,10 +179,10 @@ def set_launch_override(lpr=0, r=0, waves=0, depth=2, max_wg=0, cpl=1):
     _check(lib.qgemv_set_launch_override(lpr, r, waves, depth, max_wg, cpl), "qgemv_set_launch_override")
 
 
-def set_xs_override(mode=0, rs=0, seg=0, depth=0, nrs=0, order=-1):
+def set_xs_override(mode=0, rs=0, seg=0, depth=0, nrs=0, order=-1, wg_per_cu=-1):
     """Row-streaming one-token kernel: mode 0 built-in, -1 off (lane-group
     kernels), 1 forced with the given fields (0 / -1 = built-in value)."""
-    _check(lib.qgemv_set_xs_override(mode, rs, seg, depth, nrs, order), "qgemv_set_xs_override")
+    _check(lib.qgemv_set_xs_override(mode, rs, seg, depth, nrs, order, wg_per_cu), "qgemv_set_xs_override")
 
 
 def prefill_plan(fmt, nmat, rows, cols, n_tok, part_elems=0, cus=256):

@@ -48,6 +48,7 @@ using gemv_detail::dot_q4_chunk;
 using gemv_detail::half_lo;
 using gemv_detail::silu_mul;
 using gemv_detail::f32x4;
+using gemv_detail::static_for;
 
 struct XsParams {
     const uint8_t *q[2];  // packed tensors (quant plane at offset 0)
@@ -62,7 +63,7 @@ struct XsParams {
     uint32_t soff;        // scale-plane offset
     int lprow;            // lanes per row: 32 * segments >= nchunk
     int rs;               // rows per row-step
-    int nrs;              // row-steps per workgroup (a multiple of D)
+    int nrs;              // row-steps per workgroup
     int ga, gb;           // global row-step of local step i in workgroup b: i * ga + b * gb
                           // (ga = 1, gb = nrs: consecutive steps; ga = grid, gb = 1: round robin)
 };
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
         }
     };
 #pragma unroll
-    for (int s = 0; s < D; s++) load_step(s, s);   // nrs >= D
+    for (int s = 0; s < D; s++) load_step(s, s < p.nrs ? s : p.nrs - 1);
     __builtin_amdgcn_sched_barrier(0);
 
     // branch-free (a divergent branch here would make the compiler wait for
@@ -285,24 +286,41 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
 
     const bool writer = seg_writer<V>(lane);
     const int widx = seg_index<V>(lane);
-    for (int i0 = 0; i0 < p.nrs; i0 += D) {
+    // R <= D row-steps from i0, then their reduction (values of steps past R
+    // are 0 and not written); REFILL: issue the loads D steps ahead (full
+    // batches before the last; the last batch has nothing more to fetch)
+    auto batch = [&](int i0, auto refill, auto nsteps) {
+        constexpr int R = decltype(nsteps)::value;
         float v[V];
 #pragma unroll
         for (int s = 0; s < D; s++) {
 #pragma unroll
             for (int m = 0; m < NMAT; m++) {
-                const float tq = dot_q4_chunk(st[s][m].q, xv);
-                const float u = __builtin_fmaf(-8.0f, xsum, tq);   // sum (q - 8) x
-                v[s * NMAT + m] = live ? half_lo(st[s][m].d) * u : 0.0f;   // spare lanes: exactly 0
+                if (s < R) {
+                    const float tq = dot_q4_chunk(st[s][m].q, xv);
+                    const float u = __builtin_fmaf(-8.0f, xsum, tq);   // sum (q - 8) x
+                    v[s * NMAT + m] = live ? half_lo(st[s][m].d) * u : 0.0f;   // spare lanes: exactly 0
+                } else {
+                    v[s * NMAT + m] = 0.0f;
+                }
             }
-            const int nxt = i0 + s + D;
-            load_step(s, nxt < p.nrs ? nxt : p.nrs - 1);
+            if constexpr (decltype(refill)::value) {
+                const int nxt = i0 + s + D;
+                load_step(s, nxt < p.nrs ? nxt : p.nrs - 1);
+            }
             // keep the refill here, right after its slot is consumed
             __builtin_amdgcn_sched_barrier(0);
         }
         const float r = seg_reduce<V>(v, lane);
-        if (writer) part[(seg * p.nrs + i0) * NMAT + widx] = r;   // widx = step * NMAT + matrix
-    }
+        if (writer && widx < R * NMAT) part[(seg * p.nrs + i0) * NMAT + widx] = r;   // widx = step * NMAT + matrix
+    };
+    int i0 = 0;
+    for (; i0 + D < p.nrs; i0 += D) batch(i0, std::true_type{}, std::integral_constant<int, D>{});
+    // the last 1..D row-steps
+    static_for<D>([&](auto rr) {
+        constexpr int R = decltype(rr)::value + 1;
+        if (p.nrs - i0 == R) batch(i0, std::false_type{}, std::integral_constant<int, R>{});
+    });
     __syncthreads();
 
     // one thread per row: the row phase's segments in order
@@ -336,6 +354,7 @@ struct XsCfg {
     int depth;  // row-steps in flight per lane (ring depth, also the reduction batch)
     int nrs;    // row-steps per workgroup
     int rr;     // 1: row-steps dealt to workgroups round robin; 0: consecutive
+    int wpc;    // > 0: exactly wpc workgroups per CU (nrs follows), at most wpc resident per CU
 };
 
 // Host side (gemv_xs.hip): the configuration for a shape, or false when the

@@ -14,7 +14,7 @@ namespace {
 // built-in, -1 = never take the x-stationary kernel, 1 = take it with the
 // fields below (0 = built-in value)
 thread_local int g_xs_mode = 0;
-thread_local XsCfg g_xs_force = {0, 0, 0, 0, -1};
+thread_local XsCfg g_xs_force = {0, 0, 0, 0, -1, 0};
 
 template <int FMT, int NMAT, int EPI, int D>
 hipError_t go(const XsParams &p, int waves, int64_t nwg, size_t lds, hipStream_t s)
@@ -65,27 +65,32 @@ size_t xs_lds_bytes(const XsCfg &c, int nmat, int64_t nchunk, bool norm)
 // alone takes 144 KB; with the gain staged too, rows of up to 540 chunks fit)
 constexpr size_t kXsMaxLds = 160 * 1024;
 
+int64_t steps_of(const XsCfg &c, int64_t rows) { return (rows + c.rs - 1) / c.rs; }
+
 bool valid_cfg(const XsCfg &c, int nmat, int64_t nchunk, bool norm)
 {
+    if (c.wpc > 0 && xs_lds_bytes(c, nmat, nchunk, norm) > kXsMaxLds / c.wpc) return false;
     if (c.rs < 1 || c.rs > 8 || (c.rs & (c.rs - 1))) return false;
     if (c.seg * 32 < nchunk || c.seg > 32) return false;
     if ((c.rs * c.seg) % 2 || c.rs * c.seg / 2 > 16) return false;
     if (!(c.depth == 2 || c.depth == 4 || (c.depth == 8 && nmat == 1))) return false;
-    return c.nrs >= c.depth && c.nrs % c.depth == 0 && xs_lds_bytes(c, nmat, nchunk, norm) <= kXsMaxLds;
+    return c.nrs >= 1 && xs_lds_bytes(c, nmat, nchunk, norm) <= kXsMaxLds;
 }
 
 } // namespace
 
-extern "C" int qgemv_set_xs_override(int mode, int rs, int seg, int depth, int nrs, int order)
+extern "C" int qgemv_set_xs_override(int mode, int rs, int seg, int depth, int nrs, int order, int wg_per_cu)
 {
     if (mode == 0 || mode == -1) {
         g_xs_mode = mode;
-        g_xs_force = {0, 0, 0, 0, -1};
+        g_xs_force = {0, 0, 0, 0, -1, 0};
         return QG_OK;
     }
-    if (mode != 1 || rs < 0 || seg < 0 || depth < 0 || nrs < 0 || order < -1 || order > 1) return QG_ERR_SHAPE;
+    if (mode != 1 || rs < 0 || seg < 0 || depth < 0 || nrs < 0 || order < -1 || order > 1 || wg_per_cu < -1 ||
+        wg_per_cu > 8)
+        return QG_ERR_SHAPE;
     g_xs_mode = 1;
-    g_xs_force = {rs, seg, depth, nrs, order};
+    g_xs_force = {rs, seg, depth, nrs, order, wg_per_cu};
     return QG_OK;
 }
 
@@ -103,10 +108,10 @@ bool xs_choose(int fmt, int64_t rows, int64_t cols, int nmat, bool norm, XsCfg *
     const int seg0 = (int)((nchunk + 31) / 32);
     if (seg0 > 32) return false;
     // The built-in choice: rows per row-step and segments (padded by one when
-    // needed) for a whole number of waves, at most 16; ring depth 4; row-steps
+    // needed) for a whole number of waves, at most 16; row-steps
     // per workgroup for about three workgroups per CU (pair) or one (single
     // matrix, whose workgroups are wider).
-    XsCfg c = {0, 0, 0, 0, 1};
+    XsCfg c = {0, 0, 0, 0, 1, 0};
     for (int rs : {2, 1, 4, 8}) {
         for (int seg : {seg0, seg0 + 1}) {
             if ((rs * seg) % 2 == 0 && rs * seg / 2 <= 16 && rs * seg / 2 >= 2 && c.rs == 0) {
@@ -116,22 +121,29 @@ bool xs_choose(int fmt, int64_t rows, int64_t cols, int nmat, bool norm, XsCfg *
         }
     }
     if (c.rs == 0) return false;
-    c.depth = 4;
-    const int64_t steps = (rows + c.rs - 1) / c.rs;
+    // ring depth from back-to-back sweeps of the 27B-class FFN: 2 for the
+    // pair (two matrices already double the loads in flight), 4 for one matrix
+    c.depth = nmat == 2 ? 2 : 4;
+    const int64_t steps = steps_of(c, rows);
     const int64_t want_wg = (int64_t)cu_count() * (nmat == 2 ? 3 : 1);
     int64_t nrs = (steps + want_wg - 1) / want_wg;
-    nrs = (nrs + c.depth - 1) / c.depth * c.depth;
     // tall matrices: more workgroups rather than more LDS per workgroup
     const int64_t room = (int64_t)(kXsMaxLds / sizeof(float)) - (nchunk + 1) * (norm ? 2 * kXStride + 1 : kXStride);
-    const int64_t cap = room / ((int64_t)c.rs * c.seg * nmat) / c.depth * c.depth;
+    const int64_t cap = room / ((int64_t)c.rs * c.seg * nmat);
     if (nrs > cap) nrs = cap;
-    c.nrs = (int)(nrs < c.depth ? c.depth : nrs);
+    c.nrs = (int)(nrs < 1 ? 1 : nrs);
     if (g_xs_mode == 1) {
         if (g_xs_force.rs) c.rs = g_xs_force.rs;
         if (g_xs_force.seg) c.seg = g_xs_force.seg;
         if (g_xs_force.depth) c.depth = g_xs_force.depth;
         if (g_xs_force.nrs) c.nrs = g_xs_force.nrs;
         if (g_xs_force.rr >= 0) c.rr = g_xs_force.rr;
+        if (g_xs_force.wpc >= 0) c.wpc = g_xs_force.wpc;
+    }
+    if (c.wpc > 0) {
+        // exactly wpc workgroups per CU: the row-steps each one takes follow
+        const int64_t grid = (int64_t)c.wpc * cu_count();
+        c.nrs = (int)((steps_of(c, rows) + grid - 1) / grid);
     }
     if (!valid_cfg(c, nmat, nchunk, norm)) return false;
     *out = c;
@@ -160,10 +172,12 @@ hipError_t launch_xs(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, co
     p.rs = c.rs;
     p.nrs = c.nrs;
     const int waves = c.rs * c.seg / 2;
-    const int64_t nwg = ((rows + c.rs - 1) / c.rs + c.nrs - 1) / c.nrs;
+    const int64_t nwg = c.wpc > 0 ? (int64_t)c.wpc * cu_count() : (steps_of(c, rows) + c.nrs - 1) / c.nrs;
     p.ga = c.rr ? (int)nwg : 1;
     p.gb = c.rr ? 1 : c.nrs;
-    const size_t lds = xs_lds_bytes(c, nmat, p.nchunk, gamma != nullptr);
+    size_t lds = xs_lds_bytes(c, nmat, p.nchunk, gamma != nullptr);
+    // at most wpc resident per CU: ask for more than a (wpc+1)-th of the LDS
+    if (c.wpc > 0 && lds <= kXsMaxLds / (c.wpc + 1)) lds = kXsMaxLds / (c.wpc + 1) + 256;
     const int epi = nmat == 2 ? (gamma ? 1 : 0) : (resid ? 2 : 0);
     if (fmt != QG_Q4_0) return hipErrorInvalidValue;
     if (nmat == 1) {

@@ -285,17 +285,29 @@ int qgemv_set_launch_override(int lpr, int r, int waves, int depth, int max_wg, 
  * block of consecutive rows.  mode -1 keeps them on the lane-group kernels
  * (also the effect of any qgemv_set_launch_override shape); mode 1 forces the
  * row-streaming kernel's rows per row-step (rs 1, 2, 4 or 8), 32-lane
- * segments per row (seg: 32 * seg >= blocks per row, rs * seg even, at most
- * 32 waves' worth: rs * seg / 2 <= 16), row-steps in flight per lane (depth
- * 2 or 4; 8 for a single matrix) and row-steps per workgroup (nrs, a multiple
- * of depth) and the order in which row-steps are dealt to workgroups (order
- * 1: round robin, 0: consecutive, -1: built-in); a 0 field keeps the
- * built-in value, and a combination outside
+ * segments per row (seg: 32 * seg >= blocks per row, rs * seg even,
+ * rs * seg / 2 <= 16 waves), row-steps in flight per lane (depth 2 or 4; 8
+ * for a single matrix), row-steps per workgroup (nrs >= 1), the order in
+ * which row-steps are dealt to workgroups (order 1: round robin, 0:
+ * consecutive, -1: built-in) and wg_per_cu (1..8: exactly that many
+ * workgroups per CU, nrs following, and no more resident per CU; 0: off; -1:
+ * built-in); a 0 field keeps the built-in value, and a combination outside
  * these rules falls back to the lane-group kernels.  mode 0 restores the
  * built-in choice.  Results depend on the choice only through summation
  * order.  Per calling thread.  Returns QG_ERR_SHAPE for other modes or
- * negative fields. */
-int qgemv_set_xs_override(int mode, int rs, int seg, int depth, int nrs, int order);
+ * fields out of range. */
+int qgemv_set_xs_override(int mode, int rs, int seg, int depth, int nrs, int order, int wg_per_cu);
+
+/* Measurement export (not the hot path): read `bytes` of device memory at
+ * `buf` (16-byte aligned, a multiple of 16) as 16-byte words with a plain
+ * grid-stride kernel -- wg_per_cu (1..64) workgroups of 256 threads per CU,
+ * `unroll` (2, 4 or 8) loads in flight per thread -- so that bytes / its
+ * device time is the streaming-read rate the products' weight streams are
+ * compared against (the llmoxide blog, section 11, measures its decode
+ * against a kernel that only reads the bytes).  `out` (device, 4-byte
+ * aligned, cu_count * wg_per_cu words) is written only if the XOR of all the
+ * words read hits one fixed value.  One launch. */
+int qgemv_read_probe(const void *buf, int64_t bytes, int wg_per_cu, int unroll, uint32_t *out, void *stream);
 
 /* Measurement hook: the next product kernel that the calling thread
  * launches (a GEMV kernel of any call, or a matrix-core product with its

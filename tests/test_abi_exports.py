@@ -187,11 +187,12 @@ def test_tuning_overrides_are_per_thread(lib):
 
 def test_xs_override_refusals(lib):
     f = lib.qgemv_set_xs_override
-    f.argtypes = [ctypes.c_int] * 6
+    f.argtypes = [ctypes.c_int] * 7
     f.restype = ctypes.c_int
-    assert f(2, 0, 0, 0, 0, -1) == -2     # unknown mode
-    assert f(1, -1, 0, 0, 0, -1) == -2    # negative field
-    assert f(1, 0, 0, 0, 0, 2) == -2      # unknown order
-    assert f(1, 2, 5, 2, 12, 1) == 0
-    assert f(-1, 0, 0, 0, 0, 0) == 0
-    assert f(0, 0, 0, 0, 0, 0) == 0
+    assert f(2, 0, 0, 0, 0, -1, -1) == -2     # unknown mode
+    assert f(1, -1, 0, 0, 0, -1, -1) == -2    # negative field
+    assert f(1, 0, 0, 0, 0, 2, -1) == -2      # unknown order
+    assert f(1, 0, 0, 0, 0, -1, 9) == -2      # too many workgroups per CU
+    assert f(1, 2, 5, 2, 12, 1, 3) == 0
+    assert f(-1, 0, 0, 0, 0, 0, 0) == 0
+    assert f(0, 0, 0, 0, 0, 0, 0) == 0

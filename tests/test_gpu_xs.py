@@ -37,9 +37,10 @@ def _cfgs(nchunk, nmat):
         if (rs * seg) % 2 or rs * seg // 2 > 16 or seg > 32:
             continue
         for d in ((2, 4, 8) if nmat == 1 else (2, 4)):
-            for nrs in (d, 3 * d):
+            for nrs in (1, d, 3 * d + 1):
                 for order in (0, 1):
-                    out.append((rs, seg, d, nrs, order))
+                    out.append((rs, seg, d, nrs, order, 0))
+        out.append((rs, seg, (2, 4, 8)[rs % 3] if nmat == 1 else 2, 0, 1, 1 + rs % 3))   # whole workgroups per CU
     return out
 
 
