@@ -61,6 +61,7 @@ struct XsParams {
     int nchunk;           // cols / 32
     uint32_t row_qbytes;  // quant-plane bytes per row
     uint32_t soff;        // scale-plane offset
+    uint32_t row_sbytes;  // scale-plane bytes per row (2 * nchunk)
     int lprow;            // lanes per row: 32 * segments >= nchunk
     int rs;               // rows per row-step
     int nrs;              // row-steps per workgroup
@@ -69,6 +70,8 @@ struct XsParams {
 };
 
 enum { kEpiPlain = 0, kEpiNorm = 1, kEpiResid = 2 };
+
+constexpr int kXsMaxWaves = 16;   // waves per workgroup, at most
 
 // One row-step of one matrix in flight: the lane's 16 code bytes and f16 scale.
 struct Slot {
@@ -171,10 +174,14 @@ __device__ __forceinline__ float prep_q4(float4 (&v)[8])
     return sum;
 }
 
-template <int FMT, int NMAT, int EPI, int D>
+// PX: 16-byte pieces of x staged per thread (PX * threads >= 8 * chunks); the
+// pieces are held in registers under the first weight loads, so the smaller
+// PX that covers the row keeps more waves resident.
+template <int FMT, int NMAT, int EPI, int D, int PX>
 __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
 {
     static_assert(FMT == QG_Q4_0, "x-stationary GEMV: Q4_0");
+    static_assert(PX == 4 || PX == 8, "pieces per thread");
     constexpr int V = D * NMAT;   // chunk products per lane between reductions
     static_assert(V >= 2 && V <= 32 && (V & (V - 1)) == 0, "power-of-two batch");
     extern __shared__ float4 xs_lds4[];
@@ -192,22 +199,21 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
     const int rstep = p.ga * p.rs;
     const int last = p.rows - 1;
 
-    // LDS: x staged [nchunk + 1][36] (chunks 144 bytes apart, so the lanes' 16-byte
-    // reads of consecutive chunks fall in different banks), then (EPI 1) the
-    // gain the same way and one sum of squares per chunk, then the partial row
-    // sums [segments][nrs][NMAT]
+    // LDS: x (EPI 1: x times the gain) staged [nchunk + 1][36] (chunks 144
+    // bytes apart, so the lanes' 16-byte reads of consecutive chunks fall in
+    // different banks; one spare chunk slot), then (EPI 1) one sum of squares
+    // per wave, then the partial row sums [segments][nrs][NMAT]
     float *xsx = xs_part;
-    float *xsg = xsx + (p.nchunk + 1) * kXStride;   // each staging area has a spare chunk slot
-    float *sq = xsg + (EPI == kEpiNorm ? (p.nchunk + 1) * kXStride : 0);
-    float *part = sq + (EPI == kEpiNorm ? p.nchunk : 0);
+    float *wsq = xsx + (p.nchunk + 1) * kXStride;
+    float *part = wsq + (EPI == kEpiNorm ? kXsMaxWaves : 0);
 
     // x (and the gain) in 16-byte pieces, consecutive threads reading
-    // consecutive pieces, at most 8 per thread (threads >= chunks); issued
-    // before the weight stream so that waiting for them waits for nothing else
+    // consecutive pieces, at most PX per thread; issued before the weight
+    // stream so that waiting for them waits for nothing else
     const int npiece = p.nchunk * 8;
-    float4 xp[8], gp[8];
+    float4 xp[PX], gp[PX];
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
+    for (int k = 0; k < PX; k++) {
         int j = t + k * (int)blockDim.x;
         j = j < npiece ? j : npiece - 1;
         xp[k] = reinterpret_cast<const float4 *>(p.x)[j];
@@ -220,7 +226,9 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
         int row = row0 + i * rstep;
         row = row < last ? row : last;
         const uint32_t qo = __umul24((uint32_t)row, p.row_qbytes) + qcol;
-        const uint32_t so = __umul24((uint32_t)row, (uint32_t)p.nchunk) * 2u + scol;
+        // one 24-bit multiply-add each (a wider form made the compiler wait for
+        // the loads in flight before every refill)
+        const uint32_t so = __umul24((uint32_t)row, p.row_sbytes) + scol;
 #pragma unroll
         for (int m = 0; m < NMAT; m++) {
             st[s][m].q = *reinterpret_cast<const uint4 *>(p.q[m] + qo);
@@ -233,38 +241,39 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
 
     // branch-free (a divergent branch here would make the compiler wait for
     // the weight stream too, and keep the pieces in scratch): a piece past the
-    // end goes to the spare slot after the last chunk
+    // end goes to the spare slot after the last chunk.  EPI 1: the sum of x^2
+    // over this thread's pieces (a repeated piece past the end adds 0), and
+    // x times the gain is what is staged.
+    float ss = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
+    for (int k = 0; k < PX; k++) {
         const int j = t + k * (int)blockDim.x;
         const int at = j < npiece ? (j >> 3) * kXStride + (j & 7) * 4 : p.nchunk * kXStride;
-        *reinterpret_cast<f32x4 *>(xsx + at) = f32x4{xp[k].x, xp[k].y, xp[k].z, xp[k].w};
-        if constexpr (EPI == kEpiNorm)
-            *reinterpret_cast<f32x4 *>(xsg + at) = f32x4{gp[k].x, gp[k].y, gp[k].z, gp[k].w};
+        float4 v = xp[k];
+        if constexpr (EPI == kEpiNorm) {
+            float q = v.x * v.x;
+            q = __builtin_fmaf(v.y, v.y, q);
+            q = __builtin_fmaf(v.z, v.z, q);
+            q = __builtin_fmaf(v.w, v.w, q);
+            ss += j < npiece ? q : 0.0f;
+            v.x *= gp[k].x;
+            v.y *= gp[k].y;
+            v.z *= gp[k].z;
+            v.w *= gp[k].w;
+        }
+        *reinterpret_cast<f32x4 *>(xsx + at) = f32x4{v.x, v.y, v.z, v.w};
+    }
+    if constexpr (EPI == kEpiNorm) {
+        // wave sum by an xor butterfly (partners add the same two values, so
+        // every lane ends with the same bits), one slot per wave
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+        if (lane == 0) wsq[t >> 6] = ss;
     }
     __syncthreads();
     float4 xv[8];
 #pragma unroll
     for (int k = 0; k < 8; k++) xv[k] = *reinterpret_cast<const float4 *>(xsx + c * kXStride + k * 4);
-
-    float ss = 0.0f;   // EPI 1: this chunk's sum of x^2 (raw x, column order)
-    if constexpr (EPI == kEpiNorm) {
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-            ss = __builtin_fmaf(xv[k].x, xv[k].x, ss);
-            ss = __builtin_fmaf(xv[k].y, xv[k].y, ss);
-            ss = __builtin_fmaf(xv[k].z, xv[k].z, ss);
-            ss = __builtin_fmaf(xv[k].w, xv[k].w, ss);
-        }
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-            const float4 g = *reinterpret_cast<const float4 *>(xsg + c * kXStride + k * 4);
-            xv[k].x *= g.x;
-            xv[k].y *= g.y;
-            xv[k].z *= g.z;
-            xv[k].w *= g.w;
-        }
-    }
 #pragma unroll
     for (int k = 0; k < 8; k++) {
         xv[k].x = live ? xv[k].x : 0.0f;
@@ -276,11 +285,10 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
 
     float norm_scale = 1.0f;
     if constexpr (EPI == kEpiNorm) {
-        // every workgroup adds the same per-chunk sums in chunk order: one scale
-        if (phase == 0 && live) sq[c] = ss;
-        __syncthreads();
+        // the wave sums in wave order: the same scale in every workgroup
         float tot = 0.0f;
-        for (int k = 0; k < p.nchunk; k++) tot += sq[k];
+        const int nw = (int)blockDim.x >> 6;
+        for (int w = 0; w < nw; w++) tot += wsq[w];
         norm_scale = 1.0f / sqrtf(tot / (float)(p.nchunk * kChunk) + p.eps);
     }
 

@@ -16,10 +16,10 @@ namespace {
 thread_local int g_xs_mode = 0;
 thread_local XsCfg g_xs_force = {0, 0, 0, 0, -1, 0};
 
-template <int FMT, int NMAT, int EPI, int D>
+template <int FMT, int NMAT, int EPI, int D, int PX>
 hipError_t go(const XsParams &p, int waves, int64_t nwg, size_t lds, hipStream_t s)
 {
-    auto kern = xs_detail::gemv_xs_kernel<FMT, NMAT, EPI, D>;
+    auto kern = xs_detail::gemv_xs_kernel<FMT, NMAT, EPI, D, PX>;
     if (lds > 65536) {
         static std::atomic<int> configured[64];
         int dev = 0;
@@ -40,29 +40,37 @@ hipError_t go(const XsParams &p, int waves, int64_t nwg, size_t lds, hipStream_t
     return hipGetLastError();
 }
 
-template <int FMT, int NMAT, int EPI>
+template <int FMT, int NMAT, int EPI, int PX>
 hipError_t by_depth(const XsParams &p, int depth, int waves, int64_t nwg, size_t lds, hipStream_t s)
 {
     switch (depth) {
-    case 2: return go<FMT, NMAT, EPI, 2>(p, waves, nwg, lds, s);
-    case 4: return go<FMT, NMAT, EPI, 4>(p, waves, nwg, lds, s);
+    case 2: return go<FMT, NMAT, EPI, 2, PX>(p, waves, nwg, lds, s);
+    case 4: return go<FMT, NMAT, EPI, 4, PX>(p, waves, nwg, lds, s);
     case 8:
-        if constexpr (NMAT == 1) return go<FMT, NMAT, EPI, 8>(p, waves, nwg, lds, s);
+        if constexpr (NMAT == 1) return go<FMT, NMAT, EPI, 8, PX>(p, waves, nwg, lds, s);
         break;
     }
     return hipErrorInvalidValue;
 }
 
-// LDS of a workgroup: the partial row sums of every segment, plus (normalized
-// input) one sum of squares per chunk.
+// x's pieces per thread: 4 when they cover the row, else 8 (threads >= chunks)
+template <int FMT, int NMAT, int EPI>
+hipError_t by_pieces(const XsParams &p, int depth, int waves, int64_t nwg, size_t lds, hipStream_t s)
+{
+    if ((int64_t)p.nchunk * 8 <= (int64_t)4 * 64 * waves) return by_depth<FMT, NMAT, EPI, 4>(p, depth, waves, nwg, lds, s);
+    return by_depth<FMT, NMAT, EPI, 8>(p, depth, waves, nwg, lds, s);
+}
+
+// LDS of a workgroup: x staged with a spare chunk slot, (normalized input)
+// one sum of squares per wave, and the partial row sums of every segment.
 size_t xs_lds_bytes(const XsCfg &c, int nmat, int64_t nchunk, bool norm)
 {
-    const size_t staged = (size_t)(nchunk + 1) * kXStride * (norm ? 2 : 1) + (norm ? (size_t)nchunk : 0);
+    const size_t staged = (size_t)(nchunk + 1) * kXStride + (norm ? (size_t)xs_detail::kXsMaxWaves : 0);
     return (staged + (size_t)c.rs * c.seg * c.nrs * nmat) * sizeof(float);
 }
 
 // a workgroup's LDS may use all of a CU's 160 KB (x of a row of 1024 chunks
-// alone takes 144 KB; with the gain staged too, rows of up to 540 chunks fit)
+// alone takes 144 KB)
 constexpr size_t kXsMaxLds = 160 * 1024;
 
 int64_t steps_of(const XsCfg &c, int64_t rows) { return (rows + c.rs - 1) / c.rs; }
@@ -72,7 +80,7 @@ bool valid_cfg(const XsCfg &c, int nmat, int64_t nchunk, bool norm)
     if (c.wpc > 0 && xs_lds_bytes(c, nmat, nchunk, norm) > kXsMaxLds / c.wpc) return false;
     if (c.rs < 1 || c.rs > 8 || (c.rs & (c.rs - 1))) return false;
     if (c.seg * 32 < nchunk || c.seg > 32) return false;
-    if ((c.rs * c.seg) % 2 || c.rs * c.seg / 2 > 16) return false;
+    if ((c.rs * c.seg) % 2 || c.rs * c.seg / 2 > xs_detail::kXsMaxWaves) return false;
     if (!(c.depth == 2 || c.depth == 4 || (c.depth == 8 && nmat == 1))) return false;
     return c.nrs >= 1 && xs_lds_bytes(c, nmat, nchunk, norm) <= kXsMaxLds;
 }
@@ -128,7 +136,7 @@ bool xs_choose(int fmt, int64_t rows, int64_t cols, int nmat, bool norm, XsCfg *
     const int64_t want_wg = (int64_t)cu_count() * (nmat == 2 ? 3 : 1);
     int64_t nrs = (steps + want_wg - 1) / want_wg;
     // tall matrices: more workgroups rather than more LDS per workgroup
-    const int64_t room = (int64_t)(kXsMaxLds / sizeof(float)) - (nchunk + 1) * (norm ? 2 * kXStride + 1 : kXStride);
+    const int64_t room = (int64_t)(kXsMaxLds / sizeof(float)) - (nchunk + 1) * kXStride - (norm ? xs_detail::kXsMaxWaves : 0);
     const int64_t cap = room / ((int64_t)c.rs * c.seg * nmat);
     if (nrs > cap) nrs = cap;
     c.nrs = (int)(nrs < 1 ? 1 : nrs);
@@ -168,6 +176,7 @@ hipError_t launch_xs(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, co
     p.nchunk = (int)(cols / kChunk);
     p.row_qbytes = (uint32_t)L.row_qbytes;
     p.soff = (uint32_t)L.splane_off;
+    p.row_sbytes = (uint32_t)(2 * p.nchunk);
     p.lprow = 32 * c.seg;
     p.rs = c.rs;
     p.nrs = c.nrs;
@@ -181,11 +190,11 @@ hipError_t launch_xs(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, co
     const int epi = nmat == 2 ? (gamma ? 1 : 0) : (resid ? 2 : 0);
     if (fmt != QG_Q4_0) return hipErrorInvalidValue;
     if (nmat == 1) {
-        if (epi == 2) return by_depth<QG_Q4_0, 1, 2>(p, c.depth, waves, nwg, lds, s);
-        return by_depth<QG_Q4_0, 1, 0>(p, c.depth, waves, nwg, lds, s);
+        if (epi == 2) return by_pieces<QG_Q4_0, 1, 2>(p, c.depth, waves, nwg, lds, s);
+        return by_pieces<QG_Q4_0, 1, 0>(p, c.depth, waves, nwg, lds, s);
     }
-    if (epi == 1) return by_depth<QG_Q4_0, 2, 1>(p, c.depth, waves, nwg, lds, s);
-    return by_depth<QG_Q4_0, 2, 0>(p, c.depth, waves, nwg, lds, s);
+    if (epi == 1) return by_pieces<QG_Q4_0, 2, 1>(p, c.depth, waves, nwg, lds, s);
+    return by_pieces<QG_Q4_0, 2, 0>(p, c.depth, waves, nwg, lds, s);
 }
 
 } // namespace qg
