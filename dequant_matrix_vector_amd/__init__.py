@@ -16,7 +16,7 @@ __all__ = [
     "qgemv", "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_k", "qgemv_i8row", "qgemv_q6_k",
     "swiglu_gate_up", "swiglu_ffn", "swiglu_ffn_noalloc", "qdequant", "layout_version", "set_launch_override",
     "set_prefill_override", "set_xs_override", "prefill_plan", "swiglu_ffn_scratch_elems", "swiglu_ffn_block", "swiglu_ffn_block_scratch_elems",
-    "qgemv_argmax", "qgemv_head_argmax", "qgemv_q8act", "swiglu_ffn_q8act", "qquantize_q8_0",
+    "qgemv_argmax", "qgemv_head_argmax", "head_argmax_workspace_bytes", "qgemv_q8act", "swiglu_ffn_q8act", "qquantize_q8_0",
     "qgemv_repack_q4_0", "qgemv_repack_q8_0", "qgemv_repack_q4_k", "qgemv_repack_i8row", "qgemv_repack_q6_k",
 ]
 
@@ -66,6 +66,10 @@ lib.qgemv_argmax.argtypes = [_P, _P, _I64, _I64, _P]
 lib.qgemv_argmax.restype = _I
 lib.qgemv_head_argmax.argtypes = [_I, _P, _P, _P, _P, _I64, _I64, _I64, _P]
 lib.qgemv_head_argmax.restype = _I
+lib.qgemv_head_argmax_ws.argtypes = [_I, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]
+lib.qgemv_head_argmax_ws.restype = _I
+lib.qgemv_head_argmax_workspace_bytes.argtypes = [_I, _I64, _I64]
+lib.qgemv_head_argmax_workspace_bytes.restype = _I64
 lib.qdequant.argtypes = [_I, _P, _P, _I64, _I64, _P]
 lib.qdequant.restype = _I
 lib.qgemv_q8act.argtypes = [_I, _P, _P, _P, _I64, _I64, _I64, _P]
@@ -451,8 +455,19 @@ def qgemv_argmax(logits, n, token=None, stream=None) -> torch.Tensor:
     return token
 
 
-def qgemv_head_argmax(fmt, packed, x, rows, cols, logits=None, token=None, stream=None):
-    """(token int32 [n_tok], logits [n_tok][rows]): the head product then greedy sampling."""
+def head_argmax_workspace_bytes(fmt, rows, cols):
+    """Bytes of the zero-filled workspace the fused head needs (host only)."""
+    n = lib.qgemv_head_argmax_workspace_bytes(_fmt(fmt), rows, cols)
+    _check(n if n < 0 else 0, "qgemv_head_argmax_workspace_bytes")
+    return n
+
+
+def qgemv_head_argmax(fmt, packed, x, rows, cols, logits=None, token=None, workspace=None, fused=False, stream=None):
+    """(token int32 [n_tok], logits [n_tok][rows]): the head product and greedy
+    sampling: the product, then the argmax launch; or (fused, one token) one
+    launch, with workspace (uint8, at least head_argmax_workspace_bytes,
+    zero-filled before its first use and left ready by every call; a
+    zero-filled one is made when none is given)."""
     n_tok = _ntok(x, cols)
     logits = _y(logits, (n_tok, rows), x.device)
     if token is None:
@@ -461,7 +476,16 @@ def qgemv_head_argmax(fmt, packed, x, rows, cols, logits=None, token=None, strea
     _arg(x, "x", F32)
     _arg(logits, "logits", F32, n_tok * rows)
     _arg(token, "token", I32, n_tok)
-    _on_gpu(packed, x, logits, token)
-    _check(lib.qgemv_head_argmax(_fmt(fmt), _ptr(packed), _ptr(x), _ptr(logits), _ptr(token), rows, cols, n_tok,
-                                 _stream(stream)), "qgemv_head_argmax")
+    if not fused:
+        _on_gpu(packed, x, logits, token)
+        _check(lib.qgemv_head_argmax(_fmt(fmt), _ptr(packed), _ptr(x), _ptr(logits), _ptr(token), rows, cols, n_tok,
+                                     _stream(stream)), "qgemv_head_argmax")
+        return token, logits
+    need = head_argmax_workspace_bytes(fmt, rows, cols)
+    if workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    _arg(workspace, "workspace", U8, need)
+    _on_gpu(packed, x, logits, token, workspace)
+    _check(lib.qgemv_head_argmax_ws(_fmt(fmt), _ptr(packed), _ptr(x), _ptr(logits), _ptr(token), rows, cols, n_tok,
+                                    _ptr(workspace), workspace.numel(), _stream(stream)), "qgemv_head_argmax_ws")
     return token, logits

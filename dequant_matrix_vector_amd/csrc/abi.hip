@@ -493,6 +493,49 @@ int qgemv_head_argmax(int fmt, const void *packed, const float *x, float *logits
     return launch_argmax(logits, token, rows, n_tok, (hipStream_t)stream) == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
+// Workspace of the fused head, laid out alike for every shape (so one
+// workspace serves heads of several shapes): the counters (a top counter,
+// then 64 group counters, each on its own 128-byte line), then one 8-byte
+// candidate per workgroup (a workgroup writes at least one row, so rows
+// candidates always suffice).
+static const int64_t kAmCounterBytes = 128 * (1 + 64);
+
+int64_t qgemv_head_argmax_workspace_bytes(int fmt, int64_t rows, int64_t cols)
+{
+    if (!valid_fmt(fmt)) return QG_ERR_FORMAT;
+    Layout L;
+    if (!layout_for(fmt, rows, cols, &L)) return QG_ERR_SHAPE;
+    return kAmCounterBytes + 8 * rows;
+}
+
+int qgemv_head_argmax_ws(int fmt, const void *packed, const float *x, float *logits, int32_t *token, int64_t rows,
+                         int64_t cols, int64_t n_tok, void *workspace, int64_t workspace_bytes, void *stream)
+{
+    if (n_tok != 1) return qgemv_head_argmax(fmt, packed, x, logits, token, rows, cols, n_tok, stream);
+    Layout L;
+    int st = check_product(fmt, packed, x, logits, rows, cols, n_tok, &L);
+    if (st) return st;
+    if (!token || !workspace) return QG_ERR_NULL;
+    if (!aligned(token, 4) || !aligned(workspace, 16)) return QG_ERR_ALIGN;
+    const int64_t hdr = kAmCounterBytes;
+    if (workspace_bytes < hdr + 8 * rows) return QG_ERR_SCRATCH;
+    if (overlap(token, 4, logits, rows * 4) || overlap(token, 4, x, cols * 4) || overlap(token, 4, packed, L.total) ||
+        overlap(workspace, workspace_bytes, token, 4) || overlap(workspace, workspace_bytes, logits, rows * 4) ||
+        overlap(workspace, workspace_bytes, x, cols * 4) || overlap(workspace, workspace_bytes, packed, L.total))
+        return QG_ERR_ALIAS;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    ArgmaxOut am;
+    am.count = reinterpret_cast<uint32_t *>(ws);
+    am.cand = reinterpret_cast<uint2 *>(ws + hdr);
+    am.max_cand = (workspace_bytes - hdr) / 8;
+    am.token = token;
+    const GemvCfg cfg = choose_cfg(fmt, rows, cols, 1);
+    return launch_gemv(fmt, static_cast<const uint8_t *>(packed), x, logits, rows, cols, (hipStream_t)stream, cfg,
+                       nullptr, &am) == hipSuccess
+               ? QG_OK
+               : QG_ERR_LAUNCH;
+}
+
 // ------------------------------------------------------ Q8_0 activations --
 static bool q8act_fmt(int fmt) { return fmt == QG_Q4_0 || fmt == QG_Q8_0; }
 

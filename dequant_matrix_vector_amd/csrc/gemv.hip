@@ -13,12 +13,13 @@ namespace {
 template <int NMAT>
 hipError_t dispatch_fmt(int fmt, const GemvParams &p, const GemvCfg &c, hipStream_t s)
 {
-    // NMAT 1 with a residual, NMAT 2 with a normalized input, else plain
-    const int epi = (NMAT == 1 && p.resid) ? 2 : ((NMAT == 2 && p.gamma) ? 1 : 0);
+    // NMAT 1 with its argmax or a residual, NMAT 2 with a normalized input, else plain
+    const int epi = (NMAT == 1 && p.am_cand) ? 3 : ((NMAT == 1 && p.resid) ? 2 : ((NMAT == 2 && p.gamma) ? 1 : 0));
 #define QG_FMT(F)                                                                                  \
     case F:                                                                                        \
         if (epi == 0) return gemv_dispatch<F, NMAT, 0>(p, c, s);                                   \
         if constexpr (NMAT == 2) return gemv_dispatch<F, 2, 1>(p, c, s);                           \
+        else if (epi == 3) return gemv_dispatch<F, 1, 3>(p, c, s);                                 \
         else return gemv_dispatch<F, 1, 2>(p, c, s);
     switch (fmt) {
         QG_FMT(QG_Q4_0)
@@ -186,14 +187,15 @@ GemvCfg choose_cfg(int fmt, int64_t rows, int64_t cols, int nmat)
 }
 
 hipError_t launch_gemv(int fmt, const uint8_t *packed, const float *x, float *y, int64_t rows,
-                       int64_t cols, hipStream_t s, const GemvCfg &cfg, const float *resid)
+                       int64_t cols, hipStream_t s, const GemvCfg &cfg, const float *resid, const ArgmaxOut *am)
 {
     Layout L;
     if (!layout_for(fmt & ~kQ8Act, rows, cols, &L)) return hipErrorInvalidValue;
+    if (am && (resid || (fmt & kQ8Act))) return hipErrorInvalidValue;
     GemvCfg forced;
     XsCfg xc;
     if (!launch_override(&forced) && xs_choose(fmt, rows, cols, 1, false, &xc))
-        return launch_xs(fmt, 1, packed, nullptr, x, y, rows, cols, xc, s, nullptr, 0.0f, resid);
+        return launch_xs(fmt, 1, packed, nullptr, x, y, rows, cols, xc, s, nullptr, 0.0f, resid, am);
     GemvParams p;
     p.q[0] = packed;
     p.q[1] = packed;
@@ -208,6 +210,10 @@ hipError_t launch_gemv(int fmt, const uint8_t *packed, const float *x, float *y,
     p.resid = resid;
     p.hoff = L.hplane_off;
     p.doff = L.dplane_off;
+    p.am_cand = am ? am->cand : nullptr;
+    p.am_max = am ? am->max_cand : 0;
+    p.am_count = am ? am->count : nullptr;
+    p.am_token = am ? am->token : nullptr;
     return dispatch_fmt<1>(fmt, p, aligned_cfg(fmt, p.nchunk, cfg), s);
 }
 
@@ -235,6 +241,10 @@ hipError_t launch_gate_up(int fmt, const uint8_t *wg, const uint8_t *wu, const f
     p.resid = nullptr;
     p.hoff = L.hplane_off;
     p.doff = L.dplane_off;
+    p.am_cand = nullptr;
+    p.am_max = 0;
+    p.am_count = nullptr;
+    p.am_token = nullptr;
     return dispatch_fmt<2>(fmt, p, aligned_cfg(fmt, p.nchunk, cfg), s);
 }
 

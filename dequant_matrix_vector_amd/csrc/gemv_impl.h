@@ -83,9 +83,115 @@ struct GemvParams {
     const float *resid;   // EPI 2: residual [rows], added to y (may be y itself)
     int64_t hoff;         // Q6_K: offsets of the high-bit plane and the f16 d plane
     int64_t doff;
+    uint2 *am_cand;       // EPI 3: one (value bits, index) candidate per workgroup
+    int64_t am_max;       // EPI 3: room for candidates (workgroups) in am_cand
+    uint32_t *am_count;   // EPI 3: workgroups done (zero before the launch; left zero)
+    int32_t *am_token;    // EPI 3: the index of the largest y
 };
 
-enum { kEpiPlain = 0, kEpiNorm = 1, kEpiResid = 2 };
+enum { kEpiPlain = 0, kEpiNorm = 1, kEpiResid = 2, kEpiArgmax = 3 };
+
+// Greedy sampling fused into the product (EPI 3; the Go "llm" package's
+// Argmax, which runs on the GPU so that only the token leaves it): the first
+// index of the largest y.  An in-order scan's result has a closed form that
+// any order of comparisons reaches -- if y[0] is NaN the answer is 0 (nothing
+// compares greater); otherwise NaN never wins and the answer is the smallest
+// index whose value equals the maximum (-0 equal to +0) -- so each thread
+// keeps (value, index) under "greater value, or equal value and smaller
+// index" over the rows it writes, and candidates combine by the same rule.
+__device__ __forceinline__ void am_take(float &bv, int &bi, float v, int i)
+{
+    if (v > bv || (v == bv && i < bi)) {   // NaN v: both false, never taken
+        bv = v;
+        bi = i;
+    }
+}
+
+// The workgroup's candidate, then the launch's token.  Each workgroup writes
+// its candidate with a device-coherent store (written through to where every
+// XCD reads it), waits for that store, then counts itself done with a
+// device-scope atomic -- on one of up to kAmGroups group counters (workgroup
+// b on counter b % groups, one 128-byte line each), whose last member counts
+// its group done on the top counter, so that no counter takes more than a few
+// dozen atomics at once; the last group's finisher reads every candidate with
+// device-coherent loads and writes the token.  Each finisher sets its counter
+// back to zero for the next launch.  No cache-wide fence: nothing else
+// crosses between workgroups (whether y[0] is NaN travels in the candidate of
+// the workgroup that wrote row 0, as index -1).  Every thread of the
+// workgroup calls this once, after its last row; nan0: this thread wrote row
+// 0 and it is NaN.  count: the top counter, then the kAmGroups group
+// counters, kAmLineWords words (128 bytes) apart.
+constexpr int kAmGroups = 64;
+constexpr int kAmLineWords = 32;
+
+__device__ __forceinline__ void am_finish(float bv, int bi, bool nan0, uint2 *cand, uint32_t *count, int32_t *token)
+{
+    __shared__ float am_v[16];
+    __shared__ int am_i[16];
+    __shared__ int am_n[16];
+    __shared__ int am_last;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    auto wg_reduce = [&](float &v, int &i, bool &n) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(v, off, 64);
+            const int oi = __shfl_xor(i, off, 64);
+            n = __shfl_xor((int)n, off, 64) != 0 || n;
+            am_take(v, i, ov, oi);
+        }
+        if (lane == 0) {
+            am_v[wave] = v;
+            am_i[wave] = i;
+            am_n[wave] = n;
+        }
+        __syncthreads();
+        v = am_v[0];
+        i = am_i[0];
+        n = am_n[0] != 0;
+        for (int w = 1; w < nw; w++) {
+            am_take(v, i, am_v[w], am_i[w]);
+            n = n || am_n[w] != 0;
+        }
+        __syncthreads();
+    };
+    wg_reduce(bv, bi, nan0);
+    if (threadIdx.x == 0) {
+        const uint32_t idx = nan0 ? 0xFFFFFFFFu : (uint32_t)bi;
+        __hip_atomic_store(reinterpret_cast<uint64_t *>(cand) + blockIdx.x,
+                           (uint64_t)__builtin_bit_cast(uint32_t, bv) | ((uint64_t)idx << 32), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        // the candidate is written through before the count can be seen
+        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        const uint32_t grid = gridDim.x, groups = grid < kAmGroups ? grid : kAmGroups;
+        const uint32_t grp = blockIdx.x % groups;
+        const uint32_t members = (grid - grp + groups - 1) / groups;   // workgroups b < grid with b % groups == grp
+        uint32_t *sub = count + kAmLineWords * (1 + grp);
+        int last = 0;
+        if (__hip_atomic_fetch_add(sub, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1) {
+            __hip_atomic_store(sub, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == groups - 1;
+        }
+        am_last = last;
+    }
+    __syncthreads();
+    if (!am_last) return;
+    float v = -__builtin_inff();
+    int i = 0x7FFFFFFF;   // loses to every value, -inf included
+    bool n = false;
+    for (int j = threadIdx.x; j < (int)gridDim.x; j += blockDim.x) {
+        const uint64_t c = __hip_atomic_load(reinterpret_cast<const uint64_t *>(cand) + j, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(c >> 32) == 0xFFFFFFFFu) n = true;
+        else am_take(v, i, __builtin_bit_cast(float, (uint32_t)c), (int)(c >> 32));
+    }
+    wg_reduce(v, i, n);
+    if (threadIdx.x == 0) {
+        *token = n ? 0 : i;
+        __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
 
 __device__ __forceinline__ float half_lo(uint32_t v)
 {
@@ -548,6 +654,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
     constexpr bool NORM = EPI == kEpiNorm;
     constexpr int BF = FMT & 7;   // the weight format (FMT may carry kQ8Act)
     static_assert((FMT & kQ8Act) == 0 || EPI == kEpiPlain, "Q8_0 activations: plain epilogue only");
+    static_assert(EPI != kEpiArgmax || NMAT == 1, "argmax of one product");
     extern __shared__ float4 qg_lds[];
     float *xs = reinterpret_cast<float *>(qg_lds);
 
@@ -673,6 +780,9 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
         norm_scale = 1.0f / sqrtf(tot / (float)(p.nchunk * kChunk) + p.eps);
     }
 
+    float am_v = -__builtin_inff();   // EPI 3: this thread's best (value, index) so far
+    int am_i = 0x7FFFFFFF;
+    bool am_nan0 = false;            // EPI 3: this thread wrote row 0 and it is NaN
     for (; batch < nbatch; batch += bstride) {
         float rv[R];   // EPI 2: the residual of this lane group's rows, loaded before the weight stream's waits
         if constexpr (EPI == kEpiResid) {
@@ -759,12 +869,17 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
                         for (int m = 0; m < NMAT; m++) v[m] *= norm_scale;
                     }
                     if constexpr (EPI == kEpiResid) v[0] += rv[r];
+                    if constexpr (EPI == kEpiArgmax) {
+                        am_take(am_v, am_i, v[0], (int)row);
+                        if (row == 0 && v[0] != v[0]) am_nan0 = true;
+                    }
                     if (NMAT == 1) p.y[row] = v[0];
                     else p.y[row] = silu_mul(v[0], v[NMAT - 1]);
                 }
             }
         }
     }
+    if constexpr (EPI == kEpiArgmax) am_finish(am_v, am_i, am_nan0, p.am_cand, p.am_count, p.am_token);
 }
 
 template <int FMT, int LPR, int R, int NMAT, int D, int CPL, int EPI>
@@ -774,6 +889,7 @@ hipError_t go(const GemvParams &p, const GemvCfg &c, hipStream_t s)
     const int64_t batches = (p.rows + G * R - 1) / (G * R);
     int64_t nwg = (batches + c.waves - 1) / c.waves;
     if (c.max_wg > 0 && nwg > c.max_wg) nwg = c.max_wg;
+    if (EPI == kEpiArgmax && nwg > p.am_max) return hipErrorInvalidValue;
     // NORM: 16 more floats after the spare chunk for the wave sums of x^2
     const size_t lds = gemv_lds_bytes((int64_t)p.nchunk * kChunk) + (EPI == kEpiNorm ? 64 : 0);
     auto kern = gemv_kernel<FMT, LPR, R, NMAT, D, CPL, EPI>;
@@ -835,7 +951,8 @@ hipError_t dispatch(const GemvParams &p, const GemvCfg &c, hipStream_t s)
 } // namespace gemv_detail
 
 // Per-format entry points, each instantiated in its own translation unit.
-// EPI: plain, the normalized-input gate/up (NMAT 2) or the residual down (NMAT 1).
+// EPI: plain, the normalized-input gate/up (NMAT 2), the residual down (NMAT 1)
+// or the product with its argmax (NMAT 1).
 template <int FMT, int NMAT, int EPI>
 hipError_t gemv_dispatch(const gemv_detail::GemvParams &p, const GemvCfg &c, hipStream_t s);
 

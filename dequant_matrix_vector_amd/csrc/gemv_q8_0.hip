@@ -27,4 +27,10 @@ hipError_t gemv_dispatch<QG_Q8_0, 1, 2>(const gemv_detail::GemvParams &p, const 
     return gemv_detail::dispatch<QG_Q8_0, 1, gemv_detail::kEpiResid>(p, c, s);
 }
 
+template <>
+hipError_t gemv_dispatch<QG_Q8_0, 1, 3>(const gemv_detail::GemvParams &p, const GemvCfg &c, hipStream_t s)
+{
+    return gemv_detail::dispatch<QG_Q8_0, 1, gemv_detail::kEpiArgmax>(p, c, s);
+}
+
 } // namespace qg

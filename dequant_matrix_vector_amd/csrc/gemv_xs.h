@@ -49,6 +49,8 @@ using gemv_detail::half_lo;
 using gemv_detail::silu_mul;
 using gemv_detail::f32x4;
 using gemv_detail::static_for;
+using gemv_detail::am_take;
+using gemv_detail::am_finish;
 
 struct XsParams {
     const uint8_t *q[2];  // packed tensors (quant plane at offset 0)
@@ -67,9 +69,12 @@ struct XsParams {
     int nrs;              // row-steps per workgroup
     int ga, gb;           // global row-step of local step i in workgroup b: i * ga + b * gb
                           // (ga = 1, gb = nrs: consecutive steps; ga = grid, gb = 1: round robin)
+    uint2 *am_cand;       // EPI 3: one (value bits, index) candidate per workgroup
+    uint32_t *am_count;   // EPI 3: workgroups done (zero before the launch; left zero)
+    int32_t *am_token;    // EPI 3: the index of the largest y
 };
 
-enum { kEpiPlain = 0, kEpiNorm = 1, kEpiResid = 2 };
+enum { kEpiPlain = 0, kEpiNorm = 1, kEpiResid = 2, kEpiArgmax = 3 };
 
 constexpr int kXsMaxWaves = 16;   // waves per workgroup, at most
 
@@ -182,6 +187,7 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
 {
     static_assert(FMT == QG_Q4_0, "x-stationary GEMV: Q4_0");
     static_assert(PX == 4 || PX == 8, "pieces per thread");
+    static_assert(EPI != kEpiArgmax || NMAT == 1, "argmax of one product");
     constexpr int V = D * NMAT;   // chunk products per lane between reductions
     static_assert(V >= 2 && V <= 32 && (V & (V - 1)) == 0, "power-of-two batch");
     extern __shared__ float4 xs_lds4[];
@@ -332,6 +338,9 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
     __syncthreads();
 
     // one thread per row: the row phase's segments in order
+    float am_v = -__builtin_inff();   // EPI 3: this thread's best (value, index)
+    int am_i = 0x7FFFFFFF;
+    bool am_nan0 = false;            // EPI 3: this thread wrote row 0 and it is NaN
     for (int j = t; j < p.rs * p.nrs; j += blockDim.x) {
         const int ph = j % p.rs, i = j / p.rs;
         const int row = blockIdx.x * p.gb * p.rs + i * rstep + ph;
@@ -348,9 +357,14 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
             for (int m = 0; m < NMAT; m++) a[m] *= norm_scale;
         }
         if constexpr (EPI == kEpiResid) a[0] += p.resid[row];
+        if constexpr (EPI == kEpiArgmax) {
+            am_take(am_v, am_i, a[0], row);
+            if (row == 0 && a[0] != a[0]) am_nan0 = true;
+        }
         if constexpr (NMAT == 1) p.y[row] = a[0];
         else p.y[row] = silu_mul(a[0], a[NMAT - 1]);
     }
+    if constexpr (EPI == kEpiArgmax) am_finish(am_v, am_i, am_nan0, p.am_cand, p.am_count, p.am_token);
 }
 
 } // namespace xs_detail
@@ -370,6 +384,6 @@ struct XsCfg {
 bool xs_choose(int fmt, int64_t rows, int64_t cols, int nmat, bool norm, XsCfg *c);
 hipError_t launch_xs(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, const float *x, float *y,
                      int64_t rows, int64_t cols, const XsCfg &c, hipStream_t s, const float *gamma, float eps,
-                     const float *resid);
+                     const float *resid, const ArgmaxOut *am = nullptr);
 
 } // namespace qg

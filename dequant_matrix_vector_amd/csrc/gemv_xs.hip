@@ -160,7 +160,7 @@ bool xs_choose(int fmt, int64_t rows, int64_t cols, int nmat, bool norm, XsCfg *
 
 hipError_t launch_xs(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, const float *x, float *y,
                      int64_t rows, int64_t cols, const XsCfg &c, hipStream_t s, const float *gamma, float eps,
-                     const float *resid)
+                     const float *resid, const ArgmaxOut *am)
 {
     Layout L;
     if (!layout_for(fmt, rows, cols, &L)) return hipErrorInvalidValue;
@@ -184,12 +184,17 @@ hipError_t launch_xs(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, co
     const int64_t nwg = c.wpc > 0 ? (int64_t)c.wpc * cu_count() : (steps_of(c, rows) + c.nrs - 1) / c.nrs;
     p.ga = c.rr ? (int)nwg : 1;
     p.gb = c.rr ? 1 : c.nrs;
+    p.am_cand = am ? am->cand : nullptr;
+    p.am_count = am ? am->count : nullptr;
+    p.am_token = am ? am->token : nullptr;
+    if (am && (nmat != 1 || nwg > am->max_cand)) return hipErrorInvalidValue;
     size_t lds = xs_lds_bytes(c, nmat, p.nchunk, gamma != nullptr);
     // at most wpc resident per CU: ask for more than a (wpc+1)-th of the LDS
     if (c.wpc > 0 && lds <= kXsMaxLds / (c.wpc + 1)) lds = kXsMaxLds / (c.wpc + 1) + 256;
-    const int epi = nmat == 2 ? (gamma ? 1 : 0) : (resid ? 2 : 0);
+    const int epi = nmat == 2 ? (gamma ? 1 : 0) : (am ? 3 : (resid ? 2 : 0));
     if (fmt != QG_Q4_0) return hipErrorInvalidValue;
     if (nmat == 1) {
+        if (epi == 3) return by_pieces<QG_Q4_0, 1, 3>(p, c.depth, waves, nwg, lds, s);
         if (epi == 2) return by_pieces<QG_Q4_0, 1, 2>(p, c.depth, waves, nwg, lds, s);
         return by_pieces<QG_Q4_0, 1, 0>(p, c.depth, waves, nwg, lds, s);
     }

@@ -69,11 +69,24 @@ int cu_count();
 extern "C" int qgemv_set_launch_override(int lpr, int r, int waves, int depth, int max_wg, int cpl);
 bool launch_override(GemvCfg *c);
 
+// Greedy sampling fused into a one-token product: every workgroup's
+// candidate, counters of finished workgroups (a top counter and group
+// counters, each on its own 128-byte line; zero before the launch, left zero
+// by it) and the token.
+struct ArgmaxOut {
+    uint2 *cand;       // max_cand entries
+    int64_t max_cand;  // the launch fails if it would take more workgroups
+    uint32_t *count;   // top counter, then 64 group counters, each 32 words apart
+    int32_t *token;
+};
+
 // Kernel launchers (enqueue only; arguments already validated).
 // resid (may equal y): y = resid + W x.  gamma: the input is RMS-normalized
-// with that gain and eps before the gate/up products.
+// with that gain and eps before the gate/up products.  am: also the index of
+// the largest y (plain product, no resid).
 hipError_t launch_gemv(int fmt, const uint8_t *packed, const float *x, float *y, int64_t rows,
-                       int64_t cols, hipStream_t s, const GemvCfg &cfg, const float *resid = nullptr);
+                       int64_t cols, hipStream_t s, const GemvCfg &cfg, const float *resid = nullptr,
+                       const ArgmaxOut *am = nullptr);
 hipError_t launch_gate_up(int fmt, const uint8_t *wg, const uint8_t *wu, const float *x, float *h,
                           int64_t ffn, int64_t d_model, hipStream_t s, const GemvCfg &cfg,
                           const float *gamma = nullptr, float eps = 0.0f);

@@ -68,9 +68,12 @@ def _check_head(t, n_tok, seed):
     pk = G.upload(t)
     x = np.random.default_rng(seed).standard_normal((n_tok, t.cols)).astype(np.float32)
     xd = G.torch.from_numpy(x).to(G.dev())
-    tok, logits = G.qg().qgemv_head_argmax(t.fmt, pk, xd, t.rows, t.cols)
+    tok, logits = G.qg().qgemv_head_argmax(t.fmt, pk, xd, t.rows, t.cols, fused=True)
     G.torch.cuda.synchronize()
     tok, logits = tok.cpu().numpy(), logits.cpu().numpy()
+    tok2, logits2 = G.qg().qgemv_head_argmax(t.fmt, pk, xd, t.rows, t.cols)
+    G.torch.cuda.synchronize()
+    assert np.array_equal(tok, tok2.cpu().numpy()) and np.array_equal(logits, logits2.cpu().numpy())
     yr, S = oracle.gemv(t.fmt, t.raw, x, t.rows, t.cols, row_scale=t.row_scale)
     rel = G.rel_for(t.fmt, n_tok)
     for k in range(n_tok):
@@ -101,3 +104,95 @@ def test_head_argmax_matrix_cores():
     # a Q4_0 head at 8 tokens runs the product on the matrix cores first
     t = synth.make_tensor("q4_0", 4096, 1024, np.random.default_rng(45))
     _check_head(t, 8, 46)
+
+
+# ------------------------------------------------------------ fused head --
+# qgemv_head_argmax_ws at one token: one launch, the argmax fused into the
+# product's epilogue (workgroup candidates, the last workgroup combines them).
+# Bars: the logits bit-identical to the two-launch path's (the same product
+# kernel), the token identical to its token and to the oracle argmax of the
+# device logits; the workspace reused call after call with its counter back
+# at zero; ties, NaN at index 0 and NaN elsewhere by the in-order rule.
+
+FUSED_SHAPES = {"q4_0": [(1, 64), (7, 288), (131, 576), (4099, 2048), (40000, 576)],
+                "q8_0": [(1, 32), (7, 288), (131, 576), (4099, 2048), (40000, 576)],
+                "i8row": [(1, 32), (7, 288), (131, 576), (4099, 2048)],
+                "q4_k": [(1, 256), (7, 512), (131, 768), (4099, 2048)],
+                "q6_k": [(1, 256), (7, 512), (131, 768), (4099, 2048)]}
+
+
+def _head(t, pk, x, fused, ws=None):
+    xd = G.torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(G.dev())
+    tok, logits = G.qg().qgemv_head_argmax(t.fmt, pk, xd, t.rows, t.cols, workspace=ws, fused=fused)
+    G.torch.cuda.synchronize()
+    return int(tok.cpu().numpy()[0]), logits.cpu().numpy().reshape(-1)
+
+
+@pytest.mark.parametrize("fmt,rows,cols", [(f, r, c) for f, sh in FUSED_SHAPES.items() for r, c in sh])
+def test_fused_head_matches_two_launches(fmt, rows, cols):
+    rng = np.random.default_rng(rows + cols + len(fmt))
+    t = synth.make_tensor(fmt, rows, cols, rng)
+    pk = G.upload(t)
+    x = rng.standard_normal(cols).astype(np.float32)
+    modes = [0, -1] if fmt == "q4_0" else [0]     # Q4_0: the row-streaming and the lane-group kernels
+    try:
+        for mode in modes:
+            G.qg().set_xs_override(mode)
+            tf, lf = _head(t, pk, x, True)
+            t2, l2 = _head(t, pk, x, False)
+            assert np.array_equal(lf, l2), f"mode {mode}: fused logits differ"
+            assert tf == t2 == oracle.argmax(lf), f"mode {mode}: token {tf} vs {t2}"
+    finally:
+        G.qg().set_xs_override(0)
+
+
+def test_fused_head_workspace_reused():
+    # one workspace through calls of several shapes and inputs: each token
+    # right, every counter back at zero after every call
+    rng = np.random.default_rng(4700)
+    heads = [synth.make_tensor("q8_0", r, c, rng) for r, c in ((40000, 576), (300, 288), (4099, 2048))]
+    heads.append(synth.make_tensor("q4_0", 20000, 1024, rng))
+    pks = [G.upload(t) for t in heads]
+    need = max(G.qg().head_argmax_workspace_bytes(t.fmt, t.rows, t.cols) for t in heads)
+    ws = G.torch.zeros(need, dtype=G.torch.uint8, device=G.dev())
+    counters = 128 * (1 + 64)   # the top and 64 group counters, a line each
+    for k in range(12):
+        t, pk = heads[k % 4], pks[k % 4]
+        x = rng.standard_normal(t.cols).astype(np.float32)
+        tok, logits = _head(t, pk, x, True, ws)
+        assert tok == oracle.argmax(logits), k
+        assert int(ws[:counters].sum().cpu()) == 0, f"call {k}: a counter left at nonzero"
+
+
+def _q8_0_rows(d_rows, codes):
+    """A Q8_0 tensor with per-row constant f16 scales (given as uint16 bits) and given codes."""
+    rows, cols = codes.shape
+    d = np.repeat(np.asarray(d_rows, np.uint16)[:, None], cols // 32, axis=1).view(np.float16)
+    return synth.QTensor("w", "q8_0", rows, cols, synth.pack_q8_0(d, codes.astype(np.int8)))
+
+
+@pytest.mark.parametrize("rows", [300, 40000])
+def test_fused_head_ties_and_nan(rows):
+    cols = 64
+    x = np.ones(cols, np.float32)
+    one, two, inf = 0x3C00, 0x4000, 0x7C00      # f16 1.0, 2.0, +inf
+    codes = np.full((rows, cols), 3, np.int64)
+    base = np.full(rows, one, np.uint16)
+    cases = []
+    # tie: two rows far apart share the largest logit -> the first of them
+    d = base.copy(); d[[rows // 3, rows - 2]] = two
+    cases.append((d, codes.copy()))
+    # NaN at row 0 (scale inf times code 0) -> 0, whatever the largest is
+    d = base.copy(); d[0] = inf; c = codes.copy(); c[0] = 0; d[rows // 2] = two
+    cases.append((d, c))
+    # NaN in the middle, the maximum after it -> the maximum
+    d = base.copy(); d[5] = inf; c = codes.copy(); c[5] = 0; d[rows - 1] = two
+    cases.append((d, c))
+    # every logit equal -> 0
+    cases.append((base.copy(), codes.copy()))
+    for k, (d, c) in enumerate(cases):
+        t = _q8_0_rows(d, c)
+        pk = G.upload(t)
+        tok, logits = _head(t, pk, x, True)
+        assert tok == oracle.argmax(logits), (k, tok)
+        assert tok == [rows // 3, 0, rows - 1, 0][k], (k, tok)
