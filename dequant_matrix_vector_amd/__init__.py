@@ -16,7 +16,8 @@ __all__ = [
     "qgemv", "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_k", "qgemv_i8row", "qgemv_q6_k",
     "swiglu_gate_up", "swiglu_ffn", "swiglu_ffn_noalloc", "qdequant", "layout_version", "set_launch_override",
     "set_prefill_override", "set_xs_override", "prefill_plan", "swiglu_ffn_scratch_elems", "swiglu_ffn_block", "swiglu_ffn_block_scratch_elems",
-    "qgemv_argmax", "qgemv_head_argmax", "head_argmax_workspace_bytes", "qgemv_q8act", "swiglu_ffn_q8act", "qquantize_q8_0",
+    "qgemv_argmax", "qgemv_head_argmax", "head_argmax_workspace_bytes", "qgemv_q8act", "swiglu_ffn_q8act", "q8act_workspace_bytes",
+    "swiglu_ffn_q8act_scratch_elems", "qquantize_q8_0",
     "qgemv_repack_q4_0", "qgemv_repack_q8_0", "qgemv_repack_q4_k", "qgemv_repack_i8row", "qgemv_repack_q6_k",
 ]
 
@@ -76,6 +77,12 @@ lib.qgemv_q8act.argtypes = [_I, _P, _P, _P, _I64, _I64, _I64, _P]
 lib.qgemv_q8act.restype = _I
 lib.swiglu_ffn_q8act.argtypes = [_I, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]
 lib.swiglu_ffn_q8act.restype = _I
+lib.swiglu_ffn_q8act_scratch_elems.argtypes = [_I, _I64, _I64, _I64]
+lib.swiglu_ffn_q8act_scratch_elems.restype = _I64
+lib.qgemv_q8act_ws.argtypes = [_I, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]
+lib.qgemv_q8act_ws.restype = _I
+lib.qgemv_q8act_workspace_bytes.argtypes = [_I, _I64, _I64, _I64]
+lib.qgemv_q8act_workspace_bytes.restype = _I64
 lib.qquantize_q8_0.argtypes = [_P, _P, _I64, _I64, _P]
 lib.qquantize_q8_0.restype = _I
 lib.qgemv_set_launch_override.argtypes = [_I, _I, _I, _I, _I, _I]
@@ -372,25 +379,52 @@ def swiglu_ffn_noalloc(fmt, wg, wu, wd, x, d_model, ffn, out=None, stream=None) 
     return out
 
 
-def qgemv_q8act(fmt, packed, x, rows, cols, y=None, stream=None) -> torch.Tensor:
-    """y [n_tok][rows] = W xq, xq the Q8_0 representation of x (Q4_0, Q8_0 weights)."""
+def q8act_workspace_bytes(fmt, rows, cols, n_tok) -> int:
+    """Bytes of workspace for the batched Q8_0-activation product (host only)."""
+    n = lib.qgemv_q8act_workspace_bytes(_fmt(fmt), rows, cols, n_tok)
+    _check(n if n < 0 else 0, "qgemv_q8act_workspace_bytes")
+    return n
+
+
+def qgemv_q8act(fmt, packed, x, rows, cols, y=None, workspace=None, stream=None) -> torch.Tensor:
+    """y [n_tok][rows] = W xq, xq the Q8_0 representation of x (Q4_0, Q8_0
+    weights).  Several tokens: the batched launches, with workspace (uint8, at
+    least the quantized activations' bytes; q8act_workspace_bytes for the
+    built-in K split; made when none is given)."""
     n_tok = _ntok(x, cols)
     y = _y(y, (rows,) if x.dim() == 1 else (n_tok, rows), x.device)
     _packed(packed, fmt, rows, cols)
     _arg(x, "x", F32)
     _arg(y, "y", F32, n_tok * rows)
-    _on_gpu(packed, x, y)
-    _check(lib.qgemv_q8act(_fmt(fmt), _ptr(packed), _ptr(x), _ptr(y), rows, cols, n_tok, _stream(stream)),
-           "qgemv_q8act")
+    if n_tok == 1:
+        _on_gpu(packed, x, y)
+        _check(lib.qgemv_q8act(_fmt(fmt), _ptr(packed), _ptr(x), _ptr(y), rows, cols, n_tok, _stream(stream)),
+               "qgemv_q8act")
+        return y
+    if workspace is None:
+        workspace = torch.empty(q8act_workspace_bytes(fmt, rows, cols, n_tok), dtype=torch.uint8, device=x.device)
+    _arg(workspace, "workspace", torch.uint8)
+    _on_gpu(packed, x, y, workspace)
+    _check(lib.qgemv_q8act_ws(_fmt(fmt), _ptr(packed), _ptr(x), _ptr(y), rows, cols, n_tok, _ptr(workspace),
+                              workspace.numel(), _stream(stream)), "qgemv_q8act_ws")
     return y
 
 
+def swiglu_ffn_q8act_scratch_elems(fmt, d_model, ffn, n_tok) -> int:
+    v = lib.swiglu_ffn_q8act_scratch_elems(_fmt(fmt), d_model, ffn, n_tok)
+    _check(v if v < 0 else 0, "swiglu_ffn_q8act_scratch_elems")
+    return v
+
+
 def swiglu_ffn_q8act(fmt, wg, wu, wd, x, d_model, ffn, out=None, h_scratch=None, stream=None):
-    """(out, h): the SwiGLU FFN with x and h quantized to Q8_0 before their products."""
+    """(out, h): the SwiGLU FFN with x and h quantized to Q8_0 before their
+    products; h_scratch made with swiglu_ffn_q8act_scratch_elems floats (the
+    batched path for several tokens) when none is given."""
     n_tok = _ntok(x, d_model)
     out = _y(out, (n_tok, d_model), x.device)
     if h_scratch is None:
-        h_scratch = torch.empty(n_tok * ffn, dtype=torch.float32, device=x.device)
+        h_scratch = torch.empty(swiglu_ffn_q8act_scratch_elems(fmt, d_model, ffn, n_tok), dtype=torch.float32,
+                                device=x.device)
     _ffn_args(fmt, wg, wu, wd, x, out, h_scratch, d_model, ffn, n_tok)
     _on_gpu(wg, wu, wd, x, out, h_scratch)
     _check(lib.swiglu_ffn_q8act(_fmt(fmt), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(x), _ptr(out), _ptr(h_scratch),

@@ -564,6 +564,25 @@ int swiglu_ffn_q8act(int fmt, const void *wg, const void *wu, const void *wd, co
     const int st = check_ffn(fmt, wg, wu, wd, x, out, h_scratch, h_scratch_elems, d_model, ffn, n_tok, &Lg, &Ld);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
+    if (n_tok > 1 && prefill_enabled()) {
+        // the batched path when the scratch holds h, the quantized
+        // activations and (if room is left) partial sums
+        const int64_t ho = align_up(n_tok * ffn, kPlaneAlign / 4);
+        const int64_t xb = q8act_x_bytes(d_model > ffn ? d_model : ffn, n_tok);
+        if (h_scratch_elems >= ho + xb / 4) {
+            uint8_t *ws = reinterpret_cast<uint8_t *>(h_scratch + ho);
+            float *part = h_scratch + ho + xb / 4;
+            const int64_t pe = h_scratch_elems - ho - xb / 4;
+            const uint8_t *g8 = static_cast<const uint8_t *>(wg), *u8 = static_cast<const uint8_t *>(wu);
+            if (launch_q8act_quantize(x, ws, d_model, n_tok, s) != hipSuccess ||
+                launch_q8act_mfma(fmt, 2, g8, u8, ws, h_scratch, ffn, d_model, n_tok, part, pe, s) != hipSuccess ||
+                launch_q8act_quantize(h_scratch, ws, ffn, n_tok, s) != hipSuccess ||
+                launch_q8act_mfma(fmt, 1, static_cast<const uint8_t *>(wd), nullptr, ws, out, d_model, ffn, n_tok,
+                                  part, pe, s) != hipSuccess)
+                return QG_ERR_LAUNCH;
+            return QG_OK;
+        }
+    }
     const GemvCfg cg = choose_cfg(fmt, ffn, d_model, 2);
     const GemvCfg cd = choose_cfg(fmt, d_model, ffn, 1);
     for (int64_t t = 0; t < n_tok; t++) {
@@ -577,6 +596,59 @@ int swiglu_ffn_q8act(int fmt, const void *wg, const void *wu, const void *wd, co
             return QG_ERR_LAUNCH;
     }
     return QG_OK;
+}
+
+// Partial-sum floats the batched Q8_0-activation product splits K into (0: none).
+static int64_t q8act_part_elems(int nmat, int64_t rows, int64_t cols, int64_t n_tok)
+{
+    const Q8mPlan c = q8act_mfma_plan(nmat, rows, cols, n_tok, INT64_MAX);
+    return c.ksplit > 1 ? (int64_t)c.ksplit * nmat * n_tok * rows : 0;
+}
+
+int64_t qgemv_q8act_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t n_tok)
+{
+    if (!q8act_fmt(fmt)) return QG_ERR_FORMAT;
+    Layout L;
+    if (n_tok < 1 || n_tok >= (int64_t(1) << 31) || !layout_for(fmt, rows, cols, &L)) return QG_ERR_SHAPE;
+    if (n_tok == 1) return 0;
+    return q8act_x_bytes(cols, n_tok) + 4 * q8act_part_elems(1, rows, cols, n_tok);
+}
+
+int qgemv_q8act_ws(int fmt, const void *packed, const float *x, float *y, int64_t rows, int64_t cols, int64_t n_tok,
+                   void *workspace, int64_t workspace_bytes, void *stream)
+{
+    if (!q8act_fmt(fmt)) return QG_ERR_FORMAT;
+    Layout L;
+    int st = check_product(fmt, packed, x, y, rows, cols, n_tok, &L);
+    if (st) return st;
+    if (n_tok == 1 || !prefill_enabled()) return qgemv_q8act(fmt, packed, x, y, rows, cols, n_tok, stream);
+    const int64_t xb = q8act_x_bytes(cols, n_tok);
+    if (!workspace) return QG_ERR_NULL;
+    if (workspace_bytes < xb) return QG_ERR_SCRATCH;
+    if (!aligned(workspace, kPlaneAlign)) return QG_ERR_ALIGN;
+    if (overlap(workspace, workspace_bytes, x, n_tok * cols * 4) ||
+        overlap(workspace, workspace_bytes, y, n_tok * rows * 4) || overlap(workspace, workspace_bytes, packed, L.total))
+        return QG_ERR_ALIAS;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    hipStream_t s = (hipStream_t)stream;
+    if (launch_q8act_quantize(x, ws, cols, n_tok, s) != hipSuccess ||
+        launch_q8act_mfma(fmt, 1, static_cast<const uint8_t *>(packed), nullptr, ws, y, rows, cols, n_tok,
+                          reinterpret_cast<float *>(ws + xb), (workspace_bytes - xb) / 4, s) != hipSuccess)
+        return QG_ERR_LAUNCH;
+    return QG_OK;
+}
+
+int64_t swiglu_ffn_q8act_scratch_elems(int fmt, int64_t d_model, int64_t ffn, int64_t n_tok)
+{
+    if (!q8act_fmt(fmt)) return QG_ERR_FORMAT;
+    Layout Lg, Ld;
+    if (n_tok < 1 || n_tok >= (int64_t(1) << 31) || !layout_for(fmt, ffn, d_model, &Lg) ||
+        !layout_for(fmt, d_model, ffn, &Ld))
+        return QG_ERR_SHAPE;
+    if (n_tok == 1) return n_tok * ffn;
+    const int64_t pg = q8act_part_elems(2, ffn, d_model, n_tok), pd = q8act_part_elems(1, d_model, ffn, n_tok);
+    return align_up(n_tok * ffn, kPlaneAlign / 4) + q8act_x_bytes(d_model > ffn ? d_model : ffn, n_tok) / 4 +
+           (pg > pd ? pg : pd);
 }
 
 int qquantize_q8_0(const float *x, void *blocks, int64_t n, int64_t n_tok, void *stream)

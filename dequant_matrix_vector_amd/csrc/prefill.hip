@@ -289,6 +289,7 @@ extern "C" int qgemv_prefill_plan(int fmt, int nmat, int64_t rows, int64_t cols,
 }
 
 bool prefill_enabled() { return g_pf_override.mtr >= 0; }
+PrefillCfg prefill_override() { return g_pf_override; }
 
 bool prefill_format(int fmt)
 {

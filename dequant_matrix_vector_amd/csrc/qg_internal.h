@@ -107,6 +107,7 @@ struct PrefillCfg {
 };
 extern "C" int qgemv_set_prefill_override(int mtr, int ntw, int waves, int run, int ksplit);
 bool prefill_enabled();   // false after qgemv_set_prefill_override(-1, ...): per-token GEMV loop instead
+PrefillCfg prefill_override();   // the calling thread's tuning override (mtr 0: none)
 bool prefill_format(int fmt);   // formats the matrix-core path takes
 // Floats of partial sums the built-in choice splits K into (0: no split).
 int64_t prefill_part_elems(int fmt, int nmat, int64_t rows, int64_t cols, int64_t n_tok);
@@ -122,6 +123,22 @@ hipError_t launch_prefill(int fmt, int nmat, const uint8_t *w0, const uint8_t *w
                           int64_t rows, int64_t cols, int64_t n_tok, float *part, int64_t part_elems,
                           hipStream_t s, const float *resid = nullptr, const uint16_t *xb = nullptr,
                           uint16_t *yb = nullptr);
+// Q8_0 activations with several tokens (q8act_mfma.hip).  First every x row
+// is quantized once into a workspace (q8act_x_bytes of it: the blocks' codes
+// as binary16 operand slots, then their scales); then the product multiplies
+// the codes on the matrix cores.  nmat == 1: y = W0 xq; nmat == 2:
+// y = silu(W0 xq) * (W1 xq).  Q4_0 or Q8_0 weights.  part (part_elems
+// floats, may be null) lets K split over workgroups, the partial sums added
+// by a second launch in range order.
+struct Q8mPlan {
+    int mtr, ntw, ksplit, spk;
+};
+Q8mPlan q8act_mfma_plan(int nmat, int64_t rows, int64_t cols, int64_t n_tok, int64_t part_elems);
+int64_t q8act_x_bytes(int64_t cols, int64_t n_tok);
+hipError_t launch_q8act_quantize(const float *x, uint8_t *ws, int64_t cols, int64_t n_tok, hipStream_t s);
+hipError_t launch_q8act_mfma(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, const uint8_t *xws, float *y,
+                             int64_t rows, int64_t cols, int64_t n_tok, float *part, int64_t part_elems,
+                             hipStream_t s);
 // xb[i] = bf16(x[i]) (nearest even), n % 4 == 0, both 16-byte aligned.
 hipError_t launch_to_bf16(const float *x, uint16_t *xb, int64_t n, hipStream_t s);
 // Raw Q8_0 blocks (f16 d, 32 int8) of activation rows x [n_tok][n], n a multiple of 32.

@@ -276,13 +276,43 @@ int64_t qgemv_head_argmax_workspace_bytes(int fmt, int64_t rows, int64_t cols);
  * activations).  Q4_0 and Q8_0 weights only (QG_ERR_FORMAT otherwise); same
  * arguments, layouts and checks as qgemv and swiglu_ffn.  swiglu_ffn_q8act
  * quantizes x before the gate/up pair and h before the down product (h,
- * fp32, is left in the scratch as in swiglu_ffn; n_tok * ffn floats
- * suffice).  One launch per product and token. */
+ * fp32, is left in the scratch as in swiglu_ffn).  qgemv_q8act: one launch
+ * per token.  swiglu_ffn_q8act: with n_tok * ffn floats of scratch, two
+ * launches per token; with n_tok > 1 and at least
+ * swiglu_ffn_q8act_scratch_elems() floats, the batched path of
+ * qgemv_q8act_ws for both products (the quantized activations, then any
+ * partial sums, live in the scratch behind h, which starts the scratch
+ * aligned up to 64 floats); between the two, the batched path without a K
+ * split when the quantized activations fit. */
 int qgemv_q8act(int fmt, const void *packed, const float *x, float *y, int64_t rows, int64_t cols,
                 int64_t n_tok, void *stream);
 int swiglu_ffn_q8act(int fmt, const void *wg, const void *wu, const void *wd, const float *x,
                      float *out, float *h_scratch, int64_t h_scratch_elems, int64_t d_model,
                      int64_t ffn, int64_t n_tok, void *stream);
+/* Floats of scratch for the batched path of swiglu_ffn_q8act (n_tok * ffn
+ * when n_tok == 1), or a negative status (QG_ERR_FORMAT, QG_ERR_SHAPE). */
+int64_t swiglu_ffn_q8act_scratch_elems(int fmt, int64_t d_model, int64_t ffn, int64_t n_tok);
+
+/* The same product for several tokens in a fixed number of launches (the
+ * Go "llm" package's ExactGGML mode quantizes the prompt's activations too):
+ * one launch quantizes every token's blocks into `workspace` (device,
+ * 256-byte aligned, not overlapping packed, x or y), one multiplies on the
+ * matrix cores -- the 32-term block sums of 16 rows by 16 tokens as one
+ * binary16 matrix-core product of the codes (small integers: exact products
+ * and sums in fp32), each scaled by d_w * d_x and added in fp32, the bound
+ * above unchanged -- and, when the workspace also holds partial sums of a K
+ * split, a third adds them in a fixed order (deterministic).  workspace_bytes
+ * >= qgemv_q8act_workspace_bytes() allows the built-in K split; less (down to
+ * the quantized activations alone) narrows it; less than that: QG_ERR_SCRATCH
+ * (QG_ERR_NULL without a workspace).  n_tok == 1, or the matrix-core path
+ * turned off by qgemv_set_prefill_override(-1, ...): qgemv_q8act, the
+ * workspace unused.  The workspace's contents are scratch (nothing carries
+ * over between calls).  Calls that share a workspace must not overlap. */
+int qgemv_q8act_ws(int fmt, const void *packed, const float *x, float *y, int64_t rows, int64_t cols,
+                   int64_t n_tok, void *workspace, int64_t workspace_bytes, void *stream);
+/* Bytes of workspace for qgemv_q8act_ws with the built-in K split (0 when
+ * n_tok == 1), or a negative status (QG_ERR_FORMAT, QG_ERR_SHAPE). */
+int64_t qgemv_q8act_workspace_bytes(int fmt, int64_t rows, int64_t cols, int64_t n_tok);
 
 /* Test export: the activation quantizer above on its own.  x: fp32
  * [n_tok][n] (16-byte aligned), n a multiple of 32; blocks: n_tok * n/32 raw
@@ -356,8 +386,11 @@ int qgemv_time_next_launch(void *start_event, void *stop_event);
  * library does not build (it would spill registers or overflow the LDS) runs
  * as the nearest built one.  mtr == 0 restores the built-in choice; mtr == -1
  * turns the matrix-core path off, so that n_tok > 1 loops the GEMV over the
- * tokens (fp32 accuracy), for comparisons.  Per calling thread, as
- * qgemv_set_launch_override.  Returns QG_ERR_SHAPE for other values. */
+ * tokens (fp32 accuracy), for comparisons.  The batched Q8_0-activation
+ * products (qgemv_q8act_ws, swiglu_ffn_q8act) take mtr, ntw (8 as 4) and
+ * ksplit from it, and loop over the tokens after mtr == -1.  Per calling
+ * thread, as qgemv_set_launch_override.  Returns QG_ERR_SHAPE for other
+ * values. */
 int qgemv_set_prefill_override(int mtr, int ntw, int waves, int run, int ksplit);
 
 /* The tile and K split the matrix-core path picks for one product (tuning and

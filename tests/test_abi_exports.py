@@ -77,6 +77,20 @@ def test_refusals_before_any_device_call(lib):
     lib.qgemv_q8act.argtypes = [ctypes.c_int, P, P, P, I64, I64, I64, P]
     assert lib.qgemv_q8act(2, fake, fake, fake, 4, 256, 1, None) == -4
     assert lib.qgemv_q8act(4, fake, fake, fake, 4, 256, 1, None) == -4
+    lib.qgemv_q8act_ws.argtypes = [ctypes.c_int, P, P, P, I64, I64, I64, P, I64, P]
+    assert lib.qgemv_q8act_ws(2, fake, fake, fake, 4, 256, 8, fake, 1 << 20, None) == -4
+    lib.qgemv_q8act_workspace_bytes.argtypes = [ctypes.c_int, I64, I64, I64]
+    lib.qgemv_q8act_workspace_bytes.restype = I64
+    lib.swiglu_ffn_q8act_scratch_elems.argtypes = [ctypes.c_int, I64, I64, I64]
+    lib.swiglu_ffn_q8act_scratch_elems.restype = I64
+    # host-only sizes: one token needs no workspace; several need at least the
+    # quantized activations (64 + 4 bytes per block)
+    assert lib.qgemv_q8act_workspace_bytes(0, 100, 256, 1) == 0
+    assert lib.qgemv_q8act_workspace_bytes(0, 100, 256, 8) >= 8 * 8 * 68
+    assert lib.qgemv_q8act_workspace_bytes(2, 100, 256, 8) == -4
+    assert lib.qgemv_q8act_workspace_bytes(0, 100, 250, 8) == -2
+    assert lib.swiglu_ffn_q8act_scratch_elems(0, 576, 1536, 1) == 1536
+    assert lib.swiglu_ffn_q8act_scratch_elems(1, 576, 1536, 8) >= 8 * 1536 + 8 * 48 * 68 // 4
     lib.qquantize_q8_0.argtypes = [P, P, I64, I64, P]
     assert lib.qquantize_q8_0(fake, fake, 48, 1, None) == -2
     assert lib.qquantize_q8_0(fake, fake, 64, 0, None) == -2

@@ -71,6 +71,9 @@ def test_ffn_refusals():
     refused("h_scratch: needs at least", qg.swiglu_ffn_q8act, "q4_0", wg, wu, wd, x, d, f, out=out,
             h_scratch=h[:-8])
     refused("live on the GPU", qg.swiglu_ffn, "q4_0", wg, wu, wd, x, d, f, out=out, h_scratch=h)
+    x3 = torch.zeros((3, d), dtype=F32)
+    refused("workspace: expected torch.uint8", qg.qgemv_q8act, "q4_0", wg, x3, f, d,
+            workspace=torch.zeros(qg.q8act_workspace_bytes("q4_0", f, d, 3), dtype=F32))
 
 
 def test_head_argmax_quantize_dequant_repack_refusals():

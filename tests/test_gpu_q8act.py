@@ -189,3 +189,187 @@ def test_fullsize_27b_ffn_q8act():
     tens = synth.gen_workload(w)
     x = synth.gen_x(w, w.d_model, 1)
     _check_ffn_q8act("q4_0", tens, x, w.d_model, w.ffn, "27B-class FFN q8act")
+
+
+# ---- several tokens: one launch per product on the matrix cores ----------
+#
+# The batched path quantizes each token's x blocks inside the kernel with the
+# same rule and multiplies the codes on the matrix cores (binary16 integer
+# operands, exact fp32 block sums), then scales each block sum by d_w * d_x:
+# the same fp32 bound as one token.
+
+def _oracle_q8act_rows(fmt, raw, x, rows, cols, threads=16):
+    """oracle.gemv_q8act over row ranges on a thread pool (the raw blocks of
+    Q4_0 and Q8_0 are whole rows in order, so a range is a slice; each row's
+    sum is the same as in one call)."""
+    from concurrent.futures import ThreadPoolExecutor
+    rb = (cols // 32) * (18 if fmt == "q4_0" else 34)
+    raw = np.ascontiguousarray(raw).reshape(rows, rb)
+    threads = max(1, min(threads, rows // 64 or 1))
+    cuts = np.linspace(0, rows, threads + 1).astype(int)
+    with ThreadPoolExecutor(threads) as pool:
+        parts = list(pool.map(lambda ab: oracle.gemv_q8act(fmt, raw[ab[0]:ab[1]].reshape(-1), x, int(ab[1] - ab[0]),
+                                                           cols), zip(cuts[:-1], cuts[1:])))
+    return np.concatenate([p[0] for p in parts], axis=-1), np.concatenate([p[1] for p in parts], axis=-1)
+
+
+BATCH_SHAPES = {"q4_0": [(1, 32), (45, 576), (203, 1536), (64, 4096), (130, 160)],
+                "q8_0": [(1, 32), (45, 576), (131, 2048), (67, 1056)]}
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n_tok", [2, 3, 16, 17, 40, 70])
+def test_gemv_q8act_batched_within_bound(fmt, n_tok):
+    for k, (rows, cols) in enumerate(BATCH_SHAPES[fmt]):
+        rng = np.random.default_rng(3600 + 10 * n_tok + k)
+        t = synth.make_tensor(fmt, rows, cols, rng)
+        x = rng.standard_normal((n_tok, cols)).astype(np.float32)
+        x[n_tok // 2, :32] = 0.0                                        # a zero block
+        y = G.qg().qgemv_q8act(fmt, G.upload(t), G.torch.from_numpy(x).to(G.dev()), rows, cols)
+        G.torch.cuda.synchronize()
+        yr, S = oracle.gemv_q8act(fmt, t.raw, x, rows, cols)
+        G.check_bound(y.cpu().numpy(), yr, S, what=f"q8act batched {fmt} {rows}x{cols} n_tok={n_tok}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_q8act_batched_every_tile(fmt):
+    # every built tile, K unsplit, split in 3 and 7, and as many ranges as
+    # super-steps (33 asked, 9 taken: 1056 columns are 33 blocks)
+    rows, cols, n_tok = 203, 1056, 37
+    rng = np.random.default_rng(3700)
+    t = synth.make_tensor(fmt, rows, cols, rng)
+    pk = G.upload(t)
+    x = rng.standard_normal((n_tok, cols)).astype(np.float32)
+    xd = G.torch.from_numpy(x).to(G.dev())
+    yr, S = oracle.gemv_q8act(fmt, t.raw, x, rows, cols)
+    try:
+        for mtr, ntw, ks in ((1, 1, 0), (1, 2, 0), (1, 4, 0), (2, 1, 0), (2, 2, 0), (2, 4, 0), (1, 1, 1), (1, 1, 3),
+                             (2, 4, 7), (1, 2, 33)):
+            G.qg().set_prefill_override(mtr, ntw, 4, 1, ks)
+            y = G.qg().qgemv_q8act(fmt, pk, xd, rows, cols)
+            G.torch.cuda.synchronize()
+            G.check_bound(y.cpu().numpy(), yr, S, what=f"q8act batched {fmt} tile {mtr} {ntw} ksplit {ks}")
+    finally:
+        G.qg().set_prefill_override(0)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_q8act_batched_exact_inputs_bit_exact(fmt):
+    # power-of-two weight scales, activations k * 2^-e with a code of 127 in
+    # every block: each block sum is an exact integer times a power of two and
+    # every partial sum is exact, so y equals the oracle's bit for bit
+    rng = np.random.default_rng(3800)
+    rows, cols, n_tok = 150, 1024, 21
+    if fmt == "q4_0":
+        d = (2.0 ** rng.integers(-6, -2, (rows, cols // 32))).astype(np.float16)
+        raw = synth.pack_q4_0(d, rng.integers(0, 16, (rows, cols)))
+    else:
+        d = (2.0 ** rng.integers(-8, -4, (rows, cols // 32))).astype(np.float16)
+        raw = synth.pack_q8_0(d, rng.integers(-127, 128, (rows, cols)).astype(np.int8))
+    t = synth.QTensor("w", fmt, rows, cols, raw)
+    kx = rng.integers(-127, 128, (n_tok, cols))
+    kx[:, ::32] = 127
+    x = (kx * 2.0 ** -rng.integers(3, 6, (n_tok, 1))).astype(np.float32)
+    y = G.qg().qgemv_q8act(fmt, G.upload(t), G.torch.from_numpy(x).to(G.dev()), rows, cols)
+    G.torch.cuda.synchronize()
+    yr, _ = oracle.gemv_q8act(fmt, t.raw, x, rows, cols)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), yr)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_q8act_batched_matches_token_loop_scaled(fmt):
+    # the batched launch against the per-token GEMV loop (both within the
+    # bound of the oracle), and exact doubling when x doubles
+    rows, cols, n_tok = 300, 2048, 24
+    rng = np.random.default_rng(3900)
+    t = synth.make_tensor(fmt, rows, cols, rng)
+    pk = G.upload(t)
+    x = rng.standard_normal((n_tok, cols)).astype(np.float32)
+    run = lambda v: G.qg().qgemv_q8act(fmt, pk, G.torch.from_numpy(v).to(G.dev()), rows, cols).cpu().numpy()
+    yb, yb2, y4 = run(x), run(x), run(x * np.float32(4))
+    assert np.array_equal(yb, yb2) and np.array_equal(y4, np.float32(4) * yb)
+    try:
+        G.qg().set_prefill_override(-1)
+        yl = run(x)
+    finally:
+        G.qg().set_prefill_override(0)
+    yr, S = oracle.gemv_q8act(fmt, t.raw, x, rows, cols)
+    G.check_bound(yb, yr, S, what="batched")
+    G.check_bound(yl, yr, S, what="token loop")
+
+
+def test_gemv_q8act_batched_workspace_sizes():
+    # the workspace's size decides the K split only: the least that holds the
+    # quantized activations, and more, give results within the bound; less
+    # is refused
+    fmt, rows, cols, n_tok = "q4_0", 130, 2048, 20
+    rng = np.random.default_rng(4100)
+    t = synth.make_tensor(fmt, rows, cols, rng)
+    pk = G.upload(t)
+    x = rng.standard_normal((n_tok, cols)).astype(np.float32)
+    xd = G.torch.from_numpy(x).to(G.dev())
+    yr, S = oracle.gemv_q8act(fmt, t.raw, x, rows, cols)
+    xb = n_tok * (cols // 32) * 64 + n_tok * (cols // 32) * 4          # both multiples of 256 here
+    full = G.qg().q8act_workspace_bytes(fmt, rows, cols, n_tok)
+    assert full > xb
+    for nb in (xb, xb + 3 * 4 * rows * n_tok, full, full + 4096):
+        ws = G.torch.empty(nb, dtype=G.torch.uint8, device=G.dev())
+        y = G.qg().qgemv_q8act(fmt, pk, xd, rows, cols, workspace=ws)
+        G.torch.cuda.synchronize()
+        G.check_bound(y.cpu().numpy(), yr, S, what=f"workspace {nb}")
+    with pytest.raises(G.qg().QGemvError):
+        G.qg().qgemv_q8act(fmt, pk, xd, rows, cols, workspace=G.torch.empty(xb - 256, dtype=G.torch.uint8,
+                                                                             device=G.dev()))
+
+
+def test_swiglu_ffn_q8act_scratch_sizes():
+    # h_scratch of n_tok * ffn floats: the per-token loop; the full size: the
+    # batched launches; both within the bounds, stage by stage
+    fmt, d_model, ffn, n_tok = "q8_0", 576, 1536, 12
+    rng = np.random.default_rng(4200)
+    tens = [synth.make_tensor(fmt, ffn, d_model, rng), synth.make_tensor(fmt, ffn, d_model, rng),
+            synth.make_tensor(fmt, d_model, ffn, rng)]
+    pk = [G.upload(t) for t in tens]
+    x = rng.standard_normal((n_tok, d_model)).astype(np.float32)
+    xd = G.torch.from_numpy(x).to(G.dev())
+    for elems in (n_tok * ffn, G.qg().swiglu_ffn_q8act_scratch_elems(fmt, d_model, ffn, n_tok)):
+        h_s = G.torch.empty(elems, dtype=G.torch.float32, device=G.dev())
+        out, h = G.qg().swiglu_ffn_q8act(fmt, pk[0], pk[1], pk[2], xd, d_model, ffn, h_scratch=h_s)
+        G.torch.cuda.synchronize()
+        out, h = out.cpu().numpy(), h.cpu().numpy()
+        r = {}
+        r["g"], r["Sg"] = oracle.gemv_q8act(fmt, tens[0].raw, x, ffn, d_model)
+        r["u"], r["Su"] = oracle.gemv_q8act(fmt, tens[1].raw, x, ffn, d_model)
+        r["h"] = G.silu64(r["g"]) * r["u"]
+        assert np.all(np.abs(h - r["h"]) <= G.h_bound(r)), f"scratch {elems}: h outside its bound"
+        yr, S = oracle.gemv_q8act(fmt, tens[2].raw, h, d_model, ffn)
+        G.check_bound(out, yr, S, what=f"scratch {elems} down")
+
+
+@pytest.mark.parametrize("fmt,n_tok", [("q4_0", 8), ("q8_0", 17), ("q4_0", 40)])
+def test_swiglu_ffn_q8act_batched(fmt, n_tok):
+    d_model, ffn = 576, 1536
+    rng = np.random.default_rng(4000 + n_tok)
+    tens = [synth.make_tensor(fmt, ffn, d_model, rng), synth.make_tensor(fmt, ffn, d_model, rng),
+            synth.make_tensor(fmt, d_model, ffn, rng)]
+    x = rng.standard_normal((n_tok, d_model)).astype(np.float32)
+    _check_ffn_q8act(fmt, tens, x, d_model, ffn, f"ffn q8act {fmt} n_tok={n_tok}")
+
+
+@pytest.mark.parametrize("n_tok", [8, 128])
+def test_fullsize_27b_ffn_q8act_batched_every_row(n_tok):
+    w = synth.CFG5
+    tens = synth.gen_workload(w)
+    x = synth.gen_x(w, w.d_model, n_tok)
+    pk = [G.upload(t) for t in tens]
+    out, h = G.qg().swiglu_ffn_q8act("q4_0", pk[0], pk[1], pk[2], G.torch.from_numpy(x).to(G.dev()), w.d_model,
+                                     w.ffn)
+    G.torch.cuda.synchronize()
+    out, h = out.cpu().numpy(), h.cpu().numpy()
+    r = {}
+    r["g"], r["Sg"] = _oracle_q8act_rows("q4_0", tens[0].raw, x, w.ffn, w.d_model)
+    r["u"], r["Su"] = _oracle_q8act_rows("q4_0", tens[1].raw, x, w.ffn, w.d_model)
+    r["h"] = G.silu64(r["g"]) * r["u"]
+    assert np.all(np.abs(h - r["h"]) <= G.h_bound(r)), f"27B q8act n_tok={n_tok}: h outside its bound"
+    yr, S = _oracle_q8act_rows("q4_0", tens[2].raw, h, w.d_model, w.ffn)
+    G.check_bound(out, yr, S, what=f"27B q8act n_tok={n_tok} down")
