@@ -389,6 +389,22 @@ def extra_report(qg, synth, torch, np, dev, graph_iters=20):
             rep["cfg5_ffn_q8act"] = {"workload": w.name + ", x and h quantized to Q8_0 (integer dot products)",
                                      "n_tok": 1, "us_per_step": round(uq, 2), "ffn_f32_us_per_step": round(uf, 2),
                                      "GBs": round(wbytes / uq / 1e3, 1)}
+    # several tokens with x and h quantized to Q8_0: the batched launches
+    # (quantize, gate/up, reduce, quantize, down, reduce)
+    for n_tok in (8, 128):
+        x = torch.randn((n_tok, w.d_model), device=dev)
+        out = torch.empty_like(x)
+        hq = torch.empty(qg.swiglu_ffn_q8act_scratch_elems("q4_0", w.d_model, w.ffn, n_tok), device=dev)
+
+        def q8b(i):
+            c = copies[i % ncopy]
+            qg.swiglu_ffn_q8act("q4_0", c[0], c[1], c[2], x, w.d_model, w.ffn, out=out, h_scratch=hq)
+
+        uq = _graph_us(torch, q8b, graph_iters)
+        rep[f"cfg5_ffn_q8act_n{n_tok}"] = {
+            "workload": w.name + f", x and h quantized to Q8_0, {n_tok} tokens (matrix cores, exact block sums)",
+            "n_tok": n_tok, "us_per_step": round(uq, 2), "GBs": round(wbytes / uq / 1e3, 1),
+            "TOPs": round(2 * n_tok * (wbytes * 32 // 18) / uq / 1e6, 1)}
     del copies
     torch.cuda.empty_cache()
     for w, idx in ((synth.CFG2, 7), (synth.CFG4, 3)):

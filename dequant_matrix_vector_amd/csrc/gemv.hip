@@ -194,8 +194,11 @@ hipError_t launch_gemv(int fmt, const uint8_t *packed, const float *x, float *y,
     if (am && (resid || (fmt & kQ8Act))) return hipErrorInvalidValue;
     GemvCfg forced;
     XsCfg xc;
+    RowsCfg rc;
     if (!launch_override(&forced) && xs_choose(fmt, rows, cols, 1, false, &xc))
         return launch_xs(fmt, 1, packed, nullptr, x, y, rows, cols, xc, s, nullptr, 0.0f, resid, am);
+    if (!launch_override(&forced) && rows_choose(fmt, rows, cols, &rc))
+        return launch_rows(fmt, packed, x, y, rows, cols, rc, s, resid, am);
     GemvParams p;
     p.q[0] = packed;
     p.q[1] = packed;

@@ -379,6 +379,10 @@ struct XsCfg {
     int wpc;    // > 0: exactly wpc workgroups per CU (nrs follows), at most wpc resident per CU
 };
 
+// The calling thread's forced fields (mode 1 of qgemv_set_xs_override; 0 or
+// -1 fields: built-in), or false.
+bool xs_forced(XsCfg *c);
+
 // Host side (gemv_xs.hip): the configuration for a shape, or false when the
 // x-stationary kernel does not take it.
 bool xs_choose(int fmt, int64_t rows, int64_t cols, int nmat, bool norm, XsCfg *c);

@@ -87,6 +87,15 @@ bool valid_cfg(const XsCfg &c, int nmat, int64_t nchunk, bool norm)
 
 } // namespace
 
+int xs_mode() { return g_xs_mode; }
+
+bool xs_forced(XsCfg *c)
+{
+    if (g_xs_mode != 1) return false;
+    *c = g_xs_force;
+    return true;
+}
+
 extern "C" int qgemv_set_xs_override(int mode, int rs, int seg, int depth, int nrs, int order, int wg_per_cu)
 {
     if (mode == 0 || mode == -1) {

@@ -80,6 +80,21 @@ struct ArgmaxOut {
     int32_t *token;
 };
 
+// One-token Q8_0 products with short rows (gemv_rows.hip): a lane per block
+// position, rows packed across the lanes.  rows_choose: false when the kernel
+// does not take the shape (or the row-streaming kernels are switched off).
+struct RowsCfg {
+    int threads, rps, nrs, grid, depth;
+};
+bool rows_choose(int fmt, int64_t rows, int64_t cols, RowsCfg *c);
+// resid (may be null) is added to y; am (may be null): greedy sampling fused in.
+hipError_t launch_rows(int fmt, const uint8_t *packed, const float *x, float *y, int64_t rows, int64_t cols,
+                       const RowsCfg &c, hipStream_t s, const float *resid, const ArgmaxOut *am);
+// The row-streaming tuning mode of the calling thread (qgemv_set_xs_override):
+// -1 = off, 0 = built-in, 1 = forced shape.
+int xs_mode();
+
+
 // Kernel launchers (enqueue only; arguments already validated).
 // resid (may equal y): y = resid + W x.  gamma: the input is RMS-normalized
 // with that gain and eps before the gate/up products.  am: also the index of

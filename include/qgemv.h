@@ -338,8 +338,11 @@ int qgemv_set_launch_override(int lpr, int r, int waves, int depth, int max_wg, 
 /* Tuning hook for the one-token products of Q4_0 matrices whose rows have at
  * most 1024 blocks: by default these run on a row-streaming kernel in which
  * each lane keeps one block's activations in registers and streams that
- * block of consecutive rows.  mode -1 keeps them on the lane-group kernels
- * (also the effect of any qgemv_set_launch_override shape); mode 1 forces the
+ * block of consecutive rows.  (Q8_0 matrices whose rows have at most 64
+ * blocks run on a row-packed kernel: one lane per block position, the rows
+ * laid across the lanes without gaps.)  mode -1 keeps both on the lane-group
+ * kernels (also the effect of any qgemv_set_launch_override shape); mode 1
+ * forces the
  * row-streaming kernel's rows per row-step (rs 1, 2, 4 or 8), 32-lane
  * segments per row (seg: 32 * seg >= blocks per row, rs * seg even,
  * rs * seg / 2 <= 16 waves), row-steps in flight per lane (depth 2 or 4; 8
@@ -348,8 +351,10 @@ int qgemv_set_launch_override(int lpr, int r, int waves, int depth, int max_wg, 
  * consecutive, -1: built-in) and wg_per_cu (1..8: exactly that many
  * workgroups per CU, nrs following, and no more resident per CU; 0: off; -1:
  * built-in); a 0 field keeps the built-in value, and a combination outside
- * these rules falls back to the lane-group kernels.  mode 0 restores the
- * built-in choice.  Results depend on the choice only through summation
+ * these rules falls back to the lane-group kernels (the row-packed Q8_0
+ * kernel takes depth 2, 4 or 8, nrs and wg_per_cu from the same fields, and
+ * falls back when its row-steps would not fit 64 KB of LDS).  mode 0
+ * restores the built-in choice.  Results depend on the choice only through summation
  * order.  Per calling thread.  Returns QG_ERR_SHAPE for other modes or
  * fields out of range. */
 int qgemv_set_xs_override(int mode, int rs, int seg, int depth, int nrs, int order, int wg_per_cu);
