@@ -373,3 +373,41 @@ def test_fullsize_27b_ffn_q8act_batched_every_row(n_tok):
     assert np.all(np.abs(h - r["h"]) <= G.h_bound(r)), f"27B q8act n_tok={n_tok}: h outside its bound"
     yr, S = _oracle_q8act_rows("q4_0", tens[2].raw, h, w.d_model, w.ffn)
     G.check_bound(out, yr, S, what=f"27B q8act n_tok={n_tok} down")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n_tok", [5, 20])
+def test_gemv_q8act_batched_edge_scales_within_bound(fmt, n_tok):
+    # every row's weight scales in one binary16 binade (subnormal to the top,
+    # either sign, some zeros), Q8_0 codes over -128..127 (one row all -128)
+    from tests.test_gpu_scale_edges import make, row_binade_f16
+    rows, cols = 131, 2048
+    rng = np.random.default_rng(4500 + 10 * FMTS.index(fmt) + n_tok)
+    t = make(fmt, rows, cols, rng, row_binade_f16)
+    x = rng.standard_normal((n_tok, cols)).astype(np.float32)
+    y = G.qg().qgemv_q8act(fmt, G.upload(t), G.torch.from_numpy(x).to(G.dev()), rows, cols)
+    G.torch.cuda.synchronize()
+    yr, S = oracle.gemv_q8act(fmt, t.raw, x, rows, cols)
+    G.check_bound(y.cpu().numpy(), yr, S, what=f"q8act batched {fmt} edge scales n_tok={n_tok}")
+
+
+def test_gemv_q8act_batched_extreme_codes_bit_exact():
+    # Q8_0 weight codes at the ends of the range (-128, -127, 127, 0) and
+    # activation codes of +-127, one power-of-two scale for all weights and
+    # one for all activations: y = 2^-11 * sum q k, whose every partial sum
+    # is an integer of at most 1024 * 128 * 127 < 2^24 units, exact in fp32,
+    # so y equals the oracle bit for bit; the decode of -128 (the byte 0x80)
+    # included
+    rng = np.random.default_rng(4600)
+    rows, cols, n_tok = 77, 1024, 18
+    d = np.full((rows, cols // 32), 2.0 ** -6, np.float16)
+    q = rng.choice(np.array([-128, -127, 127, 0], np.int8), (rows, cols))
+    q[5] = -128                                                          # the extreme row sums
+    t = synth.QTensor("w", "q8_0", rows, cols, synth.pack_q8_0(d, q))
+    kx = rng.choice(np.array([-127, 127]), (n_tok, cols))
+    kx[3] = -127
+    x = (kx * 2.0 ** -5).astype(np.float32)
+    y = G.qg().qgemv_q8act("q8_0", G.upload(t), G.torch.from_numpy(x).to(G.dev()), rows, cols)
+    G.torch.cuda.synchronize()
+    yr, _ = oracle.gemv_q8act("q8_0", t.raw, x, rows, cols)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), yr)
