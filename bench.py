@@ -57,8 +57,8 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the read-ceiling probe and the back-to-back graph passes (short profiled runs)")
     ap.add_argument("--workloads", default="",
-                    help="comma-separated keys of the per-workload report to run (e.g. cfg5_n8,cfg5_n128); "
-                         "default: all")
+                    help="comma-separated keys of the per-workload report to run (e.g. cfg5_n8,cfg5_n128; "
+                         "'extras': the FFN block, Q8_0-activation and head-plus-sampling steps); default: all")
     return ap.parse_args()
 
 
@@ -322,7 +322,7 @@ def workload_report(qg, synth, torch, np, dev, graph_iters=20, only=()):
             rep[key]["pct_bf16_mfma_peak"] = round(100 * flops / us / 1e6 / BF16_MFMA_PEAK_TFLOPS, 1)
         del copies, g
         torch.cuda.empty_cache()
-    if not only:
+    if not only or "extras" in only:
         rep.update(extra_report(qg, synth, torch, np, dev, graph_iters))
     return rep
 
