@@ -226,6 +226,18 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
         if constexpr (EPI == kEpiNorm) gp[k] = reinterpret_cast<const float4 *>(p.gamma)[j];
     }
 
+    // EPI 2: the residual of the row this thread finishes first, read now so
+    // that its latency hides under the weight stream (y may be the residual
+    // itself: only this workgroup writes its rows, after this read)
+    float rpre = 0.0f;
+    if constexpr (EPI == kEpiResid) {
+        // branch-free, as the x loads: a clamped row, used only where valid
+        const int ph = t % p.rs, i = t / p.rs;
+        int row = blockIdx.x * p.gb * p.rs + i * p.ga * p.rs + ph;
+        row = row < p.rows - 1 ? row : p.rows - 1;
+        rpre = p.resid[row];
+    }
+
     Slot st[D][NMAT];
     const uint32_t qcol = (uint32_t)c * 16u, scol = p.soff + (uint32_t)c * 2u;
     auto load_step = [&](int s, int i) {
@@ -356,7 +368,7 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
 #pragma unroll
             for (int m = 0; m < NMAT; m++) a[m] *= norm_scale;
         }
-        if constexpr (EPI == kEpiResid) a[0] += p.resid[row];
+        if constexpr (EPI == kEpiResid) a[0] += j == t ? rpre : p.resid[row];
         if constexpr (EPI == kEpiArgmax) {
             am_take(am_v, am_i, a[0], row);
             if (row == 0 && a[0] != a[0]) am_nan0 = true;
