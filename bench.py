@@ -1,8 +1,9 @@
 """Benchmark: weight-stream GB/s of the batch-1 quantized SwiGLU FFN on one MI355X.
 
 Workload (one step): the 27B-class dense FFN, Q4_0, d_model 5120, ffn 17408,
-one token: h = silu(Wg x) * (Wu x) (the fused gate/up GEMV kernel), then
-out = Wd h (the GEMV kernel) -- exactly the two launches swiglu_ffn makes.
+one token, one swiglu_ffn call: h = silu(Wg x) * (Wu x) (the fused gate/up
+GEMV kernel, which also clears out), then out = Wd h (the GEMV kernel over
+the two column halves of Wd, each adding its half-row sums into out).
 Synthetic seeded weights and activations (synth.CFG5), repacked once at load.
 Enough packed copies of the three matrices rotate through the steps that the
 working set is >= 1 GiB (over 4x the 256 MB Infinity Cache), so each step
@@ -14,12 +15,15 @@ value = algorithmic weight bytes per step (150,405,120 B: 18 B per 32 weights)
 roofline: the dominant kernel (fused gate/up, 100,270,080 B per launch) timed
 with HIP events on the stream it runs on, against 8 TB/s HBM: the same K steps
 run a second time with each launch carrying its own start/stop events
-(qgemv_time_next_launch: the library launches it with hipExtLaunchKernel), so
-the events hold the dispatch's own start and end -- the duration rocprofv3's
-kernel trace reports.  Timed launches leave gaps between the kernels (as
+(two pairs queued with qgemv_time_next_launch before each swiglu_ffn call:
+the library launches both kernels with hipExtLaunchKernel), so the events
+hold each dispatch's own start and end -- the durations rocprofv3's kernel
+trace reports.  Timed launches leave gaps between the kernels (as
 hipEventRecord pairs do), hence a pass of their own.
-Also reported: the same two kernels back to back (a HIP graph of 32 launches
-of one product over the rotating copies), and the read ceiling -- what a plain
+Also reported: back to back (HIP graphs of 32 launches over the rotating
+copies) the gate/up product alone (swiglu_gate_up, the same kernel) and the
+whole block (swiglu_ffn), whose difference is the down product's share as the
+step runs it; and the read ceiling -- what a plain
 16-byte grid-stride read kernel (qgemv_read_probe) streams over 1 GiB and,
 back to back, over rotating slices of each product's size -- with each
 kernel's fraction of it.
@@ -471,6 +475,8 @@ def main():
     xd = torch.from_numpy(x).to(dev)
     h = torch.empty((1, ffn), dtype=torch.float32, device=dev)
     out = torch.empty((1, d_model), dtype=torch.float32, device=dev)
+    scratch_elems = qg.swiglu_ffn_scratch_elems("q4_0", d_model, ffn, 1)
+    hs = torch.empty(scratch_elems, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
 
@@ -480,20 +486,20 @@ def main():
     fq = qg.FORMATS["q4_0"]
     gu_args = [(fq, g.data_ptr(), u.data_ptr(), xd.data_ptr(), h.data_ptr(), d_model, ffn, 1, sptr)
                for g, u, _ in copies]
-    dn_args = [(fq, dn.data_ptr(), h.data_ptr(), out.data_ptr(), d_model, ffn, 1, sptr) for _, _, dn in copies]
-    gate_up_call, down_call = qg.lib.swiglu_gate_up, qg.lib.qgemv
+    ffn_args = [(fq, g.data_ptr(), u.data_ptr(), dn.data_ptr(), xd.data_ptr(), out.data_ptr(), hs.data_ptr(),
+                 scratch_elems, d_model, ffn, 1, sptr) for g, u, dn in copies]
+    gate_up_call, ffn_call = qg.lib.swiglu_gate_up, qg.lib.swiglu_ffn
     evs = TimingEvents(4 * a.steps)
     time_next, ev_handles = qg.lib.qgemv_time_next_launch, evs.ev
 
     def step(i, timed=False):
-        if timed and time_next(ev_handles[4 * i], ev_handles[4 * i + 1]) != 0:
+        # timed: the call's gate/up launch takes the first pair, its down
+        # launch the second
+        if timed and (time_next(ev_handles[4 * i], ev_handles[4 * i + 1]) != 0 or
+                      time_next(ev_handles[4 * i + 2], ev_handles[4 * i + 3]) != 0):
             raise RuntimeError("qgemv_time_next_launch failed")
-        if gate_up_call(*gu_args[i % ncopy]) != 0:
-            raise RuntimeError("swiglu_gate_up failed")
-        if timed and time_next(ev_handles[4 * i + 2], ev_handles[4 * i + 3]) != 0:
-            raise RuntimeError("qgemv_time_next_launch failed")
-        if down_call(*dn_args[i % ncopy]) != 0:
-            raise RuntimeError("qgemv failed")
+        if ffn_call(*ffn_args[i % ncopy]) != 0:
+            raise RuntimeError("swiglu_ffn failed")
 
     for i in range(a.warmup):
         step(i)
@@ -520,26 +526,29 @@ def main():
     dn_avg = float(np.mean(dn_ms))
     achieved = gu_bytes / (gu_avg * 1e-3) / 1e9
 
-    # the same kernels back to back (no events between them): a HIP graph of
-    # 32 launches of one product over the rotating copies
+    # back to back (no events between them): HIP graphs of 32 gate/up
+    # launches and of 32 blocks over the rotating copies; the down product's
+    # share is their difference
     def gu_launch(i, s):
         a = gu_args[i % ncopy]
         if gate_up_call(*a[:-1], s) != 0:
             raise RuntimeError("swiglu_gate_up failed")
 
-    def dn_launch(i, s):
-        a = dn_args[i % ncopy]
-        if down_call(*a[:-1], s) != 0:
-            raise RuntimeError("qgemv failed")
+    def ffn_launch(i, s):
+        a = ffn_args[i % ncopy]
+        if ffn_call(*a[:-1], s) != 0:
+            raise RuntimeError("swiglu_ffn failed")
 
-    gu_b2b = dn_b2b = float("nan")
+    gu_b2b = dn_b2b = ffn_b2b = float("nan")
     if not a.no_extras:
         gu_b2b = back_to_back_us(torch, gu_launch)
-        dn_b2b = back_to_back_us(torch, dn_launch)
+        ffn_b2b = back_to_back_us(torch, ffn_launch)
+        dn_b2b = ffn_b2b - gu_b2b
 
     detail = {
         "gate_up_us": round(gu_avg * 1e3, 2), "down_us": round(dn_avg * 1e3, 2),
         "gate_up_us_back_to_back": round(gu_b2b, 2), "down_us_back_to_back": round(dn_b2b, 2),
+        "ffn_us_back_to_back": round(ffn_b2b, 2),
         "gate_up_GBs_back_to_back": round(gu_bytes / gu_b2b / 1e3, 1),
         "down_GBs_back_to_back": round(tens[2].weight_bytes / dn_b2b / 1e3, 1),
         "gate_up_GBs": round(achieved, 1),
@@ -551,7 +560,7 @@ def main():
     }
     if a.no_extras:
         for k in ("gate_up_us_back_to_back", "down_us_back_to_back", "gate_up_GBs_back_to_back",
-                  "down_GBs_back_to_back"):
+                  "down_GBs_back_to_back", "ffn_us_back_to_back"):
             detail[k] = None
     if a.warm:
         g, u, dn = copies[0]

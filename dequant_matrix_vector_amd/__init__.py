@@ -15,7 +15,7 @@ __all__ = [
     "FORMATS", "QGemvError", "lib", "packed_bytes", "max_cols", "repack",
     "qgemv", "qgemv_q4_0", "qgemv_q8_0", "qgemv_q4_k", "qgemv_i8row", "qgemv_q6_k",
     "swiglu_gate_up", "swiglu_ffn", "swiglu_ffn_noalloc", "qdequant", "layout_version", "set_launch_override",
-    "set_prefill_override", "set_xs_override", "prefill_plan", "swiglu_ffn_scratch_elems", "swiglu_ffn_block", "swiglu_ffn_block_scratch_elems",
+    "set_prefill_override", "set_xs_override", "set_ffn_khalf", "prefill_plan", "swiglu_ffn_scratch_elems", "swiglu_ffn_block", "swiglu_ffn_block_scratch_elems",
     "qgemv_argmax", "qgemv_head_argmax", "head_argmax_workspace_bytes", "qgemv_q8act", "swiglu_ffn_q8act", "q8act_workspace_bytes",
     "swiglu_ffn_q8act_scratch_elems", "qquantize_q8_0",
     "qgemv_repack_q4_0", "qgemv_repack_q8_0", "qgemv_repack_q4_k", "qgemv_repack_i8row", "qgemv_repack_q6_k",
@@ -91,6 +91,8 @@ lib.qgemv_set_prefill_override.argtypes = [_I, _I, _I, _I, _I]
 lib.qgemv_set_prefill_override.restype = _I
 lib.qgemv_set_xs_override.argtypes = [_I, _I, _I, _I, _I, _I, _I]
 lib.qgemv_set_xs_override.restype = _I
+lib.qgemv_set_ffn_khalf.argtypes = [_I]
+lib.qgemv_set_ffn_khalf.restype = _I
 lib.qgemv_read_probe.argtypes = [_P, _I64, _I, _I, _P, _P]
 lib.qgemv_read_probe.restype = _I
 lib.qgemv_time_next_launch.argtypes = [_P, _P]
@@ -194,6 +196,12 @@ def set_xs_override(mode=0, rs=0, seg=0, depth=0, nrs=0, order=-1, wg_per_cu=-1)
     """Row-streaming one-token kernel: mode 0 built-in, -1 off (lane-group
     kernels), 1 forced with the given fields (0 / -1 = built-in value)."""
     _check(lib.qgemv_set_xs_override(mode, rs, seg, depth, nrs, order, wg_per_cu), "qgemv_set_xs_override")
+
+
+def set_ffn_khalf(mode=0):
+    """One-token Q4_0 SwiGLU block: its down product in K halves (atomic adds
+    of two half-row sums onto a cleared output): 0 built-in, 1 off, 2 on."""
+    _check(lib.qgemv_set_ffn_khalf(mode), "qgemv_set_ffn_khalf")
 
 
 def prefill_plan(fmt, nmat, rows, cols, n_tok, part_elems=0, cus=256):

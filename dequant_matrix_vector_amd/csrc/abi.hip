@@ -350,15 +350,22 @@ int swiglu_ffn(int fmt, const void *wg, const void *wu, const void *wd, const fl
     }
     const GemvCfg cg = choose_cfg(fmt, ffn, d_model, 2);
     const GemvCfg cd = choose_cfg(fmt, d_model, ffn, 1);
+    // K halves for the down product: the gate/up launch clears its output
+    // (out is disjoint from x), each half adds into it
+    const bool kh = ffn_down_khalf(fmt, d_model, ffn);
     for (int64_t t = 0; t < n_tok; t++) {
         if (launch_gate_up(fmt, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), x + t * d_model,
-                           h_scratch + t * ffn, ffn, d_model, s, cg) != hipSuccess)
+                           h_scratch + t * ffn, ffn, d_model, s, cg, nullptr, 0.0f, kh ? out + t * d_model : nullptr,
+                           kh ? d_model : 0) != hipSuccess)
             return QG_ERR_LAUNCH;
     }
     for (int64_t t = 0; t < n_tok; t++) {
-        if (launch_gemv(fmt, static_cast<const uint8_t *>(wd), h_scratch + t * ffn, out + t * d_model, d_model, ffn,
-                        s, cd) != hipSuccess)
-            return QG_ERR_LAUNCH;
+        const hipError_t e =
+            kh ? launch_down_khalf(fmt, static_cast<const uint8_t *>(wd), h_scratch + t * ffn, out + t * d_model,
+                                   d_model, ffn, s)
+               : launch_gemv(fmt, static_cast<const uint8_t *>(wd), h_scratch + t * ffn, out + t * d_model, d_model,
+                             ffn, s, cd);
+        if (e != hipSuccess) return QG_ERR_LAUNCH;
     }
     return QG_OK;
 }

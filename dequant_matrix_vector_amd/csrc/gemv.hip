@@ -54,23 +54,36 @@ GemvCfg aligned_cfg(int fmt, int nchunk, GemvCfg c)
 } // namespace
 
 namespace {
-thread_local hipEvent_t t_start = nullptr, t_stop = nullptr;
+// the calling thread's queued (start, stop) pairs, oldest first
+constexpr int kTimedMax = 4;
+thread_local hipEvent_t t_ev[kTimedMax][2];
+thread_local int t_pending = 0;
 } // namespace
 
 bool take_launch_timing(hipEvent_t *start, hipEvent_t *stop)
 {
-    if (!t_start) return false;
-    *start = t_start;
-    *stop = t_stop;
-    t_start = t_stop = nullptr;
+    if (t_pending == 0) return false;
+    *start = t_ev[0][0];
+    *stop = t_ev[0][1];
+    for (int i = 1; i < t_pending; i++) {
+        t_ev[i - 1][0] = t_ev[i][0];
+        t_ev[i - 1][1] = t_ev[i][1];
+    }
+    t_pending--;
     return true;
 }
 
 extern "C" int qgemv_time_next_launch(void *start_event, void *stop_event)
 {
     if ((start_event == nullptr) != (stop_event == nullptr)) return QG_ERR_NULL;
-    t_start = static_cast<hipEvent_t>(start_event);
-    t_stop = static_cast<hipEvent_t>(stop_event);
+    if (start_event == nullptr) {
+        t_pending = 0;
+        return QG_OK;
+    }
+    if (t_pending == kTimedMax) return QG_ERR_SHAPE;
+    t_ev[t_pending][0] = static_cast<hipEvent_t>(start_event);
+    t_ev[t_pending][1] = static_cast<hipEvent_t>(stop_event);
+    t_pending++;
     return QG_OK;
 }
 
@@ -220,16 +233,48 @@ hipError_t launch_gemv(int fmt, const uint8_t *packed, const float *x, float *y,
     return dispatch_fmt<1>(fmt, p, aligned_cfg(fmt, p.nchunk, cfg), s);
 }
 
+namespace {
+// tuning switch of the calling thread (qgemv_set_ffn_khalf): 0 built-in, 1 off, 2 on
+thread_local int g_khalf_mode = 0;
+} // namespace
+
+extern "C" int qgemv_set_ffn_khalf(int mode)
+{
+    if (mode < 0 || mode > 2) return QG_ERR_SHAPE;
+    g_khalf_mode = mode;
+    return QG_OK;
+}
+
+bool ffn_down_khalf(int fmt, int64_t d_model, int64_t ffn)
+{
+    GemvCfg forced;
+    XsCfg a, b;
+    if (g_khalf_mode == 1 || launch_override(&forced)) return false;
+    // built in from rows of 256 chunks on (the 27B-class down, 544 chunks:
+    // half rows of 272)
+    if (g_khalf_mode == 0 && ffn / kChunk < 256) return false;
+    return xs_choose(fmt, ffn, d_model, 2, false, &a) && xs_choose(fmt, d_model, ffn, 1, false, &b, true);
+}
+
+hipError_t launch_down_khalf(int fmt, const uint8_t *wd, const float *h, float *out, int64_t d_model, int64_t ffn,
+                             hipStream_t s)
+{
+    XsCfg c;
+    if (!xs_choose(fmt, d_model, ffn, 1, false, &c, true)) return hipErrorInvalidValue;
+    return launch_xs(fmt, 1, wd, nullptr, h, out, d_model, ffn, c, s, nullptr, 0.0f, nullptr);
+}
+
 hipError_t launch_gate_up(int fmt, const uint8_t *wg, const uint8_t *wu, const float *x, float *h,
                           int64_t ffn, int64_t d_model, hipStream_t s, const GemvCfg &cfg, const float *gamma,
-                          float eps)
+                          float eps, float *zero, int64_t nzero)
 {
     Layout L;
     if (!layout_for(fmt & ~kQ8Act, ffn, d_model, &L)) return hipErrorInvalidValue;
     GemvCfg forced;
     XsCfg xc;
-    if (!launch_override(&forced) && xs_choose(fmt, ffn, d_model, 2, gamma != nullptr, &xc))
-        return launch_xs(fmt, 2, wg, wu, x, h, ffn, d_model, xc, s, gamma, eps, nullptr);
+    const bool on_xs = !launch_override(&forced) && xs_choose(fmt, ffn, d_model, 2, gamma != nullptr, &xc);
+    if (zero && (!on_xs || gamma)) return hipErrorInvalidValue;
+    if (on_xs) return launch_xs(fmt, 2, wg, wu, x, h, ffn, d_model, xc, s, gamma, eps, nullptr, nullptr, zero, nzero);
     GemvParams p;
     p.q[0] = wg;
     p.q[1] = wu;

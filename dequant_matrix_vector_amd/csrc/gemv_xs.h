@@ -33,6 +33,12 @@
 //     segments' sums in segment order (deterministic) and applies the
 //     epilogue: silu(g) * u for the gate/up pair (NMAT 2), the RMSNorm scale
 //     (EPI 1) or the residual (EPI 2).
+//   * K halves (EPI 4, one matrix): each workgroup takes one half of the
+//     columns of its rows (even workgroups the first, odd ones the second),
+//     so it stages half of x, and adds its half-row sums into y, which holds
+//     zeros before the launch, with an atomic add.  Each y then takes exactly
+//     two adds onto an exact zero, (0 + a) + b = a + b = b + a, so the
+//     result does not depend on which half lands first.
 //
 // Compared with the lane-group kernel (gemv_impl.h) this stages nothing in
 // LDS before streaming (a workgroup of the 27B-class down product would
@@ -64,7 +70,8 @@ struct XsParams {
     uint32_t row_qbytes;  // quant-plane bytes per row
     uint32_t soff;        // scale-plane offset
     uint32_t row_sbytes;  // scale-plane bytes per row (2 * nchunk)
-    int lprow;            // lanes per row: 32 * segments >= nchunk
+    int lprow;            // lanes per row: 32 * segments >= the chunks of a K part
+    int kchunks;          // chunks per K part (EPI 4: the first half's; else nchunk)
     int rs;               // rows per row-step
     int nrs;              // row-steps per workgroup
     int ga, gb;           // global row-step of local step i in workgroup b: i * ga + b * gb
@@ -72,9 +79,11 @@ struct XsParams {
     uint2 *am_cand;       // EPI 3: one (value bits, index) candidate per workgroup
     uint32_t *am_count;   // EPI 3: workgroups done (zero before the launch; left zero)
     int32_t *am_token;    // EPI 3: the index of the largest y
+    float *zero;          // NMAT 2, EPI 0: a vector set to zero after the products (may be null)
+    int nzero;            // its length
 };
 
-enum { kEpiPlain = 0, kEpiNorm = 1, kEpiResid = 2, kEpiArgmax = 3 };
+enum { kEpiPlain = 0, kEpiNorm = 1, kEpiResid = 2, kEpiArgmax = 3, kEpiKHalf = 4 };
 
 constexpr int kXsMaxWaves = 16;   // waves per workgroup, at most
 
@@ -188,6 +197,7 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
     static_assert(FMT == QG_Q4_0, "x-stationary GEMV: Q4_0");
     static_assert(PX == 4 || PX == 8, "pieces per thread");
     static_assert(EPI != kEpiArgmax || NMAT == 1, "argmax of one product");
+    static_assert(EPI != kEpiKHalf || NMAT == 1, "K halves of one product");
     constexpr int V = D * NMAT;   // chunk products per lane between reductions
     static_assert(V >= 2 && V <= 32 && (V & (V - 1)) == 0, "power-of-two batch");
     extern __shared__ float4 xs_lds4[];
@@ -195,34 +205,41 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
 
     const int t = threadIdx.x;
     const int lane = t & 63;
+    // EPI 4: K half kh of the rows of workgroup bid; else the whole row
+    constexpr bool KH = EPI == kEpiKHalf;
+    const int kh = KH ? (int)(blockIdx.x & 1u) : 0;
+    const int bid = KH ? (int)(blockIdx.x >> 1) : (int)blockIdx.x;
+    const int c0 = kh * p.kchunks;                                  // first chunk of the part
+    const int nck = KH ? min(p.kchunks, p.nchunk - c0) : p.nchunk;  // chunks of the part
     const int phase = t / p.lprow;
     const int craw = t - phase * p.lprow;
-    const bool live = craw < p.nchunk;
-    const int c = live ? craw : p.nchunk - 1;   // spare lanes read a valid chunk, contribute 0
+    const bool live = craw < nck;
+    const int c = live ? craw : nck - 1;   // spare lanes read a valid chunk, contribute 0
     const int seg = t >> 5;
     const int nseg = p.lprow >> 5;
-    const int row0 = blockIdx.x * p.gb * p.rs + phase;   // row of local step i: row0 + i * ga * rs
+    const int row0 = bid * p.gb * p.rs + phase;   // row of local step i: row0 + i * ga * rs
     const int rstep = p.ga * p.rs;
     const int last = p.rows - 1;
 
-    // LDS: x (EPI 1: x times the gain) staged [nchunk + 1][36] (chunks 144
-    // bytes apart, so the lanes' 16-byte reads of consecutive chunks fall in
-    // different banks; one spare chunk slot), then (EPI 1) one sum of squares
-    // per wave, then the partial row sums [segments][nrs][NMAT]
+    // LDS: x's part (EPI 1: x times the gain) staged [kchunks + 1][36]
+    // (chunks 144 bytes apart, so the lanes' 16-byte reads of consecutive
+    // chunks fall in different banks; one spare chunk slot), then (EPI 1) one
+    // sum of squares per wave, then the partial row sums [segments][nrs][NMAT]
     float *xsx = xs_part;
-    float *wsq = xsx + (p.nchunk + 1) * kXStride;
+    float *wsq = xsx + (p.kchunks + 1) * kXStride;
     float *part = wsq + (EPI == kEpiNorm ? kXsMaxWaves : 0);
 
     // x (and the gain) in 16-byte pieces, consecutive threads reading
     // consecutive pieces, at most PX per thread; issued before the weight
     // stream so that waiting for them waits for nothing else
-    const int npiece = p.nchunk * 8;
+    const int npiece = nck * 8;
+    const float4 *xpart = reinterpret_cast<const float4 *>(p.x) + c0 * 8;
     float4 xp[PX], gp[PX];
 #pragma unroll
     for (int k = 0; k < PX; k++) {
         int j = t + k * (int)blockDim.x;
         j = j < npiece ? j : npiece - 1;
-        xp[k] = reinterpret_cast<const float4 *>(p.x)[j];
+        xp[k] = xpart[j];
         if constexpr (EPI == kEpiNorm) gp[k] = reinterpret_cast<const float4 *>(p.gamma)[j];
     }
 
@@ -233,13 +250,13 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
     if constexpr (EPI == kEpiResid) {
         // branch-free, as the x loads: a clamped row, used only where valid
         const int ph = t % p.rs, i = t / p.rs;
-        int row = blockIdx.x * p.gb * p.rs + i * p.ga * p.rs + ph;
+        int row = bid * p.gb * p.rs + i * p.ga * p.rs + ph;
         row = row < p.rows - 1 ? row : p.rows - 1;
         rpre = p.resid[row];
     }
 
     Slot st[D][NMAT];
-    const uint32_t qcol = (uint32_t)c * 16u, scol = p.soff + (uint32_t)c * 2u;
+    const uint32_t qcol = (uint32_t)(c0 + c) * 16u, scol = p.soff + (uint32_t)(c0 + c) * 2u;
     auto load_step = [&](int s, int i) {
         int row = row0 + i * rstep;
         row = row < last ? row : last;
@@ -266,7 +283,7 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
 #pragma unroll
     for (int k = 0; k < PX; k++) {
         const int j = t + k * (int)blockDim.x;
-        const int at = j < npiece ? (j >> 3) * kXStride + (j & 7) * 4 : p.nchunk * kXStride;
+        const int at = j < npiece ? (j >> 3) * kXStride + (j & 7) * 4 : nck * kXStride;
         float4 v = xp[k];
         if constexpr (EPI == kEpiNorm) {
             float q = v.x * v.x;
@@ -355,7 +372,7 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
     bool am_nan0 = false;            // EPI 3: this thread wrote row 0 and it is NaN
     for (int j = t; j < p.rs * p.nrs; j += blockDim.x) {
         const int ph = j % p.rs, i = j / p.rs;
-        const int row = blockIdx.x * p.gb * p.rs + i * rstep + ph;
+        const int row = bid * p.gb * p.rs + i * rstep + ph;
         if (row > last) continue;
         float a[NMAT];
 #pragma unroll
@@ -373,10 +390,18 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
             am_take(am_v, am_i, a[0], row);
             if (row == 0 && a[0] != a[0]) am_nan0 = true;
         }
-        if constexpr (NMAT == 1) p.y[row] = a[0];
+        if constexpr (KH) __hip_atomic_fetch_add(p.y + row, a[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else if constexpr (NMAT == 1) p.y[row] = a[0];
         else p.y[row] = silu_mul(a[0], a[NMAT - 1]);
     }
     if constexpr (EPI == kEpiArgmax) am_finish(am_v, am_i, am_nan0, p.am_cand, p.am_count, p.am_token);
+    if constexpr (NMAT == 2 && EPI == kEpiPlain) {
+        // the next product's output, cleared for its K halves' adds
+        if (p.zero != nullptr) {
+            const int stride = (int)(gridDim.x * blockDim.x);
+            for (int j = (int)(blockIdx.x * blockDim.x) + t; j < p.nzero; j += stride) p.zero[j] = 0.0f;
+        }
+    }
 }
 
 } // namespace xs_detail
@@ -389,6 +414,7 @@ struct XsCfg {
     int nrs;    // row-steps per workgroup
     int rr;     // 1: row-steps dealt to workgroups round robin; 0: consecutive
     int wpc;    // > 0: exactly wpc workgroups per CU (nrs follows), at most wpc resident per CU
+    int kp;     // K parts: 2 = each row's two column halves in different workgroups (EPI 4), else 1
 };
 
 // The calling thread's forced fields (mode 1 of qgemv_set_xs_override; 0 or
@@ -396,10 +422,13 @@ struct XsCfg {
 bool xs_forced(XsCfg *c);
 
 // Host side (gemv_xs.hip): the configuration for a shape, or false when the
-// x-stationary kernel does not take it.
-bool xs_choose(int fmt, int64_t rows, int64_t cols, int nmat, bool norm, XsCfg *c);
+// x-stationary kernel does not take it.  khalf (one matrix, no epilogue): the
+// K-halves form, whose y must hold zeros before the launch.
+bool xs_choose(int fmt, int64_t rows, int64_t cols, int nmat, bool norm, XsCfg *c, bool khalf = false);
+// zero (gate/up pair without the norm, may be null): nzero floats set to zero
+// after the products.
 hipError_t launch_xs(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, const float *x, float *y,
                      int64_t rows, int64_t cols, const XsCfg &c, hipStream_t s, const float *gamma, float eps,
-                     const float *resid, const ArgmaxOut *am = nullptr);
+                     const float *resid, const ArgmaxOut *am = nullptr, float *zero = nullptr, int64_t nzero = 0);
 
 } // namespace qg

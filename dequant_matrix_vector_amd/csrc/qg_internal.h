@@ -59,7 +59,8 @@ struct GemvCfg {
 GemvCfg choose_cfg(int fmt, int64_t rows, int64_t cols, int nmat);
 
 // Measurement hook (qgemv_time_next_launch): true, with the calling thread's
-// pending start/stop events, once; the GEMV launcher then launches with them.
+// oldest queued start/stop events, which it dequeues; the launcher then
+// launches with them.
 bool take_launch_timing(hipEvent_t *start, hipEvent_t *stop);
 
 // Compute units of the current device (cached per device; 256 if the query fails).
@@ -102,9 +103,20 @@ int xs_mode();
 hipError_t launch_gemv(int fmt, const uint8_t *packed, const float *x, float *y, int64_t rows,
                        int64_t cols, hipStream_t s, const GemvCfg &cfg, const float *resid = nullptr,
                        const ArgmaxOut *am = nullptr);
+// zero (row-streaming gate/up without the norm only, else an error): nzero
+// floats set to zero after the products, for a K-halves down product.
 hipError_t launch_gate_up(int fmt, const uint8_t *wg, const uint8_t *wu, const float *x, float *h,
                           int64_t ffn, int64_t d_model, hipStream_t s, const GemvCfg &cfg,
-                          const float *gamma = nullptr, float eps = 0.0f);
+                          const float *gamma = nullptr, float eps = 0.0f, float *zero = nullptr,
+                          int64_t nzero = 0);
+// Whether the one-token FFN of this shape runs its down product in K halves:
+// both products on the row-streaming kernel, the gate/up launch clearing out
+// (qgemv_set_ffn_khalf of the calling thread; off under a launch override).
+bool ffn_down_khalf(int fmt, int64_t d_model, int64_t ffn);
+// out [d_model] += Wd h over the two column halves of Wd, one atomic add each
+// (out holds zeros before: then the result does not depend on their order).
+hipError_t launch_down_khalf(int fmt, const uint8_t *wd, const float *h, float *out, int64_t d_model, int64_t ffn,
+                             hipStream_t s);
 hipError_t launch_repack(int fmt, const void *raw, const float *row_scale, uint8_t *packed,
                          int64_t rows, int64_t cols, hipStream_t s);
 hipError_t launch_dequant(int fmt, const uint8_t *packed, float *w, int64_t rows, int64_t cols,

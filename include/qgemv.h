@@ -166,7 +166,11 @@ int swiglu_gate_up(int fmt, const void *wg, const void *wu, const float *x, floa
  * d_model * ffn >= 2^24, bf16 copies of x and h (rounded to nearest even as the matrix cores take them, so the
  * results are bit-identical; the products then read half the bytes of x and
  * h, for one short conversion launch each); with less, the products run
- * unsplit and on fp32 x and h, with the same accuracy bound.  x, out and the whole declared
+ * unsplit and on fp32 x and h, with the same accuracy bound.  One token, Q4_0
+ * with ffn >= 8192: the down product runs in K halves (qgemv_set_ffn_khalf),
+ * out cleared by the gate/up launch and each output the sum of its two
+ * half-rows, added atomically (deterministic: two additions onto zero
+ * commute).  x, out and the whole declared
  * scratch must be pairwise disjoint.  Two launches on `stream` for n_tok == 1,
  * up to six on the matrix-core path, else two per token; no host
  * synchronization. */
@@ -359,6 +363,20 @@ int qgemv_set_launch_override(int lpr, int r, int waves, int depth, int max_wg, 
  * fields out of range. */
 int qgemv_set_xs_override(int mode, int rs, int seg, int depth, int nrs, int order, int wg_per_cu);
 
+/* Tuning hook for the one-token SwiGLU block (swiglu_ffn, swiglu_ffn_noalloc
+ * with n_tok == 1, or any n_tok on the per-token loop) of Q4_0 matrices whose
+ * products both run on the row-streaming kernel: its down product can run in
+ * K halves -- each workgroup takes one half of the columns of its rows,
+ * staging half of h, and adds its half-row sums into out with an atomic add,
+ * after the gate/up launch has set out to zero.  Each output then receives
+ * exactly two additions onto an exact zero, so it does not depend on their
+ * order (runs are bit-identical); the summation order differs from the whole-row
+ * product's.  mode 0: built in (from ffn >= 8192 on); 1: off; 2: on wherever
+ * the kernel takes the shape (any ffn >= 64).  Off under
+ * qgemv_set_launch_override; qgemv_set_xs_override's fields apply to both
+ * forms.  Per calling thread.  Returns QG_ERR_SHAPE for other modes. */
+int qgemv_set_ffn_khalf(int mode);
+
 /* Measurement export (not the hot path): read `bytes` of device memory at
  * `buf` (16-byte aligned, a multiple of 16) as 16-byte words with a plain
  * grid-stride kernel -- wg_per_cu (1..64) workgroups of 256 threads per CU,
@@ -377,9 +395,12 @@ int qgemv_read_probe(const void *buf, int64_t bytes, int wg_per_cu, int unroll, 
  * end (a matrix-core product: the start of its main kernel, the end of its
  * reduce when K is split): hipEventElapsedTime gives the device time with no
  * marker packets between launches (a hipEventRecord pair costs a pipeline
- * drain of a few microseconds on each side).  Both events or neither (NULL,
- * NULL clears a pending pair); consumed by that one product; thread-local.
- * Returns QG_ERR_NULL if only one event is given. */
+ * drain of a few microseconds on each side).  Each call queues one pair, up
+ * to 4, for the thread's next product launches in order (a swiglu_ffn call
+ * with two pairs queued: its gate/up kernel, then its down kernel); each
+ * pair is consumed by one product.  Both events or neither (NULL, NULL clears
+ * the queue); thread-local.  Returns QG_ERR_NULL if only one event is given,
+ * QG_ERR_SHAPE when 4 pairs are already queued. */
 int qgemv_time_next_launch(void *start_event, void *stop_event);
 
 /* Tuning hook for the matrix-core path (n_tok > 1): force 16-row tiles

@@ -99,6 +99,14 @@ def test_refusals_before_any_device_call(lib):
     lib.qgemv_time_next_launch.argtypes = [P, P]
     assert lib.qgemv_time_next_launch(fake, None) == -1
     assert lib.qgemv_time_next_launch(None, None) == 0
+    # a queue of at most four pairs (nothing is launched, so nothing is
+    # recorded into the placeholder handles); NULL, NULL empties it
+    for _ in range(4):
+        assert lib.qgemv_time_next_launch(fake, fake) == 0
+    assert lib.qgemv_time_next_launch(fake, fake) == -2
+    assert lib.qgemv_time_next_launch(None, None) == 0
+    assert lib.qgemv_time_next_launch(fake, fake) == 0
+    assert lib.qgemv_time_next_launch(None, None) == 0
 
 
 def test_prefill_override_validation(lib):
@@ -210,3 +218,13 @@ def test_xs_override_refusals(lib):
     assert f(1, 2, 5, 2, 12, 1, 3) == 0
     assert f(-1, 0, 0, 0, 0, 0, 0) == 0
     assert f(0, 0, 0, 0, 0, 0, 0) == 0
+
+
+def test_ffn_khalf_refusals(lib):
+    f = lib.qgemv_set_ffn_khalf
+    f.argtypes = [ctypes.c_int]
+    f.restype = ctypes.c_int
+    assert f(-1) == -2
+    assert f(3) == -2
+    for m in (2, 1, 0):
+        assert f(m) == 0
