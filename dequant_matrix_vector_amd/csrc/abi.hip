@@ -461,16 +461,24 @@ int swiglu_ffn_block(int fmt, const void *wg, const void *wu, const void *wd, co
         cg.waves *= 2;
         cg.max_wg /= 2;
     }
+    // K halves for the down product when out is not x (then it does not
+    // overlap x): the gate/up launch clears out, the first half adds the
+    // residual with its sums.  In place, the residual is out's own content.
+    const bool kh = out != x && ffn_down_khalf(fmt, d_model, ffn, true);
     // every token's gate/up (which read x) before any down (which may overwrite x)
     for (int64_t t = 0; t < n_tok; t++) {
         if (launch_gate_up(fmt, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu), x + t * d_model,
-                           h_scratch + t * ffn, ffn, d_model, s, cg, gamma, eps) != hipSuccess)
+                           h_scratch + t * ffn, ffn, d_model, s, cg, gamma, eps, kh ? out + t * d_model : nullptr,
+                           kh ? d_model : 0) != hipSuccess)
             return QG_ERR_LAUNCH;
     }
     for (int64_t t = 0; t < n_tok; t++) {
-        if (launch_gemv(fmt, static_cast<const uint8_t *>(wd), h_scratch + t * ffn, out + t * d_model, d_model, ffn,
-                        s, cd, x + t * d_model) != hipSuccess)
-            return QG_ERR_LAUNCH;
+        const hipError_t e =
+            kh ? launch_down_khalf(fmt, static_cast<const uint8_t *>(wd), h_scratch + t * ffn, out + t * d_model,
+                                   d_model, ffn, s, x + t * d_model)
+               : launch_gemv(fmt, static_cast<const uint8_t *>(wd), h_scratch + t * ffn, out + t * d_model, d_model,
+                             ffn, s, cd, x + t * d_model);
+        if (e != hipSuccess) return QG_ERR_LAUNCH;
     }
     return QG_OK;
 }

@@ -245,7 +245,7 @@ extern "C" int qgemv_set_ffn_khalf(int mode)
     return QG_OK;
 }
 
-bool ffn_down_khalf(int fmt, int64_t d_model, int64_t ffn)
+bool ffn_down_khalf(int fmt, int64_t d_model, int64_t ffn, bool norm)
 {
     GemvCfg forced;
     XsCfg a, b;
@@ -253,15 +253,15 @@ bool ffn_down_khalf(int fmt, int64_t d_model, int64_t ffn)
     // built in from rows of 256 chunks on (the 27B-class down, 544 chunks:
     // half rows of 272)
     if (g_khalf_mode == 0 && ffn / kChunk < 256) return false;
-    return xs_choose(fmt, ffn, d_model, 2, false, &a) && xs_choose(fmt, d_model, ffn, 1, false, &b, true);
+    return xs_choose(fmt, ffn, d_model, 2, norm, &a) && xs_choose(fmt, d_model, ffn, 1, false, &b, true);
 }
 
 hipError_t launch_down_khalf(int fmt, const uint8_t *wd, const float *h, float *out, int64_t d_model, int64_t ffn,
-                             hipStream_t s)
+                             hipStream_t s, const float *resid)
 {
     XsCfg c;
     if (!xs_choose(fmt, d_model, ffn, 1, false, &c, true)) return hipErrorInvalidValue;
-    return launch_xs(fmt, 1, wd, nullptr, h, out, d_model, ffn, c, s, nullptr, 0.0f, nullptr);
+    return launch_xs(fmt, 1, wd, nullptr, h, out, d_model, ffn, c, s, nullptr, 0.0f, resid);
 }
 
 hipError_t launch_gate_up(int fmt, const uint8_t *wg, const uint8_t *wu, const float *x, float *h,
@@ -273,7 +273,7 @@ hipError_t launch_gate_up(int fmt, const uint8_t *wg, const uint8_t *wu, const f
     GemvCfg forced;
     XsCfg xc;
     const bool on_xs = !launch_override(&forced) && xs_choose(fmt, ffn, d_model, 2, gamma != nullptr, &xc);
-    if (zero && (!on_xs || gamma)) return hipErrorInvalidValue;
+    if (zero && !on_xs) return hipErrorInvalidValue;
     if (on_xs) return launch_xs(fmt, 2, wg, wu, x, h, ffn, d_model, xc, s, gamma, eps, nullptr, nullptr, zero, nzero);
     GemvParams p;
     p.q[0] = wg;

@@ -36,9 +36,10 @@
 //   * K halves (EPI 4, one matrix): each workgroup takes one half of the
 //     columns of its rows (even workgroups the first, odd ones the second),
 //     so it stages half of x, and adds its half-row sums into y, which holds
-//     zeros before the launch, with an atomic add.  Each y then takes exactly
-//     two adds onto an exact zero, (0 + a) + b = a + b = b + a, so the
-//     result does not depend on which half lands first.
+//     zeros before the launch, with an atomic add (the first half adds the
+//     residual too, when there is one).  Each y then takes exactly two adds
+//     onto an exact zero, (0 + a) + b = a + b = b + a, so the result does not
+//     depend on which half lands first.
 //
 // Compared with the lane-group kernel (gemv_impl.h) this stages nothing in
 // LDS before streaming (a workgroup of the 27B-class down product would
@@ -79,7 +80,7 @@ struct XsParams {
     uint2 *am_cand;       // EPI 3: one (value bits, index) candidate per workgroup
     uint32_t *am_count;   // EPI 3: workgroups done (zero before the launch; left zero)
     int32_t *am_token;    // EPI 3: the index of the largest y
-    float *zero;          // NMAT 2, EPI 0: a vector set to zero after the products (may be null)
+    float *zero;          // NMAT 2, EPI 0 or 1: a vector set to zero after the products (may be null)
     int nzero;            // its length
 };
 
@@ -390,12 +391,17 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
             am_take(am_v, am_i, a[0], row);
             if (row == 0 && a[0] != a[0]) am_nan0 = true;
         }
-        if constexpr (KH) __hip_atomic_fetch_add(p.y + row, a[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (KH) {
+            // the first half carries the residual (y and the residual are
+            // disjoint here: y held zeros before the launch)
+            if (kh == 0 && p.resid != nullptr) a[0] += p.resid[row];
+            __hip_atomic_fetch_add(p.y + row, a[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         else if constexpr (NMAT == 1) p.y[row] = a[0];
         else p.y[row] = silu_mul(a[0], a[NMAT - 1]);
     }
     if constexpr (EPI == kEpiArgmax) am_finish(am_v, am_i, am_nan0, p.am_cand, p.am_count, p.am_token);
-    if constexpr (NMAT == 2 && EPI == kEpiPlain) {
+    if constexpr (NMAT == 2 && (EPI == kEpiPlain || EPI == kEpiNorm)) {
         // the next product's output, cleared for its K halves' adds
         if (p.zero != nullptr) {
             const int stride = (int)(gridDim.x * blockDim.x);
@@ -422,11 +428,12 @@ struct XsCfg {
 bool xs_forced(XsCfg *c);
 
 // Host side (gemv_xs.hip): the configuration for a shape, or false when the
-// x-stationary kernel does not take it.  khalf (one matrix, no epilogue): the
-// K-halves form, whose y must hold zeros before the launch.
+// x-stationary kernel does not take it.  khalf (one matrix, no norm): the
+// K-halves form, whose y must hold zeros before the launch (a residual, if
+// any, must not overlap y).
 bool xs_choose(int fmt, int64_t rows, int64_t cols, int nmat, bool norm, XsCfg *c, bool khalf = false);
-// zero (gate/up pair without the norm, may be null): nzero floats set to zero
-// after the products.
+// zero (gate/up pair, may be null): nzero floats set to zero after the
+// products.
 hipError_t launch_xs(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, const float *x, float *y,
                      int64_t rows, int64_t cols, const XsCfg &c, hipStream_t s, const float *gamma, float eps,
                      const float *resid, const ArgmaxOut *am = nullptr, float *zero = nullptr, int64_t nzero = 0);

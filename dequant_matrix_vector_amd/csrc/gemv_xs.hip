@@ -146,11 +146,13 @@ bool xs_choose(int fmt, int64_t rows, int64_t cols, int nmat, bool norm, XsCfg *
     }
     if (c.rs == 0) return false;
     // ring depth from back-to-back sweeps of the 27B-class FFN: 2 for the
-    // pair (two matrices already double the loads in flight), 4 for one matrix
-    c.depth = nmat == 2 ? 2 : 4;
-    // (K halves: about one workgroup per CU over both halves)
+    // pair (two matrices already double the loads in flight), 4 for one
+    // matrix, 2 for K halves (two workgroups per CU already double the waves)
+    c.depth = nmat == 2 || khalf ? 2 : 4;
+    // (K halves: about two workgroups per CU over both halves, each staging
+    // half of x: the 27B-class block 31.9 against 32.2 us at one per CU)
     const int64_t steps = steps_of(c, rows);
-    const int64_t want_wg = (int64_t)cu_count() * (nmat == 2 ? 3 : 1) / c.kp;
+    const int64_t want_wg = (int64_t)cu_count() * (nmat == 2 ? 3 : (khalf ? 2 : 1)) / c.kp;
     int64_t nrs = (steps + want_wg - 1) / want_wg;
     // tall matrices: more workgroups rather than more LDS per workgroup
     const int64_t room = (int64_t)(kXsMaxLds / sizeof(float)) - (pchunk + 1) * kXStride - (norm ? xs_detail::kXsMaxWaves : 0);
@@ -184,8 +186,9 @@ hipError_t launch_xs(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, co
     Layout L;
     if (!layout_for(fmt, rows, cols, &L)) return hipErrorInvalidValue;
     const bool khalf = c.kp == 2;
-    if (khalf && (nmat != 1 || gamma || resid || am)) return hipErrorInvalidValue;
-    if (zero && (nmat != 2 || gamma || nzero < 0 || nzero >= (int64_t(1) << 31))) return hipErrorInvalidValue;
+    if (khalf && (nmat != 1 || gamma || am)) return hipErrorInvalidValue;
+    if (khalf && resid && resid + rows > y && y + rows > resid) return hipErrorInvalidValue;
+    if (zero && (nmat != 2 || nzero < 0 || nzero >= (int64_t(1) << 31))) return hipErrorInvalidValue;
     XsParams p;
     p.q[0] = w0;
     p.q[1] = nmat == 2 ? w1 : w0;

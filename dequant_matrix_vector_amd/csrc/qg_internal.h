@@ -103,20 +103,22 @@ int xs_mode();
 hipError_t launch_gemv(int fmt, const uint8_t *packed, const float *x, float *y, int64_t rows,
                        int64_t cols, hipStream_t s, const GemvCfg &cfg, const float *resid = nullptr,
                        const ArgmaxOut *am = nullptr);
-// zero (row-streaming gate/up without the norm only, else an error): nzero
-// floats set to zero after the products, for a K-halves down product.
+// zero (row-streaming gate/up only, else an error): nzero floats set to zero
+// after the products, for a K-halves down product.
 hipError_t launch_gate_up(int fmt, const uint8_t *wg, const uint8_t *wu, const float *x, float *h,
                           int64_t ffn, int64_t d_model, hipStream_t s, const GemvCfg &cfg,
                           const float *gamma = nullptr, float eps = 0.0f, float *zero = nullptr,
                           int64_t nzero = 0);
-// Whether the one-token FFN of this shape runs its down product in K halves:
-// both products on the row-streaming kernel, the gate/up launch clearing out
-// (qgemv_set_ffn_khalf of the calling thread; off under a launch override).
-bool ffn_down_khalf(int fmt, int64_t d_model, int64_t ffn);
-// out [d_model] += Wd h over the two column halves of Wd, one atomic add each
-// (out holds zeros before: then the result does not depend on their order).
+// Whether the one-token FFN of this shape (norm: with the RMSNorm in) runs
+// its down product in K halves: both products on the row-streaming kernel,
+// the gate/up launch clearing out (qgemv_set_ffn_khalf of the calling thread;
+// off under a launch override).
+bool ffn_down_khalf(int fmt, int64_t d_model, int64_t ffn, bool norm = false);
+// out [d_model] += Wd h (+ resid, may be null, disjoint from out) over the two
+// column halves of Wd, one atomic add each (out holds zeros before: then the
+// result does not depend on their order).
 hipError_t launch_down_khalf(int fmt, const uint8_t *wd, const float *h, float *out, int64_t d_model, int64_t ffn,
-                             hipStream_t s);
+                             hipStream_t s, const float *resid = nullptr);
 hipError_t launch_repack(int fmt, const void *raw, const float *row_scale, uint8_t *packed,
                          int64_t rows, int64_t cols, hipStream_t s);
 hipError_t launch_dequant(int fmt, const uint8_t *packed, float *w, int64_t rows, int64_t cols,

@@ -205,7 +205,10 @@ int swiglu_ffn_noalloc(int fmt, const void *wg, const void *wu, const void *wd, 
  * n_tok*ffn of them hold h on return.  With n_tok == 1, or with the
  * matrix-core path turned off, the norm is fused into the gate/up GEMV (the per-token scale factors
  * out of every dot product; the workgroup sums x^2 while staging x*gamma) and
- * the residual into the down GEMV's epilogue: two launches per token.  With
+ * the residual into the down GEMV's epilogue: two launches per token.  Out of
+ * place (out != x), Q4_0 with ffn >= 8192: the down product runs in K halves
+ * as in swiglu_ffn, the first half adding the residual with its half-row sums
+ * (deterministic); in place, on whole rows.  With
  * n_tok > 1 the matrix-core path runs a small RMSNorm launch into the scratch, then the
  * matrix-core products (residual added in the down product's epilogue or in
  * its split-K reduce). */
@@ -364,7 +367,8 @@ int qgemv_set_launch_override(int lpr, int r, int waves, int depth, int max_wg, 
 int qgemv_set_xs_override(int mode, int rs, int seg, int depth, int nrs, int order, int wg_per_cu);
 
 /* Tuning hook for the one-token SwiGLU block (swiglu_ffn, swiglu_ffn_noalloc
- * with n_tok == 1, or any n_tok on the per-token loop) of Q4_0 matrices whose
+ * and swiglu_ffn_block out of place, with n_tok == 1 or any n_tok on the
+ * per-token loop) of Q4_0 matrices whose
  * products both run on the row-streaming kernel: its down product can run in
  * K halves -- each workgroup takes one half of the columns of its rows,
  * staging half of h, and adds its half-row sums into out with an atomic add,

@@ -10,7 +10,9 @@ Stage-wise bars, S from the oracle:
   * out against x + (the oracle's down product of the device's own h), within
     the product bound plus the final add's rounding (2^-24 |out|);
   * out == x exactly when the down scales are 0; in place (out is x) equals
-    out of place bit for bit.
+    out of place bit for bit where both run the same form (out of place,
+    Q4_0 rows of 256 blocks and more run the down product in K halves, whose
+    summation order differs: test_gpu_khalf covers that form).
 Formats: all four on the GEMV path (norm fused into the gate/up staging,
 residual into the down epilogue); Q4_0 with several tokens on the matrix cores.
 """

@@ -13,6 +13,10 @@ choice), the small Q4_0 block (24 blocks: halves of 12), odd block counts
 (25: halves of 13 and 12; 33: 17 and 16), two blocks per row (halves of one),
 forced row-streaming shapes (rows per row-step, ring depth, row-steps per
 workgroup, order, workgroups per CU), and several tokens on the per-token loop.
+The FFN block out of place (RMSNorm in, residual out: the first half adds the
+residual with its sums) against the oracle's block, bit-identical over runs,
+the residual itself when the down scales are 0; in place it keeps whole rows
+(equal to the out-of-place block with the split off).
 """
 import numpy as np
 import pytest
@@ -20,6 +24,7 @@ import pytest
 import oracle
 import synth
 from tests import _gpu as G
+from tests.test_gpu_block import check_block, _run as block_run
 
 pytestmark = pytest.mark.gpu
 
@@ -111,4 +116,43 @@ def test_khalf_per_token_loop():
         _check(tens, x, out, h, d_model, ffn, "K halves, 3 tokens")
     finally:
         G.qg().set_prefill_override(0, 0, 0, 0, 0)
+        G.qg().set_ffn_khalf(0)
+
+
+@pytest.mark.parametrize("d_model,ffn", [(5120, 17408), (288, 768), (96, 800)])
+def test_khalf_block_out_of_place(d_model, ffn):
+    rng = np.random.default_rng(7300 + ffn)
+    tens = [synth.make_tensor("q4_0", ffn, d_model, rng), synth.make_tensor("q4_0", ffn, d_model, rng),
+            synth.make_tensor("q4_0", d_model, ffn, rng)]
+    x = (3.0 * rng.standard_normal((1, d_model))).astype(np.float32)
+    gamma = rng.uniform(0.2, 2.0, d_model).astype(np.float32)
+    try:
+        G.qg().set_ffn_khalf(0 if ffn >= 8192 else 2)
+        pk, out1 = check_block("q4_0", tens, x, gamma, d_model, ffn, f"K-halves block {d_model}/{ffn}")
+        out2, _ = block_run("q4_0", tens, pk, gamma, x, d_model, ffn)
+        assert np.array_equal(out1, out2)
+        # in place: whole rows, whatever the switch says
+        inp, _ = block_run("q4_0", tens, pk, gamma, x, d_model, ffn, in_place=True)
+        G.qg().set_ffn_khalf(1)
+        whole, _ = block_run("q4_0", tens, pk, gamma, x, d_model, ffn)
+        assert np.array_equal(inp, whole)
+    finally:
+        G.qg().set_ffn_khalf(0)
+
+
+def test_khalf_block_zero_down_is_the_residual():
+    d_model, ffn = 288, 768
+    rng = np.random.default_rng(7400)
+    tg = synth.make_tensor("q4_0", ffn, d_model, rng)
+    tu = synth.make_tensor("q4_0", ffn, d_model, rng)
+    dd, qd = synth.draw_q4_0(rng, d_model, ffn)
+    td = synth.QTensor("down", "q4_0", d_model, ffn, synth.pack_q4_0(np.zeros_like(dd), qd))
+    pk = [G.upload(t) for t in (tg, tu, td)]
+    x = rng.standard_normal((1, d_model)).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, d_model).astype(np.float32)
+    try:
+        G.qg().set_ffn_khalf(2)
+        out, _ = block_run("q4_0", (tg, tu, td), pk, gamma, x, d_model, ffn)
+        assert np.array_equal(out, x)
+    finally:
         G.qg().set_ffn_khalf(0)
