@@ -10,16 +10,22 @@ working set is >= 1 GiB (over 4x the 256 MB Infinity Cache), so each step
 streams its weights from HBM.
 
 value = algorithmic weight bytes per step (150,405,120 B: 18 B per 32 weights)
-        / wall time per step (K steps between two device synchronizations,
-        launched through the C ABI with nothing else between the kernels).
+        / wall time per step: the K steps (one swiglu_ffn call each, over the
+        rotating copies) captured once in a HIP graph and uploaded; the W
+        warm-up steps; then the graph launched once between two device
+        synchronizations.  This is the last pass of the headline part, after
+        the per-kernel passes below, so the device runs the step in its
+        steady state (its first milliseconds of work after an idle spell run
+        slower).  The same K steps launched one call at a time through the C
+        ABI, just before, are reported beside it (detail.value_eager_launches).
 roofline: the dominant kernel (fused gate/up, 100,270,080 B per launch) timed
-with HIP events on the stream it runs on, against 8 TB/s HBM: the same K steps
-run a second time with each launch carrying its own start/stop events
-(two pairs queued with qgemv_time_next_launch before each swiglu_ffn call:
-the library launches both kernels with hipExtLaunchKernel), so the events
-hold each dispatch's own start and end -- the durations rocprofv3's kernel
-trace reports.  Timed launches leave gaps between the kernels (as
-hipEventRecord pairs do), hence a pass of their own.
+with HIP events on the stream it runs on, against 8 TB/s HBM: the K steps
+run with each launch carrying its own start/stop events (two pairs queued
+with qgemv_time_next_launch before each swiglu_ffn call: the library
+launches both kernels with hipExtLaunchKernel), so the events hold each
+dispatch's own start and end -- the durations rocprofv3's kernel trace
+reports.  Timed launches leave gaps between the kernels (as hipEventRecord
+pairs do), hence a pass of their own.
 Also reported: back to back (HIP graphs of 32 launches over the rotating
 copies) the gate/up product alone (swiglu_gate_up, the same kernel) and the
 whole block (swiglu_ffn), whose difference is the down product's share as the
@@ -173,6 +179,20 @@ def read_ceiling(qg, torch, dev, launch_bytes=(100270080, 50135040)):
     del pool
     torch.cuda.empty_cache()
     return res
+
+
+def upload_graph(graph, stream_ptr):
+    """hipGraphUpload of a captured torch graph's executable on the stream, so
+    that its first launch carries no upload; a no-op if the runtime or torch
+    does not offer it."""
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        exe = int(graph.raw_cuda_graph_exec())
+    except (OSError, AttributeError, RuntimeError, TypeError, ValueError):
+        return False
+    hip.hipGraphUpload.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipGraphUpload.restype = ctypes.c_int
+    return hip.hipGraphUpload(ctypes.c_void_p(exe), ctypes.c_void_p(stream_ptr)) == 0
 
 
 def back_to_back_us(torch, launch, n=32, reps=5):
@@ -501,18 +521,22 @@ def main():
         if ffn_call(*ffn_args[i % ncopy]) != 0:
             raise RuntimeError("swiglu_ffn failed")
 
-    for i in range(a.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # value: the K steps with nothing but their launches (no events between the
-    # kernels, which run back to back)
-    t0 = time.perf_counter()
-    for i in range(a.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # roofline: the same K steps again, each launch carrying its own events
-    # (the timed launch path leaves the GPU idle between kernels, so this pass
+    # Order of the passes: the K steps are captured in one HIP graph first
+    # (capturing leaves the device idle for milliseconds); then the per-kernel
+    # passes and the read ceiling; then the K steps launched one call at a
+    # time; then the W warm-up steps and, right after them, the timed launch of
+    # the graph (value), so that the device is in the steady state the step
+    # runs in (after an idle spell its first milliseconds of work run slower).
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cs = torch.cuda.current_stream().cuda_stream
+        for i in range(a.steps):
+            if ffn_call(*ffn_args[i % ncopy][:-1], cs) != 0:
+                raise RuntimeError("swiglu_ffn failed")
+    uploaded = upload_graph(graph, sptr)
+
+    # roofline: the K steps with each launch carrying its own events (the
+    # timed launch path leaves the GPU idle between kernels, so this pass
     # gives kernel durations, not the step rate)
     for i in range(a.steps):
         step(i, True)
@@ -520,8 +544,6 @@ def main():
     gu_ms = [evs.ms(4 * i, 4 * i + 1) for i in range(a.steps)]
     dn_ms = [evs.ms(4 * i + 2, 4 * i + 3) for i in range(a.steps)]
     evs.close()
-    ms_per_step = wall * 1e3 / a.steps
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
     gu_avg = float(np.mean(gu_ms))
     dn_avg = float(np.mean(dn_ms))
     achieved = gu_bytes / (gu_avg * 1e-3) / 1e9
@@ -540,10 +562,33 @@ def main():
             raise RuntimeError("swiglu_ffn failed")
 
     gu_b2b = dn_b2b = ffn_b2b = float("nan")
+    ceil = None
     if not a.no_extras:
         gu_b2b = back_to_back_us(torch, gu_launch)
         ffn_b2b = back_to_back_us(torch, ffn_launch)
         dn_b2b = ffn_b2b - gu_b2b
+        ceil = read_ceiling(qg, torch, dev, (gu_bytes, tens[2].weight_bytes))
+        torch.cuda.empty_cache()
+
+    # the K steps as launches from the host, one call at a time (no events
+    # between the kernels, which run back to back)
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall_eager = time.perf_counter() - t0
+    # value: the W warm-up steps, then the K steps' graph
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del graph
+    ms_per_step = wall * 1e3 / a.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    value_eager = step_bytes / (wall_eager / a.steps) / 1e9
 
     detail = {
         "gate_up_us": round(gu_avg * 1e3, 2), "down_us": round(dn_avg * 1e3, 2),
@@ -556,6 +601,9 @@ def main():
         "ffn_device_us": round((gu_avg + dn_avg) * 1e3, 2),
         "ffn_device_GBs": round(step_bytes / ((gu_avg + dn_avg) * 1e-3) / 1e9, 1),
         "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
+        "value_eager_launches": round(value_eager, 1),
+        "value_graph_uploaded": bool(uploaded),
+        "ms_per_step_eager_launches": round(wall_eager * 1e3 / a.steps, 5),
         "rotating_copies": ncopy,
     }
     if a.no_extras:
@@ -609,8 +657,7 @@ def main():
     }
     del copies
     torch.cuda.empty_cache()
-    if not a.no_extras:
-        ceil = read_ceiling(qg, torch, dev, (gu_bytes, tens[2].weight_bytes))
+    if ceil is not None:
         rec["read_ceiling"] = dict(ceil, unit="GB/s", kernel="qgemv_read_probe (plain 16-byte grid-stride read)")
         cg = ceil[f"GBs_{gu_bytes}_per_launch"]
         rec["roofline"]["read_ceiling_per_launch"] = cg

@@ -156,3 +156,40 @@ def test_khalf_block_zero_down_is_the_residual():
         assert np.array_equal(out, x)
     finally:
         G.qg().set_ffn_khalf(0)
+
+
+def test_khalf_graph_replays():
+    # the 27B-class FFN and out-of-place block at one token (gate/up clearing
+    # out, down in K halves with atomic adds) captured in one HIP graph and
+    # replayed three times, out filled with NaN before each replay and eager
+    # calls between them: every replay equals the eager calls bit for bit
+    d_model, ffn = 5120, 17408
+    torch = G.torch
+    tens, x = _tensors(d_model, ffn, 7500)
+    pk = [G.upload(t) for t in tens]
+    xd = torch.from_numpy(x).to(G.dev())
+    gd = torch.from_numpy(np.random.default_rng(7501).uniform(0.5, 1.5, d_model).astype(np.float32)).to(G.dev())
+    sf = torch.empty(G.qg().swiglu_ffn_scratch_elems("q4_0", d_model, ffn, 1), device=G.dev())
+    sb = torch.empty(G.qg().swiglu_ffn_block_scratch_elems("q4_0", d_model, ffn, 1), device=G.dev())
+    of, ob = torch.empty((1, d_model), device=G.dev()), torch.empty((1, d_model), device=G.dev())
+
+    def calls():
+        G.qg().swiglu_ffn("q4_0", pk[0], pk[1], pk[2], xd, d_model, ffn, out=of, h_scratch=sf)
+        G.qg().swiglu_ffn_block("q4_0", pk[0], pk[1], pk[2], gd, 1e-5, xd, d_model, ffn, out=ob, h_scratch=sb)
+
+    calls()
+    torch.cuda.synchronize()
+    want_f, want_b = of.clone(), ob.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    torch.cuda.synchronize()
+    for k in range(3):
+        of.fill_(float("nan"))
+        ob.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(of, want_f) and torch.equal(ob, want_b), f"replay {k}"
+        G.qg().swiglu_ffn("q4_0", pk[0], pk[1], pk[2], xd, d_model, ffn, out=torch.empty_like(of),
+                          h_scratch=torch.empty_like(sf))   # eager work between the replays
+        torch.cuda.synchronize()
