@@ -443,7 +443,7 @@ def extra_report(qg, synth, torch, np, dev, graph_iters=20):
         tok = torch.empty(1, dtype=torch.int32, device=dev)
         ws = torch.zeros(qg.head_argmax_workspace_bytes(t.fmt, t.rows, t.cols), dtype=torch.uint8, device=dev)
 
-        def head(i):   # one launch: the argmax fused into the product
+        def head(i):   # the argmax fused into the product (candidates), then the combine launch
             qg.qgemv_head_argmax(t.fmt, hc[i % ncopy], x, t.rows, t.cols, logits=logits, token=tok, workspace=ws,
                                  fused=True)
 

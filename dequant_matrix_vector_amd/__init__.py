@@ -498,7 +498,7 @@ def qgemv_argmax(logits, n, token=None, stream=None) -> torch.Tensor:
 
 
 def head_argmax_workspace_bytes(fmt, rows, cols):
-    """Bytes of the zero-filled workspace the fused head needs (host only)."""
+    """Bytes of workspace the fused head needs (host only)."""
     n = lib.qgemv_head_argmax_workspace_bytes(_fmt(fmt), rows, cols)
     _check(n if n < 0 else 0, "qgemv_head_argmax_workspace_bytes")
     return n
@@ -506,10 +506,10 @@ def head_argmax_workspace_bytes(fmt, rows, cols):
 
 def qgemv_head_argmax(fmt, packed, x, rows, cols, logits=None, token=None, workspace=None, fused=False, stream=None):
     """(token int32 [n_tok], logits [n_tok][rows]): the head product and greedy
-    sampling: the product, then the argmax launch; or (fused, one token) one
-    launch, with workspace (uint8, at least head_argmax_workspace_bytes,
-    zero-filled before its first use and left ready by every call; a
-    zero-filled one is made when none is given)."""
+    sampling: the product, then the argmax launch over the logits; or (fused,
+    one token) the product writing one candidate per workgroup into workspace
+    (uint8, at least head_argmax_workspace_bytes; made when none is given),
+    then a one-workgroup launch combining them."""
     n_tok = _ntok(x, cols)
     logits = _y(logits, (n_tok, rows), x.device)
     if token is None:

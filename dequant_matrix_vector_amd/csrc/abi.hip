@@ -509,11 +509,11 @@ int qgemv_head_argmax(int fmt, const void *packed, const float *x, float *logits
 }
 
 // Workspace of the fused head, laid out alike for every shape (so one
-// workspace serves heads of several shapes): the counters (a top counter,
-// then 64 group counters, each on its own 128-byte line), then one 8-byte
+// workspace serves heads of several shapes): a 256-byte header whose first
+// word the product sets to its number of candidates, then one 8-byte
 // candidate per workgroup (a workgroup writes at least one row, so rows
 // candidates always suffice).
-static const int64_t kAmCounterBytes = 128 * (1 + 64);
+static const int64_t kAmCounterBytes = 256;
 
 int64_t qgemv_head_argmax_workspace_bytes(int fmt, int64_t rows, int64_t cols)
 {
@@ -543,12 +543,14 @@ int qgemv_head_argmax_ws(int fmt, const void *packed, const float *x, float *log
     am.count = reinterpret_cast<uint32_t *>(ws);
     am.cand = reinterpret_cast<uint2 *>(ws + hdr);
     am.max_cand = (workspace_bytes - hdr) / 8;
-    am.token = token;
+    int64_t ncand = 0;
+    am.grid_out = &ncand;
     const GemvCfg cfg = choose_cfg(fmt, rows, cols, 1);
-    return launch_gemv(fmt, static_cast<const uint8_t *>(packed), x, logits, rows, cols, (hipStream_t)stream, cfg,
-                       nullptr, &am) == hipSuccess
-               ? QG_OK
-               : QG_ERR_LAUNCH;
+    if (launch_gemv(fmt, static_cast<const uint8_t *>(packed), x, logits, rows, cols, (hipStream_t)stream, cfg,
+                    nullptr, &am) != hipSuccess ||
+        launch_am_combine(am.cand, ncand, token, (hipStream_t)stream) != hipSuccess)
+        return QG_ERR_LAUNCH;
+    return QG_OK;
 }
 
 // ------------------------------------------------------ Q8_0 activations --

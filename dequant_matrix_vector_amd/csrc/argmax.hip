@@ -146,7 +146,52 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax4_kernel(const float *__
     }
 }
 
+// The token from a product's workgroup candidates (the fused head), in one
+// wave: each lane scans a strided slice of the n (value bits, index) pairs
+// under the same rule, an index of 0xFFFFFFFF flagging a NaN at row 0 (then
+// the token is 0); the lanes combine through the xor tree.  n comes from the
+// host, so all of a lane's loads go out at once.
+constexpr int kCombineUnroll = 8;
+
+__global__ __launch_bounds__(64) void am_combine_kernel(const uint2 *__restrict__ cand, int n,
+                                                        int32_t *__restrict__ token)
+{
+    float bv = -__builtin_inff();
+    int bi = 0x7FFFFFFF;
+    int nan0 = 0;
+    for (int base = 0; base < n; base += 64 * kCombineUnroll) {
+        uint2 c[kCombineUnroll];
+#pragma unroll
+        for (int k = 0; k < kCombineUnroll; k++) {
+            const int j = base + k * 64 + (int)threadIdx.x;
+            c[k] = cand[j < n ? j : n - 1];
+        }
+#pragma unroll
+        for (int k = 0; k < kCombineUnroll; k++) {
+            if (base + k * 64 + (int)threadIdx.x < n) {
+                if (c[k].y == 0xFFFFFFFFu) nan0 = 1;
+                else take_better(bv, bi, __builtin_bit_cast(float, c[k].x), (int)c[k].y);
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int oi = __shfl_xor(bi, off, 64);
+        nan0 |= __shfl_xor(nan0, off, 64);
+        take_better(bv, bi, ov, oi);
+    }
+    if (threadIdx.x == 0) *token = nan0 ? 0 : bi;
+}
+
 } // namespace
+
+hipError_t launch_am_combine(const uint2 *cand, int64_t n, int32_t *token, hipStream_t s)
+{
+    if (n < 1 || n >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(am_combine_kernel, dim3(1), dim3(64), 0, s, cand, (int)n, token);
+    return hipGetLastError();
+}
 
 hipError_t launch_argmax(const float *logits, int32_t *token, int64_t n, int64_t n_tok, hipStream_t s)
 {

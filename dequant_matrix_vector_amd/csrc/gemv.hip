@@ -229,7 +229,7 @@ hipError_t launch_gemv(int fmt, const uint8_t *packed, const float *x, float *y,
     p.am_cand = am ? am->cand : nullptr;
     p.am_max = am ? am->max_cand : 0;
     p.am_count = am ? am->count : nullptr;
-    p.am_token = am ? am->token : nullptr;
+    p.am_grid = am ? am->grid_out : nullptr;
     return dispatch_fmt<1>(fmt, p, aligned_cfg(fmt, p.nchunk, cfg), s);
 }
 
@@ -292,7 +292,7 @@ hipError_t launch_gate_up(int fmt, const uint8_t *wg, const uint8_t *wu, const f
     p.am_cand = nullptr;
     p.am_max = 0;
     p.am_count = nullptr;
-    p.am_token = nullptr;
+    p.am_grid = nullptr;
     return dispatch_fmt<2>(fmt, p, aligned_cfg(fmt, p.nchunk, cfg), s);
 }
 

@@ -85,8 +85,8 @@ struct GemvParams {
     int64_t doff;
     uint2 *am_cand;       // EPI 3: one (value bits, index) candidate per workgroup
     int64_t am_max;       // EPI 3: room for candidates (workgroups) in am_cand
-    uint32_t *am_count;   // EPI 3: workgroups done (zero before the launch; left zero)
-    int32_t *am_token;    // EPI 3: the index of the largest y
+    uint32_t *am_count;   // EPI 3: where workgroup 0 stores the number of candidates
+    int64_t *am_grid;     // EPI 3, host memory: the launcher records its grid there (not read by the kernel)
 };
 
 enum { kEpiPlain = 0, kEpiNorm = 1, kEpiResid = 2, kEpiArgmax = 3 };
@@ -107,89 +107,44 @@ __device__ __forceinline__ void am_take(float &bv, int &bi, float v, int i)
     }
 }
 
-// The workgroup's candidate, then the launch's token.  Each workgroup writes
-// its candidate with a device-coherent store (written through to where every
-// XCD reads it), waits for that store, then counts itself done with a
-// device-scope atomic -- on one of up to kAmGroups group counters (workgroup
-// b on counter b % groups, one 128-byte line each), whose last member counts
-// its group done on the top counter, so that no counter takes more than a few
-// dozen atomics at once; the last group's finisher reads every candidate with
-// device-coherent loads and writes the token.  Each finisher sets its counter
-// back to zero for the next launch.  No cache-wide fence: nothing else
-// crosses between workgroups (whether y[0] is NaN travels in the candidate of
-// the workgroup that wrote row 0, as index -1).  Every thread of the
-// workgroup calls this once, after its last row; nan0: this thread wrote row
-// 0 and it is NaN.  count: the top counter, then the kAmGroups group
-// counters, kAmLineWords words (128 bytes) apart.
-constexpr int kAmGroups = 64;
-constexpr int kAmLineWords = 32;
-
-__device__ __forceinline__ void am_finish(float bv, int bi, bool nan0, uint2 *cand, uint32_t *count, int32_t *token)
+// The workgroup's candidate: the (value, index) of the rows it wrote, kept
+// under the rule above through a fixed xor tree and the waves in order, is
+// stored at cand[blockIdx.x] (index 0xFFFFFFFF: this workgroup wrote row 0
+// and it is NaN); workgroup 0 also stores the number of candidates at
+// *count.  A second, one-workgroup launch (am_combine) reduces them to the
+// token: the boundary between the launches orders every candidate store
+// before its loads, so no counter, fence or wait is needed here.  Every
+// thread of the workgroup calls this once, after its last row; nan0: this
+// thread wrote row 0 and it is NaN.
+__device__ __forceinline__ void am_finish(float bv, int bi, bool nan0, uint2 *cand, uint32_t *count)
 {
     __shared__ float am_v[16];
     __shared__ int am_i[16];
     __shared__ int am_n[16];
-    __shared__ int am_last;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    auto wg_reduce = [&](float &v, int &i, bool &n) {
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(v, off, 64);
-            const int oi = __shfl_xor(i, off, 64);
-            n = __shfl_xor((int)n, off, 64) != 0 || n;
-            am_take(v, i, ov, oi);
-        }
-        if (lane == 0) {
-            am_v[wave] = v;
-            am_i[wave] = i;
-            am_n[wave] = n;
-        }
-        __syncthreads();
-        v = am_v[0];
-        i = am_i[0];
-        n = am_n[0] != 0;
+    for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int oi = __shfl_xor(bi, off, 64);
+        nan0 = __shfl_xor((int)nan0, off, 64) != 0 || nan0;
+        am_take(bv, bi, ov, oi);
+    }
+    if (lane == 0) {
+        am_v[wave] = bv;
+        am_i[wave] = bi;
+        am_n[wave] = nan0;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float v = am_v[0];
+        int i = am_i[0];
+        bool n = am_n[0] != 0;
         for (int w = 1; w < nw; w++) {
             am_take(v, i, am_v[w], am_i[w]);
             n = n || am_n[w] != 0;
         }
-        __syncthreads();
-    };
-    wg_reduce(bv, bi, nan0);
-    if (threadIdx.x == 0) {
-        const uint32_t idx = nan0 ? 0xFFFFFFFFu : (uint32_t)bi;
-        __hip_atomic_store(reinterpret_cast<uint64_t *>(cand) + blockIdx.x,
-                           (uint64_t)__builtin_bit_cast(uint32_t, bv) | ((uint64_t)idx << 32), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        // the candidate is written through before the count can be seen
-        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("" ::: "memory");
-        const uint32_t grid = gridDim.x, groups = grid < kAmGroups ? grid : kAmGroups;
-        const uint32_t grp = blockIdx.x % groups;
-        const uint32_t members = (grid - grp + groups - 1) / groups;   // workgroups b < grid with b % groups == grp
-        uint32_t *sub = count + kAmLineWords * (1 + grp);
-        int last = 0;
-        if (__hip_atomic_fetch_add(sub, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1) {
-            __hip_atomic_store(sub, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            last = __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == groups - 1;
-        }
-        am_last = last;
-    }
-    __syncthreads();
-    if (!am_last) return;
-    float v = -__builtin_inff();
-    int i = 0x7FFFFFFF;   // loses to every value, -inf included
-    bool n = false;
-    for (int j = threadIdx.x; j < (int)gridDim.x; j += blockDim.x) {
-        const uint64_t c = __hip_atomic_load(reinterpret_cast<const uint64_t *>(cand) + j, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-        if ((uint32_t)(c >> 32) == 0xFFFFFFFFu) n = true;
-        else am_take(v, i, __builtin_bit_cast(float, (uint32_t)c), (int)(c >> 32));
-    }
-    wg_reduce(v, i, n);
-    if (threadIdx.x == 0) {
-        *token = n ? 0 : i;
-        __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        cand[blockIdx.x] = make_uint2(__builtin_bit_cast(uint32_t, v), n ? 0xFFFFFFFFu : (uint32_t)i);
+        if (blockIdx.x == 0) *count = gridDim.x;
     }
 }
 
@@ -879,7 +834,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvParams p)
             }
         }
     }
-    if constexpr (EPI == kEpiArgmax) am_finish(am_v, am_i, am_nan0, p.am_cand, p.am_count, p.am_token);
+    if constexpr (EPI == kEpiArgmax) am_finish(am_v, am_i, am_nan0, p.am_cand, p.am_count);
 }
 
 template <int FMT, int LPR, int R, int NMAT, int D, int CPL, int EPI>
@@ -890,6 +845,7 @@ hipError_t go(const GemvParams &p, const GemvCfg &c, hipStream_t s)
     int64_t nwg = (batches + c.waves - 1) / c.waves;
     if (c.max_wg > 0 && nwg > c.max_wg) nwg = c.max_wg;
     if (EPI == kEpiArgmax && nwg > p.am_max) return hipErrorInvalidValue;
+    if (EPI == kEpiArgmax && p.am_grid) *p.am_grid = nwg;
     // NORM: 16 more floats after the spare chunk for the wave sums of x^2
     const size_t lds = gemv_lds_bytes((int64_t)p.nchunk * kChunk) + (EPI == kEpiNorm ? 64 : 0);
     auto kern = gemv_kernel<FMT, LPR, R, NMAT, D, CPL, EPI>;

@@ -41,8 +41,7 @@ struct RowsParams {
     int rps;              // rows per row-step (threads / nchunk)
     int nrs;              // row-steps per workgroup
     uint2 *am_cand;       // EPI 3: one (value bits, index) candidate per workgroup
-    uint32_t *am_count;   // EPI 3: workgroups done (zero before the launch; left zero)
-    int32_t *am_token;    // EPI 3: the index of the largest y
+    uint32_t *am_count;   // EPI 3: where workgroup 0 stores the number of candidates
 };
 
 enum { kEpiPlain = 0, kEpiResid = 2, kEpiArgmax = 3 };
@@ -121,7 +120,7 @@ __global__ __launch_bounds__(1024) void gemv_rows_q8_kernel(RowsParams p)
         }
         p.y[row] = a;
     }
-    if constexpr (EPI == kEpiArgmax) am_finish(am_v, am_i, am_nan0, p.am_cand, p.am_count, p.am_token);
+    if constexpr (EPI == kEpiArgmax) am_finish(am_v, am_i, am_nan0, p.am_cand, p.am_count);
 }
 
 constexpr int kRowsMaxLds = 64 * 1024;
@@ -217,8 +216,8 @@ hipError_t launch_rows(int fmt, const uint8_t *packed, const float *x, float *y,
     p.nrs = c.nrs;
     p.am_cand = am ? am->cand : nullptr;
     p.am_count = am ? am->count : nullptr;
-    p.am_token = am ? am->token : nullptr;
     if (am && (resid || c.grid > am->max_cand)) return hipErrorInvalidValue;
+    if (am && am->grid_out) *am->grid_out = c.grid;
     const size_t lds = (size_t)c.nrs * c.threads * 4;
     using namespace rows_detail;
     if (am) {

@@ -78,8 +78,7 @@ struct XsParams {
     int ga, gb;           // global row-step of local step i in workgroup b: i * ga + b * gb
                           // (ga = 1, gb = nrs: consecutive steps; ga = grid, gb = 1: round robin)
     uint2 *am_cand;       // EPI 3: one (value bits, index) candidate per workgroup
-    uint32_t *am_count;   // EPI 3: workgroups done (zero before the launch; left zero)
-    int32_t *am_token;    // EPI 3: the index of the largest y
+    uint32_t *am_count;   // EPI 3: where workgroup 0 stores the number of candidates
     float *zero;          // NMAT 2, EPI 0 or 1: a vector set to zero after the products (may be null)
     int nzero;            // its length
 };
@@ -400,7 +399,7 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
         else if constexpr (NMAT == 1) p.y[row] = a[0];
         else p.y[row] = silu_mul(a[0], a[NMAT - 1]);
     }
-    if constexpr (EPI == kEpiArgmax) am_finish(am_v, am_i, am_nan0, p.am_cand, p.am_count, p.am_token);
+    if constexpr (EPI == kEpiArgmax) am_finish(am_v, am_i, am_nan0, p.am_cand, p.am_count);
     if constexpr (NMAT == 2 && (EPI == kEpiPlain || EPI == kEpiNorm)) {
         // the next product's output, cleared for its K halves' adds
         if (p.zero != nullptr) {

@@ -216,8 +216,8 @@ hipError_t launch_xs(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, co
     p.nzero = (int)nzero;
     p.am_cand = am ? am->cand : nullptr;
     p.am_count = am ? am->count : nullptr;
-    p.am_token = am ? am->token : nullptr;
     if (am && (nmat != 1 || nwg > am->max_cand)) return hipErrorInvalidValue;
+    if (am && am->grid_out) *am->grid_out = nwg;
     size_t lds = xs_lds_bytes(c, nmat, p.kchunks, gamma != nullptr);
     // at most wpc resident per CU: ask for more than a (wpc+1)-th of the LDS
     if (c.wpc > 0 && lds <= kXsMaxLds / (c.wpc + 1)) lds = kXsMaxLds / (c.wpc + 1) + 256;

@@ -74,12 +74,18 @@ bool launch_override(GemvCfg *c);
 // candidate, counters of finished workgroups (a top counter and group
 // counters, each on its own 128-byte line; zero before the launch, left zero
 // by it) and the token.
+// The product's candidates for greedy sampling (EPI 3): one (value bits,
+// index) per workgroup, and the number of them, which workgroup 0 stores;
+// launch_am_combine then reduces them to the token.
 struct ArgmaxOut {
-    uint2 *cand;       // max_cand entries
-    int64_t max_cand;  // the launch fails if it would take more workgroups
-    uint32_t *count;   // top counter, then 64 group counters, each 32 words apart
-    int32_t *token;
+    uint2 *cand;        // max_cand entries
+    int64_t max_cand;   // the launch fails if it would take more workgroups
+    uint32_t *count;    // the number of candidates (written by the product)
+    int64_t *grid_out;  // host memory: the launcher records its number of workgroups there
 };
+// One wave: the token from the n candidates a product launch wrote (the
+// first index of the largest value; 0 if a candidate flags row 0 as NaN).
+hipError_t launch_am_combine(const uint2 *cand, int64_t n, int32_t *token, hipStream_t s);
 
 // One-token Q8_0 products with short rows (gemv_rows.hip): a lane per block
 // position, rows packed across the lanes.  rows_choose: false when the kernel

@@ -247,18 +247,17 @@ int qgemv_head_argmax(int fmt, const void *packed, const float *x, float *logits
 
 /* The same head with the argmax fused into the product (Go "llm" package,
  * Design points: greedy sampling on the GPU, the token the only readback;
- * func Argmax: the first index of the largest logit): for n_tok == 1 one
- * launch, in which every workgroup reduces the rows it wrote to one (value,
- * index) candidate and the last workgroup to finish (a counter in the
- * workspace: 64 group counters, then one over the groups) combines the
- * candidates into the token, by the rule of
- * qgemv_argmax (first index on ties, NaN never chosen unless logits[0] is
- * NaN, then 0).  logits are written as by qgemv.  For n_tok > 1 the call is
- * qgemv_head_argmax (workspace unused).  workspace (device, 16-byte aligned,
- * caller-owned): at least qgemv_head_argmax_workspace_bytes bytes,
- * zero-filled before its first use; every call leaves its counters at zero
- * again, so it is ready for the next call without a clearing launch.  Calls
- * that share a workspace must not overlap (order them on one stream).
+ * func Argmax: the first index of the largest logit): for n_tok == 1 the
+ * product's workgroups each reduce the rows they wrote to one (value, index)
+ * candidate in the workspace (workgroup 0 also writes their number), and a
+ * one-workgroup launch combines the candidates into the token, by the rule
+ * of qgemv_argmax (first index on ties, NaN never chosen unless logits[0] is
+ * NaN, then 0): two launches, the second reading 8 bytes per workgroup
+ * instead of the logits.  logits are written as by qgemv.  For n_tok > 1 the
+ * call is qgemv_head_argmax (workspace unused).  workspace (device, 16-byte
+ * aligned, caller-owned, no initialization needed): at least
+ * qgemv_head_argmax_workspace_bytes bytes.  Calls that share a workspace
+ * must not overlap (order them on one stream).
  * Errors as qgemv, plus QG_ERR_NULL (token, workspace), QG_ERR_ALIGN,
  * QG_ERR_SCRATCH (workspace too small) and QG_ERR_ALIAS (token or workspace
  * overlapping each other or an input). */
@@ -266,7 +265,7 @@ int qgemv_head_argmax_ws(int fmt, const void *packed, const float *x, float *log
                          int64_t rows, int64_t cols, int64_t n_tok, void *workspace, int64_t workspace_bytes,
                          void *stream);
 /* Bytes of workspace qgemv_head_argmax_ws needs for a head of this shape
- * (8320 bytes of counters, then 8 * rows of candidates, the same layout for
+ * (a 256-byte header, then 8 * rows of candidates, the same layout for
  * every shape, so one workspace of the largest size serves several heads;
  * host only), or QG_ERR_FORMAT / QG_ERR_SHAPE. */
 int64_t qgemv_head_argmax_workspace_bytes(int fmt, int64_t rows, int64_t cols);

@@ -86,10 +86,10 @@ def test_head_argmax_quantize_dequant_repack_refusals():
     refused("token: needs at least", qg.qgemv_head_argmax, "q8_0", pk, torch.zeros(2 * C, dtype=F32), R, C,
             logits=torch.zeros(2 * R, dtype=F32), token=torch.zeros(1, dtype=I32))
     refused("workspace: needs at least", qg.qgemv_head_argmax, "q8_0", pk, x, R, C,
-            workspace=torch.zeros(8320 + 8 * R - 1, dtype=U8), fused=True)
+            workspace=torch.zeros(256 + 8 * R - 1, dtype=U8), fused=True)
     refused("workspace: expected torch.uint8", qg.qgemv_head_argmax, "q8_0", pk, x, R, C,
-            workspace=torch.zeros(8320 + 8 * R, dtype=F32), fused=True)
-    assert qg.head_argmax_workspace_bytes("q8_0", R, C) == 8320 + 8 * R
+            workspace=torch.zeros(256 + 8 * R, dtype=F32), fused=True)
+    assert qg.head_argmax_workspace_bytes("q8_0", R, C) == 256 + 8 * R
     refused("blocks: needs at least", qg.qquantize_q8_0, x, C, blocks=torch.zeros(C // 32 * 34 - 1, dtype=U8))
     refused("w_out: needs at least", qg.qdequant, "q8_0", pk, R, C, w_out=torch.zeros(R * C - 1, dtype=F32))
     refused("raw: needs at least", qg.qgemv_repack_q4_0, torch.zeros(R * (C // 32) * 18 - 1, dtype=U8),
