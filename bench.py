@@ -13,10 +13,10 @@ value = algorithmic weight bytes per step (150,405,120 B: 18 B per 32 weights)
         / wall time per step: the K steps (one swiglu_ffn call each, over the
         rotating copies) captured once in a HIP graph and uploaded; the W
         warm-up steps; then the graph launched once between two device
-        synchronizations.  This is the last pass of the headline part, after
-        the per-kernel passes below, so the device runs the step in its
-        steady state (its first milliseconds of work after an idle spell run
-        slower).  The same K steps launched one call at a time through the C
+        synchronizations.  It follows the per-kernel passes below, so the
+        device runs the step in its steady state (its first milliseconds of
+        work after an idle spell run slower); the read ceiling is measured
+        after it.  The same K steps launched one call at a time through the C
         ABI, just before, are reported beside it (detail.value_eager_launches).
 roofline: the dominant kernel (fused gate/up, 100,270,080 B per launch) timed
 with HIP events on the stream it runs on, against 8 TB/s HBM: the K steps
@@ -523,10 +523,12 @@ def main():
 
     # Order of the passes: the K steps are captured in one HIP graph first
     # (capturing leaves the device idle for milliseconds); then the per-kernel
-    # passes and the read ceiling; then the K steps launched one call at a
-    # time; then the W warm-up steps and, right after them, the timed launch of
-    # the graph (value), so that the device is in the steady state the step
-    # runs in (after an idle spell its first milliseconds of work run slower).
+    # passes; then the K steps launched one call at a time; then the W warm-up
+    # steps and, right after them, the timed launch of the graph (value), so
+    # that the device is in the steady state the step runs in (after an idle
+    # spell its first milliseconds of work run slower).  The read ceiling
+    # comes after: its tens of milliseconds of full-rate reads leave the next
+    # few milliseconds of kernels 3-5% slower.
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         cs = torch.cuda.current_stream().cuda_stream
@@ -567,8 +569,6 @@ def main():
         gu_b2b = back_to_back_us(torch, gu_launch)
         ffn_b2b = back_to_back_us(torch, ffn_launch)
         dn_b2b = ffn_b2b - gu_b2b
-        ceil = read_ceiling(qg, torch, dev, (gu_bytes, tens[2].weight_bytes))
-        torch.cuda.empty_cache()
 
     # the K steps as launches from the host, one call at a time (no events
     # between the kernels, which run back to back)
@@ -586,6 +586,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     del graph
+    if not a.no_extras:
+        ceil = read_ceiling(qg, torch, dev, (gu_bytes, tens[2].weight_bytes))
+        torch.cuda.empty_cache()
     ms_per_step = wall * 1e3 / a.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     value_eager = step_bytes / (wall_eager / a.steps) / 1e9
