@@ -35,6 +35,18 @@ back to back, over rotating slices of each product's size -- with each
 kernel's fraction of it.
 cpu_baseline: the CPU oracle (scalar C, binary64) on the same workload.
 
+Per-case records (a separate mode, not part of the default run): --records
+FILE writes one JSON line per case -- every matrix of every configuration at
+one token, the 27B-class matrices at 8 and 128 tokens and the others at 128
+-- with the product's graph-replay time and rate, its fraction of HBM peak
+and of a plain read of the same size, the cache-resident rate, the largest
+error in units of the bound and bit-exact dequantization on 64 sampled rows
+against the oracle, and the oracle's time on one and on all host threads
+(scaled from a block of rows).  The counter fields (HBM bytes fetched, VALU
+and LDS instructions, matrix-core utilisation) come from rocprofv3 --pmc runs
+of --counter-pass (each case's product once, 3 ms apart), given with
+--records-counters DIR,...
+
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
 """
 import argparse
@@ -66,6 +78,15 @@ def parse():
                     help="finish with a plain 256 MiB device copy (known bytes, for scaling HBM counters)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the read-ceiling probe and the back-to-back graph passes (short profiled runs)")
+    ap.add_argument("--records", default="",
+                    help="write one JSON line per case (every matrix of every config, one token and batched) "
+                         "to this file, then exit")
+    ap.add_argument("--records-counters", default="",
+                    help="with --records: comma-separated rocprofv3 output directories of --counter-pass runs "
+                         "whose counters fill the records' counter fields")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="run each case's product once, 3 ms apart, then a 256 MiB copy (for rocprofv3 --pmc), "
+                         "then exit")
     ap.add_argument("--workloads", default="",
                     help="comma-separated keys of the per-workload report to run (e.g. cfg5_n8,cfg5_n128; "
                          "'extras': the FFN block, Q8_0-activation and head-plus-sampling steps); default: all")
@@ -465,6 +486,183 @@ def extra_report(qg, synth, torch, np, dev, graph_iters=20):
     return rep
 
 
+# ----------------------------------------------------------- per-case records --
+# One JSON line per case (cfg, matrix, n_tok): device time and rate of the
+# product alone, against HBM peak, a plain read of the same size and the
+# cache-resident rate; the largest error against the oracle in units of the
+# bound and whether the device dequantizes bit-exactly, both on sampled rows;
+# the oracle's time; and, from rocprofv3 counter runs of --counter-pass, the
+# HBM bytes fetched, VALU and LDS instructions and matrix-core utilisation.
+
+RECORD_SEED = 0
+RECORD_SAMPLE_ROWS = 64
+COUNTER_GAP_S = 0.003
+
+
+def record_cases(synth):
+    """(workload, matrix index, n_tok) of every case, in a fixed order."""
+    ws = (synth.CFG1, synth.CFG2, synth.CFG3, synth.CFG4, synth.CFG5, synth.CFG6)
+    cases = [(w, i, 1) for w in ws for i in range(len(w.tensors))]
+    cases += [(synth.CFG5, i, n) for n in (8, 128) for i in range(len(synth.CFG5.tensors))]
+    cases += [(w, i, 128) for w in (synth.CFG2, synth.CFG3, synth.CFG4, synth.CFG6) for i in range(len(w.tensors))]
+    return cases
+
+
+def _case_inputs(qg, synth, torch, dev, w, i, n_tok, ncopy):
+    t = synth.gen_tensor(w, i, seed=RECORD_SEED)
+    raw = torch.from_numpy(t.raw).to(dev)
+    rs = None if t.row_scale is None else torch.from_numpy(t.row_scale).to(dev)
+    copies = [qg.repack(t.fmt, raw, t.rows, t.cols, row_scale=rs) for _ in range(ncopy)]
+    x = synth.gen_x(w, t.cols, n_tok, seed=RECORD_SEED, which=100 + i)
+    return t, copies, x
+
+
+def counter_pass(qg, synth, torch, np, dev):
+    """Each case's product once, after an idle gap, in record_cases order
+    (every input prepared first), then a 256 MiB copy whose bytes scale the
+    HBM counters."""
+    prepared = []
+    for w, i, n_tok in record_cases(synth):
+        t, copies, x = _case_inputs(qg, synth, torch, dev, w, i, n_tok, 1)
+        xd = torch.from_numpy(x).to(dev)
+        y = torch.empty((n_tok, t.rows), device=dev)
+        prepared.append((t, copies[0], xd, y))
+    torch.cuda.synchronize()
+    for t, pk, xd, y in prepared:
+        time.sleep(COUNTER_GAP_S)
+        qg.qgemv(t.fmt, pk, xd, t.rows, t.cols, y=y)
+        torch.cuda.synchronize()
+    time.sleep(COUNTER_GAP_S)
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def counters_by_case(dirs, ncases):
+    """{counter: [per-case sums]} from rocprofv3 counter CSVs of --counter-pass
+    runs: the library's product dispatches grouped by the idle gaps between
+    cases; FETCH_SIZE scaled to bytes by the closing 256 MiB copy."""
+    import csv
+    out = {}
+    for d in dirs:
+        rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
+        disp = {}
+        for r in rows:
+            key = int(r["Dispatch_Id"])
+            e = disp.setdefault(key, {"name": r["Kernel_Name"], "t0": int(r["Start_Timestamp"]), "c": {}})
+            e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        seq = sorted(disp.values(), key=lambda e: e["t0"])
+        copy = [e for e in seq if "copyBuffer" in e["name"]]
+        prod = [e for e in seq if "qg::" in e["name"] and "repack" not in e["name"] and "dequant" not in e["name"]]
+        groups, last = [], None
+        for e in prod:
+            if last is None or e["t0"] - last > COUNTER_GAP_S * 1e9 / 3:
+                groups.append({})
+            for k, v in e["c"].items():
+                groups[-1][k] = groups[-1].get(k, 0.0) + v
+            last = e["t0"]
+        if len(groups) != ncases:
+            raise RuntimeError(f"{d}: {len(groups)} dispatch groups for {ncases} cases")
+        for k in groups[0]:
+            vals = [g.get(k, 0.0) for g in groups]
+            if k == "FETCH_SIZE":
+                if not copy:
+                    raise RuntimeError(f"{d}: no calibration copy")
+                f = (256 << 10) / copy[-1]["c"]["FETCH_SIZE"]   # KiB read by the copy / KiB it reports
+                vals = [v * 1024 * f for v in vals]
+            out[k] = vals
+    return out
+
+
+def write_records(qg, synth, torch, np, dev, path, counter_dirs=()):
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    cases = record_cases(synth)
+    cnt = counters_by_case(counter_dirs, len(cases)) if counter_dirs else {}
+    pool = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    pool.random_(0, 255)
+    pout = torch.zeros(256 * 64, dtype=torch.int32, device=dev)
+    threads = max(1, min(16, os.cpu_count() or 1))
+    cpu = cpu_model()
+    ex = ThreadPoolExecutor(threads)   # one pool for every case (its start-up is not the oracle's time)
+    list(ex.map(lambda k: k, range(threads)))
+
+    def ceiling(nb):
+        # a plain read of nb bytes per launch, back to back over rotating slices
+        nb = max(16, nb // 16 * 16)
+        nslice = max(1, (1 << 30) // nb)
+        best = 0.0
+        for wpc, u in ((16, 8), (8, 4), (4, 2)):
+            def launch(k):
+                cs = torch.cuda.current_stream().cuda_stream   # the capture stream inside the graph
+                if qg.lib.qgemv_read_probe(pool.data_ptr() + (k % nslice) * nb, nb, wpc, u, pout.data_ptr(), cs):
+                    raise RuntimeError("qgemv_read_probe failed")
+            best = max(best, nb / _graph_us(torch, lambda k: launch(k), 20) / 1e3)
+        return best
+
+    with open(path, "w") as f:
+        for ci, (w, i, n_tok) in enumerate(cases):
+            wb = synth.algorithmic_bytes(*w.tensors[i][1:])
+            ncopy = int(min(20, max(1, -(-ROTATE_BYTES // wb))))
+            t, copies, x = _case_inputs(qg, synth, torch, dev, w, i, n_tok, ncopy)
+            xd = torch.from_numpy(x).to(dev)
+            y = torch.empty((n_tok, t.rows), device=dev)
+            us = _graph_us(torch, lambda k: qg.qgemv(t.fmt, copies[k % ncopy], xd, t.rows, t.cols, y=y), 20)
+            warm_us = _graph_us(torch, lambda k: qg.qgemv(t.fmt, copies[0], xd, t.rows, t.cols, y=y), 20)
+            qg.qgemv(t.fmt, copies[0], xd, t.rows, t.cols, y=y)
+            wd = qg.qdequant(t.fmt, copies[0], t.rows, t.cols)
+            torch.cuda.synchronize()
+            # sampled rows: evenly spaced, the last row included
+            sel = np.unique(np.linspace(0, t.rows - 1, min(t.rows, RECORD_SAMPLE_ROWS)).astype(np.int64))
+            ygpu = y.cpu().numpy()[:, sel].astype(np.float64)
+            wgpu = wd[torch.from_numpy(sel).to(dev)].cpu().numpy()
+            del wd
+            rsel = None if t.row_scale is None else t.row_scale[sel]
+            wref = oracle.dequant(t.fmt, np.ascontiguousarray(t.raw[sel]), len(sel), t.cols, rsel)
+            bitexact = bool(np.array_equal(wgpu.view(np.uint32), wref.view(np.uint32)))
+            yref, S = oracle.gemv(t.fmt, np.ascontiguousarray(t.raw[sel]), x, len(sel), t.cols, rsel)
+            rel = 2e-5 if n_tok == 1 else 8e-3
+            err = float(np.max(np.abs(ygpu - yref) / (rel * S + 1e-7)))
+            # the oracle's time: a block of rows on one thread, then blocks on
+            # every thread at once, scaled to all rows
+            blk = min(t.rows, max(1, int(2e7 // (t.cols * n_tok))))
+            t0 = time.perf_counter()
+            oracle.gemv(t.fmt, t.raw, x, t.rows, t.cols, t.row_scale, 0, blk)
+            one = (time.perf_counter() - t0) * t.rows / blk
+            nb_mt = min(t.rows, blk * threads)
+            cuts = np.linspace(0, nb_mt, threads + 1).astype(int)
+            t0 = time.perf_counter()
+            list(ex.map(lambda ab: oracle.gemv(t.fmt, t.raw, x, t.rows, t.cols, t.row_scale, int(ab[0]),
+                                               int(ab[1])), zip(cuts[:-1], cuts[1:])))
+            mt = (time.perf_counter() - t0) * t.rows / nb_mt
+            gbps = wb / us / 1e3
+            ceil = ceiling(wb)
+            rec = {"cfg": w.name, "matrix": t.name, "fmt": t.fmt, "rows": t.rows, "cols": t.cols, "n_tok": n_tok,
+                   "weight_bytes": wb, "kernel_us": round(us, 2), "gbps": round(gbps, 1),
+                   "pct_peak": round(100 * gbps / HBM_PEAK_GBS, 2),
+                   "pct_measured_ceiling": round(100 * gbps / ceil, 2), "measured_ceiling_gbps": round(ceil, 1),
+                   "resident": "hbm" if ncopy * wb >= ROTATE_BYTES else "cache",
+                   "path": "GEMV" if n_tok == 1 else "matrix cores",
+                   "fetch_bytes": round(cnt["FETCH_SIZE"][ci]) if "FETCH_SIZE" in cnt else None,
+                   "valu_insts": round(cnt["SQ_INSTS_VALU"][ci]) if "SQ_INSTS_VALU" in cnt else None,
+                   "lds_insts": round(cnt["SQ_INSTS_LDS"][ci]) if "SQ_INSTS_LDS" in cnt else None,
+                   "mfma_util": (round(cnt["SQ_VALU_MFMA_BUSY_CYCLES"][ci] /
+                                       (cnt["GRBM_GUI_ACTIVE"][ci] / 8 * 1024), 4)
+                                 if "SQ_VALU_MFMA_BUSY_CYCLES" in cnt and cnt["GRBM_GUI_ACTIVE"][ci] > 0 else None),
+                   "warm_gbps": round(wb / warm_us / 1e3, 1),
+                   "oracle_us_1t": round(one * 1e6, 1), "oracle_us_mt": round(mt * 1e6, 1),
+                   "host_cores": threads, "cpu_model": cpu, "max_err_ratio": round(err, 4),
+                   "dequant_bitexact": bitexact, "sample_rows": int(len(sel)), "seed": RECORD_SEED}
+            f.write(json.dumps(rec) + "\n")
+            f.flush()
+            print(f"record {ci + 1}/{len(cases)}: {w.name} {t.name} n_tok={n_tok} {us:.2f} us "
+                  f"err {err:.3g} bitexact {bitexact}", file=sys.stderr, flush=True)
+            del copies
+            torch.cuda.empty_cache()
+    ex.shutdown()
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -479,6 +677,13 @@ def main():
     import synth
 
     dev = torch.device("cuda:0")
+    if a.counter_pass:
+        counter_pass(qg, synth, torch, np, dev)
+        return
+    if a.records:
+        write_records(qg, synth, torch, np, dev, a.records,
+                      tuple(d for d in a.records_counters.split(",") if d))
+        return
     w = synth.CFG5
     d_model, ffn = w.d_model, w.ffn
     tens = synth.gen_workload(w)
