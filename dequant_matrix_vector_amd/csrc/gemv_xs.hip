@@ -1,5 +1,6 @@
 // Host side of the x-stationary GEMV (gemv_xs.h): which shapes it takes, its
 // launch configuration and the per-variant dispatch.
+#include <algorithm>
 #include <atomic>
 
 #include "gemv_xs.h"
@@ -145,14 +146,21 @@ bool xs_choose(int fmt, int64_t rows, int64_t cols, int nmat, bool norm, XsCfg *
         }
     }
     if (c.rs == 0) return false;
-    // ring depth from back-to-back sweeps of the 27B-class FFN: 2 for the
-    // pair (two matrices already double the loads in flight), 4 for one
-    // matrix, 2 for K halves (two workgroups per CU already double the waves)
-    c.depth = nmat == 2 || khalf ? 2 : 4;
-    // (K halves: about two workgroups per CU over both halves, each staging
-    // half of x: the 27B-class block 31.9 against 32.2 us at one per CU)
+    // ring depth 2 and several workgroups per CU, from back-to-back sweeps
+    // of the 27B-class matrices: the pair three per CU; one matrix as many as
+    // its staged x leaves room for in the LDS, at most three (the gate alone,
+    // 23 KB: three, 11.7 against 13.7 us at one per CU and depth 4; the down
+    // on whole rows, 78 KB: two, 13.5 against 14.3); K halves two per CU over
+    // both halves, each staging half of x (the 27B-class block 31.9 against
+    // 32.2 us at one per CU)
+    c.depth = 2;
+    int per_cu = 3;
+    if (nmat == 1) {
+        const int64_t staged = (pchunk + 1) * kXStride * (int64_t)sizeof(float) + 512;
+        per_cu = khalf ? 2 : (int)std::max<int64_t>(1, std::min<int64_t>(3, (int64_t)kXsMaxLds / staged));
+    }
     const int64_t steps = steps_of(c, rows);
-    const int64_t want_wg = (int64_t)cu_count() * (nmat == 2 ? 3 : (khalf ? 2 : 1)) / c.kp;
+    const int64_t want_wg = (int64_t)cu_count() * per_cu / c.kp;
     int64_t nrs = (steps + want_wg - 1) / want_wg;
     // tall matrices: more workgroups rather than more LDS per workgroup
     const int64_t room = (int64_t)(kXsMaxLds / sizeof(float)) - (pchunk + 1) * kXStride - (norm ? xs_detail::kXsMaxWaves : 0);
