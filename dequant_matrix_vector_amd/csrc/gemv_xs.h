@@ -33,6 +33,12 @@
 //     segments' sums in segment order (deterministic) and applies the
 //     epilogue: silu(g) * u for the gate/up pair (NMAT 2), the RMSNorm scale
 //     (EPI 1) or the residual (EPI 2).
+//   * Q8_0 activations (FMT Q4_0 | kQ8Act, plain epilogue): the lane
+//     quantizes its staged chunk of x to Q8_0 (as every other kernel of the
+//     mode does) and keeps its 32 codes, d_x and their sum; a chunk's product
+//     is then the exact integer sum of (q_w - 8) * q_x by v_dot4 on the
+//     nibbles spread to bytes, times d_w * d_x (exact: two binary16
+//     significands).
 //   * K halves (EPI 4, one matrix): each workgroup takes one half of the
 //     columns of its rows (even workgroups the first, odd ones the second),
 //     so it stages half of x, and adds its half-row sums into y, which holds
@@ -58,6 +64,7 @@ using gemv_detail::f32x4;
 using gemv_detail::static_for;
 using gemv_detail::am_take;
 using gemv_detail::am_finish;
+using gemv_detail::dot4;
 
 struct XsParams {
     const uint8_t *q[2];  // packed tensors (quant plane at offset 0)
@@ -194,7 +201,9 @@ __device__ __forceinline__ float prep_q4(float4 (&v)[8])
 template <int FMT, int NMAT, int EPI, int D, int PX>
 __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
 {
-    static_assert(FMT == QG_Q4_0, "x-stationary GEMV: Q4_0");
+    static_assert((FMT & ~kQ8Act) == QG_Q4_0, "x-stationary GEMV: Q4_0");
+    constexpr bool Q8A = (FMT & kQ8Act) != 0;   // Q8_0 activations
+    static_assert(!Q8A || EPI == kEpiPlain, "Q8_0 activations: plain epilogue");
     static_assert(PX == 4 || PX == 8, "pieces per thread");
     static_assert(EPI != kEpiArgmax || NMAT == 1, "argmax of one product");
     static_assert(EPI != kEpiKHalf || NMAT == 1, "K halves of one product");
@@ -316,7 +325,22 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
         xv[k].z = live ? xv[k].z : 0.0f;
         xv[k].w = live ? xv[k].w : 0.0f;
     }
-    const float xsum = prep_q4(xv);
+    // fp32 activations: x pre-scaled and its chunk sum; Q8_0 activations:
+    // the chunk's codes, d_x and code sum (spare lanes: all zero)
+    float xsum = 0.0f;
+    uint32_t qx[Q8A ? 8 : 1];
+    float dx = 0.0f;
+    int qxs = 0;
+    if constexpr (Q8A) {
+        Q8Chunk qc;
+        quantize_chunk_q8_0(xv, qc);
+#pragma unroll
+        for (int k = 0; k < 8; k++) qx[k] = qc.q[k];
+        dx = qc.d;
+        qxs = qc.qsum;
+    } else {
+        xsum = prep_q4(xv);
+    }
 
     float norm_scale = 1.0f;
     if constexpr (EPI == kEpiNorm) {
@@ -340,9 +364,22 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
 #pragma unroll
             for (int m = 0; m < NMAT; m++) {
                 if (s < R) {
-                    const float tq = dot_q4_chunk(st[s][m].q, xv);
-                    const float u = __builtin_fmaf(-8.0f, xsum, tq);   // sum (q - 8) x
-                    v[s * NMAT + m] = live ? half_lo(st[s][m].d) * u : 0.0f;   // spare lanes: exactly 0
+                    if constexpr (Q8A) {
+                        // word k: low nibbles are columns 4k..4k+3, high nibbles 16+4k..16+4k+3
+                        const uint32_t w[4] = {st[s][m].q.x, st[s][m].q.y, st[s][m].q.z, st[s][m].q.w};
+                        int isum = 0;
+#pragma unroll
+                        for (int k = 0; k < 4; k++) {
+                            isum = dot4(w[k] & 0x0F0F0F0Fu, qx[k], isum);
+                            isum = dot4((w[k] >> 4) & 0x0F0F0F0Fu, qx[4 + k], isum);
+                        }
+                        isum -= 8 * qxs;   // sum (q - 8) q_x, exact
+                        v[s * NMAT + m] = live ? (half_lo(st[s][m].d) * dx) * (float)isum : 0.0f;
+                    } else {
+                        const float tq = dot_q4_chunk(st[s][m].q, xv);
+                        const float u = __builtin_fmaf(-8.0f, xsum, tq);   // sum (q - 8) x
+                        v[s * NMAT + m] = live ? half_lo(st[s][m].d) * u : 0.0f;   // spare lanes: exactly 0
+                    }
                 } else {
                     v[s * NMAT + m] = 0.0f;
                 }

@@ -12,7 +12,9 @@ Bars:
   * weights with power-of-two scales and activations on the Q8_0 grid: every
     partial sum is exact, so y is bit-identical to the oracle;
   * the FFN stage by stage: h against silu(g) u of the oracle's products, out
-    against the oracle's down product of the device's own h (quantized again).
+    against the oracle's down product of the device's own h (quantized again);
+  * Q4_0 at one token on the row-streaming kernel (each lane quantizes its own
+    chunk of x): the exact-input identity under every launch shape it takes.
 """
 import numpy as np
 import pytest
@@ -107,6 +109,46 @@ def test_gemv_q8act_exact_inputs_bit_exact(fmt):
     G.torch.cuda.synchronize()
     yr, _ = oracle.gemv_q8act(fmt, t.raw, x, rows, cols)
     assert np.array_equal(y.cpu().numpy().astype(np.float64), yr)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (7, 288), (131, 576), (203, 5120), (33, 17408)])
+def test_gemv_q8act_row_streaming_every_config(rows, cols):
+    # Q4_0 weights at one token run on the row-streaming kernel, each lane
+    # quantizing its own chunk of x: exact inputs (power-of-two weight scales,
+    # activations on the Q8_0 grid) bit-identical to the oracle under the
+    # built-in and every forced launch shape; random inputs within the bound
+    # on it and on the lane-group kernel (qgemv_set_xs_override(-1))
+    from tests.test_gpu_xs import _cfgs
+    rng = np.random.default_rng(3250 + cols)
+    d = (2.0 ** rng.integers(-6, -2, (rows, cols // 32))).astype(np.float16)
+    t = synth.QTensor("w", "q4_0", rows, cols, synth.pack_q4_0(d, rng.integers(0, 16, (rows, cols))))
+    pk = G.upload(t)
+    kx = rng.integers(-127, 128, cols)
+    kx[::32] = 127
+    x = (kx * 2.0 ** -4).astype(np.float32)
+    xd = G.torch.from_numpy(x).to(G.dev())
+    yr, _ = oracle.gemv_q8act("q4_0", t.raw, x, rows, cols)
+    cfgs = [None] + _cfgs(cols // 32, 1)[::3]
+    try:
+        for cfg in cfgs:
+            if cfg is None:
+                G.qg().set_xs_override(0)
+            else:
+                G.qg().set_xs_override(1, *cfg)
+            y = G.qg().qgemv_q8act("q4_0", pk, xd, rows, cols)
+            G.torch.cuda.synchronize()
+            assert np.array_equal(y.cpu().numpy().astype(np.float64), yr), f"{rows}x{cols} cfg {cfg}"
+        tr = synth.make_tensor("q4_0", rows, cols, rng)
+        pr = G.upload(tr)
+        xr = rng.standard_normal(cols).astype(np.float32)
+        yr2, S = oracle.gemv_q8act("q4_0", tr.raw, xr, rows, cols)
+        for mode in (0, -1):
+            G.qg().set_xs_override(mode)
+            y = G.qg().qgemv_q8act("q4_0", pr, G.torch.from_numpy(xr).to(G.dev()), rows, cols)
+            G.torch.cuda.synchronize()
+            G.check_bound(y.cpu().numpy(), yr2, S, what=f"q8act {rows}x{cols} xs mode {mode}")
+    finally:
+        G.qg().set_xs_override(0)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
