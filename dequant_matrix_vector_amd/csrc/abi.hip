@@ -602,15 +602,22 @@ int swiglu_ffn_q8act(int fmt, const void *wg, const void *wu, const void *wd, co
     }
     const GemvCfg cg = choose_cfg(fmt, ffn, d_model, 2);
     const GemvCfg cd = choose_cfg(fmt, d_model, ffn, 1);
+    // K halves for the down product as in swiglu_ffn (each lane quantizes its
+    // own chunk of h, so the halves quantize exactly what whole rows would)
+    const bool kh = ffn_down_khalf(fmt | kQ8Act, d_model, ffn);
     for (int64_t t = 0; t < n_tok; t++) {
         if (launch_gate_up(fmt | kQ8Act, static_cast<const uint8_t *>(wg), static_cast<const uint8_t *>(wu),
-                           x + t * d_model, h_scratch + t * ffn, ffn, d_model, s, cg) != hipSuccess)
+                           x + t * d_model, h_scratch + t * ffn, ffn, d_model, s, cg, nullptr, 0.0f,
+                           kh ? out + t * d_model : nullptr, kh ? d_model : 0) != hipSuccess)
             return QG_ERR_LAUNCH;
     }
     for (int64_t t = 0; t < n_tok; t++) {
-        if (launch_gemv(fmt | kQ8Act, static_cast<const uint8_t *>(wd), h_scratch + t * ffn, out + t * d_model,
-                        d_model, ffn, s, cd) != hipSuccess)
-            return QG_ERR_LAUNCH;
+        const hipError_t e =
+            kh ? launch_down_khalf(fmt | kQ8Act, static_cast<const uint8_t *>(wd), h_scratch + t * ffn,
+                                   out + t * d_model, d_model, ffn, s)
+               : launch_gemv(fmt | kQ8Act, static_cast<const uint8_t *>(wd), h_scratch + t * ffn,
+                             out + t * d_model, d_model, ffn, s, cd);
+        if (e != hipSuccess) return QG_ERR_LAUNCH;
     }
     return QG_OK;
 }

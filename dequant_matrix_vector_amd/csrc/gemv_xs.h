@@ -33,7 +33,7 @@
 //     segments' sums in segment order (deterministic) and applies the
 //     epilogue: silu(g) * u for the gate/up pair (NMAT 2), the RMSNorm scale
 //     (EPI 1) or the residual (EPI 2).
-//   * Q8_0 activations (FMT Q4_0 | kQ8Act, plain epilogue): the lane
+//   * Q8_0 activations (FMT Q4_0 | kQ8Act, plain epilogue or K halves): the lane
 //     quantizes its staged chunk of x to Q8_0 (as every other kernel of the
 //     mode does) and keeps its 32 codes, d_x and their sum; a chunk's product
 //     is then the exact integer sum of (q_w - 8) * q_x by v_dot4 on the
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(1024) void gemv_xs_kernel(XsParams p)
 {
     static_assert((FMT & ~kQ8Act) == QG_Q4_0, "x-stationary GEMV: Q4_0");
     constexpr bool Q8A = (FMT & kQ8Act) != 0;   // Q8_0 activations
-    static_assert(!Q8A || EPI == kEpiPlain, "Q8_0 activations: plain epilogue");
+    static_assert(!Q8A || EPI == kEpiPlain || EPI == kEpiKHalf, "Q8_0 activations: plain epilogue or K halves");
     static_assert(PX == 4 || PX == 8, "pieces per thread");
     static_assert(EPI != kEpiArgmax || NMAT == 1, "argmax of one product");
     static_assert(EPI != kEpiKHalf || NMAT == 1, "K halves of one product");

@@ -123,7 +123,7 @@ bool xs_choose(int fmt, int64_t rows, int64_t cols, int nmat, bool norm, XsCfg *
 {
     // Q4_0 weights, with fp32 or (plain products only) Q8_0 activations
     if (g_xs_mode < 0 || (fmt & ~kQ8Act) != QG_Q4_0) return false;
-    if ((fmt & kQ8Act) && (norm || khalf)) return false;
+    if ((fmt & kQ8Act) && norm) return false;
     if (khalf && (nmat != 1 || norm)) return false;
     fmt &= ~kQ8Act;
     Layout L;
@@ -197,7 +197,7 @@ hipError_t launch_xs(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, co
     Layout L;
     const bool q8a = (fmt & kQ8Act) != 0;
     if (!layout_for(fmt & ~kQ8Act, rows, cols, &L)) return hipErrorInvalidValue;
-    if (q8a && (gamma || resid || am || zero)) return hipErrorInvalidValue;
+    if (q8a && (gamma || resid || am)) return hipErrorInvalidValue;
     const bool khalf = c.kp == 2;
     if (khalf && (nmat != 1 || gamma || am)) return hipErrorInvalidValue;
     if (khalf && resid && resid + rows > y && y + rows > resid) return hipErrorInvalidValue;
@@ -236,7 +236,8 @@ hipError_t launch_xs(int fmt, int nmat, const uint8_t *w0, const uint8_t *w1, co
     if (c.wpc > 0 && lds <= kXsMaxLds / (c.wpc + 1)) lds = kXsMaxLds / (c.wpc + 1) + 256;
     const int epi = nmat == 2 ? (gamma ? 1 : 0) : (am ? 3 : (resid ? 2 : 0));
     if (q8a) {
-        if (fmt != (QG_Q4_0 | kQ8Act) || khalf) return hipErrorInvalidValue;
+        if (fmt != (QG_Q4_0 | kQ8Act)) return hipErrorInvalidValue;
+        if (khalf) return by_pieces<QG_Q4_0 | kQ8Act, 1, 4>(p, c.depth, waves, 2 * nwg, lds, s);
         if (nmat == 1) return by_pieces<QG_Q4_0 | kQ8Act, 1, 0>(p, c.depth, waves, nwg, lds, s);
         return by_pieces<QG_Q4_0 | kQ8Act, 2, 0>(p, c.depth, waves, nwg, lds, s);
     }

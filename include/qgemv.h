@@ -284,7 +284,8 @@ int64_t qgemv_head_argmax_workspace_bytes(int fmt, int64_t rows, int64_t cols);
  * quantizes x before the gate/up pair and h before the down product (h,
  * fp32, is left in the scratch as in swiglu_ffn).  qgemv_q8act: one launch
  * per token.  swiglu_ffn_q8act: with n_tok * ffn floats of scratch, two
- * launches per token; with n_tok > 1 and at least
+ * launches per token (Q4_0 with ffn >= 8192: the down product in K halves,
+ * as in swiglu_ffn); with n_tok > 1 and at least
  * swiglu_ffn_q8act_scratch_elems() floats, the batched path of
  * qgemv_q8act_ws for both products (the quantized activations, then any
  * partial sums, live in the scratch behind h, which starts the scratch
@@ -365,9 +366,9 @@ int qgemv_set_launch_override(int lpr, int r, int waves, int depth, int max_wg, 
  * fields out of range. */
 int qgemv_set_xs_override(int mode, int rs, int seg, int depth, int nrs, int order, int wg_per_cu);
 
-/* Tuning hook for the one-token SwiGLU block (swiglu_ffn, swiglu_ffn_noalloc
- * and swiglu_ffn_block out of place, with n_tok == 1 or any n_tok on the
- * per-token loop) of Q4_0 matrices whose
+/* Tuning hook for the one-token SwiGLU block (swiglu_ffn, swiglu_ffn_noalloc,
+ * swiglu_ffn_q8act and swiglu_ffn_block out of place, with n_tok == 1 or any
+ * n_tok on the per-token loop) of Q4_0 matrices whose
  * products both run on the row-streaming kernel: its down product can run in
  * K halves -- each workgroup takes one half of the columns of its rows,
  * staging half of h, and adds its half-row sums into out with an atomic add,

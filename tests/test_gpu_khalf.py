@@ -193,3 +193,36 @@ def test_khalf_graph_replays():
         G.qg().swiglu_ffn("q4_0", pk[0], pk[1], pk[2], xd, d_model, ffn, out=torch.empty_like(of),
                           h_scratch=torch.empty_like(sf))   # eager work between the replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("d_model,ffn", [(5120, 17408), (288, 768), (96, 800)])
+def test_khalf_ffn_q8act(d_model, ffn):
+    # the Q8_0-activation FFN at one token with its down product in K halves:
+    # each lane quantizes its own chunk of h, so the halves see the blocks the
+    # whole rows would; out within the bound of the oracle's product with the
+    # device's h quantized, bit-identical over runs, NaN overwritten
+    tens, x = _tensors(d_model, ffn, 7600 + ffn)
+    pk = [G.upload(t) for t in tens]
+    t = G.torch
+    xd = t.from_numpy(x).to(G.dev())
+
+    def run():
+        out = t.full((1, d_model), float("nan"), device=G.dev())
+        o, h = G.qg().swiglu_ffn_q8act("q4_0", pk[0], pk[1], pk[2], xd, d_model, ffn, out=out)
+        t.cuda.synchronize()
+        return o.cpu().numpy(), h.cpu().numpy()
+
+    try:
+        G.qg().set_ffn_khalf(0 if ffn >= 8192 else 2)
+        o1, h1 = run()
+        o2, h2 = run()
+        assert not np.isnan(o1).any()
+        assert np.array_equal(o1, o2) and np.array_equal(h1, h2)
+        yr, S = oracle.gemv_q8act("q4_0", tens[2].raw, h1, d_model, ffn)
+        G.check_bound(o1, yr, S, what=f"q8act K halves {d_model}/{ffn}")
+        G.qg().set_ffn_khalf(1)
+        o0, h0 = run()
+        assert np.array_equal(h0, h1)
+        G.check_bound(o0, yr, S, what=f"q8act whole rows {d_model}/{ffn}")
+    finally:
+        G.qg().set_ffn_khalf(0)
