@@ -6,9 +6,10 @@
  * C ABI.  Every pointer argument except `stream` is DEVICE memory owned by the
  * caller; the library allocates nothing and keeps no mutable global state
  * beyond a lazily read per-device property cache.  The tuning and measurement
- * hooks (qgemv_set_launch_override, qgemv_set_prefill_override,
- * qgemv_time_next_launch) keep their setting per calling thread and affect
- * only that thread's later calls.  `stream` is a hipStream_t passed as void*
+ * hooks (qgemv_set_launch_override, qgemv_set_xs_override,
+ * qgemv_set_prefill_override, qgemv_set_ffn_khalf, qgemv_time_next_launch)
+ * keep their setting per calling thread and affect only that thread's later
+ * calls.  `stream` is a hipStream_t passed as void*
  * (NULL = the legacy null stream).
  *
  * Errors are returned, never thrown: every entry point validates its arguments
