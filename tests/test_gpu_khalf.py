@@ -11,6 +11,7 @@ split off, the same bound (the two forms differ only in summation order).
 Shapes: the 27B-class block (544 blocks per row, halves of 272, the built-in
 choice), the small Q4_0 block (24 blocks: halves of 12), odd block counts
 (25: halves of 13 and 12; 33: 17 and 16), two blocks per row (halves of one),
+one block per row (no halves: the split declines, whole rows),
 forced row-streaming shapes (rows per row-step, ring depth, row-steps per
 workgroup, order, workgroups per CU), and several tokens on the per-token loop.
 The FFN block out of place (RMSNorm in, residual out: the first half adds the
@@ -28,7 +29,7 @@ from tests.test_gpu_block import check_block, _run as block_run
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(5120, 17408), (288, 768), (96, 800), (64, 1056), (160, 64)]
+SHAPES = [(5120, 17408), (288, 768), (96, 800), (64, 1056), (160, 64), (64, 32)]
 
 
 def _tensors(d_model, ffn, seed):
