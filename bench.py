@@ -10,10 +10,13 @@ working set is >= 1 GiB (over 4x the 256 MB Infinity Cache), so each step
 streams its weights from HBM.
 
 value = algorithmic weight bytes per step (150,405,120 B: 18 B per 32 weights)
-        / wall time per step: the K steps (one swiglu_ffn call each, over the
+        / time per step: the K steps (one swiglu_ffn call each, over the
         rotating copies) captured once in a HIP graph and uploaded; the W
         warm-up steps; then the graph launched once between two device
-        synchronizations.  It follows the per-kernel passes below, so the
+        synchronizations, timed by HIP events recorded on the stream right
+        before and after the launch (the K steps' device time; the wall
+        clock across the launch and the closing synchronization, which adds
+        the launch latency, is detail.value_wall_clock).  It follows the per-kernel passes below, so the
         device runs the step in its steady state (its first milliseconds of
         work after an idle spell run slower); the read ceiling is measured
         after it.  The same K steps launched one call at a time through the C
@@ -782,14 +785,21 @@ def main():
         step(i)
     torch.cuda.synchronize()
     wall_eager = time.perf_counter() - t0
-    # value: the W warm-up steps, then the K steps' graph
+    # value: the W warm-up steps, then the K steps' graph, between two device
+    # synchronizations; timed by events on the stream right around the
+    # graph's launch (the K steps' device time), and by the wall clock across
+    # the launch and the closing synchronization (reported beside it)
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record(stream)
     graph.replay()
+    ev1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_graph = time.perf_counter() - t0
+    wall = ev0.elapsed_time(ev1) * 1e-3
     del graph
     if not a.no_extras:
         ceil = read_ceiling(qg, torch, dev, (gu_bytes, tens[2].weight_bytes))
@@ -797,6 +807,7 @@ def main():
     ms_per_step = wall * 1e3 / a.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     value_eager = step_bytes / (wall_eager / a.steps) / 1e9
+    value_wall = step_bytes / (wall_graph / a.steps) / 1e9
 
     detail = {
         "gate_up_us": round(gu_avg * 1e3, 2), "down_us": round(dn_avg * 1e3, 2),
@@ -809,6 +820,8 @@ def main():
         "ffn_device_us": round((gu_avg + dn_avg) * 1e3, 2),
         "ffn_device_GBs": round(step_bytes / ((gu_avg + dn_avg) * 1e-3) / 1e9, 1),
         "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
+        "value_wall_clock": round(value_wall, 1),
+        "ms_per_step_wall_clock": round(wall_graph * 1e3 / a.steps, 5),
         "value_eager_launches": round(value_eager, 1),
         "value_graph_uploaded": bool(uploaded),
         "ms_per_step_eager_launches": round(wall_eager * 1e3 / a.steps, 5),
